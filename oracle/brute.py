@@ -1,0 +1,77 @@
+"""Brute-force reference for micro shapes, pure Python loops (test infrastructure).
+
+It evaluates the gate equation literally ("Mixtral and Mixture-of-Experts,
+Explained", section "How it works"): every expert's logit, the top-k kept and
+all others set to -inf, a softmax over all E entries, and then the output as
+a DENSE sum over all E experts ``y = sum_i G(x)_i * Expert_i(x)``, where
+non-selected experts are multiplied by an exact zero.  No grouping, no
+permutation, no numpy linear algebra: it exists only to cross-check the main
+oracle (``oracle/moe_oracle.py``), which groups tokens by expert instead.
+
+Capacity (micro shapes only): a per-expert list of (token, slot, G), sorted by
+G descending then token ascending with Python's sort, first ``capacity`` kept.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Sequence
+
+
+def _dot(a: Sequence[float], b: Sequence[float]) -> float:
+    s = 0.0
+    for u, v in zip(a, b):
+        s += u * v
+    return s
+
+
+def _expert(x: Sequence[float], w1, w3, w2) -> List[float]:
+    F = len(w1)
+    h = []
+    for j in range(F):
+        g = _dot(x, w1[j])
+        u = _dot(x, w3[j])
+        h.append(g / (1.0 + math.exp(-g)) * u)
+    return [_dot(h, w2[i]) for i in range(len(w2))]
+
+
+def gate(logits: Sequence[float], k: int):
+    """Literal Softmax(TopK(logits)) over all E entries; returns (ids, full G list)."""
+    E = len(logits)
+    order = sorted(range(E), key=lambda e: (-logits[e], e))
+    top = order[:k]
+    masked = [logits[e] if e in top else -math.inf for e in range(E)]
+    m = max(masked)
+    ex = [math.exp(v - m) if v != -math.inf else 0.0 for v in masked]
+    z = sum(ex)
+    return top, [v / z for v in ex]
+
+
+def layer(x, w_gate, w1, w3, w2, k: int = 2, bias=None, capacity: int = -1):
+    """Dense brute-force layer on nested lists; returns (y, ids, G_full, keep)."""
+    T, E = len(x), len(w_gate)
+    logits = [[_dot(x[t], w_gate[e]) + (bias[e] if bias is not None else 0.0) for e in range(E)]
+              for t in range(T)]
+    ids, Gf = [], []
+    for t in range(T):
+        top, g = gate(logits[t], k)
+        ids.append(top)
+        Gf.append(g)
+    keep = [[True] * k for _ in range(T)]
+    if capacity >= 0:
+        for e in range(E):
+            cand = [(Gf[t][e], t, s) for t in range(T) for s in range(k) if ids[t][s] == e]
+            cand.sort(key=lambda c: (-c[0], c[1]))
+            for _, t, s in cand[capacity:]:
+                keep[t][s] = False
+    y = []
+    for t in range(T):
+        acc = [0.0] * len(x[t])
+        for e in range(E):                                 # dense over ALL experts
+            w = Gf[t][e]
+            if e in ids[t] and not keep[t][ids[t].index(e)]:
+                w = 0.0
+            out = _expert(x[t], w1[e], w3[e], w2[e])
+            for i in range(len(acc)):
+                acc[i] += w * out[i]
+        y.append(acc)
+    return y, ids, Gf, keep

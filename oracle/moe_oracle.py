@@ -1,0 +1,281 @@
+"""Plain fp64 CPU oracle of the sparse top-2 MoE feed-forward layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares
+no code, table or helper with the HIP path and never takes a value from it.
+
+What it computes, step by step, with the passage each step follows:
+
+1. Router logits ``x . W_g^T (+ b)`` -- "Mixtral" study notes, section "MoE
+   Layer" (``self.gate = nn.Linear(d_model, num_experts, bias=False)``); the
+   gate equation on "Mixtral and Mixture-of-Experts, Explained", section "How
+   it works".  The additive per-expert bias exists only for the skewed-routing
+   workload (added after the dot product).
+2. Top-2 by logit, largest first; equal logits go to the lower expert index.
+3. Gate weights ``G(x) = Softmax(TopK(x . W_g))`` with every non-selected
+   logit set to -inf ("Mixtral and Mixture-of-Experts, Explained", "How it
+   works"), so the two kept weights are a softmax over just the two kept
+   logits ("Mixtral 8x7B" interview article, "Step 2", worked example).
+4. Optional capacity: per expert, its assignments ranked by gate weight
+   (descending), ties to the lower token index; the first ``capacity`` are
+   kept, the rest dropped and contribute nothing ("How Mixtral 8x7B uses
+   mixture of experts", section "Routing without auxiliary loss",
+   capacity-limited dispatch).
+5. Grouping by expert: per-expert counts (the ``bincount`` of the top-2 ids,
+   same page, expert activation heatmap listing), exclusive offsets, rows of
+   one expert in ascending (token, slot) order.
+6. Each kept (token, expert): SwiGLU ``w2(silu(x w1^T) * (x w3^T))`` with
+   ``silu(z) = z * sigmoid(z)`` and no biases ("Mixtral" study notes,
+   MixtralExpert and section "SwiGLU Experts").
+7. ``y = sum_i G(x)_i * Expert_i(x)`` over kept slots; zero when nothing is
+   kept ("Mixtral and Mixture-of-Experts, Explained", "How it works";
+   ``output = torch.zeros_like(x)`` in the study notes' MoE layer).
+
+Every input is converted exactly to float64 from its stored bf16 / fp32 /
+fp8-code-times-scale value; all arithmetic is float64.  For fp8 expert weights
+the computation also includes the declared activation quantisation (see
+``oracle/fp8.py``): x and h are block-quantised per row and per 32-element
+block before the two contractions.  Parity unpinned for that emulation beyond
+the e4m3 encoder itself (the pages print no fp8 values).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Iterable, Optional
+
+import numpy as np
+import torch
+
+from . import fp8 as _fp8
+
+# Assignments whose deciding gap is below this are "near ties": the decision is
+# not fixed by the arithmetic precision of either side (exemption threshold).
+NEAR_TIE = 1e-4
+
+
+def to_f64(t) -> np.ndarray:
+    """Exact conversion of a stored tensor (fp32 / bf16 / fp64 / numpy) to float64."""
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64)
+    if t.dtype == torch.float8_e4m3fn:
+        return _fp8.e4m3_decode(t.view(torch.uint8).numpy())
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def dequant_weight(w, scale) -> np.ndarray:
+    """fp8 codes times the per-output-channel fp32 scale; plain conversion otherwise."""
+    wf = to_f64(w)
+    if scale is None:
+        return wf
+    return wf * to_f64(scale)[..., :, None]
+
+
+# ---------------------------------------------------------------- routing ---
+
+def router_logits(x: np.ndarray, w_gate: np.ndarray, bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """logits[t, e] = sum_i x[t, i] * W_g[e, i] (+ b[e]); fp64."""
+    logits = x @ w_gate.T
+    if bias is not None:
+        logits = logits + bias[None, :]
+    return logits
+
+
+@dataclasses.dataclass
+class Routing:
+    ids: np.ndarray        # [T, k] int64, slot 0 = the larger logit
+    G: np.ndarray          # [T, k] float64 gate weights
+    gap12: np.ndarray      # [T] logit(1st) - logit(2nd)
+    gap23: np.ndarray      # [T] logit(2nd) - logit(3rd)  (inf when E == k)
+
+
+def topk_gate(logits: np.ndarray, k: int = 2) -> Routing:
+    """Top-k by (logit descending, expert index ascending), then softmax over the kept logits."""
+    T, E = logits.shape
+    # A stable sort of the negated logits keeps equal logits in index order.
+    order = np.argsort(-logits, axis=1, kind="stable")
+    ids = order[:, :k]
+    kept = np.take_along_axis(logits, ids, axis=1)
+    # Softmax over the full row with non-selected logits set to -inf.
+    masked = np.full_like(logits, -np.inf)
+    np.put_along_axis(masked, ids, kept, axis=1)
+    m = masked.max(axis=1, keepdims=True)
+    ex = np.exp(masked - m)                       # exp(-inf) = 0 exactly
+    full = ex / ex.sum(axis=1, keepdims=True)
+    G = np.take_along_axis(full, ids, axis=1)
+    srt = np.take_along_axis(logits, order, axis=1)
+    gap12 = srt[:, 0] - srt[:, 1]
+    gap23 = srt[:, k - 1] - srt[:, k] if E > k else np.full(T, np.inf)
+    return Routing(ids.astype(np.int64), G, gap12, gap23)
+
+
+def capacity_select(ids: np.ndarray, G: np.ndarray, n_experts: int, capacity: int):
+    """Keep, per expert, the ``capacity`` assignments with the largest G (ties: lower token).
+
+    Returns (keep [T, k] bool, cutoff [E] float64: the smallest kept G of an
+    over-capacity expert, NaN when nothing was dropped).
+    """
+    T, k = ids.shape
+    keep = np.ones((T, k), dtype=bool)
+    cutoff = np.full(n_experts, np.nan)
+    if capacity < 0:
+        return keep, cutoff
+    tok = np.repeat(np.arange(T), k).reshape(T, k)
+    for e in range(n_experts):
+        sel = ids == e
+        t_e, g_e = tok[sel], G[sel]                    # row-major: ascending t*k+slot
+        if len(t_e) <= capacity:
+            continue
+        rank = np.lexsort((t_e, -g_e))                 # primary -G, secondary token
+        flat = np.flatnonzero(sel.ravel())             # positions t*k+slot, token-ascending
+        dropped = flat[rank[capacity:]]
+        keep.ravel()[dropped] = False
+        cutoff[e] = g_e[rank[capacity - 1]] if capacity > 0 else np.inf
+    return keep, cutoff
+
+
+@dataclasses.dataclass
+class Permutation:
+    counts: np.ndarray       # [E] int64 kept assignments per expert
+    offsets: np.ndarray      # [E+1] exclusive prefix sum
+    perm_src: np.ndarray     # [N_kept] t*k + slot of each permuted row
+    slot_to_row: np.ndarray  # [T*k] row, or -1 when dropped
+
+
+def permutation(ids: np.ndarray, keep: np.ndarray, n_experts: int) -> Permutation:
+    T, k = ids.shape
+    flat_ids = ids.ravel()
+    flat_keep = keep.ravel()
+    counts = np.array([np.count_nonzero((flat_ids == e) & flat_keep) for e in range(n_experts)],
+                      dtype=np.int64)
+    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    perm_src = np.empty(int(offsets[-1]), dtype=np.int64)
+    slot_to_row = np.full(T * k, -1, dtype=np.int64)
+    for e in range(n_experts):
+        src = np.flatnonzero((flat_ids == e) & flat_keep)   # ascending t*k+slot
+        rows = offsets[e] + np.arange(len(src))
+        perm_src[rows] = src
+        slot_to_row[src] = rows
+    return Permutation(counts, offsets, perm_src, slot_to_row)
+
+
+# ------------------------------------------------------------ expert FFN ---
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu(xr: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray):
+    """w2(silu(x w1^T) * (x w3^T)) for rows xr; nn.Linear [out, in] weights.
+
+    Returns (output rows, intermediate h)."""
+    h = silu(xr @ w1.T) * (xr @ w3.T)
+    return h @ w2.T, h
+
+
+def swiglu_act_quant(xr: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray):
+    """SwiGLU with the declared fp8 activation quantisation of x and h (fp8 weights).
+
+    x (exact in fp32) and h (rounded to fp32 first: the quantisation decision is
+    taken in fp32) are block-quantised per row and 32-element block along the
+    contraction.  Returns (output rows, dequantised h)."""
+    _, _, xq = _fp8.block_quantize(xr.astype(np.float32))
+    h = silu(xq @ w1.T) * (xq @ w3.T)
+    _, _, hq = _fp8.block_quantize(h.astype(np.float32))
+    return hq @ w2.T, hq
+
+
+# ----------------------------------------------------------- full layer ---
+
+@dataclasses.dataclass
+class OracleResult:
+    logits: np.ndarray
+    routing: Routing
+    keep: np.ndarray
+    cutoff: np.ndarray
+    perm: Permutation
+    y: np.ndarray                       # [T, d] (rows not in ``tokens`` are NaN)
+    y_perm: Optional[np.ndarray] = None # [N_kept, d] (rows not computed are NaN)
+    h: Optional[np.ndarray] = None      # [N_kept, F] when requested
+
+
+def forward(inputs, tokens: Optional[Iterable[int]] = None,
+            override: Optional[Dict[int, Iterable[int]]] = None,
+            keep_override: Optional[np.ndarray] = None,
+            want_h: bool = False) -> OracleResult:
+    """Run the layer on ``inputs`` (a MoEInputs of host tensors).
+
+    tokens: compute the expert FFN / output only for these tokens (all
+        routing, capacity and grouping steps still cover every token).
+    override: {token: (e0, e1)} routing decisions to use instead of the
+        oracle's own, accepted only for near-tie tokens (gap23 or gap12 below
+        NEAR_TIE), where either choice is correct; G is recomputed from the
+        oracle's fp64 logits of the given experts.
+    keep_override: a [T, k] keep mask replacing the capacity decision; it must
+        agree with the oracle's own except for assignments whose G lies
+        within NEAR_TIE of their expert's cutoff.
+    """
+    cfg = inputs.cfg
+    E, k = cfg.n_experts, cfg.top_k
+    x = to_f64(inputs.x)
+    bias = None if inputs.router_bias is None else to_f64(inputs.router_bias)
+    logits = router_logits(x, to_f64(inputs.w_gate), bias)
+    r = topk_gate(logits, k)
+    if override:
+        for t, pair in override.items():
+            pair = tuple(int(v) for v in pair)
+            if tuple(r.ids[t]) == pair:
+                continue
+            if not (r.gap23[t] < NEAR_TIE or r.gap12[t] < NEAR_TIE):
+                raise ValueError(f"override of token {t} is not a near tie")
+            if set(pair) != set(r.ids[t].tolist()) and not r.gap23[t] < NEAR_TIE:
+                raise ValueError(f"override of token {t} changes the expert set")
+            kl = logits[t, list(pair)]
+            ex = np.exp(kl - kl.max())
+            r.ids[t] = pair
+            r.G[t] = ex / ex.sum()
+    keep, cutoff = capacity_select(r.ids, r.G, E, cfg.capacity)
+    if keep_override is not None:
+        diff = np.argwhere(keep_override != keep)
+        for t, s in diff:
+            e = r.ids[t, s]
+            if not (abs(r.G[t, s] - cutoff[e]) < NEAR_TIE):
+                raise ValueError(f"keep override at ({t},{s}) is not at the capacity cutoff")
+        keep = keep_override.astype(bool)
+    perm = permutation(r.ids, keep, E)
+
+    T, d = x.shape
+    want = np.arange(T) if tokens is None else np.unique(np.asarray(list(tokens), dtype=np.int64))
+    want_mask = np.zeros(T, dtype=bool)
+    want_mask[want] = True
+    n_rows = int(perm.offsets[-1])
+    y_perm = np.full((n_rows, d), np.nan)
+    h_all = np.full((n_rows, cfg.d_ff), np.nan) if want_h else None
+    fp8 = cfg.w_dtype == "fp8_e4m3"
+    for e in range(E):
+        rows = np.arange(perm.offsets[e], perm.offsets[e + 1])
+        rows = rows[want_mask[perm.perm_src[rows] // k]]
+        if len(rows) == 0:
+            continue
+        xr = x[perm.perm_src[rows] // k]
+        w1 = dequant_weight(inputs.w1[e], inputs.w1_scale[e] if fp8 else None)
+        w3 = dequant_weight(inputs.w3[e], inputs.w3_scale[e] if fp8 else None)
+        w2 = dequant_weight(inputs.w2[e], inputs.w2_scale[e] if fp8 else None)
+        ffn = swiglu_act_quant if fp8 else swiglu
+        y_perm[rows], h = ffn(xr, w1, w3, w2)
+        if want_h:
+            h_all[rows] = h
+        del w1, w3, w2
+    y = np.full((T, d), np.nan)
+    y[want] = 0.0
+    for t in want:
+        for s in range(k):
+            row = perm.slot_to_row[t * k + s]
+            if row >= 0:
+                y[t] += r.G[t, s] * y_perm[row]
+    return OracleResult(logits, r, keep, cutoff, perm, y, y_perm, h_all)
+
+
+def near_tie_tokens(res: OracleResult) -> np.ndarray:
+    """Tokens whose top-2 set (gap23) or slot order (gap12) is a near tie."""
+    return np.flatnonzero((res.routing.gap23 < NEAR_TIE) | (res.routing.gap12 < NEAR_TIE))

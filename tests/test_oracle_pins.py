@@ -1,0 +1,317 @@
+"""Pins of the fp64 oracle to facts fixed by the pages and by mathematics (CPU only).
+
+Each test names what it pins.  A plausible slip in the oracle (a dropped term,
+a wrong sign, index or slot order, a transposed operand, w1/w3 swapped, the
+bias dropped, the wrong gate form) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as Fn
+
+import oracle
+from oracle import brute, fp8
+from sparse_mixture_experts_topk_amd import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+class _Inp:
+    """Minimal stand-in for MoEInputs built from float64 numpy arrays."""
+
+    def __init__(self, cfg, x, wg, w1, w3, w2, bias=None):
+        self.cfg, self.x, self.w_gate = cfg, x, wg
+        self.w1, self.w3, self.w2 = w1, w3, w2
+        self.router_bias = bias
+        self.w1_scale = self.w3_scale = self.w2_scale = None
+
+
+def _micro(T=6, d=8, F=12, E=4, seed=3, capacity=-1, bias=False):
+    g = np.random.default_rng(seed)
+    f32 = lambda *s: g.standard_normal(s).astype(np.float32).astype(np.float64)  # noqa: E731
+    cfg = synthetic.MoEConfig(name="micro", T=T, d_model=d, d_ff=F, n_experts=E, capacity=capacity,
+                              act_dtype="f32", w_dtype="f32")
+    b = f32(E) if bias else None
+    return _Inp(cfg, f32(T, d), f32(E, d) / math.sqrt(d), f32(E, F, d) / math.sqrt(d),
+                f32(E, F, d) / math.sqrt(d), f32(E, d, F) / math.sqrt(F), b)
+
+
+# ------------------------------------------------------------- routing ---
+
+def test_worked_example_printed_values():
+    """Interview article, Step 2: scores -> experts '1' and '3' (ids 0, 2), weights 0.6682 / 0.3318."""
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    scores = np.array(ex["scores"], dtype=np.float64)
+    # Router with W_g = I_8 reproduces the scores exactly as logits.
+    logits = oracle.router_logits(scores[None, :], np.eye(8))
+    r = oracle.topk_gate(logits, 2)
+    assert r.ids[0].tolist() == ex["top2_zero_based"]
+    assert [i + 1 for i in r.ids[0]] == ex["top2_one_based_as_printed"]
+    assert np.round(r.G[0], ex["printed_decimals"]).tolist() == ex["weights_as_printed"]
+    # Closed form of a two-way softmax: the logistic function of the logit gap.
+    assert abs(r.G[0, 0] - 1.0 / (1.0 + math.exp(-(2.1 - 1.4)))) < 1e-15
+
+
+def test_gate_forms_agree():
+    """Softmax(TopK(l)) (explainer) == full softmax -> top-2 -> renormalise (n4n listing)."""
+    logits = np.random.default_rng(0).standard_normal((2000, 8)) * 2.0
+    r = oracle.topk_gate(logits, 2)
+    p = torch.softmax(torch.from_numpy(logits), dim=-1)
+    w, idx = p.topk(2, dim=-1)
+    w = w / w.sum(dim=-1, keepdim=True)
+    assert np.array_equal(idx.numpy(), r.ids)
+    assert np.max(np.abs(w.numpy() - r.G)) < 1e-12
+
+
+def test_gate_weights_properties():
+    logits = np.random.default_rng(1).standard_normal((5000, 8))
+    r = oracle.topk_gate(logits, 2)
+    assert np.all(np.abs(r.G.sum(axis=1) - 1.0) <= 1e-15)   # sum of two correctly rounded quotients
+    assert np.all(r.G[:, 0] >= r.G[:, 1])
+    assert np.all(r.ids[:, 0] != r.ids[:, 1])
+    l0 = np.take_along_axis(logits, r.ids[:, :1], 1)[:, 0]
+    l1 = np.take_along_axis(logits, r.ids[:, 1:], 1)[:, 0]
+    others = logits.copy()
+    np.put_along_axis(others, r.ids, -np.inf, axis=1)
+    assert np.all(l0 >= l1) and np.all(l1 >= others.max(axis=1))
+    assert np.allclose(r.gap12, l0 - l1, rtol=0, atol=0)
+    assert np.allclose(r.gap23, l1 - others.max(axis=1), rtol=0, atol=0)
+
+
+def test_ties_go_to_lower_index():
+    logits = np.array([[1.0, 3.0, 3.0, 0.0, 3.0, -1.0, 2.0, 2.0],
+                       [0.5] * 8,
+                       [0.0, 0.0, 5.0, 0.0, 0.0, 0.0, 0.0, 5.0],
+                       [4.0, 1.0, 2.0, 2.0, 2.0, 0.0, 0.0, 0.0]])
+    r = oracle.topk_gate(logits, 2)
+    assert r.ids.tolist() == [[1, 2], [0, 1], [2, 7], [0, 2]]
+    assert r.G[1].tolist() == [0.5, 0.5] and r.G[0].tolist() == [0.5, 0.5]
+    # Duplicated router rows give exactly equal logits: the lower index wins.
+    x = np.random.default_rng(2).standard_normal((50, 16))
+    wg = np.random.default_rng(3).standard_normal((8, 16))
+    wg[5] = wg[2] = wg[6] * 3.0
+    r2 = oracle.topk_gate(oracle.router_logits(x, wg), 2)
+    both = np.isin(r2.ids, [2, 5])
+    assert not np.any(r2.ids == 5) or np.all(both.sum(axis=1)[np.any(r2.ids == 5, axis=1)] == 2)
+    pos = np.any(r2.ids == 2, axis=1) & np.any(r2.ids == 5, axis=1)
+    assert np.all(r2.ids[pos].tolist() == [[2, 5]] * int(pos.sum()))
+
+
+# ------------------------------------------- full layer vs brute force ---
+
+@pytest.mark.parametrize("capacity,bias", [(-1, False), (-1, True), (1, False), (2, True), (0, False)])
+def test_oracle_matches_dense_brute_force(capacity, bias):
+    inp = _micro(capacity=capacity, bias=bias)
+    res = oracle.forward(inp)
+    yb, ids, Gf, keep = brute.layer(inp.x.tolist(), inp.w_gate.tolist(), inp.w1.tolist(),
+                                    inp.w3.tolist(), inp.w2.tolist(), 2,
+                                    None if inp.router_bias is None else inp.router_bias.tolist(),
+                                    capacity)
+    assert res.routing.ids.tolist() == ids
+    Gb = np.array([[Gf[t][e] for e in ids[t]] for t in range(len(ids))])
+    assert np.max(np.abs(Gb - res.routing.G)) < 1e-14
+    assert res.keep.tolist() == keep
+    assert np.max(np.abs(np.array(yb) - res.y)) < 1e-12
+    if capacity == 0:
+        assert np.all(res.y == 0.0)
+
+
+def test_dense_reduction_all_experts_equal():
+    """All experts identical and sum(G) = 1  =>  the layer is one dense SwiGLU FFN."""
+    inp = _micro(T=40, d=16, F=24, E=8, seed=5)
+    for w in (inp.w1, inp.w3, inp.w2):
+        w[:] = w[0]
+    res = oracle.forward(inp)
+    xt = torch.from_numpy(inp.x)
+    dense = Fn.linear(Fn.silu(Fn.linear(xt, torch.from_numpy(inp.w1[0]))) *
+                      Fn.linear(xt, torch.from_numpy(inp.w3[0])), torch.from_numpy(inp.w2[0]))
+    assert np.max(np.abs(res.y - dense.numpy())) < 1e-12 * max(1.0, np.abs(dense.numpy()).max())
+
+
+def test_token_output_is_gate_weighted_sum_of_its_two_experts():
+    inp = _micro(T=30, d=16, F=20, E=8, seed=7, bias=True)
+    res = oracle.forward(inp)
+    xt = torch.from_numpy(inp.x)
+    for t in range(inp.cfg.T):
+        acc = torch.zeros(inp.cfg.d_model, dtype=torch.float64)
+        for s in range(2):
+            e = int(res.routing.ids[t, s])
+            ffn = Fn.linear(Fn.silu(Fn.linear(xt[t], torch.from_numpy(inp.w1[e]))) *
+                            Fn.linear(xt[t], torch.from_numpy(inp.w3[e])), torch.from_numpy(inp.w2[e]))
+            acc += res.routing.G[t, s] * ffn
+        assert np.max(np.abs(acc.numpy() - res.y[t])) < 1e-12
+
+
+def test_combine_linearity_zeroing_one_expert():
+    inp = _micro(T=32, d=8, F=12, E=8, seed=9)
+    base = oracle.forward(inp)
+    e = int(base.routing.ids[0, 0])
+    inp.w2 = inp.w2.copy()
+    inp.w2[e] = 0.0
+    cut = oracle.forward(inp)
+    for t in range(inp.cfg.T):
+        expect = base.y[t].copy()
+        for s in range(2):
+            if base.routing.ids[t, s] == e:
+                expect -= base.routing.G[t, s] * base.y_perm[base.perm.slot_to_row[2 * t + s]]
+        assert np.max(np.abs(cut.y[t] - expect)) < 1e-12
+
+
+# -------------------------------------------------- capacity + grouping ---
+
+def test_capacity_invariants():
+    g = np.random.default_rng(11)
+    T, E, k = 300, 8, 2
+    logits = g.standard_normal((T, E)) + np.array([2.0, 1.0, 0.5, 0, 0, 0, 0, 0])
+    r = oracle.topk_gate(logits, k)
+    load = np.bincount(r.ids.ravel(), minlength=E)
+    for C in (0, 1, 37, 75, 150, 10_000):
+        keep, cut = oracle.capacity_select(r.ids, r.G, E, C)
+        p = oracle.permutation(r.ids, keep, E)
+        assert p.counts.tolist() == np.minimum(load, C).tolist()
+        for e in range(E):
+            cand = sorted(((-r.G[t, s], t, s) for t in range(T) for s in range(k) if r.ids[t, s] == e))
+            kept = {(t, s) for _, t, s in cand[:C]}
+            got = {(t, s) for t in range(T) for s in range(k) if r.ids[t, s] == e and keep[t, s]}
+            assert kept == got
+        if C >= T:
+            assert keep.all()
+    # Ties in G at the cutoff go to the lower token index.
+    ids = np.zeros((6, 2), dtype=np.int64)
+    ids[:, 1] = 1
+    G = np.tile([0.6, 0.4], (6, 1))
+    keep, _ = oracle.capacity_select(ids, G, 2, 4)
+    assert keep[:, 0].tolist() == [True] * 4 + [False] * 2
+
+
+def test_permutation_invariants():
+    g = np.random.default_rng(12)
+    T, E, k = 500, 8, 2
+    r = oracle.topk_gate(g.standard_normal((T, E)), k)
+    keep = g.random((T, k)) > 0.2
+    p = oracle.permutation(r.ids, keep, E)
+    assert p.counts.tolist() == np.bincount(r.ids[keep], minlength=E).tolist()
+    assert p.offsets[0] == 0 and np.array_equal(np.diff(p.offsets), p.counts)
+    assert p.offsets[-1] == keep.sum()
+    full = oracle.permutation(r.ids, np.ones_like(keep), E)
+    assert full.counts.sum() == T * k and np.array_equal(full.counts, np.bincount(r.ids.ravel(), minlength=E))
+    for e in range(E):
+        seg = p.perm_src[p.offsets[e]:p.offsets[e + 1]]
+        assert np.all(np.diff(seg // k) > 0)                        # token-ascending, one slot each
+        assert np.all(r.ids.ravel()[seg] == e)
+    assert np.array_equal(p.slot_to_row[p.perm_src], np.arange(len(p.perm_src)))
+    assert np.all(p.slot_to_row[~keep.ravel()] == -1)
+
+
+# --------------------------------------------------------------- fp8 ---
+
+def test_e4m3_decode_matches_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = fp8.e4m3_decode(codes.numpy())
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok]) and np.nanmax(np.abs(got)) == 448.0
+
+
+def test_e4m3_encode_matches_torch_rne():
+    # every bf16 value in [-448, 448], plus exact midpoints between adjacent codes (ties)
+    bits = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    v = bits.to(torch.float64)
+    v = v[torch.isfinite(v) & (v.abs() <= 448)]
+    pos = np.sort(fp8.e4m3_decode(np.arange(127, dtype=np.uint8)))
+    mids = (pos[1:] + pos[:-1]) / 2
+    rnd = np.random.default_rng(0).uniform(-448, 448, 200_000)
+    allv = np.concatenate([v.numpy(), mids, -mids, rnd])
+    ref = torch.from_numpy(allv).to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = fp8.e4m3_encode(allv.astype(np.float32).astype(np.float64))
+    assert np.array_equal(ref, got)
+
+
+def test_block_quantize_properties():
+    g = np.random.default_rng(4)
+    a = (g.standard_normal((64, 256)) * np.exp(g.uniform(-8, 8, (64, 1)))).astype(np.float32)
+    a[3, 32:64] = 0.0
+    codes, e, deq = fp8.block_quantize(a)
+    q = fp8.e4m3_decode(codes)
+    assert np.all(np.abs(q) <= 448)
+    blocks = np.abs(a.astype(np.float64)).reshape(64, 8, 32).max(-1)
+    nz = blocks > 0
+    scaled_max = blocks * np.exp2(-e.astype(np.float64))
+    assert np.all(scaled_max[nz] > 224) and np.all(scaled_max[nz] <= 448)
+    assert e[3, 1] == 0 and np.all(deq[3, 32:64] == 0)
+    assert np.array_equal(deq, q * np.exp2(np.repeat(e, 32, axis=1)))
+    normal = np.abs(a) * np.exp2(-np.repeat(e, 32, axis=1)) >= 2.0 ** -6
+    rel = np.abs(deq - a)[normal] / np.abs(a.astype(np.float64))[normal]
+    assert np.all(rel <= 2.0 ** -4)
+    # values already on the grid (e4m3 code times the block's power of two) are unchanged
+    grid = (fp8.e4m3_decode(g.integers(0, 126, (8, 64)).astype(np.uint8)) * 2.0 ** -5)
+    grid[:, ::32] = 448 * 2.0 ** -5
+    _, _, deq2 = fp8.block_quantize(grid.astype(np.float32))
+    assert np.array_equal(deq2, grid)
+
+
+def test_fp8_weight_dequant_matches_torch():
+    w32 = torch.from_numpy(np.random.default_rng(5).standard_normal((3, 16, 64)).astype(np.float32) * 0.02)
+    q, s = synthetic.quantize_rows_e4m3(w32)
+    ref = (q.to(torch.float32).to(torch.float64) * s.to(torch.float64).unsqueeze(-1)).numpy()
+    assert np.array_equal(oracle.dequant_weight(q, s), ref)
+
+
+def test_act_quant_ffn_reduces_to_plain_ffn_on_grid_inputs():
+    """With x and h already representable, the fp8 emulation equals the plain SwiGLU."""
+    g = np.random.default_rng(6)
+    d, F = 64, 32
+    x = fp8.e4m3_decode(g.integers(0, 126, (5, d)).astype(np.uint8))
+    x[:, ::32] = 448.0
+    w1 = g.standard_normal((F, d)) * 0.0
+    w3 = g.standard_normal((F, d)) * 0.0
+    w2 = g.standard_normal((d, F))
+    y_q, _ = oracle.swiglu_act_quant(x, w1, w3, w2)      # h == 0 exactly, representable
+    y_p, _ = oracle.swiglu(x, w1, w3, w2)
+    assert np.array_equal(y_q, y_p)
+
+
+# ------------------------------------------------- configs and inputs ---
+
+def test_configs_shapes_and_capacity():
+    c = synthetic.CONFIGS
+    assert c["skewed_capacity_bf16"].capacity == 1280
+    assert synthetic.capacity_from_factor(1, 2, 8) == 0      # batch-1 edge: 0.3125 -> 0 slots
+    dec = c["decode_bf16"]
+    assert 3 * dec.d_model * dec.d_ff * 2 == 352_321_536    # bytes of one bf16 expert
+    assert all(cfg.n_experts == 8 and cfg.top_k == 2 for cfg in c.values())
+
+
+def test_zipf_bias_frozen_and_effective():
+    fit = json.load(open(os.path.join(GOLDEN, "zipf_bias_e8.json")))
+    assert np.max(np.abs(np.array(fit["bias"]) - np.array(synthetic.ZIPF12_BIAS_E8))) < 1e-4
+    cfg = synthetic.CONFIGS["skewed_capacity_bf16"]
+    inp = synthetic.make_inputs(cfg, with_weights=False)
+    r = oracle.topk_gate(oracle.router_logits(oracle.to_f64(inp.x), oracle.to_f64(inp.w_gate),
+                                              oracle.to_f64(inp.router_bias)), 2)
+    share = np.bincount(r.ids.ravel(), minlength=8) / r.ids.size
+    assert np.max(np.abs(share - np.array(fit["target_share"]))) < 0.015
+
+
+def test_inputs_are_seeded_and_prefix_consistent():
+    a = synthetic.make_inputs(synthetic.CONFIGS["tiny_fp32"])
+    b = synthetic.make_inputs(synthetic.CONFIGS["tiny_fp32"])
+    for u, v in ((a.x, b.x), (a.w1, b.w1), (a.w2, b.w2), (a.w_gate, b.w_gate)):
+        assert torch.equal(u, v)
+    assert a.x.dtype == torch.float32 and a.w1.shape == (8, 256, 128) and a.w2.shape == (8, 128, 256)
+    dec = synthetic.make_inputs(synthetic.CONFIGS["decode_bf16"], with_weights=False)
+    pre = synthetic.make_inputs(synthetic.CONFIGS["skewed_capacity_bf16"], with_weights=False)
+    assert torch.equal(dec.x, pre.x[:16])
+
+
+def test_tiny_config_oracle_runs_dropless():
+    inp = synthetic.make_inputs(synthetic.CONFIGS["tiny_fp32"])
+    res = oracle.forward(inp)
+    assert res.perm.counts.sum() == 64 * 2
+    assert np.all(res.routing.ids[:, 0] != res.routing.ids[:, 1])
+    assert np.isfinite(res.y).all() and res.y.shape == (64, 128)
