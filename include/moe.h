@@ -1,0 +1,197 @@
+/*
+ * moe.h -- C ABI of a sparse top-2 Mixture-of-Experts feed-forward layer
+ * (Mixtral 8x7B style) implemented with hand-written HIP kernels for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (pages: "Mixtral and Mixture-of-Experts, Explained", section
+ * "How it works"; "Mixtral" study notes, section "MoE Layer"):
+ *   logits  = x . W_g^T (+ b)                 router, one logit per expert
+ *   G(x)    = Softmax(TopK(logits)), k = 2     non-selected logits at -inf
+ *   y       = sum_i G(x)_i * Expert_i(x)
+ *   Expert  = w2( silu(x w1^T) * (x w3^T) )    SwiGLU, no biases
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor arguments are DEVICE pointers to row-major arrays owned by
+ *   the caller.  The library allocates no memory, keeps no mutable global
+ *   state and is re-entrant; calls on different streams may overlap.
+ * - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
+ *   stream).  Every call only enqueues work on it and returns without
+ *   waiting for the device; no call reads device memory on the host.
+ * - Host-side validation happens before anything is enqueued.  On any
+ *   error nothing is enqueued and a status other than MOE_OK is returned;
+ *   MOE_ERR_HIP means a launch failed (its HIP error is consumed).
+ * - Device contents are not validated.  Preconditions: x, W_g, weights and
+ *   scales finite; ids written by moe_route_topk (or equivalent) in [0, E).
+ * - T = 0 is legal: every call returns MOE_OK and enqueues nothing.
+ * - Expert ids count from 0.  Slot 0 of a token is its larger logit; equal
+ *   logits go to the lower expert index.
+ * - Rows of the permuted buffers are grouped by expert; inside an expert
+ *   they follow ascending token index (a token has at most one row per
+ *   expert).  Buffers indexed by row are sized for T*top_k rows, the most
+ *   any call can produce, so one set of buffers serves dropless and
+ *   capacity modes.
+ *
+ * dtypes (moe_shape_t.act_dtype / w_dtype):
+ *   act F32  + w F32       : x, W_g, y fp32; x_perm fp32; h fp32.
+ *   act BF16 + w BF16      : x, W_g, y bf16; x_perm bf16; h bf16; fp32 accumulate.
+ *   act BF16 + w FP8_E4M3  : x, W_g, y bf16; expert weights are OCP e4m3 codes
+ *                            with one fp32 scale per output channel (row of the
+ *                            [out, in] weight).  Activations are quantised for
+ *                            the fp8 matrix cores: x_perm and h are e4m3 codes
+ *                            with one power-of-two scale per row and per block
+ *                            of 32 consecutive elements, stored as an E8M0
+ *                            byte (scale = 2^(byte - 127)); the block exponent
+ *                            is ceil(log2(fp32(amax / 448))), 127 for a zero
+ *                            block.  fp32 accumulate.
+ *   Other combinations return MOE_ERR_UNSUPPORTED.
+ *
+ * Shape limits: top_k == 2; 2 <= n_experts <= 64; d_model and d_ff
+ * multiples of 64; 1 <= T <= 2^24 (or 0); capacity == MOE_DROPLESS or >= 0.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,   /* NULL required pointer, bad shape value */
+  MOE_ERR_UNSUPPORTED = 2,   /* legal but not implemented: top_k != 2, dtype combo, alignment */
+  MOE_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = 4            /* a kernel launch failed */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
+
+#define MOE_DROPLESS (-1)
+
+typedef struct {
+  int32_t T;          /* tokens (batch * seq_len, flattened) */
+  int32_t d_model;    /* hidden size d */
+  int32_t d_ff;       /* expert FFN width F */
+  int32_t n_experts;  /* E */
+  int32_t top_k;      /* must be 2 */
+  int32_t capacity;   /* MOE_DROPLESS, or slots per expert (0 drops every assignment) */
+  int32_t act_dtype;  /* moe_dtype_t of x, W_g, y */
+  int32_t w_dtype;    /* moe_dtype_t of w1, w3, w2 */
+} moe_shape_t;
+
+/* Which call a workspace is sized for. */
+typedef enum { MOE_CALL_PERMUTE = 0, MOE_CALL_GATE_UP = 1, MOE_CALL_DOWN = 2,
+               MOE_CALL_FORWARD = 3 } moe_call_t;
+
+/* Human-readable name of a status.  Never NULL. */
+const char* moe_status_string(moe_status_t status);
+
+/* Library version string, e.g. "moe-mi355x 0.1 gfx950". */
+const char* moe_version(void);
+
+/* Bytes of device workspace `call` needs for `shape` (0 is possible; a
+ * NULL workspace is accepted then).  Host-only.  Workspace contents need
+ * not be initialised and are garbage after the call.  Errors: NULL
+ * argument or invalid shape. */
+moe_status_t moe_workspace_bytes(const moe_shape_t* shape, moe_call_t call, size_t* bytes);
+
+/* Router + top-2 + gate weights.
+ * Pages: "Mixtral" study notes, MixtralMoE.forward (gate, topk, softmax over
+ * the kept logits); "Mixtral and Mixture-of-Experts, Explained", gate
+ * equation G(x) = Softmax(TopK(x . W_g)).
+ *   x            [T, d]   act dtype
+ *   w_gate       [E, d]   act dtype (nn.Linear [out, in] layout)
+ *   router_bias  [E] fp32 or NULL, added to the fp32 logits after the dot product
+ *   topk_ids     [T, 2] int32 out: slot 0 = larger logit, ties -> lower index
+ *   topk_weights [T, 2] fp32 out: w0 = 1/(1+exp(l1-l0)), w1 = 1-w0 (w0+w1 == 1 exactly)
+ *   logits       [T, E] fp32 out, or NULL
+ * Logits accumulate in fp32.  No workspace. */
+moe_status_t moe_route_topk(const moe_shape_t* shape, const void* x, const void* w_gate,
+                            const float* router_bias, int32_t* topk_ids, float* topk_weights,
+                            float* logits, void* stream);
+
+/* Capacity selection (when shape->capacity >= 0) and grouping of tokens by expert.
+ * Pages: "How Mixtral 8x7B uses mixture of experts", sections "Routing without
+ * auxiliary loss" (capacity-limited dispatch, excess dropped) and the
+ * bincount of the top-2 ids (expert activation listing); "batch tokens by
+ * expert ... scatter back" in the simplified forward pass.
+ *   topk_ids, topk_weights [T, 2] from moe_route_topk
+ *   x              [T, d] act dtype
+ *   expert_counts  [E] int32 out: kept assignments per expert
+ *   expert_offsets [E+1] int32 out: exclusive prefix sum of counts
+ *   perm_src       [T*2] int32 out: rows 0..offsets[E]-1 hold t*2+slot of each row
+ *   slot_to_row    [T*2] int32 out: row of (t, slot), -1 if dropped
+ *   drop_mask      [T*2] uint8 out or NULL: 1 = dropped by the capacity limit
+ *   x_perm         [T*2, d] out: x_perm[row] = x[perm_src[row] / 2]; fp8 configs:
+ *                  e4m3 codes [T*2, d] plus x_perm_scale [T*2, d/32] E8M0 bytes
+ *   x_perm_scale   fp8 configs only (else ignored; may be NULL)
+ * Capacity rule: per expert, assignments ranked by gate weight (descending,
+ * compared as fp32), ties to the lower token index; the first `capacity`
+ * are kept.  A dropped assignment contributes nothing and the token's other
+ * slot is not renormalised.  Workspace: moe_workspace_bytes(MOE_CALL_PERMUTE). */
+moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_ids,
+                         const float* topk_weights, const void* x, int32_t* expert_counts,
+                         int32_t* expert_offsets, int32_t* perm_src, int32_t* slot_to_row,
+                         uint8_t* drop_mask, void* x_perm, uint8_t* x_perm_scale,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Grouped expert gate/up projection with the SwiGLU product fused in:
+ * h[row] = silu(x_perm[row] . w1[e]^T) * (x_perm[row] . w3[e]^T) for every row of
+ * expert e (rows offsets[e] .. offsets[e+1]-1).
+ * Pages: "Mixtral" study notes, MixtralExpert.forward and "SwiGLU Experts".
+ *   x_perm, x_perm_scale as written by moe_permute
+ *   expert_offsets [E+1] int32 (device)
+ *   w1, w3         [E, F, d] weight dtype; w1_scale, w3_scale [E, F] fp32 (fp8 only)
+ *   h              [T*2, F] out (bf16 / fp32 / e4m3 codes); h_scale [T*2, F/32] E8M0 (fp8 only)
+ * Workspace: moe_workspace_bytes(MOE_CALL_GATE_UP). */
+moe_status_t moe_expert_gemm_gate_up(const moe_shape_t* shape, const void* x_perm,
+                                     const uint8_t* x_perm_scale, const int32_t* expert_offsets,
+                                     const void* w1, const void* w3, const float* w1_scale,
+                                     const float* w3_scale, void* h, uint8_t* h_scale,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Grouped expert down projection: y_perm[row] = h[row] . w2[e]^T (fp32 out).
+ * Pages: "Mixtral" study notes, MixtralExpert.forward (self.w2).
+ *   h, h_scale     as written by moe_expert_gemm_gate_up
+ *   expert_offsets [E+1] int32
+ *   w2             [E, d, F] weight dtype; w2_scale [E, d] fp32 (fp8 only)
+ *   y_perm         [T*2, d] fp32 out
+ * Workspace: moe_workspace_bytes(MOE_CALL_DOWN). */
+moe_status_t moe_expert_gemm_down(const moe_shape_t* shape, const void* h, const uint8_t* h_scale,
+                                  const int32_t* expert_offsets, const void* w2,
+                                  const float* w2_scale, float* y_perm, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Gate-weighted combine back to token order:
+ * y[t] = sum over kept slots s of topk_weights[t, s] * y_perm[slot_to_row[t*2+s]],
+ * 0 when both slots are dropped; cast to the act dtype (round to nearest even).
+ * Pages: "Mixtral and Mixture-of-Experts, Explained", y = sum_i G(x)_i Expert_i(x);
+ * study notes, output = zeros_like(x) then weighted accumulation.
+ *   y_perm [T*2, d] fp32; slot_to_row [T*2] int32; topk_weights [T, 2] fp32
+ *   y      [T, d] act dtype out.  No workspace. */
+moe_status_t moe_combine(const moe_shape_t* shape, const float* y_perm, const int32_t* slot_to_row,
+                         const float* topk_weights, void* y, void* stream);
+
+/* The whole layer on one stream, with no host synchronisation:
+ * route -> (capacity) -> permute -> gate/up -> down -> combine.
+ *   x [T, d], w_gate [E, d] act dtype; router_bias [E] fp32 or NULL
+ *   w1, w3 [E, F, d], w2 [E, d, F] weight dtype; w*_scale fp32 per output channel (fp8 only)
+ *   y [T, d] act dtype out
+ *   optional outputs (NULL to skip): topk_ids_out [T, 2] int32, topk_weights_out [T, 2]
+ *   fp32, expert_counts_out [E] int32, drop_mask_out [T*2] uint8, logits_out [T, E] fp32
+ * Workspace: moe_workspace_bytes(MOE_CALL_FORWARD) holds every intermediate. */
+moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const void* w_gate,
+                         const float* router_bias, const void* w1, const void* w3, const void* w2,
+                         const float* w1_scale, const float* w3_scale, const float* w2_scale,
+                         void* y, int32_t* topk_ids_out, float* topk_weights_out,
+                         int32_t* expert_counts_out, uint8_t* drop_mask_out, float* logits_out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,299 @@
+// C ABI of the MoE layer: argument validation, workspace layout, dispatch.
+// Every public function validates on the host before enqueueing anything.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "launch.hpp"
+
+namespace moe {
+
+hipError_t launch_gate_up(const moe_shape_t& s, const void* x_perm, const uint8_t* x_scale,
+                          const int32_t* offsets, const void* w1, const void* w3,
+                          const float* w1_scale, const float* w3_scale, void* h, uint8_t* h_scale,
+                          hipStream_t st) {
+  if (s.w_dtype == MOE_F32)
+    return launch_gate_up_f32(s, static_cast<const float*>(x_perm), offsets,
+                              static_cast<const float*>(w1), static_cast<const float*>(w3),
+                              static_cast<float*>(h), st);
+  if (s.w_dtype == MOE_BF16)
+    return launch_gate_up_bf16(s, static_cast<const uint16_t*>(x_perm), offsets,
+                               static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3),
+                               static_cast<uint16_t*>(h), st);
+  return launch_gate_up_fp8(s, static_cast<const uint8_t*>(x_perm), x_scale, offsets,
+                            static_cast<const uint8_t*>(w1), static_cast<const uint8_t*>(w3),
+                            w1_scale, w3_scale, static_cast<uint8_t*>(h), h_scale, st);
+}
+
+hipError_t launch_down(const moe_shape_t& s, const void* h, const uint8_t* h_scale,
+                       const int32_t* offsets, const void* w2, const float* w2_scale,
+                       float* y_perm, hipStream_t st) {
+  if (s.w_dtype == MOE_F32)
+    return launch_down_f32(s, static_cast<const float*>(h), offsets,
+                           static_cast<const float*>(w2), y_perm, st);
+  if (s.w_dtype == MOE_BF16)
+    return launch_down_bf16(s, static_cast<const uint16_t*>(h), offsets,
+                            static_cast<const uint16_t*>(w2), y_perm, st);
+  return launch_down_fp8(s, static_cast<const uint8_t*>(h), h_scale, offsets,
+                         static_cast<const uint8_t*>(w2), w2_scale, y_perm, st);
+}
+
+}  // namespace moe
+
+namespace {
+
+using moe::launch_fill_u8;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t act_bytes(int32_t dt) { return dt == MOE_F32 ? 4 : 2; }
+
+// Storage bytes of one element of x_perm / h.
+size_t perm_elem_bytes(const moe_shape_t& s) {
+  if (s.w_dtype == MOE_FP8_E4M3) return 1;
+  return act_bytes(s.act_dtype);
+}
+
+moe_status_t validate_shape(const moe_shape_t* s) {
+  if (s == nullptr) return MOE_ERR_INVALID_ARG;
+  if (s->T < 0 || s->T > (1 << 24)) return MOE_ERR_INVALID_ARG;
+  if (s->top_k < 1 || s->n_experts < 2 || s->top_k > s->n_experts) return MOE_ERR_INVALID_ARG;
+  if (s->d_model <= 0 || s->d_ff <= 0) return MOE_ERR_INVALID_ARG;
+  if (s->capacity < MOE_DROPLESS) return MOE_ERR_INVALID_ARG;
+  const bool known = (s->act_dtype == MOE_F32 || s->act_dtype == MOE_BF16) &&
+                     (s->w_dtype == MOE_F32 || s->w_dtype == MOE_BF16 || s->w_dtype == MOE_FP8_E4M3);
+  if (!known) return MOE_ERR_INVALID_ARG;
+  if (s->top_k != 2 || s->n_experts > 64) return MOE_ERR_UNSUPPORTED;
+  if (s->d_model % 64 != 0 || s->d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (s->d_model > (1 << 16) || s->d_ff > (1 << 18)) return MOE_ERR_UNSUPPORTED;
+  const bool combo = (s->act_dtype == MOE_F32 && s->w_dtype == MOE_F32) ||
+                     (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_BF16) ||
+                     (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_FP8_E4M3);
+  if (!combo) return MOE_ERR_UNSUPPORTED;
+  if (s->w_dtype == MOE_FP8_E4M3 && !moe::kFp8Available) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t check_ptrs(std::initializer_list<const void*> required,
+                        std::initializer_list<const void*> optional) {
+  for (const void* p : required) {
+    if (p == nullptr) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(p)) return MOE_ERR_INVALID_ARG;
+  }
+  for (const void* p : optional)
+    if (p != nullptr && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Workspace layout of moe_forward (each region 256-byte aligned).
+struct ForwardLayout {
+  size_t ids, weights, counts, offsets, perm_src, slot_to_row, drop, x_perm, x_scale, h, h_scale,
+      y_perm, total;
+};
+
+ForwardLayout forward_layout(const moe_shape_t& s) {
+  ForwardLayout L{};
+  const size_t A = (size_t)s.T * s.top_k;                 // assignments = max rows
+  const size_t eb = perm_elem_bytes(s);
+  const bool fp8 = s.w_dtype == MOE_FP8_E4M3;
+  size_t o = 0;
+  L.ids = o;         o += align_up(A * 4);
+  L.weights = o;     o += align_up(A * 4);
+  L.counts = o;      o += align_up(64 * 4);
+  L.offsets = o;     o += align_up(65 * 4);
+  L.perm_src = o;    o += align_up(A * 4);
+  L.slot_to_row = o; o += align_up(A * 4);
+  L.drop = o;        o += align_up(A);
+  L.x_perm = o;      o += align_up(A * s.d_model * eb);
+  L.x_scale = o;     o += fp8 ? align_up(A * (s.d_model / 32)) : 0;
+  L.h = o;           o += align_up(A * s.d_ff * eb);
+  L.h_scale = o;     o += fp8 ? align_up(A * (s.d_ff / 32)) : 0;
+  L.y_perm = o;      o += align_up(A * s.d_model * 4);
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<uint8_t*>(base) + off); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_version(void) { return "moe-mi355x 0.1 gfx950"; }
+
+moe_status_t moe_workspace_bytes(const moe_shape_t* s, moe_call_t call, size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  moe_status_t v = validate_shape(s);
+  if (v != MOE_OK) return v;
+  switch (call) {
+    case MOE_CALL_PERMUTE: *bytes = 0; return MOE_OK;
+    case MOE_CALL_GATE_UP: *bytes = 0; return MOE_OK;
+    case MOE_CALL_DOWN: *bytes = 0; return MOE_OK;
+    case MOE_CALL_FORWARD: *bytes = forward_layout(*s).total; return MOE_OK;
+  }
+  return MOE_ERR_INVALID_ARG;
+}
+
+moe_status_t moe_route_topk(const moe_shape_t* s, const void* x, const void* w_gate,
+                            const float* router_bias, int32_t* topk_ids, float* topk_weights,
+                            float* logits, void* stream) {
+  moe_status_t v = validate_shape(s);
+  if (v != MOE_OK) return v;
+  if (s->T == 0) return MOE_OK;
+  if ((v = check_ptrs({x, w_gate, topk_ids, topk_weights}, {router_bias, logits})) != MOE_OK) return v;
+  return from_hip(moe::launch_route_topk(*s, x, w_gate, router_bias, topk_ids, topk_weights, logits,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_ids, const float* topk_weights,
+                         const void* x, int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* perm_src, int32_t* slot_to_row, uint8_t* drop_mask,
+                         void* x_perm, uint8_t* x_perm_scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  moe_status_t v = validate_shape(s);
+  if (v != MOE_OK) return v;
+  if (s->T == 0) return MOE_OK;
+  if ((v = check_ptrs({topk_ids, topk_weights, x, expert_counts, expert_offsets, perm_src,
+                       slot_to_row, x_perm},
+                      {drop_mask})) != MOE_OK)
+    return v;
+  const bool fp8 = s->w_dtype == MOE_FP8_E4M3;
+  if (fp8 && x_perm_scale == nullptr) return MOE_ERR_INVALID_ARG;
+  if (s->capacity >= 0 && drop_mask == nullptr) return MOE_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  const uint8_t* drop_in = nullptr;
+  if (s->capacity >= 0) {
+    e = moe::launch_capacity_select(*s, topk_ids, topk_weights, drop_mask, st);
+    drop_in = drop_mask;
+  } else if (drop_mask != nullptr) {
+    e = launch_fill_u8(drop_mask, (int64_t)s->T * 2, 0, st);
+  }
+  if (e == hipSuccess)
+    e = moe::launch_permute_index(*s, topk_ids, drop_in, expert_counts, expert_offsets, perm_src,
+                                  slot_to_row, st);
+  if (e == hipSuccess)
+    e = moe::launch_permute_scatter(*s, x, expert_offsets, perm_src, x_perm, x_perm_scale, st);
+  return from_hip(e);
+}
+
+moe_status_t moe_expert_gemm_gate_up(const moe_shape_t* s, const void* x_perm,
+                                     const uint8_t* x_perm_scale, const int32_t* expert_offsets,
+                                     const void* w1, const void* w3, const float* w1_scale,
+                                     const float* w3_scale, void* h, uint8_t* h_scale,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  moe_status_t v = validate_shape(s);
+  if (v != MOE_OK) return v;
+  if (s->T == 0) return MOE_OK;
+  if ((v = check_ptrs({x_perm, expert_offsets, w1, w3, h}, {})) != MOE_OK) return v;
+  if (s->w_dtype == MOE_FP8_E4M3 &&
+      (x_perm_scale == nullptr || w1_scale == nullptr || w3_scale == nullptr || h_scale == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_gate_up(*s, x_perm, x_perm_scale, expert_offsets, w1, w3, w1_scale,
+                                      w3_scale, h, h_scale, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_gemm_down(const moe_shape_t* s, const void* h, const uint8_t* h_scale,
+                                  const int32_t* expert_offsets, const void* w2,
+                                  const float* w2_scale, float* y_perm, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  moe_status_t v = validate_shape(s);
+  if (v != MOE_OK) return v;
+  if (s->T == 0) return MOE_OK;
+  if ((v = check_ptrs({h, expert_offsets, w2, y_perm}, {})) != MOE_OK) return v;
+  if (s->w_dtype == MOE_FP8_E4M3 && (h_scale == nullptr || w2_scale == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  return from_hip(moe::launch_down(*s, h, h_scale, expert_offsets, w2, w2_scale, y_perm,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_combine(const moe_shape_t* s, const float* y_perm, const int32_t* slot_to_row,
+                         const float* topk_weights, void* y, void* stream) {
+  moe_status_t v = validate_shape(s);
+  if (v != MOE_OK) return v;
+  if (s->T == 0) return MOE_OK;
+  if ((v = check_ptrs({y_perm, slot_to_row, topk_weights, y}, {})) != MOE_OK) return v;
+  return from_hip(moe::launch_combine(*s, y_perm, slot_to_row, topk_weights, y,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_gate,
+                         const float* router_bias, const void* w1, const void* w3, const void* w2,
+                         const float* w1_scale, const float* w3_scale, const float* w2_scale,
+                         void* y, int32_t* topk_ids_out, float* topk_weights_out,
+                         int32_t* expert_counts_out, uint8_t* drop_mask_out, float* logits_out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status_t v = validate_shape(s);
+  if (v != MOE_OK) return v;
+  if (s->T == 0) return MOE_OK;
+  if ((v = check_ptrs({x, w_gate, w1, w3, w2, y},
+                      {router_bias, topk_ids_out, topk_weights_out, expert_counts_out,
+                       drop_mask_out, logits_out})) != MOE_OK)
+    return v;
+  const bool fp8 = s->w_dtype == MOE_FP8_E4M3;
+  if (fp8 && (w1_scale == nullptr || w3_scale == nullptr || w2_scale == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  const ForwardLayout L = forward_layout(*s);
+  if (workspace == nullptr || workspace_bytes < L.total || !aligned16(workspace))
+    return MOE_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(workspace, L.ids);
+  float* gw = topk_weights_out ? topk_weights_out : at<float>(workspace, L.weights);
+  int32_t* counts = expert_counts_out ? expert_counts_out : at<int32_t>(workspace, L.counts);
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* perm_src = at<int32_t>(workspace, L.perm_src);
+  int32_t* slot_to_row = at<int32_t>(workspace, L.slot_to_row);
+  uint8_t* drop = drop_mask_out ? drop_mask_out : at<uint8_t>(workspace, L.drop);
+  void* x_perm = at<void>(workspace, L.x_perm);
+  uint8_t* x_scale = fp8 ? at<uint8_t>(workspace, L.x_scale) : nullptr;
+  void* h = at<void>(workspace, L.h);
+  uint8_t* h_scale = fp8 ? at<uint8_t>(workspace, L.h_scale) : nullptr;
+  float* y_perm = at<float>(workspace, L.y_perm);
+
+  hipError_t e = moe::launch_route_topk(*s, x, w_gate, router_bias, ids, gw, logits_out, st);
+  const uint8_t* drop_in = nullptr;
+  if (e == hipSuccess) {
+    if (s->capacity >= 0) {
+      e = moe::launch_capacity_select(*s, ids, gw, drop, st);
+      drop_in = drop;
+    } else if (drop_mask_out != nullptr) {
+      e = launch_fill_u8(drop_mask_out, (int64_t)s->T * 2, 0, st);
+    }
+  }
+  if (e == hipSuccess)
+    e = moe::launch_permute_index(*s, ids, drop_in, counts, offsets, perm_src, slot_to_row, st);
+  if (e == hipSuccess) e = moe::launch_permute_scatter(*s, x, offsets, perm_src, x_perm, x_scale, st);
+  if (e == hipSuccess)
+    e = moe::launch_gate_up(*s, x_perm, x_scale, offsets, w1, w3, w1_scale, w3_scale, h, h_scale, st);
+  if (e == hipSuccess) e = moe::launch_down(*s, h, h_scale, offsets, w2, w2_scale, y_perm, st);
+  if (e == hipSuccess) e = moe::launch_combine(*s, y_perm, slot_to_row, gw, y, st);
+  return from_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Gate-weighted combine back to token order.
+//
+// Pages: "Mixtral and Mixture-of-Experts, Explained", y = sum_i G(x)_i *
+// Expert_i(x); "Mixtral" study notes, MoE forward (output = zeros_like(x),
+// then each expert's rows accumulated with their gate weight).
+//
+// One workgroup per token row: y[t] = G0 * y_perm[row0] + G1 * y_perm[row1]
+// over the kept slots (a dropped slot has row -1 and adds nothing), computed
+// in fp32 as fma(G1, b, G0 * a) and rounded once to the activation dtype.
+// Gathers instead of scatter-adds, so there are no atomics and the result is
+// deterministic.  HBM-bound: reads the kept y_perm rows, writes y once.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
+                                                      const int32_t* __restrict__ slot_to_row,
+                                                      const float* __restrict__ gw, int d,
+                                                      void* __restrict__ y) {
+  const int t = blockIdx.x;
+  const int2 rows = reinterpret_cast<const int2*>(slot_to_row)[t];
+  const float2 g = reinterpret_cast<const float2*>(gw)[t];
+  const float4* a = rows.x >= 0 ? reinterpret_cast<const float4*>(y_perm + (int64_t)rows.x * d) : nullptr;
+  const float4* b = rows.y >= 0 ? reinterpret_cast<const float4*>(y_perm + (int64_t)rows.y * d) : nullptr;
+  for (int c = threadIdx.x; c < d / 4; c += blockDim.x) {
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a != nullptr) {
+      const float4 v = a[c];
+      r = make_float4(g.x * v.x, g.x * v.y, g.x * v.z, g.x * v.w);
+    }
+    if (b != nullptr) {
+      const float4 v = b[c];
+      r = make_float4(fmaf(g.y, v.x, r.x), fmaf(g.y, v.y, r.y), fmaf(g.y, v.z, r.z),
+                      fmaf(g.y, v.w, r.w));
+    }
+    if constexpr (BF16) {
+      reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + (int64_t)t * d)[c] =
+          make_uint2(pack_bf16x2(r.x, r.y), pack_bf16x2(r.z, r.w));
+    } else {
+      reinterpret_cast<float4*>(static_cast<float*>(y) + (int64_t)t * d)[c] = r;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_shape_t& s, const float* y_perm, const int32_t* slot_to_row,
+                          const float* weights, void* y, hipStream_t st) {
+  if (s.act_dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(s.T), dim3(256), 0, st, y_perm, slot_to_row,
+                       weights, s.d_model, y);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(s.T), dim3(256), 0, st, y_perm, slot_to_row,
+                       weights, s.d_model, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,90 @@
+// Host-side launchers of the MoE kernels (internal to libmoe).  Each takes a
+// validated shape; the C ABI in api.cpp does the validation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Router GEMV + top-2 + two-way softmax.
+hipError_t launch_route_topk(const moe_shape_t& s, const void* x, const void* w_gate,
+                             const float* bias, int32_t* ids, float* weights, float* logits,
+                             hipStream_t st);
+
+// Capacity selection: writes drop_mask[T*2] (1 = dropped).
+hipError_t launch_capacity_select(const moe_shape_t& s, const int32_t* ids, const float* weights,
+                                  uint8_t* drop_mask, hipStream_t st);
+
+// Counts, offsets, perm_src, slot_to_row (drop_mask may be NULL: nothing dropped).
+hipError_t launch_permute_index(const moe_shape_t& s, const int32_t* ids, const uint8_t* drop_mask,
+                                int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                                int32_t* slot_to_row, hipStream_t st);
+
+// x_perm[row] = x[perm_src[row] / 2] (fp8: block-quantised codes + E8M0 scales).
+hipError_t launch_permute_scatter(const moe_shape_t& s, const void* x, const int32_t* offsets,
+                                  const int32_t* perm_src, void* x_perm, uint8_t* x_perm_scale,
+                                  hipStream_t st);
+
+// Grouped gate/up (dual weight, SwiGLU epilogue) and down GEMMs.
+hipError_t launch_gate_up(const moe_shape_t& s, const void* x_perm, const uint8_t* x_scale,
+                          const int32_t* offsets, const void* w1, const void* w3,
+                          const float* w1_scale, const float* w3_scale, void* h, uint8_t* h_scale,
+                          hipStream_t st);
+hipError_t launch_down(const moe_shape_t& s, const void* h, const uint8_t* h_scale,
+                       const int32_t* offsets, const void* w2, const float* w2_scale,
+                       float* y_perm, hipStream_t st);
+
+// Fill n bytes with v (a kernel, so that the call can sit inside a captured graph).
+hipError_t launch_fill_u8(uint8_t* p, int64_t n, uint8_t v, hipStream_t st);
+
+hipError_t launch_combine(const moe_shape_t& s, const float* y_perm, const int32_t* slot_to_row,
+                          const float* weights, void* y, hipStream_t st);
+
+// fp32 generic GEMM path (act F32 + w F32).
+hipError_t launch_gate_up_f32(const moe_shape_t& s, const float* x_perm, const int32_t* offsets,
+                              const float* w1, const float* w3, float* h, hipStream_t st);
+hipError_t launch_down_f32(const moe_shape_t& s, const float* h, const int32_t* offsets,
+                           const float* w2, float* y_perm, hipStream_t st);
+
+// bf16 paths.
+hipError_t launch_gate_up_bf16(const moe_shape_t& s, const uint16_t* x_perm,
+                               const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
+                               uint16_t* h, hipStream_t st);
+hipError_t launch_down_bf16(const moe_shape_t& s, const uint16_t* h, const int32_t* offsets,
+                            const uint16_t* w2, float* y_perm, hipStream_t st);
+
+// Whether the fp8 matrix-core path is built in.
+constexpr bool kFp8Available = false;
+
+// fp8 paths (e4m3 weights with per-channel fp32 scales, block-scaled e4m3 activations).
+hipError_t launch_gate_up_fp8(const moe_shape_t& s, const uint8_t* x_perm, const uint8_t* x_scale,
+                              const int32_t* offsets, const uint8_t* w1, const uint8_t* w3,
+                              const float* w1_scale, const float* w3_scale, uint8_t* h,
+                              uint8_t* h_scale, hipStream_t st);
+hipError_t launch_down_fp8(const moe_shape_t& s, const uint8_t* h, const uint8_t* h_scale,
+                           const int32_t* offsets, const uint8_t* w2, const float* w2_scale,
+                           float* y_perm, hipStream_t st);
+
+// Largest number of rows any expert can receive: each token picks an expert at most once.
+inline int64_t max_rows_per_expert(const moe_shape_t& s) {
+  int64_t m = s.T;
+  if (s.capacity >= 0 && s.capacity < m) m = s.capacity;
+  return m;
+}
+
+// Upper bound of sum_e ceil(count_e / rows_per_tile) given sum_e count_e <= T*k.
+inline int64_t max_token_tiles(const moe_shape_t& s, int rows_per_tile) {
+  int64_t total = (int64_t)s.T * s.top_k;
+  if (s.capacity >= 0) total = std::min<int64_t>(total, (int64_t)s.capacity * s.n_experts);
+  int64_t t = (total + rows_per_tile - 1) / rows_per_tile + s.n_experts;
+  int64_t per_expert = (max_rows_per_expert(s) + rows_per_tile - 1) / rows_per_tile;
+  return std::min<int64_t>(t, per_expert * s.n_experts);
+}
+
+}  // namespace moe

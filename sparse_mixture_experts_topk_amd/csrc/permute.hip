@@ -1,0 +1,288 @@
+// Grouping of token assignments by expert, with the optional capacity limit.
+//
+// Pages: "How Mixtral 8x7B uses mixture of experts" -- capacity-limited
+// dispatch ("Routing without auxiliary loss": over-capacity tokens are
+// dropped), the per-expert bincount of the top-2 ids (expert activation
+// listing) and "batch tokens by expert, run experts in parallel, scatter
+// back" (simplified forward pass).
+//
+// capacity_select: one workgroup per expert.  Each assignment gets the
+//   64-bit key (fp32 bits of its gate weight) << 32 | (0xffffffff - token),
+//   unique inside an expert and ordered exactly like "higher weight first,
+//   lower token on ties".  An MSB-first radix select (8 passes of 8-bit
+//   digits, LDS histograms) finds the key of rank `capacity`; assignments
+//   with a key at or above it are kept.  Index-only, order-independent and
+//   therefore deterministic.
+// permute_index: one workgroup of 1024 lanes.  Pass 1 counts kept
+//   assignments per expert with LDS atomics (order-free).  Pass 2 walks the
+//   tokens in chunks of 1024; per expert a wavefront ballot + popcount gives
+//   each assignment its rank among earlier tokens of the chunk, and a scan
+//   over the 16 wavefronts places the chunk after the previous ones, so rows
+//   inside an expert follow ascending token order (stable, deterministic).
+// permute_scatter: one wavefront per permuted row copies x[token] in 16-byte
+//   vectors; for fp8 experts each lane quantises 32-element blocks to e4m3
+//   with a power-of-two (E8M0) block scale.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ uint64_t capacity_key(const float* w, int i) {
+  const uint32_t gbits = __float_as_uint(w[i]);  // gate weights are >= +0: bits are monotone
+  const uint32_t tok = (uint32_t)(i >> 1);
+  return ((uint64_t)gbits << 32) | (uint64_t)(0xffffffffu - tok);
+}
+
+__global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __restrict__ ids,
+                                                               const float* __restrict__ w,
+                                                               int n_assign, int capacity,
+                                                               uint8_t* __restrict__ drop) {
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ uint32_t hist[256];
+  __shared__ int s_count;
+  __shared__ int s_digit;
+  __shared__ int s_remaining;
+
+  if (tid == 0) s_count = 0;
+  __syncthreads();
+  int mine = 0;
+  for (int i = tid; i < n_assign; i += blockDim.x) mine += (ids[i] == e);
+  atomicAdd(&s_count, mine);
+  __syncthreads();
+  const int n_e = s_count;
+
+  if (n_e <= capacity) {
+    for (int i = tid; i < n_assign; i += blockDim.x)
+      if (ids[i] == e) drop[i] = 0;
+    return;
+  }
+  if (capacity == 0) {
+    for (int i = tid; i < n_assign; i += blockDim.x)
+      if (ids[i] == e) drop[i] = 1;
+    return;
+  }
+
+  uint64_t prefix = 0, mask = 0;
+  int remaining = capacity;  // rank (1-based, from the top) still to locate
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n_assign; i += blockDim.x) {
+      if (ids[i] != e) continue;
+      const uint64_t key = capacity_key(w, i);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t above = 0;  // keys in this bucket range with a larger digit
+      for (int b = 255; b > tid; --b) above += hist[b];
+      if ((int)above < remaining && (int)(above + hist[tid]) >= remaining) {
+        s_digit = tid;
+        s_remaining = remaining - (int)above;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint64_t)s_digit << shift;
+    mask |= (uint64_t)255 << shift;
+    remaining = s_remaining;
+    __syncthreads();
+  }
+  // `prefix` is now the exact key of rank `capacity`; keys are unique.
+  for (int i = tid; i < n_assign; i += blockDim.x)
+    if (ids[i] == e) drop[i] = capacity_key(w, i) >= prefix ? 0 : 1;
+}
+
+constexpr int kIndexThreads = 1024;
+constexpr int kIndexWaves = kIndexThreads / kWave;
+
+__global__ __launch_bounds__(kIndexThreads) void permute_index_kernel(
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ drop, int T, int E,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+    int32_t* __restrict__ slot_to_row) {
+  __shared__ int s_count[64];
+  __shared__ int s_base[64];
+  __shared__ int s_wave[kIndexWaves][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  if (tid < 64) s_count[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < 2 * T; i += kIndexThreads)
+    if (drop == nullptr || drop[i] == 0) atomicAdd(&s_count[ids[i]], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      offsets[e] = run;
+      s_base[e] = run;
+      counts[e] = s_count[e];
+      run += s_count[e];
+    }
+    offsets[E] = run;
+  }
+  __syncthreads();
+
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < T; c0 += kIndexThreads) {
+    const int t = c0 + tid;
+    int e0 = -1, e1 = -1;
+    if (t < T) {
+      const int2 p = reinterpret_cast<const int2*>(ids)[t];
+      e0 = p.x;
+      e1 = p.y;
+      if (drop != nullptr) {
+        if (drop[2 * t]) e0 = -1;
+        if (drop[2 * t + 1]) e1 = -1;
+      }
+    }
+    int rank0 = 0, rank1 = 0;
+    for (int e = 0; e < E; ++e) {
+      const uint64_t b = __ballot(e0 == e || e1 == e);
+      if (lane == 0) s_wave[wave][e] = __popcll(b);
+      const int r = __popcll(b & lt_mask);
+      if (e0 == e) rank0 = r;
+      if (e1 == e) rank1 = r;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int run = s_base[tid];
+      for (int w = 0; w < kIndexWaves; ++w) {
+        const int c = s_wave[w][tid];
+        s_wave[w][tid] = run;
+        run += c;
+      }
+      s_base[tid] = run;
+    }
+    __syncthreads();
+    if (t < T) {
+      int row0 = -1, row1 = -1;
+      if (e0 >= 0) {
+        row0 = s_wave[wave][e0] + rank0;
+        perm_src[row0] = 2 * t;
+      }
+      if (e1 >= 0) {
+        row1 = s_wave[wave][e1] + rank1;
+        perm_src[row1] = 2 * t + 1;
+      }
+      reinterpret_cast<int2*>(slot_to_row)[t] = make_int2(row0, row1);
+    }
+    __syncthreads();
+  }
+}
+
+// One wavefront per row; 16-byte vectors.
+__global__ __launch_bounds__(256) void permute_scatter_copy_kernel(
+    const uint8_t* __restrict__ x, const int32_t* __restrict__ offsets, int E,
+    const int32_t* __restrict__ perm_src, int row_bytes, uint8_t* __restrict__ x_perm,
+    int max_rows) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= max_rows || row >= offsets[E]) return;
+  const int tok = perm_src[row] >> 1;
+  const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)tok * row_bytes);
+  uint4* dst = reinterpret_cast<uint4*>(x_perm + (int64_t)row * row_bytes);
+  for (int c = lane; c < row_bytes / 16; c += kWave) dst[c] = src[c];
+}
+
+// E8M0 exponent of a block: ceil(log2(fp32(amax / 448))) clamped to [-127, 127];
+// 0 for an all-zero block.
+__device__ __forceinline__ int block_exponent(float amax) {
+  if (amax == 0.0f) return 0;
+  const uint32_t bits = __float_as_uint(amax / 448.0f);
+  const int ex = (int)((bits >> 23) & 255u);
+  const uint32_t man = bits & 0x7fffffu;
+  if (ex == 0) return man > (1u << 22) ? -126 : -127;  // subnormal quotient
+  return man == 0 ? ex - 127 : ex - 126;
+}
+
+// 32 bf16 values -> 32 e4m3 codes with scale 2^e (exact multiply by 2^-e, one rounding).
+__device__ __forceinline__ void quantize_block32_bf16(const uint4* src, uint4* dst, uint8_t* sc) {
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = src[i];
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(v);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+  const int e = block_exponent(amax);
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal float for e in [-127, 126]
+  uint32_t out[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int packed = 0;
+    packed = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w[2 * i]) * inv, bf16_hi(w[2 * i]) * inv, packed, false);
+    packed = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w[2 * i + 1]) * inv, bf16_hi(w[2 * i + 1]) * inv, packed, true);
+    out[i] = (uint32_t)packed;
+  }
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  *sc = (uint8_t)(e + 127);
+}
+
+__global__ __launch_bounds__(256) void permute_scatter_fp8_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets, int E,
+    const int32_t* __restrict__ perm_src, int d, uint8_t* __restrict__ x_perm,
+    uint8_t* __restrict__ x_scale, int max_rows) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= max_rows || row >= offsets[E]) return;
+  const int tok = perm_src[row] >> 1;
+  const int nblk = d / 32;
+  for (int b = lane; b < nblk; b += kWave) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)tok * d + b * 32);
+    uint4* dst = reinterpret_cast<uint4*>(x_perm + (int64_t)row * d + b * 32);
+    quantize_block32_bf16(src, dst, x_scale + (int64_t)row * nblk + b);
+  }
+}
+
+__global__ void fill_u8_kernel(uint8_t* __restrict__ p, int64_t n, uint8_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+}  // namespace
+
+hipError_t launch_capacity_select(const moe_shape_t& s, const int32_t* ids, const float* weights,
+                                  uint8_t* drop_mask, hipStream_t st) {
+  hipLaunchKernelGGL(capacity_select_kernel, dim3(s.n_experts), dim3(1024), 0, st, ids, weights,
+                     2 * s.T, s.capacity, drop_mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_index(const moe_shape_t& s, const int32_t* ids, const uint8_t* drop_mask,
+                                int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                                int32_t* slot_to_row, hipStream_t st) {
+  hipLaunchKernelGGL(permute_index_kernel, dim3(1), dim3(kIndexThreads), 0, st, ids, drop_mask,
+                     s.T, s.n_experts, counts, offsets, perm_src, slot_to_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_scatter(const moe_shape_t& s, const void* x, const int32_t* offsets,
+                                  const int32_t* perm_src, void* x_perm, uint8_t* x_perm_scale,
+                                  hipStream_t st) {
+  const int max_rows = 2 * s.T;
+  const int blocks = (max_rows + 3) / 4;
+  if (s.w_dtype == MOE_FP8_E4M3) {
+    hipLaunchKernelGGL(permute_scatter_fp8_kernel, dim3(blocks), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), offsets, s.n_experts, perm_src, s.d_model,
+                       static_cast<uint8_t*>(x_perm), x_perm_scale, max_rows);
+  } else {
+    const int es = s.act_dtype == MOE_F32 ? 4 : 2;
+    hipLaunchKernelGGL(permute_scatter_copy_kernel, dim3(blocks), dim3(256), 0, st,
+                       static_cast<const uint8_t*>(x), offsets, s.n_experts, perm_src,
+                       s.d_model * es, static_cast<uint8_t*>(x_perm), max_rows);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u8(uint8_t* p, int64_t n, uint8_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(fill_u8_kernel, dim3(blocks), dim3(256), 0, st, p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace moe
