@@ -35,6 +35,14 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal (streamed data that is read exactly once).
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Grouped-GEMM tile lookup: the linear tile index `t` of a grid that covers,
 // expert by expert, ceil(count_e / rows_per_tile) token tiles times
 // `n_tiles` channel tiles.  Token tiles vary fastest inside an expert so

@@ -115,6 +115,131 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 router on the matrix cores.  A 512-lane workgroup owns 16 tokens; its
+// 8 wavefronts split K, each accumulating D[expert][token] = W_g . x^T with
+// v_mfma_f32_16x16x32_bf16 (A = 16 router rows, B = 16 token rows, zero rows
+// past E / T), for EB blocks of 16 experts.  Partial tiles are summed through
+// LDS in a fixed order; wavefront 0 then holds, per lane, token (lane & 15)
+// and experts 16 eb + 4 (lane >> 4) + r.  Each lane keeps its local top-2
+// and two xor-shuffle merges (16, 32) give the token's top-2.  Exact in the
+// sense that matters: bf16 products are exact in fp32 and accumulate in fp32.
+constexpr int kRouteWaves = 8;
+
+struct Cand {
+  float v;
+  int i;
+};
+__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
+  return a.v > b.v || (a.v == b.v && a.i < b.i);
+}
+__device__ __forceinline__ void merge2(Cand& a0, Cand& a1, const Cand& b0, const Cand& b1) {
+  Cand f, s;
+  if (better(a0, b0)) { f = a0; s = better(a1, b0) ? a1 : b0; }
+  else { f = b0; s = better(a0, b1) ? a0 : b1; }
+  a0 = f;
+  a1 = s;
+}
+
+template <int EB>
+__global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias,
+    int T, int d, int E, int32_t* __restrict__ ids, float* __restrict__ wout,
+    float* __restrict__ logits) {
+  __shared__ f32x4_t part[kRouteWaves - 1][EB][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok0 = blockIdx.x * 16;
+  const int r = lane & 15, g = lane >> 4;
+  const bool tok_ok = tok0 + r < T;
+  const uint16_t* px = x + (int64_t)(tok_ok ? tok0 + r : 0) * d + g * 8;
+  const uint16_t* pw[EB];
+  bool w_ok[EB];
+#pragma unroll
+  for (int eb = 0; eb < EB; ++eb) {
+    w_ok[eb] = eb * 16 + r < E;
+    pw[eb] = wg + (int64_t)(w_ok[eb] ? eb * 16 + r : 0) * d + g * 8;
+  }
+  f32x4_t acc[EB];
+#pragma unroll
+  for (int eb = 0; eb < EB; ++eb) acc[eb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nblk = d / 32;
+  const int b0 = wave * nblk / kRouteWaves, b1 = (wave + 1) * nblk / kRouteWaves;
+  constexpr int U = 4;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  for (int b = b0; b < b1; b += U) {
+    uint4 xa[U], wa[U][EB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = b + u < b1;
+      xa[u] = (in && tok_ok) ? *reinterpret_cast<const uint4*>(px + (b + u) * 32) : z;
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb)
+        wa[u][eb] = (in && w_ok[eb]) ? *reinterpret_cast<const uint4*>(pw[eb] + (b + u) * 32) : z;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb)
+        acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][eb]), as_bf16x8(xa[u]),
+                                                           acc[eb], 0, 0, 0);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) part[wave - 1][eb][lane] = acc[eb];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kRouteWaves - 1; ++w)
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) acc[eb] += part[w][eb][lane];
+
+  const int tok = tok0 + r;
+  Cand c0{-INFINITY, 1 << 30}, c1{-INFINITY, 1 << 30};
+#pragma unroll
+  for (int eb = 0; eb < EB; ++eb) {
+    const int ebase = eb * 16 + 4 * g;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = ebase + q;
+      if (e >= E) continue;
+      float l = acc[eb][q];
+      if (bias != nullptr) l += bias[e];
+      acc[eb][q] = l;
+      const Cand c{l, e};
+      if (better(c, c0)) { c1 = c0; c0 = c; }
+      else if (better(c, c1)) { c1 = c; }
+    }
+    if (logits != nullptr && tok < T) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (ebase + q < E) logits[(int64_t)tok * E + ebase + q] = acc[eb][q];
+    }
+  }
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const Cand o0{__shfl_xor(c0.v, o), __shfl_xor(c0.i, o)};
+    const Cand o1{__shfl_xor(c1.v, o), __shfl_xor(c1.i, o)};
+    merge2(c0, c1, o0, o1);
+  }
+  if (g == 0 && tok < T) {
+    const float w0 = 1.0f / (1.0f + expf(c1.v - c0.v));
+    reinterpret_cast<int2*>(ids)[tok] = make_int2(c0.i, c1.i);
+    reinterpret_cast<float2*>(wout)[tok] = make_float2(w0, 1.0f - w0);
+  }
+}
+
+template <int EB>
+hipError_t launch_mfma(const moe_shape_t& s, const void* x, const void* wg, const float* bias,
+                       int32_t* ids, float* w, float* logits, hipStream_t st) {
+  const int blocks = (s.T + 15) / 16;
+  hipLaunchKernelGGL((route_topk_mfma_kernel<EB>), dim3(blocks), dim3(kRouteWaves * 64), 0, st,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), bias, s.T,
+                     s.d_model, s.n_experts, ids, w, logits);
+  return hipGetLastError();
+}
+
 template <int EP, bool BF16>
 hipError_t launch_ep(const moe_shape_t& s, const void* x, const void* wg, const float* bias,
                      int32_t* ids, float* w, float* logits, hipStream_t st) {
@@ -140,8 +265,11 @@ hipError_t launch_dtype(const moe_shape_t& s, const void* x, const void* wg, con
 hipError_t launch_route_topk(const moe_shape_t& s, const void* x, const void* w_gate,
                              const float* bias, int32_t* ids, float* weights, float* logits,
                              hipStream_t st) {
-  if (s.act_dtype == MOE_BF16)
-    return launch_dtype<true>(s, x, w_gate, bias, ids, weights, logits, st);
+  if (s.act_dtype == MOE_BF16) {
+    if (s.n_experts <= 16) return launch_mfma<1>(s, x, w_gate, bias, ids, weights, logits, st);
+    if (s.n_experts <= 32) return launch_mfma<2>(s, x, w_gate, bias, ids, weights, logits, st);
+    return launch_mfma<4>(s, x, w_gate, bias, ids, weights, logits, st);
+  }
   return launch_dtype<false>(s, x, w_gate, bias, ids, weights, logits, st);
 }
 
