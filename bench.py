@@ -34,6 +34,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8_e4m3": 5000.0, "f32": 157.3}   # dense matri
 DEFAULTS = {"decode_bf16": (200, 20), "prefill_bf16": (20, 3), "skewed_capacity_bf16": (20, 3),
             "longctx_fp8": (10, 3), "tiny_fp32": (200, 20)}
 KERNEL_SOURCES = ("sparse_mixture_experts_topk_amd/csrc/gemm_bf16.hip",
+                  "sparse_mixture_experts_topk_amd/csrc/gemm_bf16_decode.hip",
                   "sparse_mixture_experts_topk_amd/csrc/gemm_fp8.hip",
                   "sparse_mixture_experts_topk_amd/csrc/gemm_f32.hip")
 

@@ -76,6 +76,9 @@ moe_status_t validate_shape(const moe_shape_t* s) {
                      (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_FP8_E4M3);
   if (!combo) return MOE_ERR_UNSUPPORTED;
   if (s->w_dtype == MOE_FP8_E4M3 && !moe::kFp8Available) return MOE_ERR_UNSUPPORTED;
+  // fp8: one K slice of the matrix-core tile is 128 elements
+  if (s->w_dtype == MOE_FP8_E4M3 && (s->d_model % 128 != 0 || s->d_ff % 128 != 0))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -1,4 +1,5 @@
-// bf16 grouped expert GEMMs on the gfx950 matrix cores (fp32 accumulate).
+// bf16 grouped expert GEMMs on the gfx950 matrix cores (fp32 accumulate):
+// the many-tokens-per-expert (prefill) kernel and the bf16 dispatch.
 //
 // Pages: "Mixtral" study notes, MixtralExpert.forward = w2(silu(w1 x) * w3 x)
 // (nn.Linear weights [out, in], no biases) and section "SwiGLU Experts";
@@ -12,30 +13,29 @@
 // consecutive channels, which the epilogue stores as 8-byte (bf16 h) or
 // 16-byte (fp32 y_perm) vectors.
 //
-// Prefill kernel (many tokens per expert): 256 lanes, a 256 x 256 tile
-// (weights x tokens; the dual gate/up variant holds 128 w1 rows and the same
-// 128 w3 rows so silu(g) * u is formed in registers), K staged 64 at a time
-// through two LDS buffers of 2 x 32 KiB.  Rows are 128 bytes in LDS with the
-// 16-byte chunks XOR-swizzled by (row & 7), so the fragment reads of 8
-// consecutive rows hit distinct banks.  Global reads use buffer resources
-// bounded to the tile's valid rows: rows past the expert's last token or the
-// last channel read as zero without a branch.  The next K slice is fetched
-// into registers while the current one feeds v_mfma_f32_32x32x16_bf16, LDS
-// fragments are read one 16-wide substep ahead of the matrix instructions,
-// and there is one barrier per slice.  Each wavefront owns 128 x 128 of the
-// tile: 16 accumulator blocks, 256 fp32 per lane.  Tiles are scheduled expert
-// by expert with token tiles fastest and remapped so that consecutive tiles
-// run on the same XCD and share its L2 copy of the weight tile.
-//
-// Decode kernel (few tokens per expert): weight streaming.  One wavefront
-// owns 16 output channels (dual: of w1 and of w3) x up to 16 tokens over all
-// of K, reading each weight row once with non-temporal 16-byte loads, the
-// next K block prefetched into registers while v_mfma_f32_16x16x32_bf16
-// consumes the current one.
+// Prefill kernel: 256 lanes, a 256 x 256 tile (weights x tokens; the dual
+// gate/up variant holds 128 w1 rows and the same 128 w3 rows so silu(g) * u
+// is formed in registers), K staged 64 at a time through two LDS buffers of
+// 2 x 32 KiB.  Rows are 128 bytes in LDS with the 16-byte chunks XOR-swizzled
+// by (row & 7), so the fragment reads of 8 consecutive rows hit distinct
+// banks.  Global reads use buffer resources bounded to the tile's valid rows:
+// rows past the expert's last token or the last channel read as zero without
+// a branch.  The next K slice is fetched into registers while the current one
+// feeds v_mfma_f32_32x32x16_bf16, LDS fragments are read one 16-wide substep
+// ahead of the matrix instructions, and there is one barrier per slice.  Each
+// wavefront owns 128 x 128 of the tile: 16 accumulator blocks, 256 fp32 per
+// lane.  Tiles are scheduled expert by expert with token tiles fastest and
+// remapped so that consecutive tiles run on the same XCD and share its L2
+// copy of the weight tile.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace moe {
+
+hipError_t launch_decode_bf16(const moe_shape_t& s, bool dual, const uint16_t* act,
+                              const int32_t* offsets, const uint16_t* wa, const uint16_t* wb,
+                              int N, int K, void* out, hipStream_t st);
+
 namespace {
 
 // silu(g) * u for a bf16 result: hardware exp2 and reciprocal (about 1 ulp
@@ -56,8 +56,6 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, 
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-
-// ------------------------------------------------------------ prefill ---
 
 constexpr int PF_ROWS = 256;         // rows of each LDS operand tile
 constexpr int PF_BK = 64;            // K per stage (128 bytes per row)
@@ -242,99 +240,6 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
   }
 }
 
-// ------------------------------------------------------------- decode ---
-
-template <bool DUAL, int KB, int MIN_WAVES>
-__global__ __launch_bounds__(256, MIN_WAVES) void grouped_gemm_bf16_decode(
-    const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
-    const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, int N, int K,
-    void* __restrict__ out, int tok_tiles) {
-  constexpr int NC = KB / 32;          // 16-byte chunks per lane per K block
-  const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int groups = N / 16;
-  const int cg = wid % groups;
-  const int rest = wid / groups;
-  const int tt = rest % tok_tiles;
-  const int e = rest / tok_tiles;
-  if (e >= E) return;
-  const int row0 = offsets[e] + tt * 16;
-  const int rows = min(16, offsets[e + 1] - row0);
-  if (rows <= 0) return;
-
-  // Lane (r, g) feeds row r; MFMA j of a K block takes the 32 consecutive
-  // elements k0 + 32 j .. + 31, lane group g its 8-element chunk g, so the 4
-  // lanes of a row read 64 contiguous bytes per load instruction.
-  const int r = lane & 15, g = lane >> 4;
-  const int64_t kofs = (int64_t)g * 8;
-  const uint16_t* pa = wa + ((int64_t)e * N + cg * 16 + r) * K + kofs;
-  const uint16_t* pb = DUAL ? wb + ((int64_t)e * N + cg * 16 + r) * K + kofs : nullptr;
-  const bool tok_ok = r < rows;
-  const uint16_t* px = act + (int64_t)(row0 + (tok_ok ? r : 0)) * K + kofs;
-
-  f32x4_t acc_a = {0.f, 0.f, 0.f, 0.f}, acc_b = {0.f, 0.f, 0.f, 0.f};
-  uint4 ca[NC], cb[NC], cx[NC], na[NC], nb[NC], nx[NC];
-  auto load = [&](int k0, uint4* A, uint4* B, uint4* X) {
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      A[j] = load_stream16(pa + k0 + j * 32);
-      if constexpr (DUAL) B[j] = load_stream16(pb + k0 + j * 32);
-      X[j] = tok_ok ? *reinterpret_cast<const uint4*>(px + k0 + j * 32) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  load(0, ca, cb, cx);
-  for (int k0 = 0; k0 < K; k0 += KB) {
-    const bool more = k0 + KB < K;
-    if (more) load(k0 + KB, na, nb, nx);
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      acc_a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ca[j]), as_bf16x8(cx[j]), acc_a, 0, 0, 0);
-      if constexpr (DUAL)
-        acc_b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cb[j]), as_bf16x8(cx[j]), acc_b, 0, 0, 0);
-    }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < NC; ++j) {
-        ca[j] = na[j];
-        if constexpr (DUAL) cb[j] = nb[j];
-        cx[j] = nx[j];
-      }
-    }
-  }
-
-  // 16x16 accumulator: lane holds token column (lane & 15), channels 4 * (lane >> 4) + 0..3.
-  const int tcol = lane & 15;
-  if (tcol >= rows) return;
-  const int c = cg * 16 + (lane >> 4) * 4;
-  const int64_t orow = row0 + tcol;
-  if constexpr (DUAL) {
-    float hv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hv[i] = swiglu_fast(acc_a[i], acc_b[i]);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow * N + c) =
-        make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-  } else {
-    *reinterpret_cast<float4*>(static_cast<float*>(out) + orow * N + c) =
-        make_float4(acc_a[0], acc_a[1], acc_a[2], acc_a[3]);
-  }
-}
-
-template <bool DUAL, int KB>
-hipError_t launch_decode(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
-                         const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
-                         hipStream_t st) {
-  const int tok_tiles = (int)((max_rows_per_expert(s) + 15) / 16);
-  const int64_t waves = (int64_t)s.n_experts * tok_tiles * (N / 16);
-  const int64_t blocks = (waves + 3) / 4;
-  if (blocks <= 0) return hipSuccess;   // no expert can hold a row (capacity 0)
-  // dual, 64-wide K blocks: 7 wavefronts per SIMD (no spills) keep a whole
-  // Mixtral-size grid (8 experts x 896 channel groups) resident at once
-  constexpr int MIN_WAVES = (DUAL && KB == 64) ? 7 : 2;
-  hipLaunchKernelGGL((grouped_gemm_bf16_decode<DUAL, KB, MIN_WAVES>), dim3((unsigned)blocks), dim3(256), 0,
-                     st, act, offsets, s.n_experts, wa, wb, N, K, out, tok_tiles);
-  return hipGetLastError();
-}
-
 template <bool DUAL>
 hipError_t launch_prefill(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                           const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
@@ -349,34 +254,24 @@ hipError_t launch_prefill(const moe_shape_t& s, const uint16_t* act, const int32
   return hipGetLastError();
 }
 
-// Decode (weight streaming) while no expert can hold more than this many rows.
+// Weight streaming (decode kernels) while no expert can hold more than this many rows.
 constexpr int kDecodeMaxRows = 64;
-
-template <bool DUAL>
-hipError_t launch_bf16(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
-                       const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
-                       hipStream_t st) {
-  if (max_rows_per_expert(s) <= kDecodeMaxRows) {
-    // dual: 2 + 2 weight loads per K block, few registers, so every wavefront
-    // of the grid is resident at once; single: 8 loads in flight per lane.
-    if (!DUAL && K % 256 == 0) return launch_decode<DUAL, 256>(s, act, offsets, wa, wb, N, K, out, st);
-    if (!DUAL && K % 128 == 0) return launch_decode<DUAL, 128>(s, act, offsets, wa, wb, N, K, out, st);
-    return launch_decode<DUAL, 64>(s, act, offsets, wa, wb, N, K, out, st);
-  }
-  return launch_prefill<DUAL>(s, act, offsets, wa, wb, N, K, out, st);
-}
 
 }  // namespace
 
 hipError_t launch_gate_up_bf16(const moe_shape_t& s, const uint16_t* x_perm,
                                const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                                uint16_t* h, hipStream_t st) {
-  return launch_bf16<true>(s, x_perm, offsets, w1, w3, s.d_ff, s.d_model, h, st);
+  if (max_rows_per_expert(s) <= kDecodeMaxRows)
+    return launch_decode_bf16(s, true, x_perm, offsets, w1, w3, s.d_ff, s.d_model, h, st);
+  return launch_prefill<true>(s, x_perm, offsets, w1, w3, s.d_ff, s.d_model, h, st);
 }
 
 hipError_t launch_down_bf16(const moe_shape_t& s, const uint16_t* h, const int32_t* offsets,
                             const uint16_t* w2, float* y_perm, hipStream_t st) {
-  return launch_bf16<false>(s, h, offsets, w2, nullptr, s.d_model, s.d_ff, y_perm, st);
+  if (max_rows_per_expert(s) <= kDecodeMaxRows)
+    return launch_decode_bf16(s, false, h, offsets, w2, nullptr, s.d_model, s.d_ff, y_perm, st);
+  return launch_prefill<false>(s, h, offsets, w2, nullptr, s.d_model, s.d_ff, y_perm, st);
 }
 
 }  // namespace moe

@@ -60,7 +60,7 @@ hipError_t launch_down_bf16(const moe_shape_t& s, const uint16_t* h, const int32
                             const uint16_t* w2, float* y_perm, hipStream_t st);
 
 // Whether the fp8 matrix-core path is built in.
-constexpr bool kFp8Available = false;
+constexpr bool kFp8Available = true;
 
 // fp8 paths (e4m3 weights with per-channel fp32 scales, block-scaled e4m3 activations).
 hipError_t launch_gate_up_fp8(const moe_shape_t& s, const uint8_t* x_perm, const uint8_t* x_scale,

@@ -63,6 +63,8 @@ def S(**kw):
     (dict(top_k=3), 2), (dict(n_experts=65), 2), (dict(d_model=100), 2), (dict(d_ff=4000), 2),
     (dict(act_dtype="f32", w_dtype="bf16"), 2), (dict(act_dtype="bf16", w_dtype="f32"), 2),
     (dict(act_dtype="f32", w_dtype="f32"), 0), (dict(capacity=0), 0), (dict(T=0), 0),
+    (dict(w_dtype="fp8_e4m3"), 0), (dict(w_dtype="fp8_e4m3", d_model=4160), 2),
+    (dict(w_dtype="fp8_e4m3", d_ff=14400), 2), (dict(act_dtype="f32", w_dtype="fp8_e4m3"), 2),
 ])
 def test_workspace_query_validates_shape(kw, expected):
     n = ctypes.c_size_t(0)

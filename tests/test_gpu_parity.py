@@ -61,9 +61,21 @@ def run_staged_and_check(cfg, inputs=None, tokens=None, check_h=True):
         xs = st["x_perm"][torch.from_numpy(rows).cuda()].cpu()
         src = inputs.x[torch.from_numpy(res.perm.perm_src[rows] // 2)]
         assert torch.equal(xs, src), "x_perm is not an exact copy of x"
+    else:
+        # fp8: x_perm holds block-quantised codes; they must equal the oracle's exactly
+        codes, ex, _ = oracle.fp8.block_quantize(oracle.to_f64(inputs.x)[res.perm.perm_src[rows] // 2])
+        idx = torch.from_numpy(rows).cuda()
+        assert np.array_equal(to_np(st["x_perm"][idx]), codes), "fp8 x codes differ"
+        assert np.array_equal(to_np(st["x_perm_scale"][idx]).astype(np.int64) - 127, ex), "x scales differ"
     h_fro = np.nan
     if check_h:
-        h_gpu = to_np(st["h"][torch.from_numpy(rows).cuda()].float())
+        idx = torch.from_numpy(rows).cuda()
+        if cfg.w_dtype == "fp8_e4m3":
+            q = oracle.fp8.e4m3_decode(to_np(st["h"][idx]))
+            sc = np.repeat(to_np(st["h_scale"][idx]).astype(np.int64) - 127, 32, axis=1)
+            h_gpu = q * np.exp2(sc)
+        else:
+            h_gpu = to_np(st["h"][idx].float())
         h_fro, _ = assert_close(h_gpu, res.h[rows], key, "h (gate/up + SwiGLU)")
     yp = to_np(st["y_perm"][torch.from_numpy(rows).cuda()])
     yp_fro, _ = assert_close(yp, res.y_perm[rows], key, "y_perm (down)")
@@ -280,3 +292,35 @@ def test_prefill_config_fused_forward_sampled():
     y = to_np(buf.y.float())[toks]
     fro, mx = assert_close(y, res.y[toks], "bf16", "prefill y")
     say(f"  y rel_frob={fro:.3e} rel_max={mx:.3e}")
+
+
+# -------------------------------------------------------------- fp8 path ---
+
+def fp8_mid_cfg(name, **kw):
+    base = dict(name=name, T=700, d_model=512, d_ff=384, n_experts=8, act_dtype="bf16",
+                w_dtype="fp8_e4m3", x_std=1.0, wg_std=512 ** -0.5, w13_std=0.05, w2_std=0.05,
+                seed=21)
+    base.update(kw)
+    return synthetic.MoEConfig(**base)
+
+
+def test_fp8_mid_staged():
+    # 8 experts x ~175 rows: one ragged token tile per expert; F = 384 -> 3 channel tiles
+    run_staged_and_check(fp8_mid_cfg("fp8_mid"))
+
+
+def test_fp8_mid_many_tiles_and_capacity():
+    run_staged_and_check(fp8_mid_cfg("fp8_e2", T=900, n_experts=2, d_ff=640, seed=22))
+    run_staged_and_check(fp8_mid_cfg("fp8_cap", T=800, capacity=150, router_bias="zipf1.2", seed=23))
+
+
+def test_fp8_small_batch():
+    run_staged_and_check(fp8_mid_cfg("fp8_t16", T=16, seed=24))
+
+
+def test_longctx_fp8_config_sampled():
+    cfg = synthetic.CONFIGS["longctx_fp8"]
+    inp = cached_inputs("longctx_fp8")
+    base = oracle.forward(inp, tokens=[])
+    toks = sample_tokens(base, n_random=16)
+    run_staged_and_check(cfg, inputs=inp, tokens=toks, check_h=True)
