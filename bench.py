@@ -158,7 +158,8 @@ def main():
         moe.moe_route_topk(shape, d.x, d.w_gate, d.router_bias, st["topk_ids"],
                            st["topk_weights"], None, stream)
         moe.moe_permute(shape, st["topk_ids"], st["topk_weights"], d.x, st["expert_counts"],
-                        st["expert_offsets"], st["perm_src"], st["slot_to_row"], st["drop_mask"],
+                        st["expert_offsets"], st["perm_src"], st["slot_to_row"],
+                        st["drop_mask"] if cfg.capacity >= 0 else None,
                         st["x_perm"], st["x_perm_scale"], None, stream)
         if timed:
             ev0[i].record(stream)

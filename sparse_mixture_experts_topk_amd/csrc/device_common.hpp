@@ -37,6 +37,14 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// XOR key of the 16-byte-chunk swizzle of 128-byte LDS rows.  A 16-byte LDS
+// read is served 16 lanes per cycle across 64 four-byte banks: with one row
+// per lane, rows of equal parity share a 32-bank half, so rows i and i + 8
+// must get different chunks as well as rows 0..7 among themselves.
+// (row & 7) ^ (bit 3 of row) gives distinct chunks to any 8 consecutive rows
+// and to each parity class of any 16 consecutive rows.
+__device__ __forceinline__ int lds_swizzle_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 // 16-byte load marked non-temporal (streamed data that is read exactly once).
 __device__ __forceinline__ uint4 load_stream16(const void* p) {
   const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));

@@ -17,8 +17,8 @@
 // gate/up variant holds 128 w1 rows and the same 128 w3 rows so silu(g) * u
 // is formed in registers), K staged 64 at a time through two LDS buffers of
 // 2 x 32 KiB.  Rows are 128 bytes in LDS with the 16-byte chunks XOR-swizzled
-// by (row & 7), so the fragment reads of 8 consecutive rows hit distinct
-// banks.  Global reads use buffer resources bounded to the tile's valid rows:
+// (lds_swizzle_key), so the fragment reads of 16 consecutive rows are free of
+// bank conflicts.  Global reads use buffer resources bounded to the tile's valid rows:
 // rows past the expert's last token or the last channel read as zero without
 // a branch.  The next K slice is fetched into registers while the current one
 // feeds v_mfma_f32_32x32x16_bf16, LDS fragments are read one 16-wide substep
@@ -63,7 +63,7 @@ constexpr int PF_TILE_BYTES = PF_ROWS * PF_BK * 2;
 constexpr int PF_THREADS = 256;
 
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
+  return row * 128 + ((chunk ^ lds_swizzle_key(row)) << 4);
 }
 
 template <bool DUAL>
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
   const int fi = lane & 31, fg = lane >> 5;
   int frag_off[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) frag_off[s] = fi * 128 + (((2 * s + fg) ^ (fi & 7)) << 4);
+  for (int s = 0; s < 4; ++s) frag_off[s] = fi * 128 + (((2 * s + fg) ^ lds_swizzle_key(fi)) << 4);
   int arow[4], brow[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) {

@@ -67,7 +67,7 @@ constexpr int F8_TILE_BYTES = F8_ROWS * F8_BK;
 constexpr int F8_THREADS = 256;
 
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
+  return row * 128 + ((chunk ^ lds_swizzle_key(row)) << 4);
 }
 
 template <bool DUAL>
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void grouped_gemm_fp8_prefill(
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      frag_off[s][c] = fi * 128 + (((4 * s + 2 * c + fg) ^ (fi & 7)) << 4);
+      frag_off[s][c] = fi * 128 + (((4 * s + 2 * c + fg) ^ lds_swizzle_key(fi)) << 4);
   int arow[4], brow[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) {

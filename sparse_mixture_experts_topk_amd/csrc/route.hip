@@ -126,19 +126,28 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 // sense that matters: bf16 products are exact in fp32 and accumulate in fp32.
 constexpr int kRouteWaves = 8;
 
-struct Cand {
-  float v;
-  int i;
-};
-__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
-  return a.v > b.v || (a.v == b.v && a.i < b.i);
+// (value, index) a ranks before b: larger value, or equal value and lower index.
+__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
 }
-__device__ __forceinline__ void merge2(Cand& a0, Cand& a1, const Cand& b0, const Cand& b1) {
-  Cand f, s;
-  if (better(a0, b0)) { f = a0; s = better(a1, b0) ? a1 : b0; }
-  else { f = b0; s = better(a0, b1) ? a0 : b1; }
-  a0 = f;
-  a1 = s;
+
+// Merge two sorted top-2 lists (v0,i0 >= v1,i1) and (w0,j0 >= w1,j1) into the first.
+// Plain scalars and selects, so everything stays in registers.
+__device__ __forceinline__ void merge2(float& v0, int& i0, float& v1, int& i1, float w0, int j0,
+                                       float w1, int j1) {
+  const bool a_first = better(v0, i0, w0, j0);
+  const float fv = a_first ? v0 : w0;
+  const int fi = a_first ? i0 : j0;
+  // runner-up: best of the loser's head and the winner's second
+  const float cv = a_first ? w0 : v0;
+  const int ci = a_first ? j0 : i0;
+  const float sv2 = a_first ? v1 : w1;
+  const int si2 = a_first ? i1 : j1;
+  const bool c_second = better(cv, ci, sv2, si2);
+  v1 = c_second ? cv : sv2;
+  i1 = c_second ? ci : si2;
+  v0 = fv;
+  i0 = fi;
 }
 
 template <int EB>
@@ -165,17 +174,24 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
 
   const int nblk = d / 32;
   const int b0 = wave * nblk / kRouteWaves, b1 = (wave + 1) * nblk / kRouteWaves;
-  constexpr int U = 4;
+  // all of a wavefront's K blocks in flight at once at d = 4096 (16 per wavefront)
+  constexpr int U = 16 / EB;
   const uint4 z = make_uint4(0, 0, 0, 0);
   for (int b = b0; b < b1; b += U) {
+    // Unconditional 16-byte loads from clamped (always valid) addresses, then a
+    // select: a conditional load would be split into guarded dword loads.
     uint4 xa[U], wa[U][EB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool in = b + u < b1;
-      xa[u] = (in && tok_ok) ? *reinterpret_cast<const uint4*>(px + (b + u) * 32) : z;
+      const int blk = in ? b + u : b0;
+      const uint4 xv = *reinterpret_cast<const uint4*>(px + blk * 32);
+      xa[u] = (in && tok_ok) ? xv : z;
 #pragma unroll
-      for (int eb = 0; eb < EB; ++eb)
-        wa[u][eb] = (in && w_ok[eb]) ? *reinterpret_cast<const uint4*>(pw[eb] + (b + u) * 32) : z;
+      for (int eb = 0; eb < EB; ++eb) {
+        const uint4 wv = *reinterpret_cast<const uint4*>(pw[eb] + blk * 32);
+        wa[u][eb] = (in && w_ok[eb]) ? wv : z;
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -196,20 +212,27 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
     for (int eb = 0; eb < EB; ++eb) acc[eb] += part[w][eb][lane];
 
   const int tok = tok0 + r;
-  Cand c0{-INFINITY, 1 << 30}, c1{-INFINITY, 1 << 30};
+  // local top-2 over this lane's experts, visited in increasing index order
+  float v0 = -INFINITY, v1 = -INFINITY;
+  int i0 = 1 << 30, i1 = 1 << 30;
 #pragma unroll
   for (int eb = 0; eb < EB; ++eb) {
     const int ebase = eb * 16 + 4 * g;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = ebase + q;
-      if (e >= E) continue;
+      const bool real = e < E;
       float l = acc[eb][q];
-      if (bias != nullptr) l += bias[e];
+      if (real && bias != nullptr) l += bias[e];
       acc[eb][q] = l;
-      const Cand c{l, e};
-      if (better(c, c0)) { c1 = c0; c0 = c; }
-      else if (better(c, c1)) { c1 = c; }
+      const float lv = real ? l : -INFINITY;
+      const int li = real ? e : (1 << 30);
+      const bool top = better(lv, li, v0, i0);
+      const bool sec = !top && better(lv, li, v1, i1);
+      v1 = top ? v0 : (sec ? lv : v1);
+      i1 = top ? i0 : (sec ? li : i1);
+      v0 = top ? lv : v0;
+      i0 = top ? li : i0;
     }
     if (logits != nullptr && tok < T) {
 #pragma unroll
@@ -219,13 +242,13 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
   }
 #pragma unroll
   for (int o = 16; o <= 32; o <<= 1) {
-    const Cand o0{__shfl_xor(c0.v, o), __shfl_xor(c0.i, o)};
-    const Cand o1{__shfl_xor(c1.v, o), __shfl_xor(c1.i, o)};
-    merge2(c0, c1, o0, o1);
+    const float w0 = __shfl_xor(v0, o), w1 = __shfl_xor(v1, o);
+    const int j0 = __shfl_xor(i0, o), j1 = __shfl_xor(i1, o);
+    merge2(v0, i0, v1, i1, w0, j0, w1, j1);
   }
   if (g == 0 && tok < T) {
-    const float w0 = 1.0f / (1.0f + expf(c1.v - c0.v));
-    reinterpret_cast<int2*>(ids)[tok] = make_int2(c0.i, c1.i);
+    const float w0 = 1.0f / (1.0f + expf(v1 - v0));
+    reinterpret_cast<int2*>(ids)[tok] = make_int2(i0, i1);
     reinterpret_cast<float2*>(wout)[tok] = make_float2(w0, 1.0f - w0);
   }
 }
