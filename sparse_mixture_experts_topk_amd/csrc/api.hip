@@ -10,6 +10,20 @@
 
 namespace moe {
 
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;   // every thread that races here stores the same value
+  }
+  return cached[dev];
+}
+
 hipError_t launch_gate_up(const moe_shape_t& s, const void* x_perm, const uint8_t* x_scale,
                           const int32_t* offsets, const void* w1, const void* w3,
                           const float* w1_scale, const float* w3_scale, void* h, uint8_t* h_scale,
@@ -68,7 +82,7 @@ moe_status_t validate_shape(const moe_shape_t* s) {
   const bool known = (s->act_dtype == MOE_F32 || s->act_dtype == MOE_BF16) &&
                      (s->w_dtype == MOE_F32 || s->w_dtype == MOE_BF16 || s->w_dtype == MOE_FP8_E4M3);
   if (!known) return MOE_ERR_INVALID_ARG;
-  if (s->top_k != 2 || s->n_experts > 64) return MOE_ERR_UNSUPPORTED;
+  if (s->top_k != 2 || s->n_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (s->d_model % 64 != 0 || s->d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (s->d_model > (1 << 16) || s->d_ff > (1 << 18)) return MOE_ERR_UNSUPPORTED;
   const bool combo = (s->act_dtype == MOE_F32 && s->w_dtype == MOE_F32) ||

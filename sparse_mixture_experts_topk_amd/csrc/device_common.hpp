@@ -36,6 +36,7 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // XOR key of the 16-byte-chunk swizzle of 128-byte LDS rows.  A 16-byte LDS
 // read is served 16 lanes per cycle across 64 four-byte banks: with one row
@@ -61,7 +62,9 @@ __device__ __forceinline__ bool locate_tile(const int32_t* __restrict__ offsets,
                                             int& row_begin, int& row_end, int& m_tile,
                                             int& n_tile) {
   for (int e = 0; e < n_experts; ++e) {
-    const int r0 = offsets[e], r1 = offsets[e + 1];
+    // the offsets are the same for every lane (also when staged in LDS)
+    const int r0 = __builtin_amdgcn_readfirstlane(offsets[e]);
+    const int r1 = __builtin_amdgcn_readfirstlane(offsets[e + 1]);
     const int mt = (r1 - r0 + rows_per_tile - 1) / rows_per_tile;
     const int tiles = mt * n_tiles;
     if (t < tiles) {

@@ -15,17 +15,18 @@
 //
 // Prefill kernel: 256 lanes, a 256 x 256 tile (weights x tokens; the dual
 // gate/up variant holds 128 w1 rows and the same 128 w3 rows so silu(g) * u
-// is formed in registers), K staged 64 at a time through two LDS buffers of
-// 2 x 32 KiB.  Rows are 128 bytes in LDS with the 16-byte chunks XOR-swizzled
-// (lds_swizzle_key), so the fragment reads of 16 consecutive rows are free of
-// bank conflicts.  Global reads use buffer resources bounded to the tile's valid rows:
-// rows past the expert's last token or the last channel read as zero without
-// a branch.  The next K slice is fetched into registers while the current one
-// feeds v_mfma_f32_32x32x16_bf16, LDS fragments are read one 16-wide substep
-// ahead of the matrix instructions, and there is one barrier per slice.  Each
-// wavefront owns 128 x 128 of the tile: 16 accumulator blocks, 256 fp32 per
-// lane.  Tiles are scheduled expert by expert with token tiles fastest and
-// remapped so that consecutive tiles run on the same XCD and share its L2
+// is formed in registers).  K advances 32 at a time through a ring of four
+// LDS stages of 2 x 16 KiB, filled by buffer loads that write LDS directly
+// (no staging registers), so three slices are in flight while one is
+// multiplied.  Rows are 64 bytes in LDS with the 16-byte chunks XOR-swizzled,
+// so the fragment reads of 16 consecutive rows are free of bank conflicts.
+// The buffer descriptors are bounded to the tile's valid rows: rows past the
+// expert's last token or the last channel load as zero without a branch.
+// Each wavefront owns 128 x 128 of the tile (16 accumulator blocks of
+// v_mfma_f32_32x32x16_bf16, 256 fp32 per lane); fragments are read one
+// 16-wide substep ahead of the matrix instructions and there is one barrier
+// per slice.  Tiles are scheduled expert by expert with token tiles fastest
+// and remapped so that consecutive tiles run on the same XCD and share its L2
 // copy of the weight tile.
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -47,210 +48,363 @@ __device__ __forceinline__ float swiglu_fast(float g, float u) {
 
 constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kBufferFlags);
-}
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 constexpr int PF_ROWS = 256;         // rows of each LDS operand tile
-constexpr int PF_BK = 64;            // K per stage (128 bytes per row)
-constexpr int PF_TILE_BYTES = PF_ROWS * PF_BK * 2;
 constexpr int PF_THREADS = 256;
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ lds_swizzle_key(row)) << 4);
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor in scalar registers (the form the LDS-DMA load takes).
+__device__ __forceinline__ i32x4_t make_desc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+  i32x4_t d;
+  d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  d.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));   // stride 0
+  d.z = __builtin_amdgcn_readfirstlane(n);
+  d.w = kBufferFlags;
+  return d;
 }
 
-template <bool DUAL>
+// Wavefront-wide load of 16 bytes per lane from a buffer straight into LDS:
+// lane l's bytes land at lds_addr + 16 l, so one instruction fills 1 KiB.
+// Offsets past the buffer's range load zeros.  The load is counted by
+// vmcnt like any vector memory read; it is written as assembly because the
+// compiler, unable to tell which LDS bytes such a load writes, would wait
+// for it to finish before every LDS read, including reads of other stages.
+// M0 (the LDS address) is declared clobbered; the kernels here use it for nothing else.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_to_lds(i32x4_t desc, int voff, int soff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(desc), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Buffer stores through a descriptor held in scalar registers (assembly, so
+// the descriptor cannot be placed in vector registers and force a per-lane
+// loop).  Offsets past the descriptor's range drop the store.  The trailing
+// wait state covers a vector-ALU write of the data registers right after a
+// store of more than 8 bytes.
+__device__ __forceinline__ void store_b64(i32x4_t desc, int voff, uint32_t lo, uint32_t hi) {
+  asm volatile("buffer_store_dwordx2 %0, %1, %2, 0 offen\n\ts_nop 0"
+               :: "v"(u32x2_t{lo, hi}), "v"(voff), "s"(desc) : "memory");
+}
+__device__ __forceinline__ void store_b128(i32x4_t desc, int voff, u32x4_t v) {
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 1"
+               :: "v"(v), "v"(voff), "s"(desc) : "memory");
+}
+
+// Wait until at most n vector-memory operations of this wavefront are pending.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | 0x0f70 | (n & 15));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// Geometry of one K slice of BK elements: LDS rows of BK * 2 bytes made of
+// CPR 16-byte chunks.  Chunk c of row r sits at chunk position c ^ key(r),
+// which spreads the fragment reads of 16 consecutive rows (one LDS phase,
+// same logical chunk) over all 64 banks.  A 1 KiB load instruction covers
+// RPI whole rows.  The weight operand has TA rows (WA 32-row blocks per
+// wavefront, two wavefront rows), the token operand PF_ROWS.
+template <int BK, int WA>
+struct TileGeom {
+  static constexpr int CPR = BK / 8;
+  static constexpr int ROW_B = BK * 2;
+  static constexpr int TA = 64 * WA;
+  static constexpr int OPA_BYTES = TA * ROW_B;
+  static constexpr int OPB_BYTES = PF_ROWS * ROW_B;
+  static constexpr int STAGE_BYTES = OPA_BYTES + OPB_BYTES;
+  static constexpr int RPI = 64 / CPR;
+  static constexpr int JA = TA / RPI / 4;              // weight loads per wavefront per slice
+  static constexpr int JB = PF_ROWS / RPI / 4;         // token loads per wavefront per slice
+  static constexpr int DMA = JA + JB;
+  static constexpr int SUB = BK / 16;                  // 16-wide matrix substeps
+  __device__ static __forceinline__ int key(int row) { return (row / (16 / CPR)) & (CPR - 1); }
+};
+
+// Tile: TA weight rows x 256 tokens.  The dual (gate/up) kernel's weight rows
+// are TA / 2 rows of w1 followed by the same TA / 2 rows of w3, so each
+// wavefront holds matching w1 and w3 accumulators and forms silu(g) * u in
+// registers.  Wavefront (wr, wc) owns weight blocks of wavefront row wr and
+// tokens wc * 128 .. wc * 128 + 127.
+//
+// The kernel is persistent: the grid is a multiple of 8 workgroups, one per
+// CU at most, and workgroup b works through tiles of XCD b % 8's share of
+// the tile list (consecutive tiles, so the workgroups of one XCD share
+// weight and token tiles in its L2), b / 8, b / 8 + grid / 8, ...  The K
+// slices of all its tiles form one stream through the LDS ring, so the
+// first slices of the next tile load while the current one finishes and
+// stores its results.
+template <bool DUAL, int BK, int NS, int WA>
 __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
     const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, int N, int K,
-    void* __restrict__ out, int n_tiles, int grid_padded) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][PF_TILE_BYTES];  // [stage][weights/tokens]
+    void* __restrict__ out, int n_tiles) {
+  using G = TileGeom<BK, WA>;
+  static_assert(G::SUB % 2 == 0 && NS >= 2 && WA % 2 == 0, "pipeline shape");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * G::STAGE_BYTES];
+  __shared__ int32_t offs[kMaxExperts + 1];
 
-  constexpr int CH_TILE = DUAL ? 128 : 256;
-  int e, r0, r1, mt, nt;
-  const int tile = xcd_remap(blockIdx.x, grid_padded);
-  if (!locate_tile(offsets, E, PF_ROWS, n_tiles, tile, e, r0, r1, mt, nt)) return;
-  const int tok0 = r0 + mt * PF_ROWS;
-  const int tok_rows = min(PF_ROWS, r1 - tok0);
-  const int ch0 = nt * CH_TILE;
-
+  constexpr int HA = WA / 2;                 // dual: w1 (or w3) blocks per wavefront
+  constexpr int CH_TILE = DUAL ? G::TA / 2 : G::TA;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index is uniform
   const int wr = wave >> 1, wc = wave & 1;
 
-  // ---- global -> register loader: 8 chunks of each operand per lane ----
-  // Lane reads 16-byte chunk (tid & 7) of rows (tid >> 3) + 32 j.
-  const int lrow = tid >> 3, lchunk = tid & 7;
-  const int64_t rowbytes = (int64_t)K * 2;
-  const __amdgpu_buffer_rsrc_t rs_t = make_rsrc(act + (int64_t)tok0 * K, tok_rows * rowbytes);
-  const __amdgpu_buffer_rsrc_t rs_w0 =
-      make_rsrc(wa + ((int64_t)e * N + ch0) * K, (int64_t)(N - ch0) * rowbytes);
-  const __amdgpu_buffer_rsrc_t rs_w1 =
-      DUAL ? make_rsrc(wb + ((int64_t)e * N + ch0) * K, (int64_t)(N - ch0) * rowbytes) : rs_w0;
-  int voff_w[8], voff_t[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    // dual: tile rows 0..127 are w1 rows, 128..255 the same w3 rows
-    const int wrow = (DUAL ? (j & 3) * 32 : j * 32) + lrow;
-    voff_w[j] = (int)(wrow * rowbytes) + lchunk * 16;
-    voff_t[j] = (int)((j * 32 + lrow) * rowbytes) + lchunk * 16;
-  }
-  const int st_off = swz(lrow, lchunk);          // + j * 32 * 128
-
-  uint4 rw[8], rt[8];
-  auto gload = [&](int k0) {
-    const int soff = k0 * 2;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      rw[j] = buf_load16((DUAL && j >= 4) ? rs_w1 : rs_w0, voff_w[j], soff);
-      rt[j] = buf_load16(rs_t, voff_t[j], soff);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      *reinterpret_cast<uint4*>(&smem[buf][0][st_off + j * 32 * 128]) = rw[j];
-      *reinterpret_cast<uint4*>(&smem[buf][1][st_off + j * 32 * 128]) = rt[j];
-    }
-  };
-
-  // ---- fragment addressing ----
-  const int fi = lane & 31, fg = lane >> 5;
-  int frag_off[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) frag_off[s] = fi * 128 + (((2 * s + fg) ^ lds_swizzle_key(fi)) << 4);
-  int arow[4], brow[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    if constexpr (DUAL) arow[a] = (a >> 1) * 128 + wr * 64 + (a & 1) * 32;  // a: 0,1 = w1; 2,3 = w3
-    else arow[a] = wr * 128 + a * 32;
-    brow[a] = wc * 128 + a * 32;
-  }
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-
-  auto read_frags = [&](int buf, int s, bf16x8_t* fa, bf16x8_t* fb) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-      fa[a] = as_bf16x8(*reinterpret_cast<const uint4*>(&smem[buf][0][arow[a] * 128 + frag_off[s]]));
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      fb[b] = as_bf16x8(*reinterpret_cast<const uint4*>(&smem[buf][1][brow[b] * 128 + frag_off[s]]));
-  };
-
-  auto mfmas = [&](const bf16x8_t* fa, const bf16x8_t* fb) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
-  };
-
-  // Software pipeline of one K slice (64 MFMAs per wavefront), one basic
-  // block: the next slice's 16 global reads and the next substep's 8
-  // fragment reads are spread between the matrix instructions, the LDS
-  // writes of the next slice fill the last substep, then one barrier.  The
-  // read of slice KT (past the end) is bounded by the buffer resources and
-  // its LDS copy is never consumed.
-  const int KT = K / PF_BK;
-  gload(0);
-  sstore(0);
+  // Expert offsets go to LDS once, so that locating a tile in the middle of
+  // the load stream issues no vector-memory read (the stream's waits count
+  // its own loads).
+  if (tid <= E) offs[tid] = offsets[tid];
   __syncthreads();
-  bf16x8_t fa0[4], fb0[4], fa1[4], fb1[4];
-  read_frags(0, 0, fa0, fb0);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    gload((kt + 1) * PF_BK);
-    read_frags(buf, 1, fa1, fb1);
-    mfmas(fa0, fb0);
-    read_frags(buf, 2, fa0, fb0);
-    mfmas(fa1, fb1);
-    read_frags(buf, 3, fa1, fb1);
-    mfmas(fa0, fb0);
-    sstore(buf ^ 1);
-    mfmas(fa1, fb1);
-    // substep 0: 16 MFMA, 16 global reads, 8 fragment reads
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);   // VMEM read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    // substeps 1, 2: 16 MFMA and 8 fragment reads each
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-    // substep 3: 16 MFMA and the 16 LDS writes of the next slice
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    __syncthreads();
-    read_frags(buf ^ 1, 0, fa0, fb0);
-  }
+  int total = 0;
+  for (int e = 0; e < E; ++e)
+    total += (__builtin_amdgcn_readfirstlane(offs[e + 1]) - __builtin_amdgcn_readfirstlane(offs[e]) +
+              PF_ROWS - 1) / PF_ROWS;
+  total *= n_tiles;
+  const int slots = gridDim.x >> 3;
+  const int per_xcd = (total + 7) >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int t_first = xcd * per_xcd + slot;
+  const int t_end = min((xcd + 1) * per_xcd, total);
+  const int n_my = t_first < t_end ? (t_end - t_first + slots - 1) / slots : 0;
+  if (n_my == 0) return;
 
-  // ---- epilogue: lane = token (fi), registers = channels ----
+  struct Tile { int e, tok0, tok_rows, ch0; };
+  auto tile_of = [&](int i) __attribute__((always_inline)) -> Tile {
+    int e, r0, r1, mt, nt;
+    locate_tile(offs, E, PF_ROWS, n_tiles, t_first + i * slots, e, r0, r1, mt, nt);
+    Tile t;   // uniform values, kept in scalar registers
+    t.e = __builtin_amdgcn_readfirstlane(e);
+    t.tok0 = __builtin_amdgcn_readfirstlane(r0 + mt * PF_ROWS);
+    t.tok_rows = __builtin_amdgcn_readfirstlane(min(PF_ROWS, r1 - t.tok0));
+    t.ch0 = __builtin_amdgcn_readfirstlane(nt * CH_TILE);
+    return t;
+  };
+
+  // ---- global -> LDS loads ----
+  // An operand slice is made of 1 KiB blocks of RPI rows; wavefront w fills
+  // blocks w, w + 4, ... of both operands.  Lane l writes chunk position
+  // l % CPR of block row l / CPR and so reads logical chunk (l % CPR) ^ key(row).
+  const int64_t rowbytes = (int64_t)K * 2;
+  constexpr int JMAX = G::JA > G::JB ? G::JA : G::JB;
+  int voff[JMAX];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int tl = wc * 128 + b * 32 + fi;      // token row within the tile
-    const bool tok_in = tl < tok_rows;
-    const int64_t orow = tok0 + tl;
-    if constexpr (DUAL) {
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = ch0 + wr * 64 + a * 32 + q * 8 + fg * 4;
-          float hv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) hv[r] = swiglu_fast(acc[a][b][q * 4 + r], acc[a + 2][b][q * 4 + r]);
-          if (tok_in && c < N)
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow * N + c) =
-                make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-        }
-    } else {
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = ch0 + wr * 128 + a * 32 + q * 8 + fg * 4;
-          if (tok_in && c < N)
-            *reinterpret_cast<float4*>(static_cast<float*>(out) + orow * N + c) =
-                make_float4(acc[a][b][q * 4 + 0], acc[a][b][q * 4 + 1], acc[a][b][q * 4 + 2],
-                            acc[a][b][q * 4 + 3]);
-        }
-    }
+  for (int j = 0; j < JMAX; ++j) {
+    const int r = (4 * j + wave) * G::RPI + lane / G::CPR;   // row within the operand tile
+    voff[j] = (int)(r * rowbytes) + (((lane % G::CPR) ^ G::key(r)) << 4);
   }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+  const int KT = K / BK;
+  const int n_slices = n_my * KT;
+
+  // Load cursor: slice ls (kt = lkt of tile li) and that tile's descriptors.
+  i32x4_t d_tok, d_w0, d_w1;
+  int li = 0, lkt = 0;
+  auto load_tile = [&]() __attribute__((always_inline)) {
+    if (li < n_my) {
+      const Tile t = tile_of(li);
+      d_tok = make_desc(act + (int64_t)t.tok0 * K, t.tok_rows * rowbytes);
+      d_w0 = make_desc(wa + ((int64_t)t.e * N + t.ch0) * K, (int64_t)(N - t.ch0) * rowbytes);
+      d_w1 = DUAL ? make_desc(wb + ((int64_t)t.e * N + t.ch0) * K, (int64_t)(N - t.ch0) * rowbytes)
+                  : d_w0;
+    }
+  };
+  load_tile();
+  // Load j (0 .. DMA - 1) of the cursor's slice into stage ls % NS: the first
+  // JA weight blocks, then JB token blocks.  Dual: weight rows TA / 2 .. TA - 1
+  // are w3 rows with the row offsets of rows 0 .. TA / 2 - 1 (TA / 2 rows is
+  // a whole number of swizzle periods).  Past the last tile the offset lies
+  // beyond every buffer's range: such loads write zeros without touching
+  // memory, into a stage that is never read again, so every iteration
+  // issues the same loads.
+  auto dma = [&](int ls, int j) __attribute__((always_inline)) {
+    const int soff = li < n_my ? lkt * BK * 2 : 0x7ff00000;
+    const uint32_t sb = lds_base + (uint32_t)((ls % NS) * G::STAGE_BYTES);
+    if (j >= G::JA) {
+      const int q = j - G::JA;
+      dma_to_lds(d_tok, voff[q], soff,
+                 __builtin_amdgcn_readfirstlane(sb + G::OPA_BYTES + (4 * q + wave) * 1024));
+    } else {
+      const bool w3 = DUAL && j >= G::JA / 2;
+      dma_to_lds(w3 ? d_w1 : d_w0, voff[w3 ? j - G::JA / 2 : j], soff,
+                 __builtin_amdgcn_readfirstlane(sb + (4 * j + wave) * 1024));
+    }
+  };
+  auto advance_load = [&]() __attribute__((always_inline)) {
+    if (++lkt == KT) {
+      lkt = 0;
+      ++li;
+      load_tile();
+    }
+  };
+
+  // ---- fragment addressing (v_mfma_f32_32x32x16_bf16: lane (fi, fg) holds
+  //      row fi, k = 8 fg .. 8 fg + 7 of the 16-wide substep) ----
+  const int fi = lane & 31, fg = lane >> 5;
+  int frag_off[G::SUB];
+#pragma unroll
+  for (int s = 0; s < G::SUB; ++s)
+    frag_off[s] = fi * G::ROW_B + (((2 * s + fg) ^ G::key(fi)) << 4);
+  int arow[WA], bfrow[4];
+#pragma unroll
+  for (int a = 0; a < WA; ++a) {
+    if constexpr (DUAL) arow[a] = (a / HA) * (G::TA / 2) + wr * (HA * 32) + (a % HA) * 32;
+    else arow[a] = wr * (WA * 32) + a * 32;
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) bfrow[b] = wc * 128 + b * 32;
+
+  f32x16_t acc[WA][4];
+
+  // fragment f of a substep of slice g: 0 .. WA - 1 weight blocks, then 4 token blocks
+  auto read_frag = [&](int g, int s, int f) __attribute__((always_inline)) -> bf16x8_t {
+    const int off = (g % NS) * G::STAGE_BYTES +
+                    (f < WA ? arow[f] * G::ROW_B : G::OPA_BYTES + bfrow[f - WA] * G::ROW_B) +
+                    frag_off[s];
+    return as_bf16x8(*reinterpret_cast<const uint4*>(&smem[off]));
+  };
+
+  // One substep: 4 WA matrix instructions, weight block a = i / 4 against
+  // token block b = i % 4.  Weight fragments are single-buffered: fa[a] is
+  // reloaded with the next substep's fragment right after its last use
+  // (b == 3); token fragments are double-buffered and the next substep's
+  // are read after the first four instructions.  With `loads`, the
+  // remaining slots carry the loads of the load cursor's slice `ls`
+  // (slot numbering continues across substeps from slot0).  With `reads`,
+  // (gn, sn) is the substep whose fragments are read.  `fresh` starts the
+  // accumulators of a new tile (zero addend).
+  bf16x8_t fa[WA], fb[2][4];
+  constexpr int NI = 4 * WA;
+  constexpr int FREE = (NI - 4) - (NI - 4) / 4;           // load slots per substep
+  auto substep = [&](int cur, int gn, int sn, int slot0, bool loads, int ls, bool reads,
+                     bool fresh) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int a = i >> 2, b = i & 3;
+      const f32x16_t c_in = fresh ? f32x16_t{} : acc[a][b];
+      acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[cur][b], c_in, 0, 0, 0);
+      if (reads && i < 4) fb[cur ^ 1][i] = read_frag(gn, sn, WA + i);
+      if (b == 3) {
+        if (reads) fa[a] = read_frag(gn, sn, a);
+      } else if (i >= 4 && loads) {
+        constexpr int SLOTS = FREE * (G::SUB - 1), PER = (G::DMA + SLOTS - 1) / SLOTS;
+        const int sl = slot0 + (i - 4) - ((i - 4) >> 2);
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+          if (sl * PER + q < G::DMA) dma(ls, sl * PER + q);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Results of the compute cursor's tile: lane = token (fi), registers = channels.
+  // Stores go through a buffer descriptor bounded to the tile's valid rows;
+  // columns past N get an offset beyond it.  Either way the store is dropped
+  // without a branch.
+  auto epilogue = [&](const Tile& t) __attribute__((always_inline)) {
+    constexpr int OB = DUAL ? 2 : 4;            // output element bytes (bf16 h, fp32 y)
+    const i32x4_t ro = make_desc(static_cast<uint8_t*>(out) + (int64_t)t.tok0 * N * OB,
+                                 (int64_t)t.tok_rows * N * OB);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int tl = wc * 128 + b * 32 + fi;      // token row within the tile
+      const int row_off = tl * N * OB;
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int a = 0; a < HA; ++a)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = t.ch0 + wr * (HA * 32) + a * 32 + q * 8 + fg * 4;
+            float hv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              hv[r] = swiglu_fast(acc[a][b][q * 4 + r], acc[a + HA][b][q * 4 + r]);
+            store_b64(ro, c < N ? row_off + c * OB : 0x7fffffff, pack_bf16x2(hv[0], hv[1]),
+                      pack_bf16x2(hv[2], hv[3]));
+            __builtin_amdgcn_sched_barrier(0);   // one block at a time: few live registers
+          }
+      } else {
+#pragma unroll
+        for (int a = 0; a < WA; ++a)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = t.ch0 + wr * (WA * 32) + a * 32 + q * 8 + fg * 4;
+            const u32x4_t v = {__float_as_uint(acc[a][b][q * 4 + 0]), __float_as_uint(acc[a][b][q * 4 + 1]),
+                               __float_as_uint(acc[a][b][q * 4 + 2]), __float_as_uint(acc[a][b][q * 4 + 3])};
+            store_b128(ro, c < N ? row_off + c * OB : 0x7fffffff, v);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+    }
+  };
+
+  // Pipeline.  Slice g of the stream lives in stage g % NS.  Iteration g runs
+  // SUB substeps.  All but the last carry the loads of slice g + NS - 1,
+  // which go to the stage that slice g - 1 used (every wavefront finished
+  // reading it before the previous barrier).  Before the last substep: wait
+  // for this wavefront's loads of slice g + 1 (the loads of later slices
+  // stay in flight), finish its LDS reads, barrier -- slice g + 1 is
+  // complete in LDS and slice g is no longer read; the last substep then
+  // reads substep 0 of slice g + 1, except in a tile's last iteration: the
+  // results are stored first and the next tile's fragments read after.
+  // Pending stores share the vector-memory counter with the loads; loads
+  // complete in order among themselves, so they only make the wait stricter.
+  // Instruction order is fixed with scheduling barriers.
+  auto iteration = [&](int g, bool first, bool last) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < G::SUB - 1; ++s)
+      substep(s & 1, g, s + 1, s * FREE, true, g + NS - 1, true, first && s == 0);
+    advance_load();
+    wait_vmcnt<G::DMA * (NS - 2)>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    substep(1, g + 1, 0, 0, false, 0, !last, false);
+  };
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) {
+#pragma unroll
+    for (int j = 0; j < G::DMA; ++j) dma(s, j);
+    advance_load();
+  }
+  wait_vmcnt<G::DMA * (NS - 2)>();
+  __builtin_amdgcn_s_barrier();
+
+  int g = 0;                      // stream index of the slice being multiplied
+  for (int ci = 0; ci < n_my; ++ci) {
+#pragma unroll
+    for (int f = 0; f < WA; ++f) fa[f] = read_frag(g, 0, f);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) fb[0][f] = read_frag(g, 0, WA + f);
+    iteration(g++, true, false);                 // KT >= 2: K is a multiple of 64
+    for (int kt = 1; kt < KT - 1; ++kt) iteration(g++, false, false);
+    iteration(g++, false, true);
+    epilogue(tile_of(ci));
+  }
+  wait_vmcnt<0>();   // the zero loads past the end land before the workgroup's LDS is released
 }
+
+// K slice, LDS ring depth and weight blocks per wavefront of the prefill kernel.
+constexpr int kPrefillBK = 32, kPrefillStages = 4, kPrefillWA = 4;
 
 template <bool DUAL>
 hipError_t launch_prefill(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                           const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
                           hipStream_t st) {
-  constexpr int CH_TILE = DUAL ? 128 : 256;
+  constexpr int CH_TILE = (DUAL ? 32 : 64) * kPrefillWA;
   const int n_tiles = (N + CH_TILE - 1) / CH_TILE;
-  const int64_t grid = max_token_tiles(s, PF_ROWS) * n_tiles;
-  const int64_t padded = (grid + 7) / 8 * 8;
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_gemm_bf16_prefill<DUAL>, dim3((unsigned)padded), dim3(PF_THREADS),
-                     0, st, act, offsets, s.n_experts, wa, wb, N, K, out, n_tiles, (int)padded);
+  const int64_t max_tiles = max_token_tiles(s, PF_ROWS) * n_tiles;
+  if (max_tiles <= 0) return hipSuccess;
+  // persistent grid: at most one workgroup per CU, a multiple of the 8 XCDs
+  const int64_t cus = device_cu_count();
+  const int64_t grid = std::max<int64_t>(8, std::min<int64_t>((max_tiles + 7) / 8 * 8, cus / 8 * 8));
+  hipLaunchKernelGGL((grouped_gemm_bf16_prefill<DUAL, kPrefillBK, kPrefillStages, kPrefillWA>),
+                     dim3((unsigned)grid), dim3(PF_THREADS), 0, st, act, offsets, s.n_experts, wa,
+                     wb, N, K, out, n_tiles);
   return hipGetLastError();
 }
 

@@ -62,6 +62,12 @@ hipError_t launch_down_bf16(const moe_shape_t& s, const uint16_t* h, const int32
 // Whether the fp8 matrix-core path is built in.
 constexpr bool kFp8Available = true;
 
+// Largest n_experts the library accepts.
+constexpr int kMaxExperts = 64;
+
+// Compute units of the current device (queried once per device).
+int device_cu_count();
+
 // fp8 paths (e4m3 weights with per-channel fp32 scales, block-scaled e4m3 activations).
 hipError_t launch_gate_up_fp8(const moe_shape_t& s, const uint8_t* x_perm, const uint8_t* x_scale,
                               const int32_t* offsets, const uint8_t* w1, const uint8_t* w3,
