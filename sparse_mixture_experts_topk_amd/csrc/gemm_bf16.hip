@@ -30,6 +30,7 @@
 // copy of the weight tile.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "lds_stream.hpp"
 
 namespace moe {
 
@@ -39,68 +40,8 @@ hipError_t launch_decode_bf16(const moe_shape_t& s, bool dual, const uint16_t* a
 
 namespace {
 
-// silu(g) * u for a bf16 result: hardware exp2 and reciprocal (about 1 ulp
-// in fp32, far below the bf16 rounding that follows).
-__device__ __forceinline__ float swiglu_fast(float g, float u) {
-  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
-  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
-}
-
-constexpr int kBufferFlags = 0x00020000;   // raw buffer, 32-bit data format
-
 constexpr int PF_ROWS = 256;         // rows of each LDS operand tile
 constexpr int PF_THREADS = 256;
-
-typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor in scalar registers (the form the LDS-DMA load takes).
-__device__ __forceinline__ i32x4_t make_desc(const void* base, int64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
-  i32x4_t d;
-  d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  d.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));   // stride 0
-  d.z = __builtin_amdgcn_readfirstlane(n);
-  d.w = kBufferFlags;
-  return d;
-}
-
-// Wavefront-wide load of 16 bytes per lane from a buffer straight into LDS:
-// lane l's bytes land at lds_addr + 16 l, so one instruction fills 1 KiB.
-// Offsets past the buffer's range load zeros.  The load is counted by
-// vmcnt like any vector memory read; it is written as assembly because the
-// compiler, unable to tell which LDS bytes such a load writes, would wait
-// for it to finish before every LDS read, including reads of other stages.
-// M0 (the LDS address) is declared clobbered; the kernels here use it for nothing else.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_to_lds(i32x4_t desc, int voff, int soff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds_addr), "v"(voff), "s"(desc), "s"(soff) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Buffer stores through a descriptor held in scalar registers (assembly, so
-// the descriptor cannot be placed in vector registers and force a per-lane
-// loop).  Offsets past the descriptor's range drop the store.  The trailing
-// wait state covers a vector-ALU write of the data registers right after a
-// store of more than 8 bytes.
-__device__ __forceinline__ void store_b64(i32x4_t desc, int voff, uint32_t lo, uint32_t hi) {
-  asm volatile("buffer_store_dwordx2 %0, %1, %2, 0 offen\n\ts_nop 0"
-               :: "v"(u32x2_t{lo, hi}), "v"(voff), "s"(desc) : "memory");
-}
-__device__ __forceinline__ void store_b128(i32x4_t desc, int voff, u32x4_t v) {
-  asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 1"
-               :: "v"(v), "v"(voff), "s"(desc) : "memory");
-}
-
-// Wait until at most n vector-memory operations of this wavefront are pending.
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | 0x0f70 | (n & 15));
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 // Geometry of one K slice of BK elements: LDS rows of BK * 2 bytes made of
 // CPR 16-byte chunks.  Chunk c of row r sits at chunk position c ^ key(r),

@@ -19,14 +19,10 @@
 // is needed.  The token operand (a few rows, L2-resident) is read directly.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "lds_stream.hpp"
 
 namespace moe {
 namespace {
-
-__device__ __forceinline__ float swiglu_fast(float g, float u) {
-  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
-  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
-}
 
 constexpr int kWavesPerBlock = 4;
 
