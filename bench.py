@@ -35,6 +35,8 @@ DEFAULTS = {"decode_bf16": (200, 20), "prefill_bf16": (20, 3), "skewed_capacity_
             "longctx_fp8": (10, 3), "tiny_fp32": (200, 20)}
 KERNEL_SOURCES = ("sparse_mixture_experts_topk_amd/csrc/gemm_bf16.hip",
                   "sparse_mixture_experts_topk_amd/csrc/gemm_bf16_decode.hip",
+                  "sparse_mixture_experts_topk_amd/csrc/lds_stream.hpp",
+                  "sparse_mixture_experts_topk_amd/csrc/device_common.hpp",
                   "sparse_mixture_experts_topk_amd/csrc/gemm_fp8.hip",
                   "sparse_mixture_experts_topk_amd/csrc/gemm_f32.hip")
 
@@ -169,7 +171,7 @@ def main():
         if timed:
             ev1[i].record(stream)
         moe.moe_expert_gemm_down(shape, st["h"], st["h_scale"], st["expert_offsets"], d.w2,
-                                 d.w2_scale, st["y_perm"], None, stream)
+                                 d.w2_scale, st["y_perm"], st["down_ws"], stream)
         moe.moe_combine(shape, st["y_perm"], st["slot_to_row"], st["topk_weights"], st["y"], stream)
 
     for i in range(warmup):

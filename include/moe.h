@@ -159,7 +159,15 @@ moe_status_t moe_expert_gemm_gate_up(const moe_shape_t* shape, const void* x_per
  *   expert_offsets [E+1] int32
  *   w2             [E, d, F] weight dtype; w2_scale [E, d] fp32 (fp8 only)
  *   y_perm         [T*2, d] fp32 out
- * Workspace: moe_workspace_bytes(MOE_CALL_DOWN). */
+ * Workspace: moe_workspace_bytes(MOE_CALL_DOWN) bytes, 16-byte aligned, device
+ * memory owned by the caller (0 for shapes that need none; then it may be
+ * NULL).  bf16 shapes with more than 64 rows per expert use it for fp32
+ * partial tiles: the tiles left over after the last full round of the
+ * persistent launch are split along K across workgroups and summed by a
+ * second kernel in K order, so results do not depend on timing.  Its
+ * contents need no initialisation and are garbage afterwards.  Too small or
+ * NULL when needed -> MOE_ERR_WORKSPACE.  Two calls that share a workspace
+ * must not run concurrently. */
 moe_status_t moe_expert_gemm_down(const moe_shape_t* shape, const void* h, const uint8_t* h_scale,
                                   const int32_t* expert_offsets, const void* w2,
                                   const float* w2_scale, float* y_perm, void* workspace,

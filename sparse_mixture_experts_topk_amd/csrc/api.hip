@@ -43,13 +43,13 @@ hipError_t launch_gate_up(const moe_shape_t& s, const void* x_perm, const uint8_
 
 hipError_t launch_down(const moe_shape_t& s, const void* h, const uint8_t* h_scale,
                        const int32_t* offsets, const void* w2, const float* w2_scale,
-                       float* y_perm, hipStream_t st) {
+                       float* y_perm, void* workspace, hipStream_t st) {
   if (s.w_dtype == MOE_F32)
     return launch_down_f32(s, static_cast<const float*>(h), offsets,
                            static_cast<const float*>(w2), y_perm, st);
   if (s.w_dtype == MOE_BF16)
     return launch_down_bf16(s, static_cast<const uint16_t*>(h), offsets,
-                            static_cast<const uint16_t*>(w2), y_perm, st);
+                            static_cast<const uint16_t*>(w2), y_perm, workspace, st);
   return launch_down_fp8(s, static_cast<const uint8_t*>(h), h_scale, offsets,
                          static_cast<const uint8_t*>(w2), w2_scale, y_perm, st);
 }
@@ -112,8 +112,14 @@ moe_status_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 // Workspace layout of moe_forward (each region 256-byte aligned).
 struct ForwardLayout {
   size_t ids, weights, counts, offsets, perm_src, slot_to_row, drop, x_perm, x_scale, h, h_scale,
-      y_perm, total;
+      y_perm, down_ws, total;
 };
+
+// Workspace of moe_expert_gemm_down: partial tiles of the split tail work
+// (bf16 many-rows path only).
+size_t down_workspace_bytes(const moe_shape_t& s) {
+  return s.w_dtype == MOE_BF16 ? moe::down_workspace_bytes_bf16(s) : 0;
+}
 
 ForwardLayout forward_layout(const moe_shape_t& s) {
   ForwardLayout L{};
@@ -133,6 +139,7 @@ ForwardLayout forward_layout(const moe_shape_t& s) {
   L.h = o;           o += align_up(A * s.d_ff * eb);
   L.h_scale = o;     o += fp8 ? align_up(A * (s.d_ff / 32)) : 0;
   L.y_perm = o;      o += align_up(A * s.d_model * 4);
+  L.down_ws = o;     o += align_up(down_workspace_bytes(s));
   L.total = o;
   return L;
 }
@@ -164,7 +171,7 @@ moe_status_t moe_workspace_bytes(const moe_shape_t* s, moe_call_t call, size_t* 
   switch (call) {
     case MOE_CALL_PERMUTE: *bytes = 0; return MOE_OK;
     case MOE_CALL_GATE_UP: *bytes = 0; return MOE_OK;
-    case MOE_CALL_DOWN: *bytes = 0; return MOE_OK;
+    case MOE_CALL_DOWN: *bytes = down_workspace_bytes(*s); return MOE_OK;
     case MOE_CALL_FORWARD: *bytes = forward_layout(*s).total; return MOE_OK;
   }
   return MOE_ERR_INVALID_ARG;
@@ -237,16 +244,17 @@ moe_status_t moe_expert_gemm_down(const moe_shape_t* s, const void* h, const uin
                                   const int32_t* expert_offsets, const void* w2,
                                   const float* w2_scale, float* y_perm, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   moe_status_t v = validate_shape(s);
   if (v != MOE_OK) return v;
   if (s->T == 0) return MOE_OK;
   if ((v = check_ptrs({h, expert_offsets, w2, y_perm}, {})) != MOE_OK) return v;
   if (s->w_dtype == MOE_FP8_E4M3 && (h_scale == nullptr || w2_scale == nullptr))
     return MOE_ERR_INVALID_ARG;
+  const size_t need = down_workspace_bytes(*s);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_down(*s, h, h_scale, expert_offsets, w2, w2_scale, y_perm,
-                                   static_cast<hipStream_t>(stream)));
+                                   need > 0 ? workspace : nullptr, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_combine(const moe_shape_t* s, const float* y_perm, const int32_t* slot_to_row,
@@ -308,7 +316,9 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_gate
   if (e == hipSuccess) e = moe::launch_permute_scatter(*s, x, offsets, perm_src, x_perm, x_scale, st);
   if (e == hipSuccess)
     e = moe::launch_gate_up(*s, x_perm, x_scale, offsets, w1, w3, w1_scale, w3_scale, h, h_scale, st);
-  if (e == hipSuccess) e = moe::launch_down(*s, h, h_scale, offsets, w2, w2_scale, y_perm, st);
+  void* down_ws = down_workspace_bytes(*s) > 0 ? at<void>(workspace, L.down_ws) : nullptr;
+  if (e == hipSuccess)
+    e = moe::launch_down(*s, h, h_scale, offsets, w2, w2_scale, y_perm, down_ws, st);
   if (e == hipSuccess) e = moe::launch_combine(*s, y_perm, slot_to_row, gw, y, st);
   return from_hip(e);
 }

@@ -65,6 +65,41 @@ struct TileGeom {
   __device__ static __forceinline__ int key(int row) { return (row / (16 / CPR)) & (CPR - 1); }
 };
 
+// Work split of a persistent launch.  The expert-major tile list (token
+// tiles fastest) is cut into 8 contiguous shares, one per XCD; the `slots`
+// workgroups of XCD x (blockIdx = slot * 8 + x) take its full tiles in
+// rounds: tiles share_begin + slot + i * slots, i < R.  The share's last
+// `tail` < slots tiles are either taken whole by the first `tail` slots
+// (data-parallel), or (split) cut along K into `slots` near-equal runs of P
+// slices, one per workgroup, each covering parts of at most two tiles; the
+// parts are written as fp32 partial tiles and summed by a second kernel in
+// K order, which keeps the result independent of timing.
+struct TileSplit {
+  int share_begin, R, tail, P;
+
+  __device__ static int total_tiles(const int32_t* offs, int E, int n_tiles) {
+    int total = 0;
+    for (int e = 0; e < E; ++e)
+      total += (__builtin_amdgcn_readfirstlane(offs[e + 1]) -
+                __builtin_amdgcn_readfirstlane(offs[e]) + PF_ROWS - 1) / PF_ROWS;
+    return total * n_tiles;
+  }
+  __device__ static TileSplit of(int total, int xcd, int slots, int KT) {
+    TileSplit t;
+    const int per_xcd = (total + 7) >> 3;
+    t.share_begin = xcd * per_xcd;
+    const int len = max(0, min(t.share_begin + per_xcd, total) - t.share_begin);
+    t.R = len / slots;
+    t.tail = len - t.R * slots;
+    t.P = (t.tail * KT + slots - 1) / slots;
+    return t;
+  }
+};
+
+// Partial tiles of the split work: 256 x 256 fp32 each, two per workgroup.
+constexpr int kPartialTileBytes = PF_ROWS * 256 * 4;
+constexpr int kMaxPersistentGroups = 256;
+
 // Tile: TA weight rows x 256 tokens.  The dual (gate/up) kernel's weight rows
 // are TA / 2 rows of w1 followed by the same TA / 2 rows of w3, so each
 // wavefront holds matching w1 and w3 accumulators and forms silu(g) * u in
@@ -78,13 +113,14 @@ struct TileGeom {
 // slices of all its tiles form one stream through the LDS ring, so the
 // first slices of the next tile load while the current one finishes and
 // stores its results.
-template <bool DUAL, int BK, int NS, int WA>
+template <bool DUAL, int BK, int NS, int WA, bool SPLIT>
 __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
     const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, int N, int K,
-    void* __restrict__ out, int n_tiles) {
+    void* __restrict__ out, float* __restrict__ partials, int n_tiles) {
   using G = TileGeom<BK, WA>;
   static_assert(G::SUB % 2 == 0 && NS >= 2 && WA % 2 == 0, "pipeline shape");
+  static_assert(!SPLIT || (!DUAL && G::TA == 256), "split runs: single 256 x 256 fp32 tiles");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * G::STAGE_BYTES];
   __shared__ int32_t offs[kMaxExperts + 1];
 
@@ -99,28 +135,40 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
   // its own loads).
   if (tid <= E) offs[tid] = offsets[tid];
   __syncthreads();
-  int total = 0;
-  for (int e = 0; e < E; ++e)
-    total += (__builtin_amdgcn_readfirstlane(offs[e + 1]) - __builtin_amdgcn_readfirstlane(offs[e]) +
-              PF_ROWS - 1) / PF_ROWS;
-  total *= n_tiles;
+  const int KT = K / BK;
   const int slots = gridDim.x >> 3;
-  const int per_xcd = (total + 7) >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int t_first = xcd * per_xcd + slot;
-  const int t_end = min((xcd + 1) * per_xcd, total);
-  const int n_my = t_first < t_end ? (t_end - t_first + slots - 1) / slots : 0;
-  if (n_my == 0) return;
+  const TileSplit sp = TileSplit::of(TileSplit::total_tiles(offs, E, n_tiles), xcd, slots, KT);
+  // this workgroup's items: whole tiles, then (split) up to two K-runs of tail tiles
+  const int n_whole = sp.R + ((!SPLIT && slot < sp.tail) ? 1 : 0);
+  const int run0 = slot * sp.P, run1 = min(run0 + sp.P, sp.tail * KT);
+  const int n_runs = (SPLIT && run0 < run1) ? (run1 - 1) / KT - run0 / KT + 1 : 0;
+  const int n_items = n_whole + n_runs;
+  if (n_items == 0) return;
 
-  struct Tile { int e, tok0, tok_rows, ch0; };
+  // Item i: its tile, K-slice range [kb, ke) and partial slot (-1: whole tile).
+  struct Tile { int e, tok0, tok_rows, ch0, kb, ke, part; };
   auto tile_of = [&](int i) __attribute__((always_inline)) -> Tile {
+    int t_idx, kb = 0, ke = KT, part = -1;
+    if (i < n_whole) {
+      t_idx = sp.share_begin + slot + i * slots;
+    } else {
+      const int j = run0 / KT + (i - n_whole);        // tail tile
+      t_idx = sp.share_begin + sp.R * slots + j;
+      kb = max(run0, j * KT) - j * KT;
+      ke = min(run1, (j + 1) * KT) - j * KT;
+      part = (int)blockIdx.x * 2 + (i - n_whole);
+    }
     int e, r0, r1, mt, nt;
-    locate_tile(offs, E, PF_ROWS, n_tiles, t_first + i * slots, e, r0, r1, mt, nt);
+    locate_tile(offs, E, PF_ROWS, n_tiles, t_idx, e, r0, r1, mt, nt);
     Tile t;   // uniform values, kept in scalar registers
     t.e = __builtin_amdgcn_readfirstlane(e);
     t.tok0 = __builtin_amdgcn_readfirstlane(r0 + mt * PF_ROWS);
     t.tok_rows = __builtin_amdgcn_readfirstlane(min(PF_ROWS, r1 - t.tok0));
     t.ch0 = __builtin_amdgcn_readfirstlane(nt * CH_TILE);
+    t.kb = __builtin_amdgcn_readfirstlane(kb);
+    t.ke = __builtin_amdgcn_readfirstlane(ke);
+    t.part = __builtin_amdgcn_readfirstlane(part);
     return t;
   };
 
@@ -137,15 +185,15 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
     voff[j] = (int)(r * rowbytes) + (((lane % G::CPR) ^ G::key(r)) << 4);
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
-  const int KT = K / BK;
-  const int n_slices = n_my * KT;
 
-  // Load cursor: slice ls (kt = lkt of tile li) and that tile's descriptors.
+  // Load cursor: slice lkt (of K) of item li, the item's end and its descriptors.
   i32x4_t d_tok, d_w0, d_w1;
-  int li = 0, lkt = 0;
+  int li = 0, lkt = 0, lke = 0;
   auto load_tile = [&]() __attribute__((always_inline)) {
-    if (li < n_my) {
+    if (li < n_items) {
       const Tile t = tile_of(li);
+      lkt = t.kb;
+      lke = t.ke;
       d_tok = make_desc(act + (int64_t)t.tok0 * K, t.tok_rows * rowbytes);
       d_w0 = make_desc(wa + ((int64_t)t.e * N + t.ch0) * K, (int64_t)(N - t.ch0) * rowbytes);
       d_w1 = DUAL ? make_desc(wb + ((int64_t)t.e * N + t.ch0) * K, (int64_t)(N - t.ch0) * rowbytes)
@@ -161,7 +209,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
   // memory, into a stage that is never read again, so every iteration
   // issues the same loads.
   auto dma = [&](int ls, int j) __attribute__((always_inline)) {
-    const int soff = li < n_my ? lkt * BK * 2 : 0x7ff00000;
+    const int soff = li < n_items ? lkt * BK * 2 : 0x7ff00000;
     const uint32_t sb = lds_base + (uint32_t)((ls % NS) * G::STAGE_BYTES);
     if (j >= G::JA) {
       const int q = j - G::JA;
@@ -174,8 +222,7 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
     }
   };
   auto advance_load = [&]() __attribute__((always_inline)) {
-    if (++lkt == KT) {
-      lkt = 0;
+    if (++lkt == lke) {
       ++li;
       load_tile();
     }
@@ -245,6 +292,11 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
   // columns past N get an offset beyond it.  Either way the store is dropped
   // without a branch.
   auto epilogue = [&](const Tile& t) __attribute__((always_inline)) {
+    // Lane coordinates made opaque here, so that the store offsets are formed
+    // per tile instead of being hoisted out of the tile loop (where they would
+    // occupy registers through the whole K loop).
+    int fi = lane & 31, fg = lane >> 5;
+    asm volatile("" : "+v"(fi), "+v"(fg));
     constexpr int OB = DUAL ? 2 : 4;            // output element bytes (bf16 h, fp32 y)
     const i32x4_t ro = make_desc(static_cast<uint8_t*>(out) + (int64_t)t.tok0 * N * OB,
                                  (int64_t)t.tok_rows * N * OB);
@@ -267,14 +319,20 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
             __builtin_amdgcn_sched_barrier(0);   // one block at a time: few live registers
           }
       } else {
+        // a K-run of a split tile goes whole to its partial slot ([token][channel], 256 x 256)
+        const bool part = SPLIT && t.part >= 0;
+        const i32x4_t dst = part ? make_desc(partials + (int64_t)t.part * (kPartialTileBytes / 4),
+                                             kPartialTileBytes)
+                                 : ro;
 #pragma unroll
         for (int a = 0; a < WA; ++a)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int c = t.ch0 + wr * (WA * 32) + a * 32 + q * 8 + fg * 4;
+            const int cl = wr * (WA * 32) + a * 32 + q * 8 + fg * 4;   // channel within the tile
+            const int c = t.ch0 + cl;
             const u32x4_t v = {__float_as_uint(acc[a][b][q * 4 + 0]), __float_as_uint(acc[a][b][q * 4 + 1]),
                                __float_as_uint(acc[a][b][q * 4 + 2]), __float_as_uint(acc[a][b][q * 4 + 3])};
-            store_b128(ro, c < N ? row_off + c * OB : 0x7fffffff, v);
+            store_b128(dst, part ? (tl * 256 + cl) * 4 : (c < N ? row_off + c * OB : 0x7fffffff), v);
             __builtin_amdgcn_sched_barrier(0);
           }
       }
@@ -316,36 +374,101 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
   __builtin_amdgcn_s_barrier();
 
   int g = 0;                      // stream index of the slice being multiplied
-  for (int ci = 0; ci < n_my; ++ci) {
+  for (int ci = 0; ci < n_items; ++ci) {
+    const Tile t = tile_of(ci);
+    const int nk = t.ke - t.kb;                  // >= 1
 #pragma unroll
     for (int f = 0; f < WA; ++f) fa[f] = read_frag(g, 0, f);
 #pragma unroll
     for (int f = 0; f < 4; ++f) fb[0][f] = read_frag(g, 0, WA + f);
-    iteration(g++, true, false);                 // KT >= 2: K is a multiple of 64
-    for (int kt = 1; kt < KT - 1; ++kt) iteration(g++, false, false);
-    iteration(g++, false, true);
-    epilogue(tile_of(ci));
+    if (nk == 1) {
+      iteration(g++, true, true);
+    } else {
+      iteration(g++, true, false);
+      for (int kt = 1; kt < nk - 1; ++kt) iteration(g++, false, false);
+      iteration(g++, false, true);
+    }
+    epilogue(t);
   }
   wait_vmcnt<0>();   // the zero loads past the end land before the workgroup's LDS is released
+}
+
+// Sum of the K-runs of each split tail tile, in K order, into y_perm.  One
+// workgroup per (XCD, tail tile, group of 16 rows): lane l covers row
+// 16 g + l / 16 and channels 4 (l % 16) + 64 c, c = 0..3, so every lane has
+// four independent 16-byte sums in flight.
+constexpr int kFixupRowGroups = PF_ROWS / 16;
+
+__global__ __launch_bounds__(256) void split_fixup_kernel(const int32_t* __restrict__ offsets, int E,
+                                                          int N, int K, int BK, int n_tiles, int slots,
+                                                          const float* __restrict__ partials,
+                                                          float* __restrict__ y) {
+  const int rg = blockIdx.x % kFixupRowGroups;
+  const int xcd = (blockIdx.x / kFixupRowGroups) & 7, j = blockIdx.x / kFixupRowGroups >> 3;
+  const int KT = K / BK;
+  const TileSplit sp = TileSplit::of(TileSplit::total_tiles(offsets, E, n_tiles), xcd, slots, KT);
+  if (j >= sp.tail) return;
+  int e, r0, r1, mt, nt;
+  locate_tile(offsets, E, PF_ROWS, n_tiles, sp.share_begin + sp.R * slots + j, e, r0, r1, mt, nt);
+  const int tok0 = r0 + mt * PF_ROWS, tok_rows = min(PF_ROWS, r1 - tok0), ch0 = nt * 256;
+  const int r = rg * 16 + (threadIdx.x >> 4);
+  if (r >= tok_rows) return;
+  const int s_lo = (j * KT) / sp.P, s_hi = min(((j + 1) * KT - 1) / sp.P, slots - 1);
+  float4 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = s_lo; s <= s_hi; ++s) {
+    const int part = (s * 8 + xcd) * 2 + (j - (s * sp.P) / KT);
+    const float* src = partials + (int64_t)part * (kPartialTileBytes / 4) + r * 256 + (threadIdx.x & 15) * 4;
+    float4 p[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) p[c] = *reinterpret_cast<const float4*>(src + 64 * c);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      acc[c].x += p[c].x; acc[c].y += p[c].y; acc[c].z += p[c].z; acc[c].w += p[c].w;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int col = ch0 + (threadIdx.x & 15) * 4 + 64 * c;
+    if (col < N) *reinterpret_cast<float4*>(y + (int64_t)(tok0 + r) * N + col) = acc[c];
+  }
 }
 
 // K slice, LDS ring depth and weight blocks per wavefront of the prefill kernel.
 constexpr int kPrefillBK = 32, kPrefillStages = 4, kPrefillWA = 4;
 
+// Workgroups of the persistent launch: one per CU, at most kMaxPersistentGroups,
+// a multiple of the 8 XCDs, and no more than there are tiles.
+int64_t persistent_grid(int64_t max_tiles) {
+  const int64_t cus = std::min<int64_t>(device_cu_count(), kMaxPersistentGroups);
+  return std::max<int64_t>(8, std::min<int64_t>((max_tiles + 7) / 8 * 8, cus / 8 * 8));
+}
+
 template <bool DUAL>
 hipError_t launch_prefill(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                           const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
-                          hipStream_t st) {
+                          float* partials, hipStream_t st) {
   constexpr int CH_TILE = (DUAL ? 32 : 64) * kPrefillWA;
   const int n_tiles = (N + CH_TILE - 1) / CH_TILE;
   const int64_t max_tiles = max_token_tiles(s, PF_ROWS) * n_tiles;
   if (max_tiles <= 0) return hipSuccess;
-  // persistent grid: at most one workgroup per CU, a multiple of the 8 XCDs
-  const int64_t cus = device_cu_count();
-  const int64_t grid = std::max<int64_t>(8, std::min<int64_t>((max_tiles + 7) / 8 * 8, cus / 8 * 8));
-  hipLaunchKernelGGL((grouped_gemm_bf16_prefill<DUAL, kPrefillBK, kPrefillStages, kPrefillWA>),
+  const int64_t grid = persistent_grid(max_tiles);
+  const bool split = !DUAL && partials != nullptr;
+  if (split) {
+    hipLaunchKernelGGL((grouped_gemm_bf16_prefill<false, kPrefillBK, kPrefillStages, kPrefillWA, true>),
+                       dim3((unsigned)grid), dim3(PF_THREADS), 0, st, act, offsets, s.n_experts, wa,
+                       wb, N, K, out, partials, n_tiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(split_fixup_kernel, dim3((unsigned)(grid * kFixupRowGroups)), dim3(256), 0, st, offsets,
+                       s.n_experts, N, K, kPrefillBK, n_tiles, (int)(grid / 8), partials,
+                       static_cast<float*>(out));
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((grouped_gemm_bf16_prefill<DUAL, kPrefillBK, kPrefillStages, kPrefillWA, false>),
                      dim3((unsigned)grid), dim3(PF_THREADS), 0, st, act, offsets, s.n_experts, wa,
-                     wb, N, K, out, n_tiles);
+                     wb, N, K, out, nullptr, n_tiles);
   return hipGetLastError();
 }
 
@@ -359,14 +482,20 @@ hipError_t launch_gate_up_bf16(const moe_shape_t& s, const uint16_t* x_perm,
                                uint16_t* h, hipStream_t st) {
   if (max_rows_per_expert(s) <= kDecodeMaxRows)
     return launch_decode_bf16(s, true, x_perm, offsets, w1, w3, s.d_ff, s.d_model, h, st);
-  return launch_prefill<true>(s, x_perm, offsets, w1, w3, s.d_ff, s.d_model, h, st);
+  return launch_prefill<true>(s, x_perm, offsets, w1, w3, s.d_ff, s.d_model, h, nullptr, st);
 }
 
 hipError_t launch_down_bf16(const moe_shape_t& s, const uint16_t* h, const int32_t* offsets,
-                            const uint16_t* w2, float* y_perm, hipStream_t st) {
+                            const uint16_t* w2, float* y_perm, void* workspace, hipStream_t st) {
   if (max_rows_per_expert(s) <= kDecodeMaxRows)
     return launch_decode_bf16(s, false, h, offsets, w2, nullptr, s.d_model, s.d_ff, y_perm, st);
-  return launch_prefill<false>(s, h, offsets, w2, nullptr, s.d_model, s.d_ff, y_perm, st);
+  return launch_prefill<false>(s, h, offsets, w2, nullptr, s.d_model, s.d_ff, y_perm,
+                               static_cast<float*>(workspace), st);
+}
+
+size_t down_workspace_bytes_bf16(const moe_shape_t& s) {
+  if (max_rows_per_expert(s) <= kDecodeMaxRows) return 0;
+  return (size_t)kMaxPersistentGroups * 2 * kPartialTileBytes;
 }
 
 }  // namespace moe

@@ -38,7 +38,7 @@ hipError_t launch_gate_up(const moe_shape_t& s, const void* x_perm, const uint8_
                           hipStream_t st);
 hipError_t launch_down(const moe_shape_t& s, const void* h, const uint8_t* h_scale,
                        const int32_t* offsets, const void* w2, const float* w2_scale,
-                       float* y_perm, hipStream_t st);
+                       float* y_perm, void* workspace, hipStream_t st);
 
 // Fill n bytes with v (a kernel, so that the call can sit inside a captured graph).
 hipError_t launch_fill_u8(uint8_t* p, int64_t n, uint8_t v, hipStream_t st);
@@ -56,8 +56,11 @@ hipError_t launch_down_f32(const moe_shape_t& s, const float* h, const int32_t* 
 hipError_t launch_gate_up_bf16(const moe_shape_t& s, const uint16_t* x_perm,
                                const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                                uint16_t* h, hipStream_t st);
+// workspace: down_workspace_bytes_bf16(s) bytes (partial tiles of the split
+// tail work), or NULL for the data-parallel schedule only.
 hipError_t launch_down_bf16(const moe_shape_t& s, const uint16_t* h, const int32_t* offsets,
-                            const uint16_t* w2, float* y_perm, hipStream_t st);
+                            const uint16_t* w2, float* y_perm, void* workspace, hipStream_t st);
+size_t down_workspace_bytes_bf16(const moe_shape_t& s);
 
 // Whether the fp8 matrix-core path is built in.
 constexpr bool kFp8Available = true;

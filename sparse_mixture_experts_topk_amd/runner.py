@@ -12,7 +12,8 @@ from typing import Optional
 import torch
 
 from . import (moe_combine, moe_expert_gemm_down, moe_expert_gemm_gate_up, moe_forward,
-               moe_permute, moe_route_topk, moe_workspace_bytes, shape_of, MOE_CALL_FORWARD)
+               moe_permute, moe_route_topk, moe_workspace_bytes, shape_of, MOE_CALL_DOWN,
+               MOE_CALL_FORWARD)
 
 
 def _dev(t: Optional[torch.Tensor], device) -> Optional[torch.Tensor]:
@@ -121,8 +122,10 @@ def staged(di: DeviceInputs, stream=None) -> dict:
     moe_expert_gemm_gate_up(shape, o["x_perm"], o["x_perm_scale"], o["expert_offsets"], di.w1,
                             di.w3, di.w1_scale, di.w3_scale, o["h"], o["h_scale"], None, stream)
     o["y_perm"] = torch.empty(A, d, dtype=torch.float32, device=dev)
+    down_ws = moe_workspace_bytes(shape, MOE_CALL_DOWN)
+    o["down_ws"] = torch.empty(down_ws, dtype=torch.uint8, device=dev) if down_ws else None
     moe_expert_gemm_down(shape, o["h"], o["h_scale"], o["expert_offsets"], di.w2, di.w2_scale,
-                         o["y_perm"], None, stream)
+                         o["y_perm"], o["down_ws"], stream)
     o["y"] = torch.empty(T, d, dtype=_act_dtype(cfg), device=dev)
     moe_combine(shape, o["y_perm"], o["slot_to_row"], o["topk_weights"], o["y"], stream)
     return o

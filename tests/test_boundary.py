@@ -83,6 +83,29 @@ def test_workspace_sizes():
     assert _status("moe_workspace_bytes", ctypes.byref(s), 0, None) == 1
 
 
+def test_down_workspace_size_and_requirement():
+    # many rows per expert (bf16): fp32 partial tiles for the split tail work
+    big = S(T=8192)
+    need = moe.moe_workspace_bytes(big, moe.MOE_CALL_DOWN)
+    assert need == 256 * 2 * 256 * 256 * 4
+    assert moe.moe_workspace_bytes(big, moe.MOE_CALL_FORWARD) >= need
+    # the weight-streaming path (<= 64 rows per expert), fp8 and fp32 need none
+    assert moe.moe_workspace_bytes(S(T=16), moe.MOE_CALL_DOWN) == 0
+    assert moe.moe_workspace_bytes(S(T=30, capacity=64), moe.MOE_CALL_DOWN) == 0
+    assert moe.moe_workspace_bytes(S(T=8192, w_dtype="fp8_e4m3"), moe.MOE_CALL_DOWN) == 0
+    assert moe.moe_workspace_bytes(S(T=8192, d_model=128, d_ff=256, act_dtype="f32",
+                                     w_dtype="f32"), moe.MOE_CALL_DOWN) == 0
+    # missing, too small or misaligned workspace is rejected on the host
+    dummy = 1 << 20
+    b = ctypes.byref(big)
+    assert _status("moe_expert_gemm_down", b, dummy, None, dummy, dummy, None, dummy, None, 0,
+                   None) == 3
+    assert _status("moe_expert_gemm_down", b, dummy, None, dummy, dummy, None, dummy, dummy,
+                   need - 1, None) == 3
+    assert _status("moe_expert_gemm_down", b, dummy, None, dummy, dummy, None, dummy, dummy + 8,
+                   need, None) == 3
+
+
 def test_calls_reject_null_and_misaligned_pointers_without_device_work():
     s = ctypes.byref(S())
     dummy = 1 << 20  # never dereferenced: validation fails first
