@@ -9,10 +9,12 @@
 // capacity_select: one workgroup per expert.  Each assignment gets the
 //   64-bit key (fp32 bits of its gate weight) << 32 | (0xffffffff - token),
 //   unique inside an expert and ordered exactly like "higher weight first,
-//   lower token on ties".  An MSB-first radix select (8 passes of 8-bit
-//   digits, LDS histograms) finds the key of rank `capacity`; assignments
-//   with a key at or above it are kept.  Index-only, order-independent and
-//   therefore deterministic.
+//   lower token on ties".  The expert's keys are gathered into LDS and sorted
+//   (bitonic network, descending); the key of rank `capacity` is the cutoff
+//   and assignments with a key at or above it are kept.  Experts with more
+//   keys than fit use an MSB-first radix select (8 passes of 8-bit digits,
+//   LDS histograms) over global memory instead.  Index-only,
+//   order-independent and therefore deterministic.
 // permute_index: one workgroup of 1024 lanes.  Pass 1 counts kept
 //   assignments per expert with LDS atomics (order-free).  Pass 2 walks the
 //   tokens in chunks of 1024; per expert a wavefront ballot + popcount gives
@@ -34,6 +36,10 @@ __device__ __forceinline__ uint64_t capacity_key(const float* w, int i) {
   return ((uint64_t)gbits << 32) | (uint64_t)(0xffffffffu - tok);
 }
 
+// Keys of one expert held in LDS by the capacity selection (larger experts
+// read their keys from global memory in every pass).
+constexpr int kCapKeysInLds = 8192;   // a power of two
+
 __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __restrict__ ids,
                                                                const float* __restrict__ w,
                                                                int n_assign, int capacity,
@@ -44,14 +50,39 @@ __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __
   __shared__ int s_count;
   __shared__ int s_digit;
   __shared__ int s_remaining;
+  __shared__ uint64_t keys[kCapKeysInLds];
 
+  // pass 0: this expert's assignments; their keys go to LDS (any order: the
+  // selection below depends only on the set of keys)
+  // (one LDS atomic per wavefront: ballot, then each lane's rank among the
+  // matching lanes below it)
   if (tid == 0) s_count = 0;
   __syncthreads();
-  int mine = 0;
-  for (int i = tid; i < n_assign; i += blockDim.x) mine += (ids[i] == e);
-  atomicAdd(&s_count, mine);
+  const int lane = tid & 63;
+  constexpr int kBatch = 4;                    // loads issued together per lane
+  for (int i0 = tid - lane; i0 < n_assign; i0 += kBatch * blockDim.x) {
+    int id[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int i = i0 + q * blockDim.x + lane;
+      id[q] = i < n_assign ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int i = i0 + q * blockDim.x + lane;
+      const bool m = id[q] == e;
+      const uint64_t bal = __ballot(m);
+      if (bal == 0) continue;
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&s_count, (int)__popcll(bal));
+      base = __shfl(base, 0);
+      const int pos = base + (int)__popcll(bal & ((1ull << lane) - 1));
+      if (m && pos < kCapKeysInLds) keys[pos] = capacity_key(w, i);
+    }
+  }
   __syncthreads();
   const int n_e = s_count;
+  const bool in_lds = n_e <= kCapKeysInLds;
 
   if (n_e <= capacity) {
     for (int i = tid; i < n_assign; i += blockDim.x)
@@ -64,35 +95,93 @@ __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __
     return;
   }
 
-  uint64_t prefix = 0, mask = 0;
-  int remaining = capacity;  // rank (1-based, from the top) still to locate
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
+  uint64_t prefix = 0;
+  if (in_lds) {
+    // Bitonic sort of the keys, descending, padded with zero keys (below every
+    // real key) to a power of two; the kept set is the first `capacity`.
+    int n = 1;
+    while (n < n_e) n <<= 1;
+    for (int i = n_e + tid; i < n; i += blockDim.x) keys[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n_assign; i += blockDim.x) {
-      if (ids[i] != e) continue;
-      const uint64_t key = capacity_key(w, i);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t above = 0;  // keys in this bucket range with a larger digit
-      for (int b = 255; b > tid; --b) above += hist[b];
-      if ((int)above < remaining && (int)(above + hist[tid]) >= remaining) {
-        s_digit = tid;
-        s_remaining = remaining - (int)above;
+    // Each step compares n / 2 pairs (i, i + j), i with bit j clear; a thread
+    // takes pairs tid, tid + 1024, ... (at most 4), loading all of them first.
+    constexpr int kPairsPerThread = kCapKeysInLds / 2 / 1024;
+    for (int k = 2; k <= n; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        uint64_t a[kPairsPerThread], b[kPairsPerThread];
+        int lo[kPairsPerThread];
+#pragma unroll
+        for (int q = 0; q < kPairsPerThread; ++q) {
+          const int pr = tid + q * 1024;
+          lo[q] = ((pr & ~(j - 1)) << 1) | (pr & (j - 1));
+          if (pr < n / 2) {
+            a[q] = keys[lo[q]];
+            b[q] = keys[lo[q] + j];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < kPairsPerThread; ++q) {
+          const int pr = tid + q * 1024;
+          if (pr < n / 2) {
+            const bool desc = (lo[q] & k) == 0;
+            if (desc ? a[q] < b[q] : a[q] > b[q]) {
+              keys[lo[q]] = b[q];
+              keys[lo[q] + j] = a[q];
+            }
+          }
+        }
+        __syncthreads();
       }
+    prefix = keys[capacity - 1];
+  } else {
+    // MSB-first radix select over the keys read from global memory.
+    __shared__ uint32_t above[256];
+    uint64_t mask = 0;
+    int remaining = capacity;  // rank (1-based, from the top) still to locate
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      for (int i = tid; i < n_assign; i += blockDim.x) {
+        if (ids[i] != e) continue;
+        const uint64_t key = capacity_key(w, i);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      // above[b] = keys of this prefix with a digit > b (parallel suffix sum)
+      if (tid < 256) above[tid] = tid < 255 ? hist[tid + 1] : 0;
+      __syncthreads();
+      for (int off = 1; off < 256; off <<= 1) {
+        const uint32_t add = (tid < 256 && tid + off < 256) ? above[tid + off] : 0;
+        __syncthreads();
+        if (tid < 256) above[tid] += add;
+        __syncthreads();
+      }
+      if (tid < 256 && (int)above[tid] < remaining && (int)(above[tid] + hist[tid]) >= remaining) {
+        s_digit = tid;
+        s_remaining = remaining - (int)above[tid];
+      }
+      __syncthreads();
+      prefix |= (uint64_t)s_digit << shift;
+      mask |= (uint64_t)255 << shift;
+      remaining = s_remaining;
+      __syncthreads();
     }
-    __syncthreads();
-    prefix |= (uint64_t)s_digit << shift;
-    mask |= (uint64_t)255 << shift;
-    remaining = s_remaining;
-    __syncthreads();
   }
   // `prefix` is now the exact key of rank `capacity`; keys are unique.
-  for (int i = tid; i < n_assign; i += blockDim.x)
-    if (ids[i] == e) drop[i] = capacity_key(w, i) >= prefix ? 0 : 1;
+  for (int i0 = tid; i0 < n_assign; i0 += kBatch * blockDim.x) {
+    int id[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int i = i0 + q * blockDim.x;
+      id[q] = i < n_assign ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int i = i0 + q * blockDim.x;
+      if (id[q] == e) drop[i] = capacity_key(w, i) >= prefix ? 0 : 1;
+    }
+  }
 }
 
 constexpr int kIndexThreads = 1024;

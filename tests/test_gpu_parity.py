@@ -200,6 +200,18 @@ def test_capacity_one_and_large():
     run_staged_and_check(mid_cfg("cap_big", T=200, n_experts=8, capacity=10_000, seed=9))
 
 
+def test_capacity_expert_beyond_lds_key_buffer():
+    # one expert receives more than 8192 assignments: its cutoff comes from the
+    # radix select over global memory instead of the in-LDS sort
+    T = 12000
+    cfg = mid_cfg("cap_many", T=T, d_model=64, d_ff=64, n_experts=8, router_bias="zipf1.2",
+                  capacity=9000, wg_std=64 ** -0.5, seed=12)
+    st, res, _ = run_staged_and_check(cfg, check_h=False)
+    loads = np.bincount(to_np(st["topk_ids"]).ravel(), minlength=8)
+    assert loads.max() > 9000 > 8192, loads
+    assert (~res.keep).sum() > 0
+
+
 def test_dense_reduction_all_experts_equal():
     """All experts equal: the layer must equal one dense SwiGLU FFN (oracle, E=1 form)."""
     cfg = mid_cfg("dense", T=700, n_experts=8, seed=10)
