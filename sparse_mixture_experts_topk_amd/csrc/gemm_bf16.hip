@@ -13,21 +13,23 @@
 // consecutive channels, which the epilogue stores as 8-byte (bf16 h) or
 // 16-byte (fp32 y_perm) vectors.
 //
-// Prefill kernel: 256 lanes, a 256 x 256 tile (weights x tokens; the dual
-// gate/up variant holds 128 w1 rows and the same 128 w3 rows so silu(g) * u
-// is formed in registers).  K advances 32 at a time through a ring of four
-// LDS stages of 2 x 16 KiB, filled by buffer loads that write LDS directly
-// (no staging registers), so three slices are in flight while one is
-// multiplied.  Rows are 64 bytes in LDS with the 16-byte chunks XOR-swizzled,
-// so the fragment reads of 16 consecutive rows are free of bank conflicts.
-// The buffer descriptors are bounded to the tile's valid rows: rows past the
-// expert's last token or the last channel load as zero without a branch.
-// Each wavefront owns 128 x 128 of the tile (16 accumulator blocks of
-// v_mfma_f32_32x32x16_bf16, 256 fp32 per lane); fragments are read one
-// 16-wide substep ahead of the matrix instructions and there is one barrier
-// per slice.  Tiles are scheduled expert by expert with token tiles fastest
-// and remapped so that consecutive tiles run on the same XCD and share its L2
-// copy of the weight tile.
+// Prefill kernel: 512 lanes (two wavefronts per SIMD), a 384 x 256 tile
+// (weights x tokens; the dual gate/up variant holds 192 w1 rows and the same
+// 192 w3 rows so silu(g) * u is formed in registers).  K advances 32 at a
+// time through a ring of three LDS stages of 24 + 16 KiB, filled by buffer
+// loads that write LDS directly (no staging registers), so two slices are in
+// flight while one is multiplied.  Rows are 64 bytes in LDS with the 16-byte
+// chunks XOR-swizzled, so the fragment reads of 16 consecutive rows are free
+// of bank conflicts.  The buffer descriptors are bounded to the tile's valid
+// rows: rows past the expert's last token or the last channel load as zero
+// without a branch.  Each wavefront owns 12 accumulator blocks of
+// v_mfma_f32_32x32x16_bf16 (192 fp32 per lane); fragments are read ahead of
+// the matrix instructions that use them and there is one barrier per slice.
+// The larger weight tile cuts the bytes moved per flop (the global -> LDS
+// path bounds this kernel) by a sixth against a 256 x 256 tile.  Tiles are
+// scheduled expert by expert with token tiles fastest and remapped so that
+// consecutive tiles run on the same XCD and share its L2 copy of the weight
+// tile.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "lds_stream.hpp"
@@ -40,28 +42,34 @@ hipError_t launch_decode_bf16(const moe_shape_t& s, bool dual, const uint16_t* a
 
 namespace {
 
-constexpr int PF_ROWS = 256;         // rows of each LDS operand tile
-constexpr int PF_THREADS = 256;
+constexpr int PF_ROWS = 256;         // token rows of a tile
 
-// Geometry of one K slice of BK elements: LDS rows of BK * 2 bytes made of
-// CPR 16-byte chunks.  Chunk c of row r sits at chunk position c ^ key(r),
-// which spreads the fragment reads of 16 consecutive rows (one LDS phase,
-// same logical chunk) over all 64 banks.  A 1 KiB load instruction covers
-// RPI whole rows.  The weight operand has TA rows (WA 32-row blocks per
-// wavefront, two wavefront rows), the token operand PF_ROWS.
-template <int BK, int WA>
+// Layout of a tile: WR x WC wavefronts, wavefront (wr, wc) owning WA 32-row
+// weight blocks of wavefront row wr against WB 32-token blocks of column wc.
+// The weight operand has TA = 32 WR WA rows, the token operand 32 WC WB =
+// PF_ROWS rows.  One K slice of BK elements is an LDS row of BK * 2 bytes
+// made of CPR 16-byte chunks; chunk c of row r sits at chunk position
+// c ^ key(r), which spreads the fragment reads of 16 consecutive rows (one
+// LDS phase, same logical chunk) over all 64 banks.  A 1 KiB load
+// instruction covers RPI whole rows.
+template <int BK, int WR, int WC, int WA, int WB>
 struct TileGeom {
+  static constexpr int NW = WR * WC;
+  static constexpr int THREADS = 64 * NW;
   static constexpr int CPR = BK / 8;
   static constexpr int ROW_B = BK * 2;
-  static constexpr int TA = 64 * WA;
+  static constexpr int TA = 32 * WR * WA;
+  static constexpr int TB = 32 * WC * WB;
   static constexpr int OPA_BYTES = TA * ROW_B;
-  static constexpr int OPB_BYTES = PF_ROWS * ROW_B;
+  static constexpr int OPB_BYTES = TB * ROW_B;
   static constexpr int STAGE_BYTES = OPA_BYTES + OPB_BYTES;
   static constexpr int RPI = 64 / CPR;
-  static constexpr int JA = TA / RPI / 4;              // weight loads per wavefront per slice
-  static constexpr int JB = PF_ROWS / RPI / 4;         // token loads per wavefront per slice
+  static constexpr int JA = TA / RPI / NW;             // weight loads per wavefront per slice
+  static constexpr int JB = TB / RPI / NW;             // token loads per wavefront per slice
   static constexpr int DMA = JA + JB;
   static constexpr int SUB = BK / 16;                  // 16-wide matrix substeps
+  static_assert(TB == PF_ROWS, "token tile");
+  static_assert(JA * RPI * NW == TA && JB * RPI * NW == TB, "whole load blocks per wavefront");
   __device__ static __forceinline__ int key(int row) { return (row / (16 / CPR)) & (CPR - 1); }
 };
 
@@ -96,15 +104,12 @@ struct TileSplit {
   }
 };
 
-// Partial tiles of the split work: 256 x 256 fp32 each, two per workgroup.
-constexpr int kPartialTileBytes = PF_ROWS * 256 * 4;
 constexpr int kMaxPersistentGroups = 256;
 
 // Tile: TA weight rows x 256 tokens.  The dual (gate/up) kernel's weight rows
-// are TA / 2 rows of w1 followed by the same TA / 2 rows of w3, so each
-// wavefront holds matching w1 and w3 accumulators and forms silu(g) * u in
-// registers.  Wavefront (wr, wc) owns weight blocks of wavefront row wr and
-// tokens wc * 128 .. wc * 128 + 127.
+// are TA / 2 rows of w1 followed by the same TA / 2 rows of w3, and a
+// wavefront's WA blocks are WA / 2 blocks of w1 and the matching blocks of
+// w3, so it forms silu(g) * u in registers.
 //
 // The kernel is persistent: the grid is a multiple of 8 workgroups, one per
 // CU at most, and workgroup b works through tiles of XCD b % 8's share of
@@ -112,15 +117,16 @@ constexpr int kMaxPersistentGroups = 256;
 // weight and token tiles in its L2), b / 8, b / 8 + grid / 8, ...  The K
 // slices of all its tiles form one stream through the LDS ring, so the
 // first slices of the next tile load while the current one finishes and
-// stores its results.
-template <bool DUAL, int BK, int NS, int WA, bool SPLIT>
-__global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
+// stores its results.  Split K-runs go to fp32 partial tiles [token][TA].
+template <bool DUAL, int BK, int NS, int WR, int WC, int WA, int WB, bool SPLIT>
+__global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
     const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, int N, int K,
     void* __restrict__ out, float* __restrict__ partials, int n_tiles) {
-  using G = TileGeom<BK, WA>;
-  static_assert(G::SUB % 2 == 0 && NS >= 2 && WA % 2 == 0, "pipeline shape");
-  static_assert(!SPLIT || (!DUAL && G::TA == 256), "split runs: single 256 x 256 fp32 tiles");
+  using G = TileGeom<BK, WR, WC, WA, WB>;
+  static_assert(G::SUB % 2 == 0 && NS >= 2 && (!DUAL || WA % 2 == 0) && WB >= 2, "pipeline shape");
+  static_assert(!SPLIT || !DUAL, "split runs: single GEMM");
+  static_assert(!DUAL || (G::TA / 2) % 16 == 0, "w3 rows start on a swizzle period");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * G::STAGE_BYTES];
   __shared__ int32_t offs[kMaxExperts + 1];
 
@@ -128,7 +134,18 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
   constexpr int CH_TILE = DUAL ? G::TA / 2 : G::TA;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index is uniform
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave / WC, wc = wave % WC;
+  // With two wavefronts per SIMD the accumulators and fragments leave few
+  // registers: lane-derived offsets are then formed afresh where they are
+  // used (from a lane index the compiler cannot reuse) rather than being
+  // kept live through the K loop.
+  constexpr bool LEAN = G::NW > 4 || WA * WB > 16;
+  auto lane_now = [&]() __attribute__((always_inline)) {
+    if constexpr (!LEAN) return lane;
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+  };
 
   // Expert offsets go to LDS once, so that locating a tile in the middle of
   // the load stream issues no vector-memory read (the stream's waits count
@@ -174,16 +191,22 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
 
   // ---- global -> LDS loads ----
   // An operand slice is made of 1 KiB blocks of RPI rows; wavefront w fills
-  // blocks w, w + 4, ... of both operands.  Lane l writes chunk position
+  // blocks w, w + NW, ... of both operands.  Lane l writes chunk position
   // l % CPR of block row l / CPR and so reads logical chunk (l % CPR) ^ key(row).
+  // The w3 rows of a dual tile are reached through a descriptor whose base
+  // lies TA / 2 rows before the w3 tile (TA / 2 is a whole number of
+  // swizzle periods, so the chunk keys are those of the LDS rows).  Loads j
+  // and j + 1 of a wavefront are NW * RPI rows apart, a whole number of
+  // swizzle periods, so the lane offsets of load j are those of load 0 plus
+  // j times that many rows.
   const int64_t rowbytes = (int64_t)K * 2;
-  constexpr int JMAX = G::JA > G::JB ? G::JA : G::JB;
-  int voff[JMAX];
-#pragma unroll
-  for (int j = 0; j < JMAX; ++j) {
-    const int r = (4 * j + wave) * G::RPI + lane / G::CPR;   // row within the operand tile
-    voff[j] = (int)(r * rowbytes) + (((lane % G::CPR) ^ G::key(r)) << 4);
-  }
+  static_assert((G::NW * G::RPI) % 16 == 0, "loads of a wavefront are whole swizzle periods apart");
+  auto voff_base = [&]() __attribute__((always_inline)) {
+    const int l = lane_now();
+    const int r = wave * G::RPI + l / G::CPR;       // row within the operand tile
+    return (int)(r * rowbytes) + (((l % G::CPR) ^ G::key(r)) << 4);
+  };
+  const int vstep = G::NW * G::RPI * (int)rowbytes;   // uniform
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
 
   // Load cursor: slice lkt (of K) of item li, the item's end and its descriptors.
@@ -196,29 +219,28 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
       lke = t.ke;
       d_tok = make_desc(act + (int64_t)t.tok0 * K, t.tok_rows * rowbytes);
       d_w0 = make_desc(wa + ((int64_t)t.e * N + t.ch0) * K, (int64_t)(N - t.ch0) * rowbytes);
-      d_w1 = DUAL ? make_desc(wb + ((int64_t)t.e * N + t.ch0) * K, (int64_t)(N - t.ch0) * rowbytes)
+      d_w1 = DUAL ? make_desc(wb + ((int64_t)t.e * N + t.ch0 - G::TA / 2) * K,
+                              (int64_t)(N - t.ch0 + G::TA / 2) * rowbytes)
                   : d_w0;
     }
   };
   load_tile();
   // Load j (0 .. DMA - 1) of the cursor's slice into stage ls % NS: the first
-  // JA weight blocks, then JB token blocks.  Dual: weight rows TA / 2 .. TA - 1
-  // are w3 rows with the row offsets of rows 0 .. TA / 2 - 1 (TA / 2 rows is
-  // a whole number of swizzle periods).  Past the last tile the offset lies
-  // beyond every buffer's range: such loads write zeros without touching
+  // JA weight blocks, then JB token blocks.  Past the last tile the offset
+  // lies beyond every buffer's range: such loads write zeros without touching
   // memory, into a stage that is never read again, so every iteration
   // issues the same loads.
-  auto dma = [&](int ls, int j) __attribute__((always_inline)) {
+  auto dma = [&](int ls, int j, int vb) __attribute__((always_inline)) {
     const int soff = li < n_items ? lkt * BK * 2 : 0x7ff00000;
     const uint32_t sb = lds_base + (uint32_t)((ls % NS) * G::STAGE_BYTES);
     if (j >= G::JA) {
       const int q = j - G::JA;
-      dma_to_lds(d_tok, voff[q], soff,
-                 __builtin_amdgcn_readfirstlane(sb + G::OPA_BYTES + (4 * q + wave) * 1024));
+      dma_to_lds(d_tok, vb + q * vstep, soff,
+                 __builtin_amdgcn_readfirstlane(sb + G::OPA_BYTES + (G::NW * q + wave) * 1024));
     } else {
-      const bool w3 = DUAL && j >= G::JA / 2;
-      dma_to_lds(w3 ? d_w1 : d_w0, voff[w3 ? j - G::JA / 2 : j], soff,
-                 __builtin_amdgcn_readfirstlane(sb + (4 * j + wave) * 1024));
+      const int blk = G::NW * j + wave;                 // uniform
+      const bool w3 = DUAL && blk * G::RPI >= G::TA / 2;
+      dma_to_lds(w3 ? d_w1 : d_w0, vb + j * vstep, soff, __builtin_amdgcn_readfirstlane(sb + blk * 1024));
     }
   };
   auto advance_load = [&]() __attribute__((always_inline)) {
@@ -230,58 +252,64 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
 
   // ---- fragment addressing (v_mfma_f32_32x32x16_bf16: lane (fi, fg) holds
   //      row fi, k = 8 fg .. 8 fg + 7 of the 16-wide substep) ----
-  const int fi = lane & 31, fg = lane >> 5;
-  int frag_off[G::SUB];
-#pragma unroll
-  for (int s = 0; s < G::SUB; ++s)
-    frag_off[s] = fi * G::ROW_B + (((2 * s + fg) ^ G::key(fi)) << 4);
-  int arow[WA], bfrow[4];
+  auto frag_offset = [&](int s) __attribute__((always_inline)) {
+    const int l = lane_now(), fi = l & 31, fg = l >> 5;
+    return fi * G::ROW_B + (((2 * s + fg) ^ G::key(fi)) << 4);
+  };
+  int arow[WA], bfrow[WB];
 #pragma unroll
   for (int a = 0; a < WA; ++a) {
     if constexpr (DUAL) arow[a] = (a / HA) * (G::TA / 2) + wr * (HA * 32) + (a % HA) * 32;
     else arow[a] = wr * (WA * 32) + a * 32;
   }
 #pragma unroll
-  for (int b = 0; b < 4; ++b) bfrow[b] = wc * 128 + b * 32;
+  for (int b = 0; b < WB; ++b) bfrow[b] = wc * (WB * 32) + b * 32;
 
-  f32x16_t acc[WA][4];
+  f32x16_t acc[WA][WB];
 
-  // fragment f of a substep of slice g: 0 .. WA - 1 weight blocks, then 4 token blocks
-  auto read_frag = [&](int g, int s, int f) __attribute__((always_inline)) -> bf16x8_t {
+  // fragment f of a substep (lane offset fo) of slice g: 0 .. WA - 1 weight
+  // blocks, then WB token blocks
+  auto read_frag = [&](int g, int fo, int f) __attribute__((always_inline)) -> bf16x8_t {
     const int off = (g % NS) * G::STAGE_BYTES +
-                    (f < WA ? arow[f] * G::ROW_B : G::OPA_BYTES + bfrow[f - WA] * G::ROW_B) +
-                    frag_off[s];
+                    (f < WA ? arow[f] * G::ROW_B : G::OPA_BYTES + bfrow[f - WA] * G::ROW_B) + fo;
     return as_bf16x8(*reinterpret_cast<const uint4*>(&smem[off]));
   };
 
-  // One substep: 4 WA matrix instructions, weight block a = i / 4 against
-  // token block b = i % 4.  Weight fragments are single-buffered: fa[a] is
+  // One substep: WA * WB matrix instructions, weight block a = i / WB against
+  // token block b = i % WB.  Weight fragments are single-buffered: fa[a] is
   // reloaded with the next substep's fragment right after its last use
-  // (b == 3); token fragments are double-buffered and the next substep's
-  // are read after the first four instructions.  With `loads`, the
+  // (b == WB - 1).  Token fragments are double-buffered, the next substep's
+  // read after the first WB instructions, when the accumulators leave room
+  // for it; otherwise fb[b] is reloaded after its last use (a == WA - 1)
+  // and the other wavefront on the SIMD covers the wait.  With `loads`, the
   // remaining slots carry the loads of the load cursor's slice `ls`
   // (slot numbering continues across substeps from slot0).  With `reads`,
-  // (gn, sn) is the substep whose fragments are read.  `fresh` starts the
-  // accumulators of a new tile (zero addend).
-  bf16x8_t fa[WA], fb[2][4];
-  constexpr int NI = 4 * WA;
-  constexpr int FREE = (NI - 4) - (NI - 4) / 4;           // load slots per substep
-  auto substep = [&](int cur, int gn, int sn, int slot0, bool loads, int ls, bool reads,
-                     bool fresh) __attribute__((always_inline)) {
+  // (gn, sn) is the substep whose fragments are read.
+  constexpr bool FB2 = WA * WB * 16 + 4 * (WA + 2 * WB) <= 2048 / G::NW - 32;
+  bf16x8_t fa[WA], fb[FB2 ? 2 : 1][WB];
+  constexpr int NI = WA * WB;
+  constexpr int FREE = (WA - 1) * (WB - 1);               // load slots per substep
+  auto substep = [&](int cur, int gn, int sn, int slot0, bool loads, int ls, bool reads)
+                     __attribute__((always_inline)) {
+    const int fo = reads ? frag_offset(sn) : 0;
+    const int vb = loads ? voff_base() : 0;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int a = i >> 2, b = i & 3;
-      const f32x16_t c_in = fresh ? f32x16_t{} : acc[a][b];
-      acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[cur][b], c_in, 0, 0, 0);
-      if (reads && i < 4) fb[cur ^ 1][i] = read_frag(gn, sn, WA + i);
-      if (b == 3) {
-        if (reads) fa[a] = read_frag(gn, sn, a);
-      } else if (i >= 4 && loads) {
+      const int a = i / WB, b = i % WB;
+      acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[FB2 ? cur : 0][b], acc[a][b], 0, 0, 0);
+      if constexpr (FB2) {
+        if (reads && i < WB) fb[cur ^ 1][i] = read_frag(gn, fo, WA + i);
+      } else {
+        if (reads && a == WA - 1) fb[0][b] = read_frag(gn, fo, WA + b);
+      }
+      if (b == WB - 1) {
+        if (reads) fa[a] = read_frag(gn, fo, a);
+      } else if (a >= 1 && loads) {
         constexpr int SLOTS = FREE * (G::SUB - 1), PER = (G::DMA + SLOTS - 1) / SLOTS;
-        const int sl = slot0 + (i - 4) - ((i - 4) >> 2);
+        const int sl = slot0 + (a - 1) * (WB - 1) + b;
 #pragma unroll
         for (int q = 0; q < PER; ++q)
-          if (sl * PER + q < G::DMA) dma(ls, sl * PER + q);
+          if (sl * PER + q < G::DMA) dma(ls, sl * PER + q, vb);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -301,8 +329,8 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
     const i32x4_t ro = make_desc(static_cast<uint8_t*>(out) + (int64_t)t.tok0 * N * OB,
                                  (int64_t)t.tok_rows * N * OB);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int tl = wc * 128 + b * 32 + fi;      // token row within the tile
+    for (int b = 0; b < WB; ++b) {
+      const int tl = wc * (WB * 32) + b * 32 + fi;      // token row within the tile
       const int row_off = tl * N * OB;
       if constexpr (DUAL) {
 #pragma unroll
@@ -317,12 +345,13 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
             store_b64(ro, c < N ? row_off + c * OB : 0x7fffffff, pack_bf16x2(hv[0], hv[1]),
                       pack_bf16x2(hv[2], hv[3]));
             __builtin_amdgcn_sched_barrier(0);   // one block at a time: few live registers
+            if (q == 3) acc[a][b] = acc[a + HA][b] = f32x16_t{};   // the next tile starts from zero
           }
       } else {
-        // a K-run of a split tile goes whole to its partial slot ([token][channel], 256 x 256)
+        // a K-run of a split tile goes whole to its partial slot ([token][channel], 256 x TA)
         const bool part = SPLIT && t.part >= 0;
-        const i32x4_t dst = part ? make_desc(partials + (int64_t)t.part * (kPartialTileBytes / 4),
-                                             kPartialTileBytes)
+        const i32x4_t dst = part ? make_desc(partials + (int64_t)t.part * (PF_ROWS * G::TA),
+                                             PF_ROWS * G::TA * 4)
                                  : ro;
 #pragma unroll
         for (int a = 0; a < WA; ++a)
@@ -332,8 +361,9 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
             const int c = t.ch0 + cl;
             const u32x4_t v = {__float_as_uint(acc[a][b][q * 4 + 0]), __float_as_uint(acc[a][b][q * 4 + 1]),
                                __float_as_uint(acc[a][b][q * 4 + 2]), __float_as_uint(acc[a][b][q * 4 + 3])};
-            store_b128(dst, part ? (tl * 256 + cl) * 4 : (c < N ? row_off + c * OB : 0x7fffffff), v);
+            store_b128(dst, part ? (tl * G::TA + cl) * 4 : (c < N ? row_off + c * OB : 0x7fffffff), v);
             __builtin_amdgcn_sched_barrier(0);
+            if (q == 3) acc[a][b] = f32x16_t{};   // the next tile starts from zero
           }
       }
     }
@@ -351,58 +381,61 @@ __global__ __launch_bounds__(PF_THREADS, 1) void grouped_gemm_bf16_prefill(
   // Pending stores share the vector-memory counter with the loads; loads
   // complete in order among themselves, so they only make the wait stricter.
   // Instruction order is fixed with scheduling barriers.
-  auto iteration = [&](int g, bool first, bool last) __attribute__((always_inline)) {
+  auto iteration = [&](int g, bool last) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < G::SUB - 1; ++s)
-      substep(s & 1, g, s + 1, s * FREE, true, g + NS - 1, true, first && s == 0);
+      substep(s & 1, g, s + 1, s * FREE, true, g + NS - 1, true);
     advance_load();
     wait_vmcnt<G::DMA * (NS - 2)>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    substep(1, g + 1, 0, 0, false, 0, !last, false);
+    substep(1, g + 1, 0, 0, false, 0, !last);
   };
 
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) {
+    const int vb = voff_base();
 #pragma unroll
-    for (int j = 0; j < G::DMA; ++j) dma(s, j);
+    for (int j = 0; j < G::DMA; ++j) dma(s, j, vb);
     advance_load();
   }
   wait_vmcnt<G::DMA * (NS - 2)>();
   __builtin_amdgcn_s_barrier();
 
+#pragma unroll
+  for (int a = 0; a < WA; ++a)
+#pragma unroll
+    for (int b = 0; b < WB; ++b) acc[a][b] = f32x16_t{};
   int g = 0;                      // stream index of the slice being multiplied
   for (int ci = 0; ci < n_items; ++ci) {
     const Tile t = tile_of(ci);
     const int nk = t.ke - t.kb;                  // >= 1
+    const int fo = frag_offset(0);
 #pragma unroll
-    for (int f = 0; f < WA; ++f) fa[f] = read_frag(g, 0, f);
+    for (int f = 0; f < WA; ++f) fa[f] = read_frag(g, fo, f);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) fb[0][f] = read_frag(g, 0, WA + f);
-    if (nk == 1) {
-      iteration(g++, true, true);
-    } else {
-      iteration(g++, true, false);
-      for (int kt = 1; kt < nk - 1; ++kt) iteration(g++, false, false);
-      iteration(g++, false, true);
-    }
-    epilogue(t);
+    for (int f = 0; f < WB; ++f) fb[0][f] = read_frag(g, fo, WA + f);
+    for (int kt = 0; kt < nk - 1; ++kt) iteration(g++, false);
+    iteration(g++, true);
+    epilogue(t);                  // stores the tile and zeroes the accumulators
   }
   wait_vmcnt<0>();   // the zero loads past the end land before the workgroup's LDS is released
 }
 
 // Sum of the K-runs of each split tail tile, in K order, into y_perm.  One
 // workgroup per (XCD, tail tile, group of 16 rows): lane l covers row
-// 16 g + l / 16 and channels 4 (l % 16) + 64 c, c = 0..3, so every lane has
-// four independent 16-byte sums in flight.
+// 16 g + l / 16 and channels 4 (l % 16) + 64 c, c < CH / 64, so every lane
+// has CH / 64 independent 16-byte sums in flight.
 constexpr int kFixupRowGroups = PF_ROWS / 16;
 
+template <int CH>
 __global__ __launch_bounds__(256) void split_fixup_kernel(const int32_t* __restrict__ offsets, int E,
                                                           int N, int K, int BK, int n_tiles, int slots,
                                                           const float* __restrict__ partials,
                                                           float* __restrict__ y) {
+  constexpr int CPL = CH / 64;
   const int rg = blockIdx.x % kFixupRowGroups;
   const int xcd = (blockIdx.x / kFixupRowGroups) & 7, j = blockIdx.x / kFixupRowGroups >> 3;
   const int KT = K / BK;
@@ -410,33 +443,42 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(const int32_t* __restr
   if (j >= sp.tail) return;
   int e, r0, r1, mt, nt;
   locate_tile(offsets, E, PF_ROWS, n_tiles, sp.share_begin + sp.R * slots + j, e, r0, r1, mt, nt);
-  const int tok0 = r0 + mt * PF_ROWS, tok_rows = min(PF_ROWS, r1 - tok0), ch0 = nt * 256;
+  const int tok0 = r0 + mt * PF_ROWS, tok_rows = min(PF_ROWS, r1 - tok0), ch0 = nt * CH;
   const int r = rg * 16 + (threadIdx.x >> 4);
   if (r >= tok_rows) return;
   const int s_lo = (j * KT) / sp.P, s_hi = min(((j + 1) * KT - 1) / sp.P, slots - 1);
-  float4 acc[4];
+  float4 acc[CPL];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = 0; c < CPL; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = s_lo; s <= s_hi; ++s) {
     const int part = (s * 8 + xcd) * 2 + (j - (s * sp.P) / KT);
-    const float* src = partials + (int64_t)part * (kPartialTileBytes / 4) + r * 256 + (threadIdx.x & 15) * 4;
-    float4 p[4];
+    const float* src = partials + (int64_t)part * (PF_ROWS * CH) + r * CH + (threadIdx.x & 15) * 4;
+    float4 p[CPL];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) p[c] = *reinterpret_cast<const float4*>(src + 64 * c);
+    for (int c = 0; c < CPL; ++c) p[c] = *reinterpret_cast<const float4*>(src + 64 * c);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < CPL; ++c) {
       acc[c].x += p[c].x; acc[c].y += p[c].y; acc[c].z += p[c].z; acc[c].w += p[c].w;
     }
   }
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < CPL; ++c) {
     const int col = ch0 + (threadIdx.x & 15) * 4 + 64 * c;
     if (col < N) *reinterpret_cast<float4*>(y + (int64_t)(tok0 + r) * N + col) = acc[c];
   }
 }
 
-// K slice, LDS ring depth and weight blocks per wavefront of the prefill kernel.
-constexpr int kPrefillBK = 32, kPrefillStages = 4, kPrefillWA = 4;
+// Shapes of the prefill kernels: K slice, LDS ring depth, wavefront grid and
+// blocks per wavefront.  Both run 8 wavefronts (two per SIMD, 192
+// accumulators each) on a 384 x 256 tile: gate/up as 2 x 4 wavefronts of
+// 3 + 3 (w1, w3) blocks x 2 token blocks, down as 4 x 2 wavefronts of 3 x 4.
+template <bool DUAL> struct PrefillCfg;
+template <> struct PrefillCfg<true> { static constexpr int BK = 32, NS = 3, WR = 2, WC = 4, WA = 6, WB = 2; };
+template <> struct PrefillCfg<false> { static constexpr int BK = 32, NS = 3, WR = 4, WC = 2, WA = 3, WB = 4; };
+template <bool DUAL>
+using PrefillGeom = TileGeom<PrefillCfg<DUAL>::BK, PrefillCfg<DUAL>::WR, PrefillCfg<DUAL>::WC, PrefillCfg<DUAL>::WA,
+                             PrefillCfg<DUAL>::WB>;
+constexpr int64_t kPartialTileBytes = (int64_t)PF_ROWS * PrefillGeom<false>::TA * 4;
 
 // Workgroups of the persistent launch: one per CU, at most kMaxPersistentGroups,
 // a multiple of the 8 XCDs, and no more than there are tiles.
@@ -449,25 +491,28 @@ template <bool DUAL>
 hipError_t launch_prefill(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                           const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
                           float* partials, hipStream_t st) {
-  constexpr int CH_TILE = (DUAL ? 32 : 64) * kPrefillWA;
+  using C = PrefillCfg<DUAL>;
+  using G = PrefillGeom<DUAL>;
+  constexpr int CH_TILE = DUAL ? G::TA / 2 : G::TA;
   const int n_tiles = (N + CH_TILE - 1) / CH_TILE;
   const int64_t max_tiles = max_token_tiles(s, PF_ROWS) * n_tiles;
   if (max_tiles <= 0) return hipSuccess;
   const int64_t grid = persistent_grid(max_tiles);
-  const bool split = !DUAL && partials != nullptr;
-  if (split) {
-    hipLaunchKernelGGL((grouped_gemm_bf16_prefill<false, kPrefillBK, kPrefillStages, kPrefillWA, true>),
-                       dim3((unsigned)grid), dim3(PF_THREADS), 0, st, act, offsets, s.n_experts, wa,
-                       wb, N, K, out, partials, n_tiles);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(split_fixup_kernel, dim3((unsigned)(grid * kFixupRowGroups)), dim3(256), 0, st, offsets,
-                       s.n_experts, N, K, kPrefillBK, n_tiles, (int)(grid / 8), partials,
-                       static_cast<float*>(out));
-    return hipGetLastError();
+  if constexpr (!DUAL) {
+    if (partials != nullptr) {   // split tail: K-runs into partial tiles, then their sum
+      hipLaunchKernelGGL((grouped_gemm_bf16_prefill<false, C::BK, C::NS, C::WR, C::WC, C::WA, C::WB, true>),
+                         dim3((unsigned)grid), dim3(G::THREADS), 0, st, act, offsets, s.n_experts, wa,
+                         wb, N, K, out, partials, n_tiles);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(split_fixup_kernel<G::TA>, dim3((unsigned)(grid * kFixupRowGroups)), dim3(256), 0,
+                         st, offsets, s.n_experts, N, K, C::BK, n_tiles, (int)(grid / 8), partials,
+                         static_cast<float*>(out));
+      return hipGetLastError();
+    }
   }
-  hipLaunchKernelGGL((grouped_gemm_bf16_prefill<DUAL, kPrefillBK, kPrefillStages, kPrefillWA, false>),
-                     dim3((unsigned)grid), dim3(PF_THREADS), 0, st, act, offsets, s.n_experts, wa,
+  hipLaunchKernelGGL((grouped_gemm_bf16_prefill<DUAL, C::BK, C::NS, C::WR, C::WC, C::WA, C::WB, false>),
+                     dim3((unsigned)grid), dim3(G::THREADS), 0, st, act, offsets, s.n_experts, wa,
                      wb, N, K, out, nullptr, n_tiles);
   return hipGetLastError();
 }

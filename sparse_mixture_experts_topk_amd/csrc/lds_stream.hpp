@@ -15,7 +15,7 @@ typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 // zeros or are dropped.
 __device__ __forceinline__ i32x4_t make_desc(const void* base, int64_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+  const int n = bytes <= 0 ? 0 : bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;   // empty when negative
   i32x4_t d;
   d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   d.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));   // stride 0
