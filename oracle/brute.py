@@ -10,6 +10,12 @@ oracle (``oracle/moe_oracle.py``), which groups tokens by expert instead.
 
 Capacity (micro shapes only): a per-expert list of (token, slot, G), sorted by
 G descending then token ascending with Python's sort, first ``capacity`` kept.
+Overflow fallback ("How Mixtral 8x7B uses mixture of experts", section
+"Routing without auxiliary loss": excess tokens go to the next-best expert):
+each dropped slot is offered, in slot order, to the token's experts ranked
+3rd, 4th, ... by logit; every expert takes such offers, ranked by the slot's
+G then token, into the slots it left free, and the output weights the
+fallback expert's output by that G.
 """
 from __future__ import annotations
 
@@ -46,8 +52,12 @@ def gate(logits: Sequence[float], k: int):
     return top, [v / z for v in ex]
 
 
-def layer(x, w_gate, w1, w3, w2, k: int = 2, bias=None, capacity: int = -1):
-    """Dense brute-force layer on nested lists; returns (y, ids, G_full, keep)."""
+def layer(x, w_gate, w1, w3, w2, k: int = 2, bias=None, capacity: int = -1,
+          overflow: str = "drop"):
+    """Dense brute-force layer on nested lists; returns (y, ids, G_full, keep).
+
+    With overflow == "next_best" (and a capacity), ``keep`` holds per slot the
+    expert that finally processes it, or None when it is dropped."""
     T, E = len(x), len(w_gate)
     logits = [[_dot(x[t], w_gate[e]) + (bias[e] if bias is not None else 0.0) for e in range(E)]
               for t in range(T)]
@@ -63,6 +73,30 @@ def layer(x, w_gate, w1, w3, w2, k: int = 2, bias=None, capacity: int = -1):
             cand.sort(key=lambda c: (-c[0], c[1]))
             for _, t, s in cand[capacity:]:
                 keep[t][s] = False
+    if capacity >= 0 and overflow == "next_best":
+        final = [[ids[t][s] if keep[t][s] else None for s in range(k)] for t in range(T)]
+        offers = {}                                        # expert -> [(G, t, s)]
+        for t in range(T):
+            ranked = sorted(range(E), key=lambda e: (-logits[t][e], e))[k:]
+            dropped = [s for s in range(k) if not keep[t][s]]
+            for j, s in enumerate(dropped):
+                if j < len(ranked):
+                    offers.setdefault(ranked[j], []).append((Gf[t][ids[t][s]], t, s))
+        for e, cand in offers.items():
+            used = sum(1 for t in range(T) for s in range(k) if final[t][s] == e)
+            cand.sort(key=lambda c: (-c[0], c[1]))
+            for _, t, s in cand[:max(0, capacity - used)]:
+                final[t][s] = e
+        y = []
+        for t in range(T):
+            acc = [0.0] * len(x[t])
+            for e in range(E):                             # dense over ALL experts
+                w = sum(Gf[t][ids[t][s]] for s in range(k) if final[t][s] == e)
+                out = _expert(x[t], w1[e], w3[e], w2[e])
+                for i in range(len(acc)):
+                    acc[i] += w * out[i]
+            y.append(acc)
+        return y, ids, Gf, final
     y = []
     for t in range(T):
         acc = [0.0] * len(x[t])

@@ -21,6 +21,15 @@ What it computes, step by step, with the passage each step follows:
    kept, the rest dropped and contribute nothing ("How Mixtral 8x7B uses
    mixture of experts", section "Routing without auxiliary loss",
    capacity-limited dispatch).
+4b. Optional overflow fallback (same section: the excess goes to a fallback,
+   typically the token's next-best expert; the dispatch sketch puts the
+   remaining tokens in an overflow buffer).  Reading: an assignment dropped
+   in step 4 moves to the best-ranked expert outside the token's top-2 --
+   the 3rd-ranked one, or, when both of the token's slots were dropped, the
+   3rd-ranked for slot 0 and the 4th-ranked for slot 1 -- keeping its gate
+   weight.  Each expert takes such candidates into the slots step 4 left
+   free (capacity minus what it kept), ranked by the same key; the rest stay
+   dropped.  One round only.
 5. Grouping by expert: per-expert counts (the ``bincount`` of the top-2 ids,
    same page, expert activation heatmap listing), exclusive offsets, rows of
    one expert in ascending (token, slot) order.
@@ -86,6 +95,9 @@ class Routing:
     G: np.ndarray          # [T, k] float64 gate weights
     gap12: np.ndarray      # [T] logit(1st) - logit(2nd)
     gap23: np.ndarray      # [T] logit(2nd) - logit(3rd)  (inf when E == k)
+    next_ids: np.ndarray   # [T, 2] int64: 3rd- and 4th-ranked experts (-1 when E is smaller)
+    gap34: np.ndarray      # [T] logit(3rd) - logit(4th)  (inf when absent)
+    gap45: np.ndarray      # [T] logit(4th) - logit(5th)  (inf when absent)
 
 
 def topk_gate(logits: np.ndarray, k: int = 2) -> Routing:
@@ -105,7 +117,13 @@ def topk_gate(logits: np.ndarray, k: int = 2) -> Routing:
     srt = np.take_along_axis(logits, order, axis=1)
     gap12 = srt[:, 0] - srt[:, 1]
     gap23 = srt[:, k - 1] - srt[:, k] if E > k else np.full(T, np.inf)
-    return Routing(ids.astype(np.int64), G, gap12, gap23)
+    nxt = np.full((T, 2), -1, dtype=np.int64)
+    for j in range(2):
+        if E > k + j:
+            nxt[:, j] = order[:, k + j]
+    gap34 = srt[:, k] - srt[:, k + 1] if E > k + 1 else np.full(T, np.inf)
+    gap45 = srt[:, k + 1] - srt[:, k + 2] if E > k + 2 else np.full(T, np.inf)
+    return Routing(ids.astype(np.int64), G, gap12, gap23, nxt, gap34, gap45)
 
 
 def capacity_select(ids: np.ndarray, G: np.ndarray, n_experts: int, capacity: int):
@@ -131,6 +149,48 @@ def capacity_select(ids: np.ndarray, G: np.ndarray, n_experts: int, capacity: in
         keep.ravel()[dropped] = False
         cutoff[e] = g_e[rank[capacity - 1]] if capacity > 0 else np.inf
     return keep, cutoff
+
+
+def fallback_targets(keep: np.ndarray, next_ids: np.ndarray) -> np.ndarray:
+    """Expert each dropped assignment falls back to (-1: kept, or no such expert).
+
+    One dropped slot goes to the 3rd-ranked expert; when both slots of a token
+    are dropped, slot 0 goes to the 3rd-ranked and slot 1 to the 4th-ranked."""
+    T, k = keep.shape
+    target = np.full((T, k), -1, dtype=np.int64)
+    for t in range(T):
+        dropped = [s for s in range(k) if not keep[t, s]]
+        for j, s in enumerate(dropped):
+            target[t, s] = next_ids[t, j]
+    return target
+
+
+def fallback_select(ids: np.ndarray, next_ids: np.ndarray, G: np.ndarray, keep: np.ndarray,
+                    n_experts: int, capacity: int):
+    """Second capacity round for the assignments ``capacity_select`` dropped.
+
+    Returns (final_ids [T, k], status [T, k] uint8 -- 0 kept by its top-2
+    expert, 1 dropped, 2 kept by its fallback expert -- and cutoff [E]: the
+    smallest G an expert took in this round when candidates were left over,
+    +inf when it had no free slot for them, NaN otherwise)."""
+    T, k = ids.shape
+    final = ids.copy()
+    status = np.where(keep, 0, 1).astype(np.uint8)
+    cutoff = np.full(n_experts, np.nan)
+    target = fallback_targets(keep, next_ids)
+    tok = np.repeat(np.arange(T), k).reshape(T, k)
+    for e in range(n_experts):
+        free = capacity - int(np.count_nonzero((ids == e) & keep))
+        sel = target == e
+        t_e, g_e = tok[sel], G[sel]
+        rank = np.lexsort((t_e, -g_e))                 # primary -G, secondary token
+        flat = np.flatnonzero(sel.ravel())
+        taken = flat[rank[:free]]
+        status.ravel()[taken] = 2
+        final.ravel()[taken] = e
+        if len(t_e) > free:
+            cutoff[e] = g_e[rank[free - 1]] if free > 0 else np.inf
+    return final, status, cutoff
 
 
 @dataclasses.dataclass
@@ -191,18 +251,23 @@ def swiglu_act_quant(xr: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndar
 class OracleResult:
     logits: np.ndarray
     routing: Routing
-    keep: np.ndarray
+    keep: np.ndarray                    # [T, k] final: the assignment contributes
     cutoff: np.ndarray
     perm: Permutation
     y: np.ndarray                       # [T, d] (rows not in ``tokens`` are NaN)
     y_perm: Optional[np.ndarray] = None # [N_kept, d] (rows not computed are NaN)
     h: Optional[np.ndarray] = None      # [N_kept, F] when requested
+    status: Optional[np.ndarray] = None     # [T, k] 0 kept / 1 dropped / 2 kept by the fallback
+    final_ids: Optional[np.ndarray] = None  # [T, k] expert that processes each slot
+    cutoff2: Optional[np.ndarray] = None    # [E] cutoff of the fallback round
 
 
 def forward(inputs, tokens: Optional[Iterable[int]] = None,
             override: Optional[Dict[int, Iterable[int]]] = None,
             keep_override: Optional[np.ndarray] = None,
-            want_h: bool = False) -> OracleResult:
+            want_h: bool = False,
+            next_override: Optional[Dict[int, Iterable[int]]] = None,
+            status_override: Optional[np.ndarray] = None) -> OracleResult:
     """Run the layer on ``inputs`` (a MoEInputs of host tensors).
 
     tokens: compute the expert FFN / output only for these tokens (all
@@ -214,6 +279,12 @@ def forward(inputs, tokens: Optional[Iterable[int]] = None,
     keep_override: a [T, k] keep mask replacing the capacity decision; it must
         agree with the oracle's own except for assignments whose G lies
         within NEAR_TIE of their expert's cutoff.
+    next_override: {token: (n0, n1)} 3rd/4th-ranked experts to use instead
+        of the oracle's, accepted only where a logit gap among ranks 2..5 is
+        below NEAR_TIE.
+    status_override: a [T, k] fallback-round status (0/1/2) replacing the
+        oracle's, accepted only where it differs at a fallback cutoff near
+        tie (G within NEAR_TIE of the target expert's cutoff).
     """
     cfg = inputs.cfg
     E, k = cfg.n_experts, cfg.top_k
@@ -242,7 +313,30 @@ def forward(inputs, tokens: Optional[Iterable[int]] = None,
             if not (abs(r.G[t, s] - cutoff[e]) < NEAR_TIE):
                 raise ValueError(f"keep override at ({t},{s}) is not at the capacity cutoff")
         keep = keep_override.astype(bool)
-    perm = permutation(r.ids, keep, E)
+    status = final_ids = cutoff2 = None
+    if cfg.capacity >= 0 and getattr(cfg, "overflow", "drop") == "next_best":
+        if next_override:
+            for t, pair in next_override.items():
+                pair = tuple(int(v) for v in pair)
+                if tuple(r.next_ids[t]) == pair:
+                    continue
+                if not min(r.gap23[t], r.gap34[t], r.gap45[t]) < NEAR_TIE:
+                    raise ValueError(f"next-expert override of token {t} is not a near tie")
+                r.next_ids[t] = pair
+        final_ids, status, cutoff2 = fallback_select(r.ids, r.next_ids, r.G, keep, E, cfg.capacity)
+        if status_override is not None:
+            target = fallback_targets(keep, r.next_ids)
+            for t, s_ in np.argwhere(status_override != status):
+                e = target[t, s_]
+                if status[t, s_] == 0 or status_override[t, s_] == 0 or e < 0 or \
+                        not abs(r.G[t, s_] - cutoff2[e]) < NEAR_TIE:
+                    raise ValueError(f"status override at ({t},{s_}) is not at a fallback cutoff")
+            status = status_override.astype(np.uint8)
+            final_ids = np.where(status == 2, target, r.ids)
+        keep = status != 1
+        perm = permutation(final_ids, keep, E)
+    else:
+        perm = permutation(r.ids, keep, E)
 
     T, d = x.shape
     want = np.arange(T) if tokens is None else np.unique(np.asarray(list(tokens), dtype=np.int64))
@@ -273,9 +367,15 @@ def forward(inputs, tokens: Optional[Iterable[int]] = None,
             row = perm.slot_to_row[t * k + s]
             if row >= 0:
                 y[t] += r.G[t, s] * y_perm[row]
-    return OracleResult(logits, r, keep, cutoff, perm, y, y_perm, h_all)
+    return OracleResult(logits, r, keep, cutoff, perm, y, y_perm, h_all, status, final_ids, cutoff2)
 
 
 def near_tie_tokens(res: OracleResult) -> np.ndarray:
     """Tokens whose top-2 set (gap23) or slot order (gap12) is a near tie."""
     return np.flatnonzero((res.routing.gap23 < NEAR_TIE) | (res.routing.gap12 < NEAR_TIE))
+
+
+def near_tie_next_tokens(res: OracleResult) -> np.ndarray:
+    """Tokens whose 3rd/4th-ranked experts (the fallback targets) are a near tie."""
+    r = res.routing
+    return np.flatnonzero(np.minimum(np.minimum(r.gap23, r.gap34), r.gap45) < NEAR_TIE)

@@ -48,6 +48,7 @@ class MoEConfig:
     n_experts: int = 8
     top_k: int = 2
     capacity: int = -1          # -1: dropless; else slots per expert (0 drops all)
+    overflow: str = "drop"      # over-capacity assignments: "drop" | "next_best" (fallback round)
     act_dtype: str = "bf16"     # x, w_gate, y: "f32" | "bf16"
     w_dtype: str = "bf16"       # w1/w3/w2: "f32" | "bf16" | "fp8_e4m3"
     x_std: float = 1.0

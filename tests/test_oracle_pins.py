@@ -30,11 +30,11 @@ class _Inp:
         self.w1_scale = self.w3_scale = self.w2_scale = None
 
 
-def _micro(T=6, d=8, F=12, E=4, seed=3, capacity=-1, bias=False):
+def _micro(T=6, d=8, F=12, E=4, seed=3, capacity=-1, bias=False, overflow="drop"):
     g = np.random.default_rng(seed)
     f32 = lambda *s: g.standard_normal(s).astype(np.float32).astype(np.float64)  # noqa: E731
     cfg = synthetic.MoEConfig(name="micro", T=T, d_model=d, d_ff=F, n_experts=E, capacity=capacity,
-                              act_dtype="f32", w_dtype="f32")
+                              act_dtype="f32", w_dtype="f32", overflow=overflow)
     b = f32(E) if bias else None
     return _Inp(cfg, f32(T, d), f32(E, d) / math.sqrt(d), f32(E, F, d) / math.sqrt(d),
                 f32(E, F, d) / math.sqrt(d), f32(E, d, F) / math.sqrt(F), b)
@@ -118,6 +118,91 @@ def test_oracle_matches_dense_brute_force(capacity, bias):
     assert np.max(np.abs(np.array(yb) - res.y)) < 1e-12
     if capacity == 0:
         assert np.all(res.y == 0.0)
+
+
+@pytest.mark.parametrize("T,E,capacity,bias,seed", [(6, 4, 1, False, 3), (6, 4, 2, True, 3),
+                                                     (6, 4, 0, False, 3), (9, 5, 2, False, 7),
+                                                     (8, 3, 2, True, 4), (7, 2, 3, False, 5),
+                                                     (12, 6, 3, True, 9)])
+def test_fallback_matches_dense_brute_force(T, E, capacity, bias, seed):
+    """Overflow fallback: grouped oracle vs the literal per-slot offers of brute.layer."""
+    inp = _micro(T=T, E=E, seed=seed, capacity=capacity, bias=bias, overflow="next_best")
+    res = oracle.forward(inp)
+    yb, ids, Gf, final = brute.layer(inp.x.tolist(), inp.w_gate.tolist(), inp.w1.tolist(),
+                                     inp.w3.tolist(), inp.w2.tolist(), 2,
+                                     None if inp.router_bias is None else inp.router_bias.tolist(),
+                                     capacity, overflow="next_best")
+    assert res.routing.ids.tolist() == ids
+    for t in range(T):
+        for s in range(2):
+            if final[t][s] is None:
+                assert res.status[t, s] == 1
+            else:
+                assert res.status[t, s] in (0, 2) and res.final_ids[t, s] == final[t][s]
+                assert (res.status[t, s] == 2) == (final[t][s] != ids[t][s])
+    assert np.max(np.abs(np.array(yb) - res.y)) < 1e-12
+    if capacity == 0:
+        assert np.all(res.y == 0.0) and np.all(res.status == 1)
+
+
+def test_fallback_worked_example():
+    """Hand-worked case, E = 4, capacity 1, logits fed through W_g = I.
+
+    t0 logits (4, 3, 2, 1):     top-2 (0, 1), G = (s, 1-s) with s = 1/(1+e^-1); ranks 3, 4 = (2, 3)
+    t1 logits (3, 4, 1, 2):     top-2 (1, 0), G = (s, 1-s); ranks 3, 4 = (3, 2)
+    t2 logits (3.5, 0, .5, .25): top-2 (0, 2), G = (u, 1-u), u = 1/(1+e^-3); ranks 3, 4 = (3, 1)
+    Capacity round: e0 gets t0s0 (s), t1s1 (1-s), t2s0 (u) -> keeps t2s0 (u > s).
+    e1 gets t0s1 (1-s), t1s0 (s) -> keeps t1s0.  e2 keeps t2s1.  e3 gets nothing.
+    Fallback: t0 lost both slots -> s0 offered to e2, s1 to e3; t1 lost s1 -> offered to e3.
+    e2 has no free slot: t0s0 stays dropped.  e3 has one: t0s1 and t1s1 tie on G = 1-s,
+    the lower token wins -> t0s1 kept at e3, t1s1 dropped.
+    """
+    logits = np.array([[4, 3, 2, 1], [3, 4, 1, 2], [3.5, 0, 0.5, 0.25]], dtype=np.float64)
+    r = oracle.topk_gate(oracle.router_logits(logits, np.eye(4)), 2)
+    assert r.ids.tolist() == [[0, 1], [1, 0], [0, 2]]
+    assert r.next_ids.tolist() == [[2, 3], [3, 2], [3, 1]]
+    keep, _ = oracle.capacity_select(r.ids, r.G, 4, 1)
+    assert keep.tolist() == [[False, False], [True, False], [True, True]]
+    final, status, cut2 = oracle.fallback_select(r.ids, r.next_ids, r.G, keep, 4, 1)
+    assert status.tolist() == [[1, 2], [0, 1], [0, 0]]
+    assert final[0, 1] == 3 and final[1, 0] == 1 and final[2].tolist() == [0, 2]
+    assert cut2[2] == np.inf and abs(cut2[3] - (1 - 1 / (1 + math.exp(-1)))) < 1e-15
+    p = oracle.permutation(final, status != 1, 4)
+    assert p.counts.tolist() == [1, 1, 1, 1]
+    assert p.perm_src.tolist() == [4, 2, 5, 1]          # e0: t2s0, e1: t1s0, e2: t2s1, e3: t0s1
+
+
+def test_fallback_invariants():
+    g = np.random.default_rng(21)
+    T, E, k = 400, 8, 2
+    logits = g.standard_normal((T, E)) + np.array([2.0, 1.0, 0.5, 0, 0, 0, 0, -0.5])
+    r = oracle.topk_gate(logits, k)
+    for C in (0, 1, 20, 60, 100, 200, 800):
+        keep, _ = oracle.capacity_select(r.ids, r.G, E, C)
+        final, status, _ = oracle.fallback_select(r.ids, r.next_ids, r.G, keep, E, C)
+        assert np.all(status[keep] == 0) and np.all(status[~keep] != 0)
+        kept = status != 1
+        counts = np.bincount(final[kept], minlength=E)
+        assert np.all(counts <= C)
+        assert kept.sum() >= keep.sum()
+        for t, s in np.argwhere(status == 2):
+            e = final[t, s]
+            assert e not in r.ids[t] and e in r.next_ids[t]
+            assert e == (r.next_ids[t, s] if not keep[t].any() else r.next_ids[t, 0])
+        # per expert: the fallback round fills exactly min(free slots, offers)
+        target = oracle.fallback_targets(keep, r.next_ids)
+        for e in range(E):
+            free = C - int(np.count_nonzero((r.ids == e) & keep))
+            offers = int(np.count_nonzero(target == e))
+            assert int(np.count_nonzero((status == 2) & (final == e))) == min(free, offers)
+        if C >= T * k:
+            assert np.all(status == 0)
+    # next-ranked experts are the 3rd and 4th by (logit desc, index asc), distinct from the top-2
+    assert np.all(r.next_ids[:, 0] != r.next_ids[:, 1])
+    assert not np.any(np.isin(r.next_ids[:, :1], r.ids) & (r.next_ids[:, :1] == r.ids[:, :1]))
+    srt = np.sort(-logits, axis=1)
+    assert np.allclose(-srt[:, 2], logits[np.arange(T), r.next_ids[:, 0]])
+    assert np.allclose(-srt[:, 3], logits[np.arange(T), r.next_ids[:, 1]])
 
 
 def test_dense_reduction_all_experts_equal():
