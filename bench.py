@@ -157,9 +157,11 @@ def main():
 
     def step(i, timed):
         d = copies[i % len(copies)]
+        fallback = cfg.capacity >= 0 and cfg.overflow == "next_best"
         moe.moe_route_topk(shape, d.x, d.w_gate, d.router_bias, st["topk_ids"],
-                           st["topk_weights"], None, stream)
-        moe.moe_permute(shape, st["topk_ids"], st["topk_weights"], d.x, st["expert_counts"],
+                           st["topk_weights"], None, st["next_ids"] if fallback else None, stream)
+        moe.moe_permute(shape, st["topk_ids"], st["topk_weights"],
+                        st["next_ids"] if fallback else None, d.x, st["expert_counts"],
                         st["expert_offsets"], st["perm_src"], st["slot_to_row"],
                         st["drop_mask"] if cfg.capacity >= 0 else None,
                         st["x_perm"], st["x_perm_scale"], None, stream)
@@ -224,6 +226,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
                    "n_experts": cfg.n_experts, "top_k": cfg.top_k,
                    "capacity": None if cfg.capacity < 0 else cfg.capacity,
+                   "overflow": cfg.overflow if cfg.capacity >= 0 else None,
                    "act_dtype": cfg.act_dtype, "w_dtype": cfg.w_dtype,
                    "weight_copies_alternated": len(copies)},
         "fused_ms_per_step": round(fused_ms, 4),

@@ -71,6 +71,22 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
 
 #define MOE_DROPLESS (-1)
 
+/* What happens to an assignment the capacity limit drops (moe_shape_t.overflow).
+ * Pages: "How Mixtral 8x7B uses mixture of experts", section "Routing without
+ * auxiliary loss": over-capacity tokens are dropped and handled by a
+ * fallback, typically the next-best expert.
+ *   MOE_OVERFLOW_DROP       it contributes nothing.
+ *   MOE_OVERFLOW_NEXT_BEST  one fallback round: a dropped slot is offered to the
+ *     token's best expert outside its top-2 (3rd-ranked by logit; when both
+ *     slots of the token were dropped, slot 0 to the 3rd- and slot 1 to the
+ *     4th-ranked), keeping its gate weight.  Each expert takes the offers into
+ *     the slots the capacity round left free (capacity minus what it kept),
+ *     ranked like the capacity round (gate weight descending, then token
+ *     ascending); the other offers stay dropped.  The ranking ties to the
+ *     lower expert index, like the top-2. */
+#define MOE_OVERFLOW_DROP 0
+#define MOE_OVERFLOW_NEXT_BEST 1
+
 typedef struct {
   int32_t T;          /* tokens (batch * seq_len, flattened) */
   int32_t d_model;    /* hidden size d */
@@ -80,6 +96,7 @@ typedef struct {
   int32_t capacity;   /* MOE_DROPLESS, or slots per expert (0 drops every assignment) */
   int32_t act_dtype;  /* moe_dtype_t of x, W_g, y */
   int32_t w_dtype;    /* moe_dtype_t of w1, w3, w2 */
+  int32_t overflow;   /* MOE_OVERFLOW_DROP or MOE_OVERFLOW_NEXT_BEST (ignored when dropless) */
 } moe_shape_t;
 
 /* Which call a workspace is sized for. */
@@ -108,10 +125,14 @@ moe_status_t moe_workspace_bytes(const moe_shape_t* shape, moe_call_t call, size
  *   topk_ids     [T, 2] int32 out: slot 0 = larger logit, ties -> lower index
  *   topk_weights [T, 2] fp32 out: w0 = 1/(1+exp(l1-l0)), w1 = 1-w0 (w0+w1 == 1 exactly)
  *   logits       [T, E] fp32 out, or NULL
+ *   next_ids     [T, 2] int32 out, or NULL: the 3rd- and 4th-ranked experts of
+ *                each token (same order: logit descending, ties -> lower index),
+ *                -1 where n_experts is too small.  moe_permute needs them for
+ *                MOE_OVERFLOW_NEXT_BEST.
  * Logits accumulate in fp32.  No workspace. */
 moe_status_t moe_route_topk(const moe_shape_t* shape, const void* x, const void* w_gate,
                             const float* router_bias, int32_t* topk_ids, float* topk_weights,
-                            float* logits, void* stream);
+                            float* logits, int32_t* next_ids, void* stream);
 
 /* Capacity selection (when shape->capacity >= 0) and grouping of tokens by expert.
  * Pages: "How Mixtral 8x7B uses mixture of experts", sections "Routing without
@@ -119,21 +140,28 @@ moe_status_t moe_route_topk(const moe_shape_t* shape, const void* x, const void*
  * bincount of the top-2 ids (expert activation listing); "batch tokens by
  * expert ... scatter back" in the simplified forward pass.
  *   topk_ids, topk_weights [T, 2] from moe_route_topk
+ *   next_ids       [T, 2] from moe_route_topk; required with a capacity and
+ *                  MOE_OVERFLOW_NEXT_BEST, else ignored (may be NULL)
  *   x              [T, d] act dtype
  *   expert_counts  [E] int32 out: kept assignments per expert
  *   expert_offsets [E+1] int32 out: exclusive prefix sum of counts
  *   perm_src       [T*2] int32 out: rows 0..offsets[E]-1 hold t*2+slot of each row
  *   slot_to_row    [T*2] int32 out: row of (t, slot), -1 if dropped
- *   drop_mask      [T*2] uint8 out or NULL: 1 = dropped by the capacity limit
+ *   drop_mask      [T*2] uint8 out or NULL: 0 = kept by its top-2 expert,
+ *                  1 = dropped, 2 = kept by its fallback expert (NEXT_BEST)
  *   x_perm         [T*2, d] out: x_perm[row] = x[perm_src[row] / 2]; fp8 configs:
  *                  e4m3 codes [T*2, d] plus x_perm_scale [T*2, d/32] E8M0 bytes
  *   x_perm_scale   fp8 configs only (else ignored; may be NULL)
  * Capacity rule: per expert, assignments ranked by gate weight (descending,
  * compared as fp32), ties to the lower token index; the first `capacity`
  * are kept.  A dropped assignment contributes nothing and the token's other
- * slot is not renormalised.  Workspace: moe_workspace_bytes(MOE_CALL_PERMUTE). */
+ * slot is not renormalised; with MOE_OVERFLOW_NEXT_BEST the fallback round
+ * above runs next and the rows of each expert include the slots it took
+ * (still one row per token and expert, in ascending token order).
+ * Workspace: moe_workspace_bytes(MOE_CALL_PERMUTE). */
 moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_ids,
-                         const float* topk_weights, const void* x, int32_t* expert_counts,
+                         const float* topk_weights, const int32_t* next_ids, const void* x,
+                         int32_t* expert_counts,
                          int32_t* expert_offsets, int32_t* perm_src, int32_t* slot_to_row,
                          uint8_t* drop_mask, void* x_perm, uint8_t* x_perm_scale,
                          void* workspace, size_t workspace_bytes, void* stream);
@@ -189,7 +217,10 @@ moe_status_t moe_combine(const moe_shape_t* shape, const float* y_perm, const in
  *   w1, w3 [E, F, d], w2 [E, d, F] weight dtype; w*_scale fp32 per output channel (fp8 only)
  *   y [T, d] act dtype out
  *   optional outputs (NULL to skip): topk_ids_out [T, 2] int32, topk_weights_out [T, 2]
- *   fp32, expert_counts_out [E] int32, drop_mask_out [T*2] uint8, logits_out [T, E] fp32
+ *   fp32, expert_counts_out [E] int32, drop_mask_out [T*2] uint8 (0 / 1 / 2 as in
+ *   moe_permute), logits_out [T, E] fp32
+ * topk_ids_out are the router's choices; with MOE_OVERFLOW_NEXT_BEST a slot
+ * whose drop mask is 2 was processed by its fallback expert instead.
  * Workspace: moe_workspace_bytes(MOE_CALL_FORWARD) holds every intermediate. */
 moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const void* w_gate,
                          const float* router_bias, const void* w1, const void* w3, const void* w2,

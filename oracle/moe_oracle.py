@@ -260,6 +260,7 @@ class OracleResult:
     status: Optional[np.ndarray] = None     # [T, k] 0 kept / 1 dropped / 2 kept by the fallback
     final_ids: Optional[np.ndarray] = None  # [T, k] expert that processes each slot
     cutoff2: Optional[np.ndarray] = None    # [E] cutoff of the fallback round
+    keep1: Optional[np.ndarray] = None      # [T, k] kept by the capacity round (before any fallback)
 
 
 def forward(inputs, tokens: Optional[Iterable[int]] = None,
@@ -313,6 +314,7 @@ def forward(inputs, tokens: Optional[Iterable[int]] = None,
             if not (abs(r.G[t, s] - cutoff[e]) < NEAR_TIE):
                 raise ValueError(f"keep override at ({t},{s}) is not at the capacity cutoff")
         keep = keep_override.astype(bool)
+    keep1 = keep
     status = final_ids = cutoff2 = None
     if cfg.capacity >= 0 and getattr(cfg, "overflow", "drop") == "next_best":
         if next_override:
@@ -367,7 +369,8 @@ def forward(inputs, tokens: Optional[Iterable[int]] = None,
             row = perm.slot_to_row[t * k + s]
             if row >= 0:
                 y[t] += r.G[t, s] * y_perm[row]
-    return OracleResult(logits, r, keep, cutoff, perm, y, y_perm, h_all, status, final_ids, cutoff2)
+    return OracleResult(logits, r, keep, cutoff, perm, y, y_perm, h_all, status, final_ids, cutoff2,
+                        keep1)
 
 
 def near_tie_tokens(res: OracleResult) -> np.ndarray:

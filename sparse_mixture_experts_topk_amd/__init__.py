@@ -15,15 +15,17 @@ import torch
 
 from . import _lib
 from ._lib import (MOE_BF16, MOE_CALL_DOWN, MOE_CALL_FORWARD, MOE_CALL_GATE_UP,
-                   MOE_CALL_PERMUTE, MOE_DROPLESS, MOE_F32, MOE_FP8_E4M3, MoeShape)
+                   MOE_CALL_PERMUTE, MOE_DROPLESS, MOE_F32, MOE_FP8_E4M3, MOE_OVERFLOW_DROP,
+                   MOE_OVERFLOW_NEXT_BEST, MoeShape)
 
 __all__ = ["MoEError", "MoeShape", "make_shape", "moe_status_string", "moe_version",
            "moe_workspace_bytes", "moe_route_topk", "moe_permute", "moe_expert_gemm_gate_up",
            "moe_expert_gemm_down", "moe_combine", "moe_forward", "MOE_F32", "MOE_BF16",
            "MOE_FP8_E4M3", "MOE_DROPLESS", "MOE_CALL_PERMUTE", "MOE_CALL_GATE_UP",
-           "MOE_CALL_DOWN", "MOE_CALL_FORWARD"]
+           "MOE_CALL_DOWN", "MOE_CALL_FORWARD", "MOE_OVERFLOW_DROP", "MOE_OVERFLOW_NEXT_BEST"]
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
+_OVF = {"drop": MOE_OVERFLOW_DROP, "next_best": MOE_OVERFLOW_NEXT_BEST}
 
 
 class MoEError(RuntimeError):
@@ -33,16 +35,17 @@ class MoEError(RuntimeError):
 
 
 def make_shape(T: int, d_model: int, d_ff: int, n_experts: int = 8, top_k: int = 2,
-               capacity: int = MOE_DROPLESS, act_dtype="bf16", w_dtype="bf16") -> MoeShape:
+               capacity: int = MOE_DROPLESS, act_dtype="bf16", w_dtype="bf16",
+               overflow="drop") -> MoeShape:
     a = _DT.get(act_dtype, act_dtype)
     w = _DT.get(w_dtype, w_dtype)
-    return MoeShape(T, d_model, d_ff, n_experts, top_k, capacity, a, w)
+    return MoeShape(T, d_model, d_ff, n_experts, top_k, capacity, a, w, _OVF.get(overflow, overflow))
 
 
 def shape_of(cfg) -> MoeShape:
     """Shape of a synthetic.MoEConfig."""
     return make_shape(cfg.T, cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, cfg.capacity,
-                      cfg.act_dtype, cfg.w_dtype)
+                      cfg.act_dtype, cfg.w_dtype, cfg.overflow)
 
 
 def _p(t: Optional[torch.Tensor]):
@@ -86,17 +89,18 @@ def moe_workspace_bytes(shape: MoeShape, call: int = MOE_CALL_FORWARD) -> int:
 
 
 def moe_route_topk(shape, x, w_gate, router_bias, topk_ids, topk_weights, logits=None,
-                   stream=None):
+                   next_ids=None, stream=None):
     _check("moe_route_topk", _lib.load().moe_route_topk(
         ctypes.byref(shape), _p(x), _p(w_gate), _p(router_bias), _p(topk_ids), _p(topk_weights),
-        _p(logits), _stream(stream)))
+        _p(logits), _p(next_ids), _stream(stream)))
 
 
-def moe_permute(shape, topk_ids, topk_weights, x, expert_counts, expert_offsets, perm_src,
-                slot_to_row, drop_mask, x_perm, x_perm_scale=None, workspace=None, stream=None):
+def moe_permute(shape, topk_ids, topk_weights, next_ids, x, expert_counts, expert_offsets,
+                perm_src, slot_to_row, drop_mask, x_perm, x_perm_scale=None, workspace=None,
+                stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("moe_permute", _lib.load().moe_permute(
-        ctypes.byref(shape), _p(topk_ids), _p(topk_weights), _p(x), _p(expert_counts),
+        ctypes.byref(shape), _p(topk_ids), _p(topk_weights), _p(next_ids), _p(x), _p(expert_counts),
         _p(expert_offsets), _p(perm_src), _p(slot_to_row), _p(drop_mask), _p(x_perm),
         _p(x_perm_scale), _p(workspace), ws_bytes, _stream(stream)))
 

@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_DROPLESS = -1
+MOE_OVERFLOW_DROP, MOE_OVERFLOW_NEXT_BEST = 0, 1
 MOE_CALL_PERMUTE, MOE_CALL_GATE_UP, MOE_CALL_DOWN, MOE_CALL_FORWARD = range(4)
 
 # Every symbol include/moe.h declares.
@@ -21,7 +22,7 @@ class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("w_dtype", ctypes.c_int32)]
+                ("w_dtype", ctypes.c_int32), ("overflow", ctypes.c_int32)]
 
 
 P = ctypes.c_void_p
@@ -33,8 +34,8 @@ _SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [I32]),
     "moe_version": (ctypes.c_char_p, []),
     "moe_workspace_bytes": (I32, [SHAPE, I32, ctypes.POINTER(SZ)]),
-    "moe_route_topk": (I32, [SHAPE, P, P, P, P, P, P, P]),
-    "moe_permute": (I32, [SHAPE, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+    "moe_route_topk": (I32, [SHAPE, P, P, P, P, P, P, P, P]),
+    "moe_permute": (I32, [SHAPE, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
     "moe_expert_gemm_gate_up": (I32, [SHAPE, P, P, P, P, P, P, P, P, P, P, SZ, P]),
     "moe_expert_gemm_down": (I32, [SHAPE, P, P, P, P, P, P, P, SZ, P]),
     "moe_combine": (I32, [SHAPE, P, P, P, P, P]),

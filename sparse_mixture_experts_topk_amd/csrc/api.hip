@@ -79,6 +79,8 @@ moe_status_t validate_shape(const moe_shape_t* s) {
   if (s->top_k < 1 || s->n_experts < 2 || s->top_k > s->n_experts) return MOE_ERR_INVALID_ARG;
   if (s->d_model <= 0 || s->d_ff <= 0) return MOE_ERR_INVALID_ARG;
   if (s->capacity < MOE_DROPLESS) return MOE_ERR_INVALID_ARG;
+  if (s->overflow != MOE_OVERFLOW_DROP && s->overflow != MOE_OVERFLOW_NEXT_BEST)
+    return MOE_ERR_INVALID_ARG;
   const bool known = (s->act_dtype == MOE_F32 || s->act_dtype == MOE_BF16) &&
                      (s->w_dtype == MOE_F32 || s->w_dtype == MOE_BF16 || s->w_dtype == MOE_FP8_E4M3);
   if (!known) return MOE_ERR_INVALID_ARG;
@@ -111,9 +113,14 @@ moe_status_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 // Workspace layout of moe_forward (each region 256-byte aligned).
 struct ForwardLayout {
-  size_t ids, weights, counts, offsets, perm_src, slot_to_row, drop, x_perm, x_scale, h, h_scale,
-      y_perm, down_ws, total;
+  size_t ids, weights, next_ids, counts, offsets, perm_src, slot_to_row, drop, x_perm, x_scale, h,
+      h_scale, y_perm, down_ws, total;
 };
+
+// The overflow fallback round runs (and needs the 3rd/4th-ranked experts).
+bool fallback_on(const moe_shape_t& s) {
+  return s.capacity >= 0 && s.overflow == MOE_OVERFLOW_NEXT_BEST;
+}
 
 // Workspace of moe_expert_gemm_down: partial tiles of the split tail work
 // (bf16 many-rows path only).
@@ -129,6 +136,7 @@ ForwardLayout forward_layout(const moe_shape_t& s) {
   size_t o = 0;
   L.ids = o;         o += align_up(A * 4);
   L.weights = o;     o += align_up(A * 4);
+  L.next_ids = o;    o += fallback_on(s) ? align_up(A * 4) : 0;
   L.counts = o;      o += align_up(64 * 4);
   L.offsets = o;     o += align_up(65 * 4);
   L.perm_src = o;    o += align_up(A * 4);
@@ -179,17 +187,19 @@ moe_status_t moe_workspace_bytes(const moe_shape_t* s, moe_call_t call, size_t* 
 
 moe_status_t moe_route_topk(const moe_shape_t* s, const void* x, const void* w_gate,
                             const float* router_bias, int32_t* topk_ids, float* topk_weights,
-                            float* logits, void* stream) {
+                            float* logits, int32_t* next_ids, void* stream) {
   moe_status_t v = validate_shape(s);
   if (v != MOE_OK) return v;
   if (s->T == 0) return MOE_OK;
-  if ((v = check_ptrs({x, w_gate, topk_ids, topk_weights}, {router_bias, logits})) != MOE_OK) return v;
+  if ((v = check_ptrs({x, w_gate, topk_ids, topk_weights}, {router_bias, logits, next_ids})) != MOE_OK)
+    return v;
   return from_hip(moe::launch_route_topk(*s, x, w_gate, router_bias, topk_ids, topk_weights, logits,
-                                         static_cast<hipStream_t>(stream)));
+                                         next_ids, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_ids, const float* topk_weights,
-                         const void* x, int32_t* expert_counts, int32_t* expert_offsets,
+                         const int32_t* next_ids, const void* x, int32_t* expert_counts,
+                         int32_t* expert_offsets,
                          int32_t* perm_src, int32_t* slot_to_row, uint8_t* drop_mask,
                          void* x_perm, uint8_t* x_perm_scale, void* workspace,
                          size_t workspace_bytes, void* stream) {
@@ -200,23 +210,25 @@ moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_ids, const fl
   if (s->T == 0) return MOE_OK;
   if ((v = check_ptrs({topk_ids, topk_weights, x, expert_counts, expert_offsets, perm_src,
                        slot_to_row, x_perm},
-                      {drop_mask})) != MOE_OK)
+                      {drop_mask, next_ids})) != MOE_OK)
     return v;
   const bool fp8 = s->w_dtype == MOE_FP8_E4M3;
   if (fp8 && x_perm_scale == nullptr) return MOE_ERR_INVALID_ARG;
   if (s->capacity >= 0 && drop_mask == nullptr) return MOE_ERR_INVALID_ARG;
+  if (fallback_on(*s) && next_ids == nullptr) return MOE_ERR_INVALID_ARG;
+  const int32_t* next = fallback_on(*s) ? next_ids : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   const uint8_t* drop_in = nullptr;
   if (s->capacity >= 0) {
-    e = moe::launch_capacity_select(*s, topk_ids, topk_weights, drop_mask, st);
+    e = moe::launch_capacity_select(*s, topk_ids, topk_weights, next, drop_mask, st);
     drop_in = drop_mask;
   } else if (drop_mask != nullptr) {
     e = launch_fill_u8(drop_mask, (int64_t)s->T * 2, 0, st);
   }
   if (e == hipSuccess)
-    e = moe::launch_permute_index(*s, topk_ids, drop_in, expert_counts, expert_offsets, perm_src,
-                                  slot_to_row, st);
+    e = moe::launch_permute_index(*s, topk_ids, drop_in, next, expert_counts, expert_offsets,
+                                  perm_src, slot_to_row, st);
   if (e == hipSuccess)
     e = moe::launch_permute_scatter(*s, x, expert_offsets, perm_src, x_perm, x_perm_scale, st);
   return from_hip(e);
@@ -300,19 +312,20 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_gate
   void* h = at<void>(workspace, L.h);
   uint8_t* h_scale = fp8 ? at<uint8_t>(workspace, L.h_scale) : nullptr;
   float* y_perm = at<float>(workspace, L.y_perm);
+  int32_t* next = fallback_on(*s) ? at<int32_t>(workspace, L.next_ids) : nullptr;
 
-  hipError_t e = moe::launch_route_topk(*s, x, w_gate, router_bias, ids, gw, logits_out, st);
+  hipError_t e = moe::launch_route_topk(*s, x, w_gate, router_bias, ids, gw, logits_out, next, st);
   const uint8_t* drop_in = nullptr;
   if (e == hipSuccess) {
     if (s->capacity >= 0) {
-      e = moe::launch_capacity_select(*s, ids, gw, drop, st);
+      e = moe::launch_capacity_select(*s, ids, gw, next, drop, st);
       drop_in = drop;
     } else if (drop_mask_out != nullptr) {
       e = launch_fill_u8(drop_mask_out, (int64_t)s->T * 2, 0, st);
     }
   }
   if (e == hipSuccess)
-    e = moe::launch_permute_index(*s, ids, drop_in, counts, offsets, perm_src, slot_to_row, st);
+    e = moe::launch_permute_index(*s, ids, drop_in, next, counts, offsets, perm_src, slot_to_row, st);
   if (e == hipSuccess) e = moe::launch_permute_scatter(*s, x, offsets, perm_src, x_perm, x_scale, st);
   if (e == hipSuccess)
     e = moe::launch_gate_up(*s, x_perm, x_scale, offsets, w1, w3, w1_scale, w3_scale, h, h_scale, st);

@@ -12,19 +12,22 @@
 
 namespace moe {
 
-// Router GEMV + top-2 + two-way softmax.
+// Router GEMV + top-2 + two-way softmax (+ 3rd/4th-ranked experts when next_ids != NULL).
 hipError_t launch_route_topk(const moe_shape_t& s, const void* x, const void* w_gate,
                              const float* bias, int32_t* ids, float* weights, float* logits,
-                             hipStream_t st);
+                             int32_t* next_ids, hipStream_t st);
 
-// Capacity selection: writes drop_mask[T*2] (1 = dropped).
+// Capacity selection: writes drop_mask[T*2] (0 kept, 1 dropped); with
+// MOE_OVERFLOW_NEXT_BEST a second round re-offers the dropped assignments to
+// next_ids and marks the ones taken with 2.
 hipError_t launch_capacity_select(const moe_shape_t& s, const int32_t* ids, const float* weights,
-                                  uint8_t* drop_mask, hipStream_t st);
+                                  const int32_t* next_ids, uint8_t* drop_mask, hipStream_t st);
 
-// Counts, offsets, perm_src, slot_to_row (drop_mask may be NULL: nothing dropped).
+// Counts, offsets, perm_src, slot_to_row (drop_mask may be NULL: nothing
+// dropped; next_ids is read for slots marked 2).
 hipError_t launch_permute_index(const moe_shape_t& s, const int32_t* ids, const uint8_t* drop_mask,
-                                int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                                int32_t* slot_to_row, hipStream_t st);
+                                const int32_t* next_ids, int32_t* counts, int32_t* offsets,
+                                int32_t* perm_src, int32_t* slot_to_row, hipStream_t st);
 
 // x_perm[row] = x[perm_src[row] / 2] (fp8: block-quantised codes + E8M0 scales).
 hipError_t launch_permute_scatter(const moe_shape_t& s, const void* x, const int32_t* offsets,

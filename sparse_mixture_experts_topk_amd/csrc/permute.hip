@@ -15,6 +15,14 @@
 //   keys than fit use an MSB-first radix select (8 passes of 8-bit digits,
 //   LDS histograms) over global memory instead.  Index-only,
 //   order-independent and therefore deterministic.
+//   Overflow fallback ("Routing without auxiliary loss": the excess goes to
+//   the next-best expert): a second launch of the same selection in which
+//   an assignment belongs to its fallback expert if the first round dropped
+//   it (the 3rd-ranked expert; with both slots of the token dropped, 3rd for
+//   slot 0 and 4th for slot 1), and each expert's capacity is what the first
+//   round left free.  Taken assignments are marked 2.  The round only turns
+//   marks 1 into 2, so "dropped in the first round" (mark != 0) reads the
+//   same in every workgroup while others write.
 // permute_index: one workgroup of 1024 lanes.  Pass 1 counts kept
 //   assignments per expert with LDS atomics (order-free).  Pass 2 walks the
 //   tokens in chunks of 1024; per expert a wavefront ballot + popcount gives
@@ -40,9 +48,30 @@ __device__ __forceinline__ uint64_t capacity_key(const float* w, int i) {
 // read their keys from global memory in every pass).
 constexpr int kCapKeysInLds = 8192;   // a power of two
 
+// Fallback expert of assignment i = 2 t + s that the capacity round dropped:
+// the token's 3rd-ranked expert, or its 4th for slot 1 when slot 0 was
+// dropped too (-1 where there is no such expert).
+__device__ __forceinline__ int fallback_expert(const uint8_t* drop, const int32_t* next, int i) {
+  const int t = i >> 1;
+  const int j = ((i & 1) && drop[2 * t] != 0) ? 1 : 0;
+  return next[2 * t + j];
+}
+
+// Expert that finally processes assignment i (-1: dropped).
+__device__ __forceinline__ int final_expert(const int32_t* ids, const uint8_t* drop,
+                                            const int32_t* next, int i) {
+  if (drop == nullptr) return ids[i];
+  const uint8_t m = drop[i];
+  return m == 0 ? ids[i] : m == 2 ? fallback_expert(drop, next, i) : -1;
+}
+
+// FALLBACK = false: the capacity round over the top-2 assignments (marks 0/1).
+// FALLBACK = true: the fallback round over the assignments the first marked 1.
+template <bool FALLBACK>
 __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __restrict__ ids,
                                                                const float* __restrict__ w,
-                                                               int n_assign, int capacity,
+                                                               const int32_t* __restrict__ next,
+                                                               int n_assign, int capacity_in,
                                                                uint8_t* __restrict__ drop) {
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
@@ -50,7 +79,26 @@ __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __
   __shared__ int s_count;
   __shared__ int s_digit;
   __shared__ int s_remaining;
+  __shared__ int s_kept;
   __shared__ uint64_t keys[kCapKeysInLds];
+  // the expert this round offers assignment i to (-1: none)
+  auto expert_of = [&](int i) -> int {
+    if constexpr (!FALLBACK) return ids[i];
+    return drop[i] != 0 ? fallback_expert(drop, next, i) : -1;
+  };
+  constexpr uint8_t kKept = FALLBACK ? 2 : 0;
+  int capacity = capacity_in;
+  if constexpr (FALLBACK) {
+    // slots left free by the first round: capacity minus what it kept
+    if (tid == 0) s_kept = 0;
+    __syncthreads();
+    int mine = 0;
+    for (int i = tid; i < n_assign; i += blockDim.x) mine += (ids[i] == e && drop[i] == 0) ? 1 : 0;
+    for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o);
+    if ((tid & 63) == 0) atomicAdd(&s_kept, mine);
+    __syncthreads();
+    capacity = capacity_in - s_kept;
+  }
 
   // pass 0: this expert's assignments; their keys go to LDS (any order: the
   // selection below depends only on the set of keys)
@@ -65,7 +113,7 @@ __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       const int i = i0 + q * blockDim.x + lane;
-      id[q] = i < n_assign ? ids[i] : -1;
+      id[q] = i < n_assign ? expert_of(i) : -1;
     }
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
@@ -86,12 +134,12 @@ __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __
 
   if (n_e <= capacity) {
     for (int i = tid; i < n_assign; i += blockDim.x)
-      if (ids[i] == e) drop[i] = 0;
+      if (expert_of(i) == e) drop[i] = kKept;
     return;
   }
   if (capacity == 0) {
     for (int i = tid; i < n_assign; i += blockDim.x)
-      if (ids[i] == e) drop[i] = 1;
+      if (expert_of(i) == e) drop[i] = 1;
     return;
   }
 
@@ -143,7 +191,7 @@ __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __
       if (tid < 256) hist[tid] = 0;
       __syncthreads();
       for (int i = tid; i < n_assign; i += blockDim.x) {
-        if (ids[i] != e) continue;
+        if (expert_of(i) != e) continue;
         const uint64_t key = capacity_key(w, i);
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
@@ -174,12 +222,12 @@ __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       const int i = i0 + q * blockDim.x;
-      id[q] = i < n_assign ? ids[i] : -1;
+      id[q] = i < n_assign ? expert_of(i) : -1;
     }
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       const int i = i0 + q * blockDim.x;
-      if (id[q] == e) drop[i] = capacity_key(w, i) >= prefix ? 0 : 1;
+      if (id[q] == e) drop[i] = capacity_key(w, i) >= prefix ? kKept : 1;
     }
   }
 }
@@ -188,8 +236,9 @@ constexpr int kIndexThreads = 1024;
 constexpr int kIndexWaves = kIndexThreads / kWave;
 
 __global__ __launch_bounds__(kIndexThreads) void permute_index_kernel(
-    const int32_t* __restrict__ ids, const uint8_t* __restrict__ drop, int T, int E,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ drop,
+    const int32_t* __restrict__ next, int T, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
     int32_t* __restrict__ slot_to_row) {
   __shared__ int s_count[64];
   __shared__ int s_base[64];
@@ -198,8 +247,10 @@ __global__ __launch_bounds__(kIndexThreads) void permute_index_kernel(
 
   if (tid < 64) s_count[tid] = 0;
   __syncthreads();
-  for (int i = tid; i < 2 * T; i += kIndexThreads)
-    if (drop == nullptr || drop[i] == 0) atomicAdd(&s_count[ids[i]], 1);
+  for (int i = tid; i < 2 * T; i += kIndexThreads) {
+    const int fe = final_expert(ids, drop, next, i);
+    if (fe >= 0) atomicAdd(&s_count[fe], 1);
+  }
   __syncthreads();
   if (tid == 0) {
     int run = 0;
@@ -218,13 +269,8 @@ __global__ __launch_bounds__(kIndexThreads) void permute_index_kernel(
     const int t = c0 + tid;
     int e0 = -1, e1 = -1;
     if (t < T) {
-      const int2 p = reinterpret_cast<const int2*>(ids)[t];
-      e0 = p.x;
-      e1 = p.y;
-      if (drop != nullptr) {
-        if (drop[2 * t]) e0 = -1;
-        if (drop[2 * t + 1]) e1 = -1;
-      }
+      e0 = final_expert(ids, drop, next, 2 * t);
+      e1 = final_expert(ids, drop, next, 2 * t + 1);
     }
     int rank0 = 0, rank1 = 0;
     for (int e = 0; e < E; ++e) {
@@ -335,17 +381,21 @@ __global__ void fill_u8_kernel(uint8_t* __restrict__ p, int64_t n, uint8_t v) {
 }  // namespace
 
 hipError_t launch_capacity_select(const moe_shape_t& s, const int32_t* ids, const float* weights,
-                                  uint8_t* drop_mask, hipStream_t st) {
-  hipLaunchKernelGGL(capacity_select_kernel, dim3(s.n_experts), dim3(1024), 0, st, ids, weights,
-                     2 * s.T, s.capacity, drop_mask);
+                                  const int32_t* next_ids, uint8_t* drop_mask, hipStream_t st) {
+  hipLaunchKernelGGL(capacity_select_kernel<false>, dim3(s.n_experts), dim3(1024), 0, st, ids,
+                     weights, nullptr, 2 * s.T, s.capacity, drop_mask);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || s.overflow != MOE_OVERFLOW_NEXT_BEST) return e;
+  hipLaunchKernelGGL(capacity_select_kernel<true>, dim3(s.n_experts), dim3(1024), 0, st, ids,
+                     weights, next_ids, 2 * s.T, s.capacity, drop_mask);
   return hipGetLastError();
 }
 
 hipError_t launch_permute_index(const moe_shape_t& s, const int32_t* ids, const uint8_t* drop_mask,
-                                int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                                int32_t* slot_to_row, hipStream_t st) {
+                                const int32_t* next_ids, int32_t* counts, int32_t* offsets,
+                                int32_t* perm_src, int32_t* slot_to_row, hipStream_t st) {
   hipLaunchKernelGGL(permute_index_kernel, dim3(1), dim3(kIndexThreads), 0, st, ids, drop_mask,
-                     s.T, s.n_experts, counts, offsets, perm_src, slot_to_row);
+                     next_ids, s.T, s.n_experts, counts, offsets, perm_src, slot_to_row);
   return hipGetLastError();
 }
 

@@ -11,6 +11,8 @@
 // recursive-halving exchange (6 shuffle rounds, 63 exchanges) then leaves lane
 // L holding the full logit of (token L / EP, expert L % EP); the top-2 is a
 // butterfly arg-max inside each EP-lane group, ties going to the lower index.
+// On request the two best experts outside the top-2 (ranks 3 and 4, the
+// targets of the overflow fallback) follow with the same arg-max.
 // W_g (64 KiB at d = 4096, E = 8) stays L2-resident; x is read once.
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -35,7 +37,8 @@ __device__ __forceinline__ void load_vec(const void* base, int64_t off, float* o
 template <int EP, bool BF16>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const void* __restrict__ x, const void* __restrict__ wg, const float* __restrict__ bias, int T,
-    int d, int E, int32_t* __restrict__ ids, float* __restrict__ wout, float* __restrict__ logits) {
+    int d, int E, int32_t* __restrict__ ids, float* __restrict__ wout, float* __restrict__ logits,
+    int32_t* __restrict__ next) {
   constexpr int TPW = kWave / EP;
   constexpr int VEC = BF16 ? 8 : 4;
   const int lane = threadIdx.x & 63;
@@ -113,6 +116,27 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     reinterpret_cast<int2*>(ids)[tok] = make_int2(i0, i1);
     reinterpret_cast<float2*>(wout)[tok] = make_float2(w0, 1.0f - w0);
   }
+  if (next != nullptr) {   // ranks 3 and 4: the same arg-max outside the top-2
+    float v2 = (real && e != i0 && e != i1) ? l : -INFINITY;
+    int i2 = e;
+#pragma unroll
+    for (int o = EP / 2; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(v2, o);
+      const int oi = __shfl_xor(i2, o);
+      if (ov > v2 || (ov == v2 && oi < i2)) { v2 = ov; i2 = oi; }
+    }
+    float v3 = (real && e != i0 && e != i1 && e != i2) ? l : -INFINITY;
+    int i3 = e;
+#pragma unroll
+    for (int o = EP / 2; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(v3, o);
+      const int oi = __shfl_xor(i3, o);
+      if (ov > v3 || (ov == v3 && oi < i3)) { v3 = ov; i3 = oi; }
+    }
+    // logits are finite, so -inf marks a rank past n_experts
+    if (e == 0 && tok < T)
+      reinterpret_cast<int2*>(next)[tok] = make_int2(v2 == -INFINITY ? -1 : i2, v3 == -INFINITY ? -1 : i3);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -122,7 +146,8 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 // past E / T), for EB blocks of 16 experts.  Partial tiles are summed through
 // LDS in a fixed order; wavefront 0 then holds, per lane, token (lane & 15)
 // and experts 16 eb + 4 (lane >> 4) + r.  Each lane keeps its local top-2
-// and two xor-shuffle merges (16, 32) give the token's top-2.  Exact in the
+// and two xor-shuffle merges (16, 32) give the token's top-2 (on request a
+// second such pass outside the top-2 gives ranks 3 and 4).  Exact in the
 // sense that matters: bf16 products are exact in fp32 and accumulate in fp32.
 constexpr int kRouteWaves = 8;
 
@@ -154,7 +179,7 @@ template <int EB>
 __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias,
     int T, int d, int E, int32_t* __restrict__ ids, float* __restrict__ wout,
-    float* __restrict__ logits) {
+    float* __restrict__ logits, int32_t* __restrict__ next) {
   __shared__ f32x4_t part[kRouteWaves - 1][EB][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tok0 = blockIdx.x * 16;
@@ -251,49 +276,77 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
     reinterpret_cast<int2*>(ids)[tok] = make_int2(i0, i1);
     reinterpret_cast<float2*>(wout)[tok] = make_float2(w0, 1.0f - w0);
   }
+  if (next != nullptr) {   // ranks 3 and 4: top-2 of the experts outside the top-2
+    float u0 = -INFINITY, u1 = -INFINITY;
+    int j0 = 1 << 30, j1 = 1 << 30;
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = eb * 16 + 4 * g + q;
+        const bool cand = e < E && e != i0 && e != i1;
+        const float lv = cand ? acc[eb][q] : -INFINITY;
+        const int li = cand ? e : (1 << 30);
+        const bool top = better(lv, li, u0, j0);
+        const bool sec = !top && better(lv, li, u1, j1);
+        u1 = top ? u0 : (sec ? lv : u1);
+        j1 = top ? j0 : (sec ? li : j1);
+        u0 = top ? lv : u0;
+        j0 = top ? li : j0;
+      }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float w0 = __shfl_xor(u0, o), w1 = __shfl_xor(u1, o);
+      const int k0 = __shfl_xor(j0, o), k1 = __shfl_xor(j1, o);
+      merge2(u0, j0, u1, j1, w0, k0, w1, k1);
+    }
+    // logits are finite, so -inf marks a rank past n_experts
+    if (g == 0 && tok < T)
+      reinterpret_cast<int2*>(next)[tok] = make_int2(u0 == -INFINITY ? -1 : j0, u1 == -INFINITY ? -1 : j1);
+  }
 }
 
 template <int EB>
 hipError_t launch_mfma(const moe_shape_t& s, const void* x, const void* wg, const float* bias,
-                       int32_t* ids, float* w, float* logits, hipStream_t st) {
+                       int32_t* ids, float* w, float* logits, int32_t* next, hipStream_t st) {
   const int blocks = (s.T + 15) / 16;
   hipLaunchKernelGGL((route_topk_mfma_kernel<EB>), dim3(blocks), dim3(kRouteWaves * 64), 0, st,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), bias, s.T,
-                     s.d_model, s.n_experts, ids, w, logits);
+                     s.d_model, s.n_experts, ids, w, logits, next);
   return hipGetLastError();
 }
 
 template <int EP, bool BF16>
 hipError_t launch_ep(const moe_shape_t& s, const void* x, const void* wg, const float* bias,
-                     int32_t* ids, float* w, float* logits, hipStream_t st) {
+                     int32_t* ids, float* w, float* logits, int32_t* next, hipStream_t st) {
   constexpr int TPW = kWave / EP;
   const int waves = (s.T + TPW - 1) / TPW;
   const int blocks = (waves + 3) / 4;
   hipLaunchKernelGGL((route_topk_kernel<EP, BF16>), dim3(blocks), dim3(256), 0, st, x, wg, bias,
-                     s.T, s.d_model, s.n_experts, ids, w, logits);
+                     s.T, s.d_model, s.n_experts, ids, w, logits, next);
   return hipGetLastError();
 }
 
 template <bool BF16>
 hipError_t launch_dtype(const moe_shape_t& s, const void* x, const void* wg, const float* bias,
-                        int32_t* ids, float* w, float* logits, hipStream_t st) {
-  if (s.n_experts <= 8) return launch_ep<8, BF16>(s, x, wg, bias, ids, w, logits, st);
-  if (s.n_experts <= 16) return launch_ep<16, BF16>(s, x, wg, bias, ids, w, logits, st);
-  if (s.n_experts <= 32) return launch_ep<32, BF16>(s, x, wg, bias, ids, w, logits, st);
-  return launch_ep<64, BF16>(s, x, wg, bias, ids, w, logits, st);
+                        int32_t* ids, float* w, float* logits, int32_t* next, hipStream_t st) {
+  if (s.n_experts <= 8) return launch_ep<8, BF16>(s, x, wg, bias, ids, w, logits, next, st);
+  if (s.n_experts <= 16) return launch_ep<16, BF16>(s, x, wg, bias, ids, w, logits, next, st);
+  if (s.n_experts <= 32) return launch_ep<32, BF16>(s, x, wg, bias, ids, w, logits, next, st);
+  return launch_ep<64, BF16>(s, x, wg, bias, ids, w, logits, next, st);
 }
 
 }  // namespace
 
 hipError_t launch_route_topk(const moe_shape_t& s, const void* x, const void* w_gate,
                              const float* bias, int32_t* ids, float* weights, float* logits,
-                             hipStream_t st) {
+                             int32_t* next_ids, hipStream_t st) {
   if (s.act_dtype == MOE_BF16) {
-    if (s.n_experts <= 16) return launch_mfma<1>(s, x, w_gate, bias, ids, weights, logits, st);
-    if (s.n_experts <= 32) return launch_mfma<2>(s, x, w_gate, bias, ids, weights, logits, st);
-    return launch_mfma<4>(s, x, w_gate, bias, ids, weights, logits, st);
+    if (s.n_experts <= 16) return launch_mfma<1>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
+    if (s.n_experts <= 32) return launch_mfma<2>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
+    return launch_mfma<4>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
   }
-  return launch_dtype<false>(s, x, w_gate, bias, ids, weights, logits, st);
+  return launch_dtype<false>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
 }
 
 }  // namespace moe

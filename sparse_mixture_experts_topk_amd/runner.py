@@ -105,8 +105,9 @@ def staged(di: DeviceInputs, stream=None) -> dict:
     o["topk_ids"] = torch.empty(T, 2, dtype=torch.int32, device=dev)
     o["topk_weights"] = torch.empty(T, 2, dtype=torch.float32, device=dev)
     o["logits"] = torch.empty(T, E, dtype=torch.float32, device=dev)
+    o["next_ids"] = torch.empty(T, 2, dtype=torch.int32, device=dev)
     moe_route_topk(shape, di.x, di.w_gate, di.router_bias, o["topk_ids"], o["topk_weights"],
-                   o["logits"], stream)
+                   o["logits"], o["next_ids"], stream)
     o["expert_counts"] = torch.empty(E, dtype=torch.int32, device=dev)
     o["expert_offsets"] = torch.empty(E + 1, dtype=torch.int32, device=dev)
     o["perm_src"] = torch.full((A,), -7, dtype=torch.int32, device=dev)
@@ -114,7 +115,7 @@ def staged(di: DeviceInputs, stream=None) -> dict:
     o["drop_mask"] = torch.empty(A, dtype=torch.uint8, device=dev)
     o["x_perm"] = torch.empty(A, d, dtype=_perm_dtype(cfg), device=dev)
     o["x_perm_scale"] = torch.empty(A, d // 32, dtype=torch.uint8, device=dev) if fp8 else None
-    moe_permute(shape, o["topk_ids"], o["topk_weights"], di.x, o["expert_counts"],
+    moe_permute(shape, o["topk_ids"], o["topk_weights"], o["next_ids"], di.x, o["expert_counts"],
                 o["expert_offsets"], o["perm_src"], o["slot_to_row"], o["drop_mask"], o["x_perm"],
                 o["x_perm_scale"], None, stream)
     o["h"] = torch.empty(A, F, dtype=_perm_dtype(cfg), device=dev)

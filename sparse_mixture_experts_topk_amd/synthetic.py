@@ -84,6 +84,11 @@ CONFIGS: Dict[str, MoEConfig] = {
         name="skewed_capacity_bf16", T=4096, d_model=4096, d_ff=14336,
         capacity=capacity_from_factor(4096, 2, 8), router_bias="zipf1.2",
         description="Zipf(1.2)-skewed routing, capacity floor(1.25*T*2/E)=1280, bf16"),
+    "skewed_fallback_bf16": MoEConfig(
+        name="skewed_fallback_bf16", T=4096, d_model=4096, d_ff=14336,
+        capacity=capacity_from_factor(4096, 2, 8), router_bias="zipf1.2", overflow="next_best",
+        description="as skewed_capacity_bf16, over-capacity assignments re-offered to the "
+                    "next-best expert"),
     "longctx_fp8": MoEConfig(
         name="longctx_fp8", T=16384, d_model=4096, d_ff=14336, w_dtype="fp8_e4m3",
         description="long-context prefill, 16384 tokens, fp8 e4m3 experts with "

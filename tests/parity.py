@@ -8,9 +8,12 @@ Index outputs (expert ids, counts, offsets, row permutation, drop mask) are
 bit-exact, except tokens whose oracle 2nd/3rd logit gap is below 1e-4 (the
 expert set may differ), whose 1st/2nd gap is below 1e-4 (the slot order may
 differ), and capacity assignments whose oracle gate weight is within 1e-4 of
-their expert's cutoff.  For those the GPU's decision is substituted into the
-oracle (``oracle.forward(override=..., keep_override=...)``), which accepts it
-only at such near ties, and everything downstream is then compared exactly.
+their expert's cutoff.  With the overflow fallback also the 3rd/4th-ranked
+experts of tokens with a logit gap below 1e-4 among ranks 2..5, and fallback
+assignments within 1e-4 of their fallback expert's cutoff.  For those the
+GPU's decision is substituted into the oracle (``oracle.forward(override=...,
+keep_override=..., next_override=..., status_override=...)``), which accepts
+it only at such near ties, and everything downstream is then compared exactly.
 """
 from __future__ import annotations
 
@@ -60,6 +63,13 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
+def check_next(res, gpu_next):
+    """3rd/4th-ranked experts, exact away from near ties among ranks 2..5."""
+    r = res.routing
+    near = np.minimum(np.minimum(r.gap23, r.gap34), r.gap45) < oracle.NEAR_TIE
+    assert np.array_equal(gpu_next[~near], r.next_ids[~near]), "3rd/4th-ranked experts differ"
+
+
 def check_routing(res, gpu_ids, gpu_w, gpu_logits, logit_atol):
     """Routing parity with the near-tie exemptions; returns the override dict."""
     r = res.routing
@@ -81,17 +91,30 @@ def check_routing(res, gpu_ids, gpu_w, gpu_logits, logit_atol):
     return {int(t): tuple(int(v) for v in ids[t]) for t in range(T) if not exact[t]}
 
 
-def adjusted_oracle(inputs, gpu_ids, gpu_keep=None, tokens=None, want_h=False):
-    """Oracle result that takes the GPU's decisions at near ties only."""
+def adjusted_oracle(inputs, gpu_ids, gpu_keep=None, tokens=None, want_h=False, gpu_next=None,
+                    gpu_status=None):
+    """Oracle result that takes the GPU's decisions at near ties only.
+
+    gpu_keep: the GPU's capacity-round keep mask; gpu_next / gpu_status: its
+    3rd/4th-ranked experts and final 0/1/2 marks (overflow fallback only)."""
     base = oracle.forward(inputs, tokens=[])
     override = {int(t): tuple(int(v) for v in gpu_ids[t]) for t in oracle.near_tie_tokens(base)}
-    keep_override = None
+    nxt = None
+    if gpu_next is not None:
+        nxt = {int(t): tuple(int(v) for v in gpu_next[t]) for t in oracle.near_tie_next_tokens(base)}
+    keep_override = status_override = None
     if gpu_keep is not None and inputs.cfg.capacity >= 0:
-        mid = oracle.forward(inputs, tokens=[], override=override)
-        if not np.array_equal(mid.keep, gpu_keep):
+        mid = oracle.forward(inputs, tokens=[], override=override, next_override=nxt)
+        if not np.array_equal(mid.keep1, gpu_keep):
             keep_override = gpu_keep
+        if gpu_status is not None:
+            mid = oracle.forward(inputs, tokens=[], override=override, next_override=nxt,
+                                 keep_override=keep_override)
+            if not np.array_equal(mid.status, gpu_status):
+                status_override = gpu_status
     return base, oracle.forward(inputs, tokens=tokens, override=override,
-                                keep_override=keep_override, want_h=want_h)
+                                keep_override=keep_override, want_h=want_h, next_override=nxt,
+                                status_override=status_override)
 
 
 def check_permutation(res, st):
@@ -102,10 +125,13 @@ def check_permutation(res, st):
     assert np.array_equal(to_np(st["perm_src"])[:n], p.perm_src)
     assert np.array_equal(to_np(st["slot_to_row"]), p.slot_to_row)
     if st.get("drop_mask") is not None:
-        assert np.array_equal(to_np(st["drop_mask"]).astype(bool), ~res.keep.ravel())
+        if res.status is not None:       # overflow fallback: 0 / 1 / 2 marks
+            assert np.array_equal(to_np(st["drop_mask"]), res.status.ravel())
+        else:
+            assert np.array_equal(to_np(st["drop_mask"]).astype(bool), ~res.keep.ravel())
 
 
-@functools.lru_cache(maxsize=2)
+@functools.lru_cache(maxsize=3)
 def cached_inputs(name: str, **overrides):
     cfg = synthetic.CONFIGS[name]
     if overrides:

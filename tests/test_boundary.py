@@ -65,6 +65,8 @@ def S(**kw):
     (dict(act_dtype="f32", w_dtype="f32"), 0), (dict(capacity=0), 0), (dict(T=0), 0),
     (dict(w_dtype="fp8_e4m3"), 0), (dict(w_dtype="fp8_e4m3", d_model=4160), 2),
     (dict(w_dtype="fp8_e4m3", d_ff=14400), 2), (dict(act_dtype="f32", w_dtype="fp8_e4m3"), 2),
+    (dict(overflow=2), 1), (dict(overflow=-1), 1), (dict(overflow="next_best"), 0),
+    (dict(overflow="next_best", capacity=3), 0),
 ])
 def test_workspace_query_validates_shape(kw, expected):
     n = ctypes.c_size_t(0)
@@ -78,6 +80,10 @@ def test_workspace_sizes():
     A = 8192 * 2
     assert ws >= A * 4096 * 2 + A * 14336 * 2 + A * 4096 * 4
     assert moe.moe_workspace_bytes(s, moe.MOE_CALL_PERMUTE) == 0
+    # the fallback round keeps the 3rd/4th-ranked experts of every token
+    fb = moe.moe_workspace_bytes(S(T=8192, capacity=2560, overflow="next_best"))
+    assert fb - moe.moe_workspace_bytes(S(T=8192, capacity=2560)) == A * 4
+    assert moe.moe_workspace_bytes(S(T=8192, overflow="next_best")) == ws   # dropless: no round
     with pytest.raises(moe.MoEError):
         moe.moe_workspace_bytes(S(T=-5))
     assert _status("moe_workspace_bytes", ctypes.byref(s), 0, None) == 1
@@ -109,16 +115,23 @@ def test_down_workspace_size_and_requirement():
 def test_calls_reject_null_and_misaligned_pointers_without_device_work():
     s = ctypes.byref(S())
     dummy = 1 << 20  # never dereferenced: validation fails first
-    assert _status("moe_route_topk", s, None, dummy, None, dummy, dummy, None, None) == 1
-    assert _status("moe_route_topk", s, dummy + 2, dummy, None, dummy, dummy, None, None) == 1
+    assert _status("moe_route_topk", s, None, dummy, None, dummy, dummy, None, None, None) == 1
+    assert _status("moe_route_topk", s, dummy + 2, dummy, None, dummy, dummy, None, None, None) == 1
+    assert _status("moe_route_topk", s, dummy, dummy, None, dummy, dummy, None, dummy + 4, None) == 1
     assert _status("moe_combine", s, None, dummy, dummy, dummy, None) == 1
     assert _status("moe_expert_gemm_gate_up", s, dummy, None, None, dummy, dummy, None, None,
                    dummy, None, None, 0, None) == 1
     assert _status("moe_expert_gemm_down", s, dummy, None, dummy, None, None, None, None, 0, None) == 1
     # capacity mode needs a drop mask buffer
     sc = ctypes.byref(S(capacity=4))
-    assert _status("moe_permute", sc, dummy, dummy, dummy, dummy, dummy, dummy, dummy, None,
+    assert _status("moe_permute", sc, dummy, dummy, None, dummy, dummy, dummy, dummy, dummy, None,
                    dummy, None, None, 0, None) == 1
+    # the overflow fallback needs the 3rd/4th-ranked experts
+    sf = ctypes.byref(S(capacity=4, overflow="next_best"))
+    assert _status("moe_permute", sf, dummy, dummy, None, dummy, dummy, dummy, dummy, dummy, dummy,
+                   dummy, None, None, 0, None) == 1
+    assert _status("moe_permute", ctypes.byref(S(overflow=7)), dummy, dummy, None, dummy, dummy,
+                   dummy, dummy, dummy, dummy, dummy, None, None, 0, None) == 1
     # moe_forward: too small / missing workspace
     args = [dummy] * 6
     assert _status("moe_forward", s, dummy, dummy, None, dummy, dummy, dummy, None, None, None,
@@ -131,14 +144,14 @@ def test_calls_reject_null_and_misaligned_pointers_without_device_work():
 def test_unsupported_shapes_rejected_by_every_call():
     bad = ctypes.byref(S(top_k=4))
     dummy = 1 << 20
-    assert _status("moe_route_topk", bad, dummy, dummy, None, dummy, dummy, None, None) == 2
+    assert _status("moe_route_topk", bad, dummy, dummy, None, dummy, dummy, None, None, None) == 2
     assert _status("moe_combine", bad, dummy, dummy, dummy, dummy, None) == 2
 
 
 def test_empty_input_is_a_no_op():
     s = ctypes.byref(S(T=0))
     # all pointers NULL: T == 0 returns before any pointer check or launch
-    assert _status("moe_route_topk", s, None, None, None, None, None, None, None) == 0
+    assert _status("moe_route_topk", s, None, None, None, None, None, None, None, None) == 0
     assert _status("moe_forward", s, *([None] * 15), None, 0, None) == 0
     assert _status("moe_combine", s, None, None, None, None, None) == 0
 

@@ -12,7 +12,7 @@ import torch
 import oracle
 import sparse_mixture_experts_topk_amd as moe
 from sparse_mixture_experts_topk_amd import runner, synthetic
-from parity import (adjusted_oracle, assert_close, cached_inputs, check_permutation,
+from parity import (adjusted_oracle, assert_close, cached_inputs, check_next, check_permutation,
                     check_routing, rel_errors, sample_tokens, to_np, tol_key)
 
 pytestmark = pytest.mark.gpu
@@ -42,16 +42,22 @@ def mid_cfg(name, **kw):
 def run_staged_and_check(cfg, inputs=None, tokens=None, check_h=True):
     inputs = inputs if inputs is not None else synthetic.make_inputs(cfg)
     say(f"staged {cfg.name} T={cfg.T} d={cfg.d_model} F={cfg.d_ff} E={cfg.n_experts} "
-        f"cap={cfg.capacity} {cfg.act_dtype}/{cfg.w_dtype}")
+        f"cap={cfg.capacity} overflow={cfg.overflow} {cfg.act_dtype}/{cfg.w_dtype}")
     di = runner.DeviceInputs.from_host(inputs)
     st = runner.staged(di)
     torch.cuda.synchronize()
     gpu_ids = to_np(st["topk_ids"])
-    gpu_keep = ~to_np(st["drop_mask"]).astype(bool).reshape(-1, 2)
-    base, res = adjusted_oracle(inputs, gpu_ids, gpu_keep, tokens=tokens, want_h=check_h)
+    marks = to_np(st["drop_mask"]).reshape(-1, 2)
+    fallback = cfg.capacity >= 0 and cfg.overflow == "next_best"
+    gpu_next = to_np(st["next_ids"]) if fallback else None
+    gpu_keep = (marks == 0) if fallback else ~marks.astype(bool)
+    base, res = adjusted_oracle(inputs, gpu_ids, gpu_keep, tokens=tokens, want_h=check_h,
+                                gpu_next=gpu_next, gpu_status=marks if fallback else None)
     key = tol_key(cfg)
     logit_atol = 1e-5 if cfg.act_dtype == "f32" else 3e-4
     check_routing(base, gpu_ids, to_np(st["topk_weights"]), to_np(st["logits"]), logit_atol)
+    # the router writes the 3rd/4th-ranked experts whenever asked (runner.staged always asks)
+    check_next(base, to_np(st["next_ids"]))
     check_permutation(res, st)
     n = int(res.perm.offsets[-1])
     rows = np.arange(n) if tokens is None else np.flatnonzero(
@@ -212,6 +218,50 @@ def test_capacity_expert_beyond_lds_key_buffer():
     assert (~res.keep).sum() > 0
 
 
+def test_fallback_worked_example_through_gpu():
+    """Hand-worked overflow fallback case (oracle pin): E = 4, capacity 1, W_g = I."""
+    say("overflow fallback worked example (fp32, d=64, E=4, capacity 1)")
+    logits = [[4, 3, 2, 1], [3, 4, 1, 2], [3.5, 0, 0.5, 0.25]]
+    cfg = synthetic.MoEConfig(name="fb_worked", T=3, d_model=64, d_ff=64, n_experts=4, capacity=1,
+                              overflow="next_best", act_dtype="f32", w_dtype="f32",
+                              wg_std=64 ** -0.5, w13_std=0.1, w2_std=0.1, seed=13)
+    inp = synthetic.make_inputs(cfg)
+    x = torch.zeros(3, 64, dtype=torch.float32)
+    x[:, :4] = torch.tensor(logits, dtype=torch.float32)
+    wg = torch.zeros(4, 64, dtype=torch.float32)
+    wg[:, :4] = torch.eye(4)
+    inp.x, inp.w_gate = x, wg
+    st, res, _ = run_staged_and_check(cfg, inputs=inp)
+    assert to_np(st["topk_ids"]).tolist() == [[0, 1], [1, 0], [0, 2]]
+    assert to_np(st["next_ids"]).tolist() == [[2, 3], [3, 2], [3, 1]]
+    assert to_np(st["drop_mask"]).tolist() == [1, 2, 0, 1, 0, 0]
+    assert to_np(st["expert_counts"]).tolist() == [1, 1, 1, 1]
+    assert to_np(st["perm_src"])[:4].tolist() == [4, 2, 5, 1]
+
+
+def test_mid_capacity_fallback_zipf():
+    T = 1000
+    cfg = mid_cfg("mid_fallback", T=T, n_experts=8, capacity=synthetic.capacity_from_factor(T, 2, 8),
+                  router_bias="zipf1.2", overflow="next_best", seed=7)
+    st, res, _ = run_staged_and_check(cfg)
+    assert (res.status == 2).sum() > 0 and (res.status == 1).sum() > 0
+    assert res.perm.counts.max() <= cfg.capacity
+
+
+def test_fallback_small_expert_counts_and_both_slots():
+    # E = 3: no 4th-ranked expert; a tight capacity drops both slots of many tokens
+    run_staged_and_check(mid_cfg("fb_e3", T=400, n_experts=3, capacity=150, overflow="next_best",
+                                 router_bias=None, seed=14))
+    # E = 2: nothing to fall back to; the round changes nothing
+    st, res, _ = run_staged_and_check(mid_cfg("fb_e2", T=300, n_experts=2, capacity=200,
+                                              overflow="next_best", seed=15))
+    assert np.all(to_np(st["next_ids"]) == -1) and not np.any(res.status == 2)
+    # capacity 0: every offer finds no free slot
+    st, res, _ = run_staged_and_check(mid_cfg("fb_cap0", T=200, n_experts=8, capacity=0,
+                                              overflow="next_best", seed=16), check_h=False)
+    assert np.all(to_np(st["drop_mask"]) == 1)
+
+
 def test_dense_reduction_all_experts_equal():
     """All experts equal: the layer must equal one dense SwiGLU FFN (oracle, E=1 form)."""
     cfg = mid_cfg("dense", T=700, n_experts=8, seed=10)
@@ -229,10 +279,12 @@ def test_dense_reduction_all_experts_equal():
     assert_close(to_np(buf.y.float()), dense, "bf16", "dense reduction")
 
 
-def test_forward_matches_staged_bitwise_and_is_deterministic():
-    cfg = mid_cfg("fwd_vs_staged", T=900, n_experts=8, capacity=250, router_bias="zipf1.2", seed=11)
+@pytest.mark.parametrize("overflow", ["drop", "next_best"])
+def test_forward_matches_staged_bitwise_and_is_deterministic(overflow):
+    cfg = mid_cfg("fwd_vs_staged", T=900, n_experts=8, capacity=250, router_bias="zipf1.2", seed=11,
+                  overflow=overflow)
     inp = synthetic.make_inputs(cfg)
-    say("moe_forward vs the five staged calls; run twice")
+    say(f"moe_forward vs the five staged calls ({overflow}); run twice")
     di = runner.DeviceInputs.from_host(inp)
     st = runner.staged(di)
     b1 = runner.forward(di)
@@ -286,6 +338,16 @@ def test_skewed_capacity_config_sampled():
     st, res, _ = run_staged_and_check(cfg, inputs=inp, tokens=toks, check_h=True)
     counts = res.perm.counts
     assert counts.max() == cfg.capacity and (~res.keep).sum() > 1000
+
+
+def test_skewed_fallback_config_sampled():
+    cfg = synthetic.CONFIGS["skewed_fallback_bf16"]
+    inp = cached_inputs("skewed_fallback_bf16")
+    base = oracle.forward(inp, tokens=[])
+    toks = sample_tokens(base)
+    st, res, _ = run_staged_and_check(cfg, inputs=inp, tokens=toks, check_h=True)
+    assert res.perm.counts.max() == cfg.capacity
+    assert (res.status == 2).sum() > 500 and (res.status == 1).sum() > 0
 
 
 def test_prefill_config_fused_forward_sampled():
