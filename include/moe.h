@@ -73,8 +73,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
 
 /* What happens to an assignment the capacity limit drops (moe_shape_t.overflow).
  * Pages: "How Mixtral 8x7B uses mixture of experts", section "Routing without
- * auxiliary loss": over-capacity tokens are dropped and handled by a
- * fallback, typically the next-best expert.
+ * auxiliary loss": tokens over an expert's capacity are dropped there and
+ * handed to a fallback, most often the token's next-best expert.
  *   MOE_OVERFLOW_DROP       it contributes nothing.
  *   MOE_OVERFLOW_NEXT_BEST  one fallback round: a dropped slot is offered to the
  *     token's best expert outside its top-2 (3rd-ranked by logit; when both

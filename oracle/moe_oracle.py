@@ -21,9 +21,9 @@ What it computes, step by step, with the passage each step follows:
    kept, the rest dropped and contribute nothing ("How Mixtral 8x7B uses
    mixture of experts", section "Routing without auxiliary loss",
    capacity-limited dispatch).
-4b. Optional overflow fallback (same section: the excess goes to a fallback,
-   typically the token's next-best expert; the dispatch sketch puts the
-   remaining tokens in an overflow buffer).  Reading: an assignment dropped
+4b. Optional overflow fallback (same section: tokens over capacity are
+   handed to a fallback, most often the token's next-best expert, and the
+   dispatch sketch collects them in an overflow buffer).  Reading: an assignment dropped
    in step 4 moves to the best-ranked expert outside the token's top-2 --
    the 3rd-ranked one, or, when both of the token's slots were dropped, the
    3rd-ranked for slot 0 and the 4th-ranked for slot 1 -- keeping its gate
