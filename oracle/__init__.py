@@ -10,9 +10,9 @@ from .moe_oracle import (NEAR_TIE, OracleResult, Permutation, Routing, capacity_
                          dequant_weight, fallback_select, fallback_targets, forward,
                          near_tie_next_tokens, near_tie_tokens, permutation, router_logits,
                          silu, swiglu, swiglu_act_quant, to_f64, topk_gate)
-from . import fp8, brute
+from . import fp8, brute, mxfp4
 
 __all__ = ["NEAR_TIE", "OracleResult", "Permutation", "Routing", "capacity_select",
            "dequant_weight", "fallback_select", "fallback_targets", "forward",
            "near_tie_next_tokens", "near_tie_tokens", "permutation", "router_logits", "silu",
-           "swiglu", "swiglu_act_quant", "to_f64", "topk_gate", "fp8", "brute"]
+           "swiglu", "swiglu_act_quant", "to_f64", "topk_gate", "fp8", "brute", "mxfp4"]

@@ -41,7 +41,8 @@ What it computes, step by step, with the passage each step follows:
    ``output = torch.zeros_like(x)`` in the study notes' MoE layer).
 
 Every input is converted exactly to float64 from its stored bf16 / fp32 /
-fp8-code-times-scale value; all arithmetic is float64.  For fp8 expert weights
+fp8-code-times-scale / MXFP4-code-times-block-scale value (``oracle/mxfp4.py``;
+MXFP4 experts keep bf16 activations); all arithmetic is float64.  For fp8 expert weights
 the computation also includes the declared activation quantisation (see
 ``oracle/fp8.py``): x and h are block-quantised per row and per 32-element
 block before the two contractions.  Parity unpinned for that emulation beyond
@@ -56,6 +57,7 @@ import numpy as np
 import torch
 
 from . import fp8 as _fp8
+from . import mxfp4 as _mxfp4
 
 # Assignments whose deciding gap is below this are "near ties": the decision is
 # not fixed by the arithmetic precision of either side (exemption threshold).
@@ -71,8 +73,12 @@ def to_f64(t) -> np.ndarray:
     return t.detach().to(torch.float64).cpu().numpy()
 
 
-def dequant_weight(w, scale) -> np.ndarray:
-    """fp8 codes times the per-output-channel fp32 scale; plain conversion otherwise."""
+def dequant_weight(w, scale, w_dtype: str = "") -> np.ndarray:
+    """fp8 codes times the per-output-channel fp32 scale; MXFP4 codes times their
+    block scales; plain conversion otherwise."""
+    if w_dtype == "mxfp4":
+        return _mxfp4.dequant(w.numpy() if hasattr(w, "numpy") else w,
+                              scale.numpy() if hasattr(scale, "numpy") else scale)
     wf = to_f64(w)
     if scale is None:
         return wf
@@ -348,15 +354,16 @@ def forward(inputs, tokens: Optional[Iterable[int]] = None,
     y_perm = np.full((n_rows, d), np.nan)
     h_all = np.full((n_rows, cfg.d_ff), np.nan) if want_h else None
     fp8 = cfg.w_dtype == "fp8_e4m3"
+    scaled = cfg.w_dtype in ("fp8_e4m3", "mxfp4")
     for e in range(E):
         rows = np.arange(perm.offsets[e], perm.offsets[e + 1])
         rows = rows[want_mask[perm.perm_src[rows] // k]]
         if len(rows) == 0:
             continue
         xr = x[perm.perm_src[rows] // k]
-        w1 = dequant_weight(inputs.w1[e], inputs.w1_scale[e] if fp8 else None)
-        w3 = dequant_weight(inputs.w3[e], inputs.w3_scale[e] if fp8 else None)
-        w2 = dequant_weight(inputs.w2[e], inputs.w2_scale[e] if fp8 else None)
+        w1 = dequant_weight(inputs.w1[e], inputs.w1_scale[e] if scaled else None, cfg.w_dtype)
+        w3 = dequant_weight(inputs.w3[e], inputs.w3_scale[e] if scaled else None, cfg.w_dtype)
+        w2 = dequant_weight(inputs.w2[e], inputs.w2_scale[e] if scaled else None, cfg.w_dtype)
         ffn = swiglu_act_quant if fp8 else swiglu
         y_perm[rows], h = ffn(xr, w1, w3, w2)
         if want_h:

@@ -22,6 +22,14 @@ fp8 expert weights (long-context config): each output channel (row of the
 nn.Linear ``[out, in]`` weight) gets an fp32 scale ``s = absmax / 448`` and
 codes ``e4m3(w / s)``; the cast is torch's ``float8_e4m3fn`` conversion
 (round-to-nearest-even).  An all-zero row gets ``s = 1``.
+
+MXFP4 expert weights (4-bit decode config) follow the conversion of the OCP
+Microscaling Formats specification v1.0: per row and block of 32 consecutive
+input elements, a shared exponent ``X = floor(log2(amax)) - 2`` (2 is the
+largest E2M1 exponent), stored as the byte ``X + 127``, and elements
+``w / 2^X`` rounded to the nearest FP4 E2M1 value (ties to the even code),
+saturating at +-6.  An all-zero block gets ``X = 0``.  Two codes per byte,
+the even element in the low nibble.
 """
 from __future__ import annotations
 
@@ -50,7 +58,7 @@ class MoEConfig:
     capacity: int = -1          # -1: dropless; else slots per expert (0 drops all)
     overflow: str = "drop"      # over-capacity assignments: "drop" | "next_best" (fallback round)
     act_dtype: str = "bf16"     # x, w_gate, y: "f32" | "bf16"
-    w_dtype: str = "bf16"       # w1/w3/w2: "f32" | "bf16" | "fp8_e4m3"
+    w_dtype: str = "bf16"       # w1/w3/w2: "f32" | "bf16" | "fp8_e4m3" | "mxfp4"
     x_std: float = 1.0
     wg_std: float = 1.0 / 64.0
     w13_std: float = 0.02
@@ -89,6 +97,10 @@ CONFIGS: Dict[str, MoEConfig] = {
         capacity=capacity_from_factor(4096, 2, 8), router_bias="zipf1.2", overflow="next_best",
         description="as skewed_capacity_bf16, over-capacity assignments re-offered to the "
                     "next-best expert"),
+    "decode_mxfp4": MoEConfig(
+        name="decode_mxfp4", T=16, d_model=4096, d_ff=14336, w_dtype="mxfp4",
+        description="Mixtral-shape decode, 16 tokens, MXFP4 (E2M1 + E8M0 per 32) experts, "
+                    "bf16 activations and router, dropless"),
     "longctx_fp8": MoEConfig(
         name="longctx_fp8", T=16384, d_model=4096, d_ff=14336, w_dtype="fp8_e4m3",
         description="long-context prefill, 16384 tokens, fp8 e4m3 experts with "
@@ -103,7 +115,8 @@ class MoEInputs:
     x [T, d], w_gate [E, d] in the activation dtype; router_bias [E] fp32 or
     None; w1, w3 [E, F, d] and w2 [E, d, F] in the weight dtype (fp8 configs:
     torch.float8_e4m3fn codes) with w*_scale [E, F] / [E, d] fp32 per output
-    channel for fp8 (None otherwise).
+    channel for fp8; MXFP4: uint8 [E, F, d/2] / [E, d, F/2] packed codes with
+    uint8 [E, F, d/32] / [E, d, F/32] block scales (None otherwise).
     """
     cfg: MoEConfig
     x: torch.Tensor
@@ -145,6 +158,27 @@ def quantize_rows_e4m3(w32: torch.Tensor):
     return q, scale
 
 
+# Midpoints between consecutive E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+_E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+
+
+def quantize_blocks_mxfp4(w32: np.ndarray):
+    """[rows, cols] fp32 -> (packed E2M1 codes [rows, cols/2] uint8, E8M0 scales [rows, cols/32] uint8)."""
+    rows, cols = w32.shape
+    blk = w32.reshape(rows, cols // 32, 32)
+    amax = np.abs(blk).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0)
+    X = np.clip(X, -127, 127).astype(np.int32)
+    v = np.abs(blk) * np.exp2(-X.astype(np.float32))[..., None]       # exact power-of-two scaling
+    idx = np.searchsorted(_E2M1_MIDS, v, side="left")                  # level index 0..7
+    tie = (idx < 7) & (v == _E2M1_MIDS[np.minimum(idx, 6)])
+    idx = np.where(tie & (idx % 2 == 1), idx + 1, idx)                 # ties -> even code
+    codes = (idx | np.where(blk < 0, 8, 0)).astype(np.uint8).reshape(rows, cols)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (X + 127).astype(np.uint8)
+
+
 def _expert_matrix(parent: np.random.SeedSequence, E: int, rows: int, cols: int, std: float,
                    w_dtype: str, threads: int, experts=None):
     children = parent.spawn(E)
@@ -155,12 +189,15 @@ def _expert_matrix(parent: np.random.SeedSequence, E: int, rows: int, cols: int,
         t = torch.from_numpy(a)
         if w_dtype == "fp8_e4m3":
             return quantize_rows_e4m3(t)
+        if w_dtype == "mxfp4":
+            q, sc = quantize_blocks_mxfp4(a)
+            return (torch.from_numpy(q), torch.from_numpy(sc))
         return (t.to(_TORCH_DTYPE[w_dtype]), None)
 
     with ThreadPoolExecutor(max(1, threads)) as ex:
         parts = list(ex.map(one, ids))
     w = torch.stack([p[0] for p in parts])
-    s = torch.stack([p[1] for p in parts]) if w_dtype == "fp8_e4m3" else None
+    s = torch.stack([p[1] for p in parts]) if w_dtype in ("fp8_e4m3", "mxfp4") else None
     return w, s
 
 
@@ -193,7 +230,7 @@ def unquantized_weights(cfg: MoEConfig, threads: int = 8):
     out = []
     for ss, rows, cols, std in ((s_1, F, d, cfg.w13_std), (s_3, F, d, cfg.w13_std),
                                 (s_2, d, F, cfg.w2_std)):
-        w, _ = _expert_matrix(ss, E, rows, cols, std, "f32" if cfg.w_dtype == "fp8_e4m3" else cfg.w_dtype,
+        w, _ = _expert_matrix(ss, E, rows, cols, std, "f32" if cfg.w_dtype in ("fp8_e4m3", "mxfp4") else cfg.w_dtype,
                               threads)
         out.append(w)
     return tuple(out)

@@ -363,6 +363,89 @@ def test_act_quant_ffn_reduces_to_plain_ffn_on_grid_inputs():
 
 # ------------------------------------------------- configs and inputs ---
 
+# --------------------------------------------------------------- MXFP4 ---
+
+def test_e2m1_values_from_the_format_definition():
+    """OCP MX FP4 E2M1: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 is the sign."""
+    t = oracle.mxfp4.E2M1_TABLE
+    assert t[:8].tolist() == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert t[8:].tolist() == [-0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    assert np.signbit(t[8]) and not np.signbit(t[0])
+    # largest normal = 2^emax * (1 + 1/2) with emax = 2 (bias 1); smallest subnormal 2^(1-1) * 1/2
+    assert t[7] == 2.0 ** 2 * 1.5 and t[1] == 0.5
+
+
+def test_mxfp4_dequant_packing_and_block_scale():
+    # byte 0x72: even element = low nibble 2 (1.0), odd element = high nibble 7 (6.0)
+    packed = np.full((1, 16), 0x72, dtype=np.uint8)
+    for sbyte, mul in ((127, 1.0), (130, 8.0), (120, 2.0 ** -7)):
+        w = oracle.mxfp4.dequant(packed, np.array([[sbyte]], dtype=np.uint8))
+        assert w.shape == (1, 32)
+        assert w[0, 0::2].tolist() == [1.0 * mul] * 16 and w[0, 1::2].tolist() == [6.0 * mul] * 16
+    # two blocks with their own scales; a negative code
+    packed = np.zeros((1, 32), dtype=np.uint8)
+    packed[0, 16] = 0x0B                                # element 32 = code 11 = -1.5
+    w = oracle.mxfp4.dequant(packed, np.array([[127, 125]], dtype=np.uint8))
+    assert w[0, 32] == -1.5 / 4 and np.count_nonzero(w) == 1
+
+
+def test_mxfp4_input_quantizer_against_the_oracle_decode():
+    """The input generator's MXFP4 encoder, decoded by the oracle: grid values exact,
+    ties to the even code, shared exponent floor(log2 amax) - 2, error within half a step."""
+    X = -5
+    levels = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float32)
+    # block 0: every level (both signs) exactly; amax = 6 * 2^X -> floor(log2) - 2 = X
+    b0 = np.concatenate([levels, -levels, levels, -levels]) * np.float32(2.0 ** X)
+    # block 1: midpoints (ties) -> 0, 1, 1, 2, 2, 4, 4 and a value above 6 that saturates;
+    # amax 7 * 2^X keeps the same shared exponent
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0], dtype=np.float32)
+    b1 = np.concatenate([mids, -mids, mids, mids]) * np.float32(2.0 ** X)
+    b2 = np.zeros(32, dtype=np.float32)                                  # zero block
+    w = np.stack([np.concatenate([b0, b1, b2])])
+    packed, sc = synthetic.quantize_blocks_mxfp4(w)
+    assert sc.tolist() == [[X + 127, X + 127, 127]]
+    back = oracle.mxfp4.dequant(packed, sc)
+    assert np.array_equal(back[0, :32], b0.astype(np.float64))
+    expect = np.array([0, 1, 1, 2, 2, 4, 4, 6], dtype=np.float64) * 2.0 ** X
+    assert np.array_equal(back[0, 32:40], expect) and np.array_equal(back[0, 40:48], -expect)
+    assert np.all(back[0, 64:] == 0)
+    # random weights: shared exponent and the half-step error bound
+    g = np.random.default_rng(7)
+    w = (g.standard_normal((6, 512)) * 0.02).astype(np.float32)
+    packed, sc = synthetic.quantize_blocks_mxfp4(w)
+    back = oracle.mxfp4.dequant(packed, sc)
+    blk = w.reshape(6, 16, 32).astype(np.float64)
+    Xb = np.floor(np.log2(np.abs(blk).max(-1))) - 2
+    assert np.array_equal(sc.astype(np.int64) - 127, Xb.astype(np.int64))
+    step = np.exp2(Xb)[..., None]                       # grid spacing is <= 2 * 2^X
+    v = np.abs(blk) / step
+    gap = np.where(v < 2, 0.5, np.where(v < 4, 1.0, 2.0)) * step
+    err = np.abs(back.reshape(6, 16, 32) - blk)
+    sat = v > 6
+    assert np.all(err[~sat] <= gap[~sat] / 2 + 1e-12)
+    assert np.all(err[sat] <= (np.abs(blk) - 6 * step)[sat] + 1e-12)
+
+
+def test_mxfp4_layer_equals_layer_on_dequantized_weights():
+    """The oracle layer on MXFP4 experts is the plain layer on their exact dequantised values."""
+    cfg = synthetic.MoEConfig(name="m4", T=24, d_model=64, d_ff=96, n_experts=4, w_dtype="mxfp4",
+                              wg_std=0.125, w13_std=0.05, w2_std=0.05, seed=3)
+    inp = synthetic.make_inputs(cfg)
+    assert tuple(inp.w1.shape) == (4, 96, 32) and tuple(inp.w1_scale.shape) == (4, 96, 2)
+    assert tuple(inp.w2.shape) == (4, 64, 48) and tuple(inp.w2_scale.shape) == (4, 64, 3)
+    res = oracle.forward(inp)
+    deq = lambda w, s: np.stack([oracle.mxfp4.dequant(w[e].numpy(), s[e].numpy()) for e in range(4)])  # noqa: E731
+    plain = _Inp(cfg.replace(w_dtype="bf16"), oracle.to_f64(inp.x), oracle.to_f64(inp.w_gate),
+                 deq(inp.w1, inp.w1_scale), deq(inp.w3, inp.w3_scale), deq(inp.w2, inp.w2_scale))
+    ref = oracle.forward(plain)
+    assert np.array_equal(res.routing.ids, ref.routing.ids)
+    assert np.max(np.abs(res.y - ref.y)) == 0.0
+    # brute force on the same dequantised weights
+    yb, _, _, _ = brute.layer(plain.x.tolist(), plain.w_gate.tolist(), plain.w1.tolist(),
+                              plain.w3.tolist(), plain.w2.tolist(), 2)
+    assert np.max(np.abs(np.array(yb) - res.y)) < 1e-12
+
+
 def test_configs_shapes_and_capacity():
     c = synthetic.CONFIGS
     assert c["skewed_capacity_bf16"].capacity == 1280
