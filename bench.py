@@ -41,9 +41,13 @@ KERNEL_SOURCES = ("sparse_mixture_experts_topk_amd/csrc/gemm_bf16.hip",
                   "sparse_mixture_experts_topk_amd/csrc/gemm_f32.hip")
 
 
-def kernel_source_sha() -> str:
+# MXFP4 workloads also run the 4-bit weight-streaming kernels.
+MXFP4_SOURCES = KERNEL_SOURCES + ("sparse_mixture_experts_topk_amd/csrc/gemm_mxfp4_decode.hip",)
+
+
+def kernel_source_sha(cfg=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (MXFP4_SOURCES if cfg is not None and cfg.w_dtype == "mxfp4" else KERNEL_SOURCES):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -60,9 +64,10 @@ def gate_up_work(cfg, counts):
     d, F = cfg.d_model, cfg.d_ff
     n_kept = int(sum(counts))
     touched = int(sum(1 for c in counts if c > 0))
-    wb = {"bf16": 2, "f32": 4, "fp8_e4m3": 1}[cfg.w_dtype]
+    # weight bytes per element: MXFP4 = half a byte of code + one scale byte per 32
+    wb = {"bf16": 2, "f32": 4, "fp8_e4m3": 1, "mxfp4": 0.5 + 1 / 32}[cfg.w_dtype]
     ab = 1 if cfg.w_dtype == "fp8_e4m3" else (4 if cfg.act_dtype == "f32" else 2)
-    weight_bytes = touched * 2 * F * d * wb                  # w1 + w3 rows of touched experts
+    weight_bytes = int(touched * 2 * F * d * wb)             # w1 + w3 rows of touched experts
     act_bytes = n_kept * d * ab + n_kept * F * ab            # x_perm read + h written
     flops = 4.0 * n_kept * d * F                             # two [n, d] x [d, F] products
     return weight_bytes + act_bytes, flops, touched, n_kept
@@ -200,7 +205,7 @@ def main():
     counts = st["expert_counts"].cpu().tolist()
     nbytes, flops, touched, n_kept = gate_up_work(cfg, counts)
     decode = is_decode(cfg)
-    sha = kernel_source_sha()
+    sha = kernel_source_sha(cfg)
     traffic = read_traffic(cfg.name, sha)
     if decode:
         achieved = nbytes / (kernel_ms * 1e-3) / 1e9
@@ -221,7 +226,7 @@ def main():
         "metric": METRIC, "value": round(cfg.T * steps / elapsed, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8_e4m3": "fp8_e4m3", "f32": "f32"}[cfg.w_dtype],
+        "dtype": {"bf16": "bf16", "fp8_e4m3": "fp8_e4m3", "f32": "f32", "mxfp4": "mxfp4"}[cfg.w_dtype],
         "data": "synthetic (seeded, Mixtral-shaped; random weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
                    "n_experts": cfg.n_experts, "top_k": cfg.top_k,

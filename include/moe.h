@@ -44,6 +44,17 @@
  *                            byte (scale = 2^(byte - 127)); the block exponent
  *                            is ceil(log2(fp32(amax / 448))), 127 for a zero
  *                            block.  fp32 accumulate.
+ *   act BF16 + w MXFP4     : x, W_g, y bf16; x_perm bf16; h bf16.  Expert weights
+ *                            are OCP Microscaling FP4: E2M1 codes, two per byte
+ *                            (even element in the low nibble), [E, F, d/2] /
+ *                            [E, d, F/2] bytes, with one E8M0 scale byte
+ *                            (2^(byte - 127)) per row and block of 32
+ *                            consecutive input elements, [E, F, d/32] /
+ *                            [E, d, F/32] bytes.  The matrix cores see the
+ *                            exact dequantised weights in bf16; fp32
+ *                            accumulate.  A weight-streaming (decode) format:
+ *                            at most 64 rows per expert (T <= 64 or capacity
+ *                            <= 64), d_model and d_ff multiples of 256.
  *   Other combinations return MOE_ERR_UNSUPPORTED.
  *
  * Shape limits: top_k == 2; 2 <= n_experts <= 64; d_model and d_ff
@@ -67,7 +78,7 @@ typedef enum {
   MOE_ERR_HIP = 4            /* a kernel launch failed */
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_dtype_t;
 
 #define MOE_DROPLESS (-1)
 
@@ -172,20 +183,22 @@ moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_ids,
  * Pages: "Mixtral" study notes, MixtralExpert.forward and "SwiGLU Experts".
  *   x_perm, x_perm_scale as written by moe_permute
  *   expert_offsets [E+1] int32 (device)
- *   w1, w3         [E, F, d] weight dtype; w1_scale, w3_scale [E, F] fp32 (fp8 only)
+ *   w1, w3         [E, F, d] weight dtype (MXFP4: [E, F, d/2] bytes); w1_scale,
+ *                  w3_scale: fp8 [E, F] fp32, MXFP4 [E, F, d/32] E8M0 bytes, else unused
  *   h              [T*2, F] out (bf16 / fp32 / e4m3 codes); h_scale [T*2, F/32] E8M0 (fp8 only)
  * Workspace: moe_workspace_bytes(MOE_CALL_GATE_UP). */
 moe_status_t moe_expert_gemm_gate_up(const moe_shape_t* shape, const void* x_perm,
                                      const uint8_t* x_perm_scale, const int32_t* expert_offsets,
-                                     const void* w1, const void* w3, const float* w1_scale,
-                                     const float* w3_scale, void* h, uint8_t* h_scale,
+                                     const void* w1, const void* w3, const void* w1_scale,
+                                     const void* w3_scale, void* h, uint8_t* h_scale,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Grouped expert down projection: y_perm[row] = h[row] . w2[e]^T (fp32 out).
  * Pages: "Mixtral" study notes, MixtralExpert.forward (self.w2).
  *   h, h_scale     as written by moe_expert_gemm_gate_up
  *   expert_offsets [E+1] int32
- *   w2             [E, d, F] weight dtype; w2_scale [E, d] fp32 (fp8 only)
+ *   w2             [E, d, F] weight dtype (MXFP4: [E, d, F/2] bytes); w2_scale: fp8
+ *                  [E, d] fp32, MXFP4 [E, d, F/32] E8M0 bytes, else unused
  *   y_perm         [T*2, d] fp32 out
  * Workspace: moe_workspace_bytes(MOE_CALL_DOWN) bytes, 16-byte aligned, device
  * memory owned by the caller (0 for shapes that need none; then it may be
@@ -198,7 +211,7 @@ moe_status_t moe_expert_gemm_gate_up(const moe_shape_t* shape, const void* x_per
  * must not run concurrently. */
 moe_status_t moe_expert_gemm_down(const moe_shape_t* shape, const void* h, const uint8_t* h_scale,
                                   const int32_t* expert_offsets, const void* w2,
-                                  const float* w2_scale, float* y_perm, void* workspace,
+                                  const void* w2_scale, float* y_perm, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
 /* Gate-weighted combine back to token order:
@@ -214,7 +227,8 @@ moe_status_t moe_combine(const moe_shape_t* shape, const float* y_perm, const in
 /* The whole layer on one stream, with no host synchronisation:
  * route -> (capacity) -> permute -> gate/up -> down -> combine.
  *   x [T, d], w_gate [E, d] act dtype; router_bias [E] fp32 or NULL
- *   w1, w3 [E, F, d], w2 [E, d, F] weight dtype; w*_scale fp32 per output channel (fp8 only)
+ *   w1, w3 [E, F, d], w2 [E, d, F] weight dtype; w*_scale as for the two GEMM calls
+ *   (fp8: fp32 per output channel; MXFP4: E8M0 bytes per 32-element block)
  *   y [T, d] act dtype out
  *   optional outputs (NULL to skip): topk_ids_out [T, 2] int32, topk_weights_out [T, 2]
  *   fp32, expert_counts_out [E] int32, drop_mask_out [T*2] uint8 (0 / 1 / 2 as in
@@ -224,7 +238,7 @@ moe_status_t moe_combine(const moe_shape_t* shape, const float* y_perm, const in
  * Workspace: moe_workspace_bytes(MOE_CALL_FORWARD) holds every intermediate. */
 moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const void* w_gate,
                          const float* router_bias, const void* w1, const void* w3, const void* w2,
-                         const float* w1_scale, const float* w3_scale, const float* w2_scale,
+                         const void* w1_scale, const void* w3_scale, const void* w2_scale,
                          void* y, int32_t* topk_ids_out, float* topk_weights_out,
                          int32_t* expert_counts_out, uint8_t* drop_mask_out, float* logits_out,
                          void* workspace, size_t workspace_bytes, void* stream);

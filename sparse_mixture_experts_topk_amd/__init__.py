@@ -15,16 +15,16 @@ import torch
 
 from . import _lib
 from ._lib import (MOE_BF16, MOE_CALL_DOWN, MOE_CALL_FORWARD, MOE_CALL_GATE_UP,
-                   MOE_CALL_PERMUTE, MOE_DROPLESS, MOE_F32, MOE_FP8_E4M3, MOE_OVERFLOW_DROP,
+                   MOE_CALL_PERMUTE, MOE_DROPLESS, MOE_F32, MOE_FP8_E4M3, MOE_MXFP4, MOE_OVERFLOW_DROP,
                    MOE_OVERFLOW_NEXT_BEST, MoeShape)
 
 __all__ = ["MoEError", "MoeShape", "make_shape", "moe_status_string", "moe_version",
            "moe_workspace_bytes", "moe_route_topk", "moe_permute", "moe_expert_gemm_gate_up",
            "moe_expert_gemm_down", "moe_combine", "moe_forward", "MOE_F32", "MOE_BF16",
-           "MOE_FP8_E4M3", "MOE_DROPLESS", "MOE_CALL_PERMUTE", "MOE_CALL_GATE_UP",
+           "MOE_FP8_E4M3", "MOE_MXFP4", "MOE_DROPLESS", "MOE_CALL_PERMUTE", "MOE_CALL_GATE_UP",
            "MOE_CALL_DOWN", "MOE_CALL_FORWARD", "MOE_OVERFLOW_DROP", "MOE_OVERFLOW_NEXT_BEST"]
 
-_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3, "mxfp4": MOE_MXFP4}
 _OVF = {"drop": MOE_OVERFLOW_DROP, "next_best": MOE_OVERFLOW_NEXT_BEST}
 
 

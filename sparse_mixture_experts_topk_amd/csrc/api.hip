@@ -26,7 +26,7 @@ int device_cu_count() {
 
 hipError_t launch_gate_up(const moe_shape_t& s, const void* x_perm, const uint8_t* x_scale,
                           const int32_t* offsets, const void* w1, const void* w3,
-                          const float* w1_scale, const float* w3_scale, void* h, uint8_t* h_scale,
+                          const void* w1_scale, const void* w3_scale, void* h, uint8_t* h_scale,
                           hipStream_t st) {
   if (s.w_dtype == MOE_F32)
     return launch_gate_up_f32(s, static_cast<const float*>(x_perm), offsets,
@@ -36,13 +36,19 @@ hipError_t launch_gate_up(const moe_shape_t& s, const void* x_perm, const uint8_
     return launch_gate_up_bf16(s, static_cast<const uint16_t*>(x_perm), offsets,
                                static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3),
                                static_cast<uint16_t*>(h), st);
+  if (s.w_dtype == MOE_MXFP4)
+    return launch_gate_up_mxfp4(s, static_cast<const uint16_t*>(x_perm), offsets,
+                                static_cast<const uint8_t*>(w1), static_cast<const uint8_t*>(w1_scale),
+                                static_cast<const uint8_t*>(w3), static_cast<const uint8_t*>(w3_scale),
+                                static_cast<uint16_t*>(h), st);
   return launch_gate_up_fp8(s, static_cast<const uint8_t*>(x_perm), x_scale, offsets,
                             static_cast<const uint8_t*>(w1), static_cast<const uint8_t*>(w3),
-                            w1_scale, w3_scale, static_cast<uint8_t*>(h), h_scale, st);
+                            static_cast<const float*>(w1_scale), static_cast<const float*>(w3_scale),
+                            static_cast<uint8_t*>(h), h_scale, st);
 }
 
 hipError_t launch_down(const moe_shape_t& s, const void* h, const uint8_t* h_scale,
-                       const int32_t* offsets, const void* w2, const float* w2_scale,
+                       const int32_t* offsets, const void* w2, const void* w2_scale,
                        float* y_perm, void* workspace, hipStream_t st) {
   if (s.w_dtype == MOE_F32)
     return launch_down_f32(s, static_cast<const float*>(h), offsets,
@@ -50,8 +56,13 @@ hipError_t launch_down(const moe_shape_t& s, const void* h, const uint8_t* h_sca
   if (s.w_dtype == MOE_BF16)
     return launch_down_bf16(s, static_cast<const uint16_t*>(h), offsets,
                             static_cast<const uint16_t*>(w2), y_perm, workspace, st);
+  if (s.w_dtype == MOE_MXFP4)
+    return launch_down_mxfp4(s, static_cast<const uint16_t*>(h), offsets,
+                             static_cast<const uint8_t*>(w2), static_cast<const uint8_t*>(w2_scale),
+                             y_perm, st);
   return launch_down_fp8(s, static_cast<const uint8_t*>(h), h_scale, offsets,
-                         static_cast<const uint8_t*>(w2), w2_scale, y_perm, st);
+                         static_cast<const uint8_t*>(w2), static_cast<const float*>(w2_scale), y_perm,
+                         st);
 }
 
 }  // namespace moe
@@ -82,15 +93,22 @@ moe_status_t validate_shape(const moe_shape_t* s) {
   if (s->overflow != MOE_OVERFLOW_DROP && s->overflow != MOE_OVERFLOW_NEXT_BEST)
     return MOE_ERR_INVALID_ARG;
   const bool known = (s->act_dtype == MOE_F32 || s->act_dtype == MOE_BF16) &&
-                     (s->w_dtype == MOE_F32 || s->w_dtype == MOE_BF16 || s->w_dtype == MOE_FP8_E4M3);
+                     (s->w_dtype == MOE_F32 || s->w_dtype == MOE_BF16 || s->w_dtype == MOE_FP8_E4M3 ||
+                      s->w_dtype == MOE_MXFP4);
   if (!known) return MOE_ERR_INVALID_ARG;
   if (s->top_k != 2 || s->n_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (s->d_model % 64 != 0 || s->d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (s->d_model > (1 << 16) || s->d_ff > (1 << 18)) return MOE_ERR_UNSUPPORTED;
   const bool combo = (s->act_dtype == MOE_F32 && s->w_dtype == MOE_F32) ||
                      (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_BF16) ||
-                     (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_FP8_E4M3);
+                     (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_FP8_E4M3) ||
+                     (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_MXFP4);
   if (!combo) return MOE_ERR_UNSUPPORTED;
+  // MXFP4: weight streaming in stages of 256 elements, for few rows per expert
+  if (s->w_dtype == MOE_MXFP4 &&
+      (s->d_model % 256 != 0 || s->d_ff % 256 != 0 ||
+       moe::max_rows_per_expert(*s) > moe::kMxfp4MaxRows))
+    return MOE_ERR_UNSUPPORTED;
   if (s->w_dtype == MOE_FP8_E4M3 && !moe::kFp8Available) return MOE_ERR_UNSUPPORTED;
   // fp8: one K slice of the matrix-core tile is 128 elements
   if (s->w_dtype == MOE_FP8_E4M3 && (s->d_model % 128 != 0 || s->d_ff % 128 != 0))
@@ -236,17 +254,19 @@ moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_ids, const fl
 
 moe_status_t moe_expert_gemm_gate_up(const moe_shape_t* s, const void* x_perm,
                                      const uint8_t* x_perm_scale, const int32_t* expert_offsets,
-                                     const void* w1, const void* w3, const float* w1_scale,
-                                     const float* w3_scale, void* h, uint8_t* h_scale,
+                                     const void* w1, const void* w3, const void* w1_scale,
+                                     const void* w3_scale, void* h, uint8_t* h_scale,
                                      void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
   moe_status_t v = validate_shape(s);
   if (v != MOE_OK) return v;
   if (s->T == 0) return MOE_OK;
-  if ((v = check_ptrs({x_perm, expert_offsets, w1, w3, h}, {})) != MOE_OK) return v;
+  if ((v = check_ptrs({x_perm, expert_offsets, w1, w3, h}, {w1_scale, w3_scale})) != MOE_OK) return v;
   if (s->w_dtype == MOE_FP8_E4M3 &&
       (x_perm_scale == nullptr || w1_scale == nullptr || w3_scale == nullptr || h_scale == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if (s->w_dtype == MOE_MXFP4 && (w1_scale == nullptr || w3_scale == nullptr))
     return MOE_ERR_INVALID_ARG;
   return from_hip(moe::launch_gate_up(*s, x_perm, x_perm_scale, expert_offsets, w1, w3, w1_scale,
                                       w3_scale, h, h_scale, static_cast<hipStream_t>(stream)));
@@ -254,14 +274,15 @@ moe_status_t moe_expert_gemm_gate_up(const moe_shape_t* s, const void* x_perm,
 
 moe_status_t moe_expert_gemm_down(const moe_shape_t* s, const void* h, const uint8_t* h_scale,
                                   const int32_t* expert_offsets, const void* w2,
-                                  const float* w2_scale, float* y_perm, void* workspace,
+                                  const void* w2_scale, float* y_perm, void* workspace,
                                   size_t workspace_bytes, void* stream) {
   moe_status_t v = validate_shape(s);
   if (v != MOE_OK) return v;
   if (s->T == 0) return MOE_OK;
-  if ((v = check_ptrs({h, expert_offsets, w2, y_perm}, {})) != MOE_OK) return v;
+  if ((v = check_ptrs({h, expert_offsets, w2, y_perm}, {w2_scale})) != MOE_OK) return v;
   if (s->w_dtype == MOE_FP8_E4M3 && (h_scale == nullptr || w2_scale == nullptr))
     return MOE_ERR_INVALID_ARG;
+  if (s->w_dtype == MOE_MXFP4 && w2_scale == nullptr) return MOE_ERR_INVALID_ARG;
   const size_t need = down_workspace_bytes(*s);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return MOE_ERR_WORKSPACE;
@@ -281,7 +302,7 @@ moe_status_t moe_combine(const moe_shape_t* s, const float* y_perm, const int32_
 
 moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_gate,
                          const float* router_bias, const void* w1, const void* w3, const void* w2,
-                         const float* w1_scale, const float* w3_scale, const float* w2_scale,
+                         const void* w1_scale, const void* w3_scale, const void* w2_scale,
                          void* y, int32_t* topk_ids_out, float* topk_weights_out,
                          int32_t* expert_counts_out, uint8_t* drop_mask_out, float* logits_out,
                          void* workspace, size_t workspace_bytes, void* stream) {
@@ -290,10 +311,11 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_gate
   if (s->T == 0) return MOE_OK;
   if ((v = check_ptrs({x, w_gate, w1, w3, w2, y},
                       {router_bias, topk_ids_out, topk_weights_out, expert_counts_out,
-                       drop_mask_out, logits_out})) != MOE_OK)
+                       drop_mask_out, logits_out, w1_scale, w3_scale, w2_scale})) != MOE_OK)
     return v;
   const bool fp8 = s->w_dtype == MOE_FP8_E4M3;
-  if (fp8 && (w1_scale == nullptr || w3_scale == nullptr || w2_scale == nullptr))
+  const bool scaled = fp8 || s->w_dtype == MOE_MXFP4;
+  if (scaled && (w1_scale == nullptr || w3_scale == nullptr || w2_scale == nullptr))
     return MOE_ERR_INVALID_ARG;
   const ForwardLayout L = forward_layout(*s);
   if (workspace == nullptr || workspace_bytes < L.total || !aligned16(workspace))

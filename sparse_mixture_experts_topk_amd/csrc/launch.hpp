@@ -35,12 +35,13 @@ hipError_t launch_permute_scatter(const moe_shape_t& s, const void* x, const int
                                   hipStream_t st);
 
 // Grouped gate/up (dual weight, SwiGLU epilogue) and down GEMMs.
+// Weight scales: fp32 per output channel (fp8) or E8M0 bytes per 32-element block (MXFP4).
 hipError_t launch_gate_up(const moe_shape_t& s, const void* x_perm, const uint8_t* x_scale,
                           const int32_t* offsets, const void* w1, const void* w3,
-                          const float* w1_scale, const float* w3_scale, void* h, uint8_t* h_scale,
+                          const void* w1_scale, const void* w3_scale, void* h, uint8_t* h_scale,
                           hipStream_t st);
 hipError_t launch_down(const moe_shape_t& s, const void* h, const uint8_t* h_scale,
-                       const int32_t* offsets, const void* w2, const float* w2_scale,
+                       const int32_t* offsets, const void* w2, const void* w2_scale,
                        float* y_perm, void* workspace, hipStream_t st);
 
 // Fill n bytes with v (a kernel, so that the call can sit inside a captured graph).
@@ -82,6 +83,17 @@ hipError_t launch_gate_up_fp8(const moe_shape_t& s, const uint8_t* x_perm, const
 hipError_t launch_down_fp8(const moe_shape_t& s, const uint8_t* h, const uint8_t* h_scale,
                            const int32_t* offsets, const uint8_t* w2, const float* w2_scale,
                            float* y_perm, hipStream_t st);
+
+// MXFP4 expert weights (E2M1 codes + E8M0 block scales) with bf16 activations:
+// weight streaming for few rows per expert.
+constexpr int kMxfp4MaxRows = 64;
+hipError_t launch_gate_up_mxfp4(const moe_shape_t& s, const uint16_t* x_perm,
+                                const int32_t* offsets, const uint8_t* w1, const uint8_t* w1_scale,
+                                const uint8_t* w3, const uint8_t* w3_scale, uint16_t* h,
+                                hipStream_t st);
+hipError_t launch_down_mxfp4(const moe_shape_t& s, const uint16_t* h, const int32_t* offsets,
+                             const uint8_t* w2, const uint8_t* w2_scale, float* y_perm,
+                             hipStream_t st);
 
 // Largest number of rows any expert can receive: each token picks an expert at most once.
 inline int64_t max_rows_per_expert(const moe_shape_t& s) {

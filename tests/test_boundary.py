@@ -67,6 +67,11 @@ def S(**kw):
     (dict(w_dtype="fp8_e4m3", d_ff=14400), 2), (dict(act_dtype="f32", w_dtype="fp8_e4m3"), 2),
     (dict(overflow=2), 1), (dict(overflow=-1), 1), (dict(overflow="next_best"), 0),
     (dict(overflow="next_best", capacity=3), 0),
+    # MXFP4 experts: bf16 activations, <= 64 rows per expert, d and F multiples of 256
+    (dict(w_dtype="mxfp4"), 0), (dict(w_dtype="mxfp4", T=64), 0), (dict(w_dtype="mxfp4", T=65), 2),
+    (dict(w_dtype="mxfp4", T=5000, capacity=64), 0), (dict(w_dtype="mxfp4", T=5000, capacity=65), 2),
+    (dict(w_dtype="mxfp4", d_model=4160), 2), (dict(w_dtype="mxfp4", d_ff=14400), 2),
+    (dict(act_dtype="f32", w_dtype="mxfp4"), 2), (dict(w_dtype=4), 1),
 ])
 def test_workspace_query_validates_shape(kw, expected):
     n = ctypes.c_size_t(0)
@@ -132,6 +137,12 @@ def test_calls_reject_null_and_misaligned_pointers_without_device_work():
                    dummy, None, None, 0, None) == 1
     assert _status("moe_permute", ctypes.byref(S(overflow=7)), dummy, dummy, None, dummy, dummy,
                    dummy, dummy, dummy, dummy, dummy, None, None, 0, None) == 1
+    # MXFP4 experts need their block scales
+    s4 = ctypes.byref(S(w_dtype="mxfp4"))
+    assert _status("moe_expert_gemm_gate_up", s4, dummy, None, dummy, dummy, dummy, None, dummy,
+                   dummy, None, None, 0, None) == 1
+    assert _status("moe_expert_gemm_down", s4, dummy, None, dummy, dummy, None, dummy, None, 0,
+                   None) == 1
     # moe_forward: too small / missing workspace
     args = [dummy] * 6
     assert _status("moe_forward", s, dummy, dummy, None, dummy, dummy, dummy, None, None, None,
