@@ -16,6 +16,10 @@ each dropped slot is offered, in slot order, to the token's experts ranked
 3rd, 4th, ... by logit; every expert takes such offers, ranked by the slot's
 G then token, into the slots it left free, and the output weights the
 fallback expert's output by that G.
+
+Shared expert (``n_shared=1``; DeepSeek-V3 remark on the "Mixtral 8x7B"
+interview page): expert index E of the weight lists, added to every token's
+output with weight 1, outside the softmax and the capacity limit.
 """
 from __future__ import annotations
 
@@ -53,12 +57,13 @@ def gate(logits: Sequence[float], k: int):
 
 
 def layer(x, w_gate, w1, w3, w2, k: int = 2, bias=None, capacity: int = -1,
-          overflow: str = "drop"):
+          overflow: str = "drop", n_shared: int = 0):
     """Dense brute-force layer on nested lists; returns (y, ids, G_full, keep).
 
     With overflow == "next_best" (and a capacity), ``keep`` holds per slot the
     expert that finally processes it, or None when it is dropped."""
     T, E = len(x), len(w_gate)
+    shared = [_expert(x[t], w1[E], w3[E], w2[E]) for t in range(T)] if n_shared else None
     logits = [[_dot(x[t], w_gate[e]) + (bias[e] if bias is not None else 0.0) for e in range(E)]
               for t in range(T)]
     ids, Gf = [], []
@@ -107,5 +112,8 @@ def layer(x, w_gate, w1, w3, w2, k: int = 2, bias=None, capacity: int = -1,
             out = _expert(x[t], w1[e], w3[e], w2[e])
             for i in range(len(acc)):
                 acc[i] += w * out[i]
+        if shared is not None:                             # shared expert, weight 1
+            for i in range(len(acc)):
+                acc[i] += shared[t][i]
         y.append(acc)
     return y, ids, Gf, keep

@@ -39,6 +39,11 @@ What it computes, step by step, with the passage each step follows:
 7. ``y = sum_i G(x)_i * Expert_i(x)`` over kept slots; zero when nothing is
    kept ("Mixtral and Mixture-of-Experts, Explained", "How it works";
    ``output = torch.zeros_like(x)`` in the study notes' MoE layer).
+8. General top-k and a shared expert (the DeepSeek-V3 remark on "Mixtral 8x7B"
+   interview page: many routed experts, several active per token, plus a
+   shared one).  Reading: k experts by logit with the same gate (softmax
+   over the k kept logits); an optional shared expert, stored after the E
+   routed ones, processes every token with weight 1 and no capacity limit.
 
 Every input is converted exactly to float64 from its stored bf16 / fp32 /
 fp8-code-times-scale / MXFP4-code-times-block-scale value (``oracle/mxfp4.py``;
@@ -99,8 +104,8 @@ def router_logits(x: np.ndarray, w_gate: np.ndarray, bias: Optional[np.ndarray] 
 class Routing:
     ids: np.ndarray        # [T, k] int64, slot 0 = the larger logit
     G: np.ndarray          # [T, k] float64 gate weights
-    gap12: np.ndarray      # [T] logit(1st) - logit(2nd)
-    gap23: np.ndarray      # [T] logit(2nd) - logit(3rd)  (inf when E == k)
+    gap12: np.ndarray      # [T] smallest gap between consecutive ranks 1..k (slot order)
+    gap23: np.ndarray      # [T] logit(k-th) - logit(k+1-th): the selected set (inf when E == k)
     next_ids: np.ndarray   # [T, 2] int64: 3rd- and 4th-ranked experts (-1 when E is smaller)
     gap34: np.ndarray      # [T] logit(3rd) - logit(4th)  (inf when absent)
     gap45: np.ndarray      # [T] logit(4th) - logit(5th)  (inf when absent)
@@ -121,7 +126,7 @@ def topk_gate(logits: np.ndarray, k: int = 2) -> Routing:
     full = ex / ex.sum(axis=1, keepdims=True)
     G = np.take_along_axis(full, ids, axis=1)
     srt = np.take_along_axis(logits, order, axis=1)
-    gap12 = srt[:, 0] - srt[:, 1]
+    gap12 = (srt[:, :k - 1] - srt[:, 1:k]).min(axis=1) if k > 1 else np.full(T, np.inf)
     gap23 = srt[:, k - 1] - srt[:, k] if E > k else np.full(T, np.inf)
     nxt = np.full((T, 2), -1, dtype=np.int64)
     for j in range(2):
@@ -207,21 +212,27 @@ class Permutation:
     slot_to_row: np.ndarray  # [T*k] row, or -1 when dropped
 
 
-def permutation(ids: np.ndarray, keep: np.ndarray, n_experts: int) -> Permutation:
+def permutation(ids: np.ndarray, keep: np.ndarray, n_experts: int, n_shared: int = 0) -> Permutation:
+    """Rows grouped by expert, tokens ascending.  A shared expert (index n_experts) takes
+    every token after the routed rows; its rows' source (slot) is T*k + token, and
+    slot_to_row covers those T slots after the T*k routed ones."""
     T, k = ids.shape
     flat_ids = ids.ravel()
     flat_keep = keep.ravel()
-    counts = np.array([np.count_nonzero((flat_ids == e) & flat_keep) for e in range(n_experts)],
-                      dtype=np.int64)
-    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    counts = np.array([np.count_nonzero((flat_ids == e) & flat_keep) for e in range(n_experts)] +
+                      [T] * n_shared, dtype=np.int64)
+    offsets = np.zeros(n_experts + n_shared + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(counts)
     perm_src = np.empty(int(offsets[-1]), dtype=np.int64)
-    slot_to_row = np.full(T * k, -1, dtype=np.int64)
+    slot_to_row = np.full(T * (k + n_shared), -1, dtype=np.int64)
     for e in range(n_experts):
         src = np.flatnonzero((flat_ids == e) & flat_keep)   # ascending t*k+slot
         rows = offsets[e] + np.arange(len(src))
         perm_src[rows] = src
         slot_to_row[src] = rows
+    if n_shared:
+        perm_src[offsets[n_experts]:] = T * k + np.arange(T)
+        slot_to_row[T * k:] = offsets[n_experts] + np.arange(T)
     return Permutation(counts, offsets, perm_src, slot_to_row)
 
 
@@ -295,6 +306,7 @@ def forward(inputs, tokens: Optional[Iterable[int]] = None,
     """
     cfg = inputs.cfg
     E, k = cfg.n_experts, cfg.top_k
+    S = getattr(cfg, "n_shared", 0)
     x = to_f64(inputs.x)
     bias = None if inputs.router_bias is None else to_f64(inputs.router_bias)
     logits = router_logits(x, to_f64(inputs.w_gate), bias)
@@ -342,9 +354,9 @@ def forward(inputs, tokens: Optional[Iterable[int]] = None,
             status = status_override.astype(np.uint8)
             final_ids = np.where(status == 2, target, r.ids)
         keep = status != 1
-        perm = permutation(final_ids, keep, E)
+        perm = permutation(final_ids, keep, E, S)
     else:
-        perm = permutation(r.ids, keep, E)
+        perm = permutation(r.ids, keep, E, S)
 
     T, d = x.shape
     want = np.arange(T) if tokens is None else np.unique(np.asarray(list(tokens), dtype=np.int64))
@@ -355,12 +367,17 @@ def forward(inputs, tokens: Optional[Iterable[int]] = None,
     h_all = np.full((n_rows, cfg.d_ff), np.nan) if want_h else None
     fp8 = cfg.w_dtype == "fp8_e4m3"
     scaled = cfg.w_dtype in ("fp8_e4m3", "mxfp4")
-    for e in range(E):
+    T_k = T * k
+
+    def token_of(src):
+        return np.where(src < T_k, src // k, src - T_k)
+
+    for e in range(E + S):
         rows = np.arange(perm.offsets[e], perm.offsets[e + 1])
-        rows = rows[want_mask[perm.perm_src[rows] // k]]
+        rows = rows[want_mask[token_of(perm.perm_src[rows])]]
         if len(rows) == 0:
             continue
-        xr = x[perm.perm_src[rows] // k]
+        xr = x[token_of(perm.perm_src[rows])]
         w1 = dequant_weight(inputs.w1[e], inputs.w1_scale[e] if scaled else None, cfg.w_dtype)
         w3 = dequant_weight(inputs.w3[e], inputs.w3_scale[e] if scaled else None, cfg.w_dtype)
         w2 = dequant_weight(inputs.w2[e], inputs.w2_scale[e] if scaled else None, cfg.w_dtype)
@@ -376,12 +393,14 @@ def forward(inputs, tokens: Optional[Iterable[int]] = None,
             row = perm.slot_to_row[t * k + s]
             if row >= 0:
                 y[t] += r.G[t, s] * y_perm[row]
+        if S:
+            y[t] += y_perm[perm.offsets[E] + t]      # shared expert, weight 1
     return OracleResult(logits, r, keep, cutoff, perm, y, y_perm, h_all, status, final_ids, cutoff2,
                         keep1)
 
 
 def near_tie_tokens(res: OracleResult) -> np.ndarray:
-    """Tokens whose top-2 set (gap23) or slot order (gap12) is a near tie."""
+    """Tokens whose top-k set (gap23) or slot order (gap12) is a near tie."""
     return np.flatnonzero((res.routing.gap23 < NEAR_TIE) | (res.routing.gap12 < NEAR_TIE))
 
 

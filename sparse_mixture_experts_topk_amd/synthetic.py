@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the sparse top-2 MoE feed-forward layer.
+"""Seeded synthetic inputs for the sparse top-k MoE feed-forward layer.
 
 This module only draws and stores inputs: it holds none of the layer's
 arithmetic (no routing, no gating, no expert FFN).  Both the fp64 CPU oracle
@@ -8,7 +8,12 @@ Shapes follow the Mixtral 8x7B MoE layer described on the pages
 ("How Mixtral 8x7B uses mixture of experts", section "The architecture in one
 diagram"; "Mixtral" study notes, section "MoE Layer", classes MixtralMoE and
 MixtralExpert): 8 experts, top-2 routing, d_model = 4096 and a SwiGLU expert
-of hidden width 14336.
+of hidden width 14336.  The fine-grained configs follow the DeepSeek-V3 remark
+on the "Mixtral 8x7B" interview page (section on how MoE design changed since
+Mixtral): 256 routed experts, 8 active per token, plus one shared expert that
+every token passes through.  The page gives no expert width; the reading
+here keeps d_model = 4096 and takes "smaller experts" as d_ff = 2048 for
+routed and shared experts alike.
 
 Reading of the distribution notation: ``N(0, 1/n)`` is a variance (std
 n**-0.5), ``N(0, 0.02)`` is a standard deviation.  Every tensor has its own
@@ -53,8 +58,9 @@ class MoEConfig:
     T: int                      # tokens (batch * seq_len, flattened)
     d_model: int
     d_ff: int
-    n_experts: int = 8
+    n_experts: int = 8          # routed experts
     top_k: int = 2
+    n_shared: int = 0           # 0 or 1 shared expert, stored after the routed ones
     capacity: int = -1          # -1: dropless; else slots per expert (0 drops all)
     overflow: str = "drop"      # over-capacity assignments: "drop" | "next_best" (fallback round)
     act_dtype: str = "bf16"     # x, w_gate, y: "f32" | "bf16"
@@ -101,6 +107,16 @@ CONFIGS: Dict[str, MoEConfig] = {
         name="decode_mxfp4", T=16, d_model=4096, d_ff=14336, w_dtype="mxfp4",
         description="Mixtral-shape decode, 16 tokens, MXFP4 (E2M1 + E8M0 per 32) experts, "
                     "bf16 activations and router, dropless"),
+    "finegrained_decode_bf16": MoEConfig(
+        name="finegrained_decode_bf16", T=16, d_model=4096, d_ff=2048, n_experts=256, top_k=8,
+        n_shared=1,
+        description="fine-grained decode, bf16, 16 tokens, 256 routed experts top-8 + 1 shared "
+                    "(d_ff 2048), dropless"),
+    "finegrained_prefill_bf16": MoEConfig(
+        name="finegrained_prefill_bf16", T=8192, d_model=4096, d_ff=2048, n_experts=256, top_k=8,
+        n_shared=1,
+        description="fine-grained prefill, bf16, 8192 tokens, 256 routed experts top-8 + 1 shared "
+                    "(d_ff 2048), dropless"),
     "longctx_fp8": MoEConfig(
         name="longctx_fp8", T=16384, d_model=4096, d_ff=14336, w_dtype="fp8_e4m3",
         description="long-context prefill, 16384 tokens, fp8 e4m3 experts with "
@@ -217,9 +233,10 @@ def make_inputs(cfg: MoEConfig, threads: int = 8, with_weights: bool = True) -> 
     if not with_weights:
         z = torch.empty(0)
         return MoEInputs(cfg, x, w_gate, bias, z, z, z)
-    w1, s1 = _expert_matrix(s_1, E, F, d, cfg.w13_std, cfg.w_dtype, threads)
-    w3, s3 = _expert_matrix(s_3, E, F, d, cfg.w13_std, cfg.w_dtype, threads)
-    w2, s2 = _expert_matrix(s_2, E, d, F, cfg.w2_std, cfg.w_dtype, threads)
+    EW = E + cfg.n_shared                                # expert weights incl. the shared one
+    w1, s1 = _expert_matrix(s_1, EW, F, d, cfg.w13_std, cfg.w_dtype, threads)
+    w3, s3 = _expert_matrix(s_3, EW, F, d, cfg.w13_std, cfg.w_dtype, threads)
+    w2, s2 = _expert_matrix(s_2, EW, d, F, cfg.w2_std, cfg.w_dtype, threads)
     return MoEInputs(cfg, x, w_gate, bias, w1, w3, w2, s1, s3, s2)
 
 

@@ -4,6 +4,7 @@ Each test names what it pins.  A plausible slip in the oracle (a dropped term,
 a wrong sign, index or slot order, a transposed operand, w1/w3 swapped, the
 bias dropped, the wrong gate form) fails at least one of them.
 """
+import dataclasses
 import json
 import math
 import os
@@ -30,14 +31,23 @@ class _Inp:
         self.w1_scale = self.w3_scale = self.w2_scale = None
 
 
-def _micro(T=6, d=8, F=12, E=4, seed=3, capacity=-1, bias=False, overflow="drop"):
+def _micro(T=6, d=8, F=12, E=4, seed=3, capacity=-1, bias=False, overflow="drop", k=2, shared=0):
     g = np.random.default_rng(seed)
     f32 = lambda *s: g.standard_normal(s).astype(np.float32).astype(np.float64)  # noqa: E731
-    cfg = synthetic.MoEConfig(name="micro", T=T, d_model=d, d_ff=F, n_experts=E, capacity=capacity,
-                              act_dtype="f32", w_dtype="f32", overflow=overflow)
+    cfg = synthetic.MoEConfig(name="micro", T=T, d_model=d, d_ff=F, n_experts=E, top_k=k,
+                              n_shared=shared, capacity=capacity, act_dtype="f32", w_dtype="f32",
+                              overflow=overflow)
     b = f32(E) if bias else None
-    return _Inp(cfg, f32(T, d), f32(E, d) / math.sqrt(d), f32(E, F, d) / math.sqrt(d),
-                f32(E, F, d) / math.sqrt(d), f32(E, d, F) / math.sqrt(F), b)
+    EW = E + shared
+    return _Inp(cfg, f32(T, d), f32(E, d) / math.sqrt(d), f32(EW, F, d) / math.sqrt(d),
+                f32(EW, F, d) / math.sqrt(d), f32(EW, d, F) / math.sqrt(F), b)
+
+
+def _ffn(x, w1, w3, w2):
+    """Dense SwiGLU FFN with torch's own silu and linear (float64)."""
+    xt = x if isinstance(x, torch.Tensor) else torch.from_numpy(x)
+    return Fn.linear(Fn.silu(Fn.linear(xt, torch.from_numpy(w1))) * Fn.linear(xt, torch.from_numpy(w3)),
+                     torch.from_numpy(w2)).numpy()
 
 
 # ------------------------------------------------------------- routing ---
@@ -246,6 +256,114 @@ def test_combine_linearity_zeroing_one_expert():
         assert np.max(np.abs(cut.y[t] - expect)) < 1e-12
 
 
+# ------------------------------------------ general top-k, shared expert ---
+
+@pytest.mark.parametrize("k,E,shared,capacity,bias", [
+    (1, 4, 0, -1, False), (3, 6, 0, -1, True), (4, 8, 1, -1, False), (8, 8, 0, -1, False),
+    (8, 8, 1, -1, True), (3, 6, 1, 2, False), (1, 4, 1, 1, True), (5, 16, 0, 2, False)])
+def test_general_topk_and_shared_match_dense_brute_force(k, E, shared, capacity, bias):
+    """Routing, capacity and output for k != 2 and a shared expert vs the literal dense form."""
+    inp = _micro(T=9, E=E, k=k, shared=shared, capacity=capacity, bias=bias, seed=10 + k + E)
+    res = oracle.forward(inp)
+    yb, ids, Gf, keep = brute.layer(inp.x.tolist(), inp.w_gate.tolist(), inp.w1.tolist(),
+                                    inp.w3.tolist(), inp.w2.tolist(), k,
+                                    None if inp.router_bias is None else inp.router_bias.tolist(),
+                                    capacity, n_shared=shared)
+    assert res.routing.ids.tolist() == ids
+    Gb = np.array([[Gf[t][e] for e in ids[t]] for t in range(len(ids))])
+    assert np.max(np.abs(Gb - res.routing.G)) < 1e-14
+    assert res.keep.tolist() == keep
+    assert np.max(np.abs(np.array(yb) - res.y)) < 1e-12
+
+
+def test_top1_is_the_single_best_expert_with_weight_one():
+    """k = 1: the softmax over one kept logit is exactly 1; y = FFN of the arg-max expert."""
+    inp = _micro(T=20, d=8, F=12, E=8, k=1, seed=21)
+    res = oracle.forward(inp)
+    logits = inp.x @ inp.w_gate.T
+    assert res.routing.ids[:, 0].tolist() == np.argmax(logits, axis=1).tolist()
+    assert np.all(res.routing.G == 1.0)
+    for t in range(inp.cfg.T):
+        e = int(res.routing.ids[t, 0])
+        assert np.max(np.abs(res.y[t] - _ffn(inp.x[t], inp.w1[e], inp.w3[e], inp.w2[e]))) < 1e-12
+
+
+def test_topk_equal_to_all_experts_is_the_dense_softmax_mixture():
+    """k = E: nothing is masked, so G is the full softmax and y is the dense mixture of experts."""
+    E = 6
+    inp = _micro(T=12, d=8, F=10, E=E, k=E, seed=22, bias=True)
+    res = oracle.forward(inp)
+    logits = torch.from_numpy(inp.x @ inp.w_gate.T + inp.router_bias[None, :])
+    p = torch.softmax(logits, dim=-1).numpy()
+    Gfull = np.zeros((inp.cfg.T, E))
+    np.put_along_axis(Gfull, res.routing.ids, res.routing.G, axis=1)
+    assert np.max(np.abs(Gfull - p)) < 1e-15
+    dense = sum(p[:, e:e + 1] * _ffn(inp.x, inp.w1[e], inp.w3[e], inp.w2[e]) for e in range(E))
+    assert np.max(np.abs(res.y - dense)) < 1e-12
+    assert np.all(np.isinf(res.routing.gap23))
+
+
+def test_general_topk_gate_properties_and_ties():
+    g = np.random.default_rng(23)
+    logits = g.standard_normal((3000, 64)) * 1.5
+    for k in (1, 3, 6, 8):
+        r = oracle.topk_gate(logits, k)
+        srt = -np.sort(-logits, axis=1)
+        kept = np.take_along_axis(logits, r.ids, 1)
+        assert np.array_equal(kept, srt[:, :k])                     # the k largest, in order
+        assert np.all(np.abs(r.G.sum(axis=1) - 1.0) < 1e-14)
+        assert np.all(np.diff(r.G, axis=1) <= 0)                    # slot 0 the largest weight
+        # softmax invariance: G depends only on differences of the kept logits
+        ex = np.exp(kept - kept[:, :1])
+        assert np.max(np.abs(r.G - ex / ex.sum(axis=1, keepdims=True))) < 1e-15
+        gaps = srt[:, :k - 1] - srt[:, 1:k]
+        assert np.array_equal(r.gap12, gaps.min(axis=1) if k > 1 else np.full(len(logits), np.inf))
+        assert np.array_equal(r.gap23, srt[:, k - 1] - srt[:, k])
+    # equal logits go to the lower index for any k
+    tie = np.array([[0.0, 2.0, 1.0, 2.0, 1.0, 2.0, 1.0, 0.0]])
+    assert oracle.topk_gate(tie, 5).ids.tolist() == [[1, 3, 5, 2, 4]]
+    G = oracle.topk_gate(tie, 3).G
+    assert G.tolist() == [[1 / 3, 1 / 3, 1 / 3]] or np.max(np.abs(G - 1 / 3)) < 1e-16
+
+
+def test_shared_expert_alone_is_a_dense_ffn_and_adds_linearly():
+    """Routed experts zeroed => y is the shared expert's dense FFN; otherwise routed + shared."""
+    inp = _micro(T=15, d=8, F=12, E=8, k=3, shared=1, seed=24)
+    shared_ffn = _ffn(inp.x, inp.w1[8], inp.w3[8], inp.w2[8])
+    with_shared = oracle.forward(inp).y
+    cfg0 = synthetic.MoEConfig(name="micro", T=15, d_model=8, d_ff=12, n_experts=8, top_k=3,
+                               act_dtype="f32", w_dtype="f32")
+    routed_only = oracle.forward(_Inp(cfg0, inp.x, inp.w_gate, inp.w1[:8], inp.w3[:8], inp.w2[:8])).y
+    assert np.max(np.abs(with_shared - (routed_only + shared_ffn))) < 1e-12
+    inp.w2 = inp.w2.copy()
+    inp.w2[:8] = 0.0
+    assert np.max(np.abs(oracle.forward(inp).y - shared_ffn)) < 1e-12
+    # capacity 0 drops every routed slot but never the shared expert
+    inp.cfg = dataclasses.replace(inp.cfg, capacity=0)
+    res = oracle.forward(inp)
+    assert not res.keep.any() and np.max(np.abs(res.y - shared_ffn)) < 1e-12
+
+
+def test_permutation_with_shared_expert_rows():
+    g = np.random.default_rng(25)
+    T, E, k = 200, 16, 4
+    r = oracle.topk_gate(g.standard_normal((T, E)), k)
+    keep = g.random((T, k)) > 0.3
+    p = oracle.permutation(r.ids, keep, E, 1)
+    assert p.counts[E] == T and p.counts[:E].tolist() == np.bincount(r.ids[keep], minlength=E).tolist()
+    assert p.offsets[-1] == keep.sum() + T
+    assert p.perm_src[p.offsets[E]:].tolist() == (T * k + np.arange(T)).tolist()
+    # slot_to_row inverts perm_src over all T*(k+1) slots, dropped slots -> -1
+    assert len(p.slot_to_row) == T * (k + 1)
+    assert np.array_equal(p.slot_to_row[p.perm_src], np.arange(len(p.perm_src)))
+    assert np.all(p.slot_to_row[:T * k][~keep.ravel()] == -1)
+    routed = p.perm_src[:p.offsets[E]]
+    assert np.array_equal(p.slot_to_row[routed], np.arange(len(routed)))
+    for e in range(E):
+        seg = p.perm_src[p.offsets[e]:p.offsets[e + 1]]
+        assert np.all(np.diff(seg // k) > 0) and np.all(r.ids.ravel()[seg] == e)
+
+
 # -------------------------------------------------- capacity + grouping ---
 
 def test_capacity_invariants():
@@ -452,7 +570,10 @@ def test_configs_shapes_and_capacity():
     assert synthetic.capacity_from_factor(1, 2, 8) == 0      # batch-1 edge: 0.3125 -> 0 slots
     dec = c["decode_bf16"]
     assert 3 * dec.d_model * dec.d_ff * 2 == 352_321_536    # bytes of one bf16 expert
-    assert all(cfg.n_experts == 8 and cfg.top_k == 2 for cfg in c.values())
+    fine = {n for n in c if n.startswith("finegrained")}
+    assert all(c[n].n_experts == 8 and c[n].top_k == 2 and c[n].n_shared == 0 for n in c if n not in fine)
+    # DeepSeek-V3 remark ("Mixtral 8x7B" interview page): 256 routed, 8 active, 1 shared
+    assert fine and all((c[n].n_experts, c[n].top_k, c[n].n_shared) == (256, 8, 1) for n in fine)
 
 
 def test_zipf_bias_frozen_and_effective():
