@@ -1,9 +1,9 @@
-"""Benchmark of the sparse top-2 MoE layer on one MI355X.
+"""Benchmark of the sparse top-k MoE layer on one MI355X.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
 One step is one pass of the whole layer over one batch of synthetic input:
-router + top-2 -> (capacity) -> permute -> gate/up GEMM + SwiGLU -> down GEMM
+router + top-k -> (capacity) -> permute -> gate/up GEMM + SwiGLU -> down GEMM
 -> combine, enqueued through the C ABI on one stream.  The timed step issues
 the five boundary calls (the same kernels, in the same order, that the fused
 moe_forward enqueues) so that HIP events can bracket the dominant kernel
@@ -32,7 +32,8 @@ METRIC = "MoE-layer tokens/s + % roofline (HBM GB/s decode, MFMA TFLOP/s prefill
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8_e4m3": 5000.0, "f32": 157.3}   # dense matrix-core peaks
 DEFAULTS = {"decode_bf16": (200, 20), "prefill_bf16": (20, 3), "skewed_capacity_bf16": (20, 3),
-            "longctx_fp8": (10, 3), "tiny_fp32": (200, 20)}
+            "longctx_fp8": (10, 3), "tiny_fp32": (200, 20), "finegrained_decode_bf16": (100, 10),
+            "finegrained_prefill_bf16": (10, 3)}
 KERNEL_SOURCES = ("sparse_mixture_experts_topk_amd/csrc/gemm_bf16.hip",
                   "sparse_mixture_experts_topk_amd/csrc/gemm_bf16_decode.hip",
                   "sparse_mixture_experts_topk_amd/csrc/lds_stream.hpp",
@@ -55,12 +56,14 @@ def kernel_source_sha(cfg=None) -> str:
 
 def is_decode(cfg) -> bool:
     # the library's weight-streaming path: no expert can receive more than 64 rows
-    cap = cfg.T if cfg.capacity < 0 else min(cfg.T, cfg.capacity)
+    # (a shared expert receives all T)
+    cap = cfg.T if cfg.capacity < 0 or cfg.n_shared else min(cfg.T, cfg.capacity)
     return cap <= 64
 
 
 def gate_up_work(cfg, counts):
-    """Algorithmic bytes and flops of one gate/up launch."""
+    """Algorithmic bytes and flops of one gate/up launch (counts: rows per expert group,
+    the shared expert's included)."""
     d, F = cfg.d_model, cfg.d_ff
     n_kept = int(sum(counts))
     touched = int(sum(1 for c in counts if c > 0))
@@ -227,9 +230,11 @@ def main():
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8_e4m3": "fp8_e4m3", "f32": "f32", "mxfp4": "mxfp4"}[cfg.w_dtype],
-        "data": "synthetic (seeded, Mixtral-shaped; random weights)",
+        "data": ("synthetic (seeded, fine-grained: 256 routed experts top-8 + 1 shared; random "
+                 "weights)" if cfg.n_shared or cfg.n_experts > 8 else
+                 "synthetic (seeded, Mixtral-shaped; random weights)"),
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
-                   "n_experts": cfg.n_experts, "top_k": cfg.top_k,
+                   "n_experts": cfg.n_experts, "top_k": cfg.top_k, "n_shared": cfg.n_shared,
                    "capacity": None if cfg.capacity < 0 else cfg.capacity,
                    "overflow": cfg.overflow if cfg.capacity >= 0 else None,
                    "act_dtype": cfg.act_dtype, "w_dtype": cfg.w_dtype,

@@ -1,7 +1,8 @@
 /*
- * moe.h -- C ABI of a sparse top-2 Mixture-of-Experts feed-forward layer
- * (Mixtral 8x7B style) implemented with hand-written HIP kernels for
- * AMD Instinct MI355X (gfx950).
+ * moe.h -- C ABI of a sparse top-k Mixture-of-Experts feed-forward layer
+ * (Mixtral 8x7B style top-2, and the fine-grained many-expert form with a
+ * shared expert) implemented with hand-written HIP kernels for AMD Instinct
+ * MI355X (gfx950).
  *
  * The layer (pages: "Mixtral and Mixture-of-Experts, Explained", section
  * "How it works"; "Mixtral" study notes, section "MoE Layer"):
@@ -9,6 +10,14 @@
  *   G(x)    = Softmax(TopK(logits)), k = 2     non-selected logits at -inf
  *   y       = sum_i G(x)_i * Expert_i(x)
  *   Expert  = w2( silu(x w1^T) * (x w3^T) )    SwiGLU, no biases
+ * General form ("Mixtral 8x7B" interview page, section on how MoE design
+ * changed since Mixtral: DeepSeek-V3 routes each token to 8 of 256 experts
+ * and sends every token through one shared expert as well):
+ *   top_k = k in 1..8 of up to 256 routed experts, G = softmax over the k
+ *   kept logits, and with n_shared = 1
+ *   y      += Expert_E(x)                      shared expert, weight 1
+ *   (weights of the shared expert are stored as expert index E, after the
+ *   routed ones; it takes every token and no capacity limit applies to it).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -24,13 +33,17 @@
  * - Device contents are not validated.  Preconditions: x, W_g, weights and
  *   scales finite; ids written by moe_route_topk (or equivalent) in [0, E).
  * - T = 0 is legal: every call returns MOE_OK and enqueues nothing.
- * - Expert ids count from 0.  Slot 0 of a token is its larger logit; equal
- *   logits go to the lower expert index.
- * - Rows of the permuted buffers are grouped by expert; inside an expert
- *   they follow ascending token index (a token has at most one row per
- *   expert).  Buffers indexed by row are sized for T*top_k rows, the most
- *   any call can produce, so one set of buffers serves dropless and
- *   capacity modes.
+ * - Expert ids count from 0.  A token's slots follow its logits in
+ *   descending order (slot 0 the largest); equal logits go to the lower
+ *   expert index.
+ * - Assignment ("slot") (t, s) of token t has index t*k + s, s < k.  With a
+ *   shared expert the T extra assignments (t, shared) have indices
+ *   T*k + t.  S = n_shared, R = T*(k + S) is the number of slots.
+ * - Rows of the permuted buffers are grouped by expert (routed experts
+ *   0..E-1, then the shared expert E); inside an expert they follow
+ *   ascending token index (a token has at most one row per expert).
+ *   Buffers indexed by row are sized for R rows, the most any call can
+ *   produce, so one set of buffers serves dropless and capacity modes.
  *
  * dtypes (moe_shape_t.act_dtype / w_dtype):
  *   act F32  + w F32       : x, W_g, y fp32; x_perm fp32; h fp32.
@@ -46,19 +59,22 @@
  *                            block.  fp32 accumulate.
  *   act BF16 + w MXFP4     : x, W_g, y bf16; x_perm bf16; h bf16.  Expert weights
  *                            are OCP Microscaling FP4: E2M1 codes, two per byte
- *                            (even element in the low nibble), [E, F, d/2] /
- *                            [E, d, F/2] bytes, with one E8M0 scale byte
+ *                            (even element in the low nibble), [E+S, F, d/2] /
+ *                            [E+S, d, F/2] bytes, with one E8M0 scale byte
  *                            (2^(byte - 127)) per row and block of 32
- *                            consecutive input elements, [E, F, d/32] /
- *                            [E, d, F/32] bytes.  The matrix cores see the
+ *                            consecutive input elements, [E+S, F, d/32] /
+ *                            [E+S, d, F/32] bytes.  The matrix cores see the
  *                            exact dequantised weights in bf16; fp32
  *                            accumulate.  A weight-streaming (decode) format:
- *                            at most 64 rows per expert (T <= 64 or capacity
- *                            <= 64), d_model and d_ff multiples of 256.
+ *                            at most 64 rows per expert (T <= 64, or capacity
+ *                            <= 64 without a shared expert), d_model and d_ff
+ *                            multiples of 256.
  *   Other combinations return MOE_ERR_UNSUPPORTED.
  *
- * Shape limits: top_k == 2; 2 <= n_experts <= 64; d_model and d_ff
- * multiples of 64; 1 <= T <= 2^24 (or 0); capacity == MOE_DROPLESS or >= 0.
+ * Shape limits: 1 <= top_k <= 8 (top_k <= n_experts); 2 <= n_experts <= 256
+ * (fp32 activations: <= 64); n_shared 0 or 1; d_model and d_ff multiples
+ * of 64; 1 <= T <= 2^24 (or 0); capacity == MOE_DROPLESS or >= 0;
+ * MOE_OVERFLOW_NEXT_BEST with a capacity needs top_k == 2.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -73,7 +89,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,   /* NULL required pointer, bad shape value */
-  MOE_ERR_UNSUPPORTED = 2,   /* legal but not implemented: top_k != 2, dtype combo, alignment */
+  MOE_ERR_UNSUPPORTED = 2,   /* legal but not implemented: shape limit, dtype combo, alignment */
   MOE_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than moe_workspace_bytes() */
   MOE_ERR_HIP = 4            /* a kernel launch failed */
 } moe_status_t;
@@ -94,7 +110,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_
  *     the slots the capacity round left free (capacity minus what it kept),
  *     ranked like the capacity round (gate weight descending, then token
  *     ascending); the other offers stay dropped.  The ranking ties to the
- *     lower expert index, like the top-2. */
+ *     lower expert index, like the top-2.  Defined for top_k == 2 only. */
 #define MOE_OVERFLOW_DROP 0
 #define MOE_OVERFLOW_NEXT_BEST 1
 
@@ -102,12 +118,13 @@ typedef struct {
   int32_t T;          /* tokens (batch * seq_len, flattened) */
   int32_t d_model;    /* hidden size d */
   int32_t d_ff;       /* expert FFN width F */
-  int32_t n_experts;  /* E */
-  int32_t top_k;      /* must be 2 */
+  int32_t n_experts;  /* E routed experts */
+  int32_t top_k;      /* k, 1..8 */
   int32_t capacity;   /* MOE_DROPLESS, or slots per expert (0 drops every assignment) */
   int32_t act_dtype;  /* moe_dtype_t of x, W_g, y */
   int32_t w_dtype;    /* moe_dtype_t of w1, w3, w2 */
   int32_t overflow;   /* MOE_OVERFLOW_DROP or MOE_OVERFLOW_NEXT_BEST (ignored when dropless) */
+  int32_t n_shared;   /* S: 0, or 1 shared expert (weights at expert index E) */
 } moe_shape_t;
 
 /* Which call a workspace is sized for. */
@@ -126,17 +143,20 @@ const char* moe_version(void);
  * argument or invalid shape. */
 moe_status_t moe_workspace_bytes(const moe_shape_t* shape, moe_call_t call, size_t* bytes);
 
-/* Router + top-2 + gate weights.
+/* Router + top-k + gate weights.
  * Pages: "Mixtral" study notes, MixtralMoE.forward (gate, topk, softmax over
  * the kept logits); "Mixtral and Mixture-of-Experts, Explained", gate
  * equation G(x) = Softmax(TopK(x . W_g)).
  *   x            [T, d]   act dtype
  *   w_gate       [E, d]   act dtype (nn.Linear [out, in] layout)
  *   router_bias  [E] fp32 or NULL, added to the fp32 logits after the dot product
- *   topk_ids     [T, 2] int32 out: slot 0 = larger logit, ties -> lower index
- *   topk_weights [T, 2] fp32 out: w0 = 1/(1+exp(l1-l0)), w1 = 1-w0 (w0+w1 == 1 exactly)
+ *   topk_ids     [T, k] int32 out: the k largest logits in descending order,
+ *                ties -> lower index
+ *   topk_weights [T, k] fp32 out.  k == 2: w0 = 1/(1+exp(l1-l0)), w1 = 1-w0
+ *                (w0+w1 == 1 exactly).  Otherwise w_j = exp(l_j - l_0) / sum_i
+ *                exp(l_i - l_0) over the kept logits (k == 1: w0 = 1).
  *   logits       [T, E] fp32 out, or NULL
- *   next_ids     [T, 2] int32 out, or NULL: the 3rd- and 4th-ranked experts of
+ *   next_ids     [T, 2] int32 out, or NULL: the experts ranked k+1 and k+2 of
  *                each token (same order: logit descending, ties -> lower index),
  *                -1 where n_experts is too small.  moe_permute needs them for
  *                MOE_OVERFLOW_NEXT_BEST.
@@ -150,23 +170,24 @@ moe_status_t moe_route_topk(const moe_shape_t* shape, const void* x, const void*
  * auxiliary loss" (capacity-limited dispatch, excess dropped) and the
  * bincount of the top-2 ids (expert activation listing); "batch tokens by
  * expert ... scatter back" in the simplified forward pass.
- *   topk_ids, topk_weights [T, 2] from moe_route_topk
+ *   topk_ids, topk_weights [T, k] from moe_route_topk
  *   next_ids       [T, 2] from moe_route_topk; required with a capacity and
  *                  MOE_OVERFLOW_NEXT_BEST, else ignored (may be NULL)
  *   x              [T, d] act dtype
- *   expert_counts  [E] int32 out: kept assignments per expert
- *   expert_offsets [E+1] int32 out: exclusive prefix sum of counts
- *   perm_src       [T*2] int32 out: rows 0..offsets[E]-1 hold t*2+slot of each row
- *   slot_to_row    [T*2] int32 out: row of (t, slot), -1 if dropped
- *   drop_mask      [T*2] uint8 out or NULL: 0 = kept by its top-2 expert,
+ *   expert_counts  [E+S] int32 out: kept assignments per expert (shared: T)
+ *   expert_offsets [E+S+1] int32 out: exclusive prefix sum of counts
+ *   perm_src       [R] int32 out: rows 0..offsets[E+S]-1 hold the slot index
+ *                  (t*k+s, or T*k+t for the shared expert) of each row
+ *   slot_to_row    [R] int32 out: row of each slot, -1 if dropped
+ *   drop_mask      [T*k] uint8 out or NULL: 0 = kept by its top-k expert,
  *                  1 = dropped, 2 = kept by its fallback expert (NEXT_BEST)
- *   x_perm         [T*2, d] out: x_perm[row] = x[perm_src[row] / 2]; fp8 configs:
- *                  e4m3 codes [T*2, d] plus x_perm_scale [T*2, d/32] E8M0 bytes
+ *   x_perm         [R, d] out: x_perm[row] = x[token of perm_src[row]]; fp8 configs:
+ *                  e4m3 codes [R, d] plus x_perm_scale [R, d/32] E8M0 bytes
  *   x_perm_scale   fp8 configs only (else ignored; may be NULL)
  * Capacity rule: per expert, assignments ranked by gate weight (descending,
  * compared as fp32), ties to the lower token index; the first `capacity`
  * are kept.  A dropped assignment contributes nothing and the token's other
- * slot is not renormalised; with MOE_OVERFLOW_NEXT_BEST the fallback round
+ * slots are not renormalised; with MOE_OVERFLOW_NEXT_BEST the fallback round
  * above runs next and the rows of each expert include the slots it took
  * (still one row per token and expert, in ascending token order).
  * Workspace: moe_workspace_bytes(MOE_CALL_PERMUTE). */
@@ -182,10 +203,10 @@ moe_status_t moe_permute(const moe_shape_t* shape, const int32_t* topk_ids,
  * expert e (rows offsets[e] .. offsets[e+1]-1).
  * Pages: "Mixtral" study notes, MixtralExpert.forward and "SwiGLU Experts".
  *   x_perm, x_perm_scale as written by moe_permute
- *   expert_offsets [E+1] int32 (device)
- *   w1, w3         [E, F, d] weight dtype (MXFP4: [E, F, d/2] bytes); w1_scale,
- *                  w3_scale: fp8 [E, F] fp32, MXFP4 [E, F, d/32] E8M0 bytes, else unused
- *   h              [T*2, F] out (bf16 / fp32 / e4m3 codes); h_scale [T*2, F/32] E8M0 (fp8 only)
+ *   expert_offsets [E+S+1] int32 (device)
+ *   w1, w3         [E+S, F, d] weight dtype (MXFP4: [E+S, F, d/2] bytes); w1_scale,
+ *                  w3_scale: fp8 [E+S, F] fp32, MXFP4 [E+S, F, d/32] E8M0 bytes, else unused
+ *   h              [R, F] out (bf16 / fp32 / e4m3 codes); h_scale [R, F/32] E8M0 (fp8 only)
  * Workspace: moe_workspace_bytes(MOE_CALL_GATE_UP). */
 moe_status_t moe_expert_gemm_gate_up(const moe_shape_t* shape, const void* x_perm,
                                      const uint8_t* x_perm_scale, const int32_t* expert_offsets,
@@ -196,10 +217,10 @@ moe_status_t moe_expert_gemm_gate_up(const moe_shape_t* shape, const void* x_per
 /* Grouped expert down projection: y_perm[row] = h[row] . w2[e]^T (fp32 out).
  * Pages: "Mixtral" study notes, MixtralExpert.forward (self.w2).
  *   h, h_scale     as written by moe_expert_gemm_gate_up
- *   expert_offsets [E+1] int32
- *   w2             [E, d, F] weight dtype (MXFP4: [E, d, F/2] bytes); w2_scale: fp8
- *                  [E, d] fp32, MXFP4 [E, d, F/32] E8M0 bytes, else unused
- *   y_perm         [T*2, d] fp32 out
+ *   expert_offsets [E+S+1] int32
+ *   w2             [E+S, d, F] weight dtype (MXFP4: [E+S, d, F/2] bytes); w2_scale: fp8
+ *                  [E+S, d] fp32, MXFP4 [E+S, d, F/32] E8M0 bytes, else unused
+ *   y_perm         [R, d] fp32 out
  * Workspace: moe_workspace_bytes(MOE_CALL_DOWN) bytes, 16-byte aligned, device
  * memory owned by the caller (0 for shapes that need none; then it may be
  * NULL).  bf16 shapes with more than 64 rows per expert use it for fp32
@@ -215,11 +236,13 @@ moe_status_t moe_expert_gemm_down(const moe_shape_t* shape, const void* h, const
                                   size_t workspace_bytes, void* stream);
 
 /* Gate-weighted combine back to token order:
- * y[t] = sum over kept slots s of topk_weights[t, s] * y_perm[slot_to_row[t*2+s]],
- * 0 when both slots are dropped; cast to the act dtype (round to nearest even).
+ * y[t] = sum over kept slots s of topk_weights[t, s] * y_perm[slot_to_row[t*k+s]]
+ *        (+ y_perm[slot_to_row[T*k+t]] with a shared expert),
+ * 0 when every slot is dropped and there is no shared expert; accumulated in
+ * fp32 in slot order (shared last), cast to the act dtype (round to nearest even).
  * Pages: "Mixtral and Mixture-of-Experts, Explained", y = sum_i G(x)_i Expert_i(x);
  * study notes, output = zeros_like(x) then weighted accumulation.
- *   y_perm [T*2, d] fp32; slot_to_row [T*2] int32; topk_weights [T, 2] fp32
+ *   y_perm [R, d] fp32; slot_to_row [R] int32; topk_weights [T, k] fp32
  *   y      [T, d] act dtype out.  No workspace. */
 moe_status_t moe_combine(const moe_shape_t* shape, const float* y_perm, const int32_t* slot_to_row,
                          const float* topk_weights, void* y, void* stream);
@@ -227,11 +250,11 @@ moe_status_t moe_combine(const moe_shape_t* shape, const float* y_perm, const in
 /* The whole layer on one stream, with no host synchronisation:
  * route -> (capacity) -> permute -> gate/up -> down -> combine.
  *   x [T, d], w_gate [E, d] act dtype; router_bias [E] fp32 or NULL
- *   w1, w3 [E, F, d], w2 [E, d, F] weight dtype; w*_scale as for the two GEMM calls
+ *   w1, w3 [E+S, F, d], w2 [E+S, d, F] weight dtype; w*_scale as for the two GEMM calls
  *   (fp8: fp32 per output channel; MXFP4: E8M0 bytes per 32-element block)
  *   y [T, d] act dtype out
- *   optional outputs (NULL to skip): topk_ids_out [T, 2] int32, topk_weights_out [T, 2]
- *   fp32, expert_counts_out [E] int32, drop_mask_out [T*2] uint8 (0 / 1 / 2 as in
+ *   optional outputs (NULL to skip): topk_ids_out [T, k] int32, topk_weights_out [T, k]
+ *   fp32, expert_counts_out [E+S] int32, drop_mask_out [T*k] uint8 (0 / 1 / 2 as in
  *   moe_permute), logits_out [T, E] fp32
  * topk_ids_out are the router's choices; with MOE_OVERFLOW_NEXT_BEST a slot
  * whose drop mask is 2 was processed by its fallback expert instead.

@@ -1,4 +1,4 @@
-"""Sparse top-2 Mixture-of-Experts feed-forward layer for AMD MI355X (gfx950).
+"""Sparse top-k Mixture-of-Experts feed-forward layer for AMD MI355X (gfx950).
 
 Thin Python binding of libmoe.so (C ABI in include/moe.h).  The functions
 below carry the C names and only marshal arguments: torch tensors supply
@@ -36,16 +36,17 @@ class MoEError(RuntimeError):
 
 def make_shape(T: int, d_model: int, d_ff: int, n_experts: int = 8, top_k: int = 2,
                capacity: int = MOE_DROPLESS, act_dtype="bf16", w_dtype="bf16",
-               overflow="drop") -> MoeShape:
+               overflow="drop", n_shared: int = 0) -> MoeShape:
     a = _DT.get(act_dtype, act_dtype)
     w = _DT.get(w_dtype, w_dtype)
-    return MoeShape(T, d_model, d_ff, n_experts, top_k, capacity, a, w, _OVF.get(overflow, overflow))
+    return MoeShape(T, d_model, d_ff, n_experts, top_k, capacity, a, w, _OVF.get(overflow, overflow),
+                    n_shared)
 
 
 def shape_of(cfg) -> MoeShape:
     """Shape of a synthetic.MoEConfig."""
     return make_shape(cfg.T, cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, cfg.capacity,
-                      cfg.act_dtype, cfg.w_dtype, cfg.overflow)
+                      cfg.act_dtype, cfg.w_dtype, cfg.overflow, cfg.n_shared)
 
 
 def _p(t: Optional[torch.Tensor]):

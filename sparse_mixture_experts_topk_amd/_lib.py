@@ -22,7 +22,8 @@ class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("w_dtype", ctypes.c_int32), ("overflow", ctypes.c_int32)]
+                ("w_dtype", ctypes.c_int32), ("overflow", ctypes.c_int32),
+                ("n_shared", ctypes.c_int32)]
 
 
 P = ctypes.c_void_p

@@ -88,6 +88,7 @@ moe_status_t validate_shape(const moe_shape_t* s) {
   if (s == nullptr) return MOE_ERR_INVALID_ARG;
   if (s->T < 0 || s->T > (1 << 24)) return MOE_ERR_INVALID_ARG;
   if (s->top_k < 1 || s->n_experts < 2 || s->top_k > s->n_experts) return MOE_ERR_INVALID_ARG;
+  if (s->n_shared < 0) return MOE_ERR_INVALID_ARG;
   if (s->d_model <= 0 || s->d_ff <= 0) return MOE_ERR_INVALID_ARG;
   if (s->capacity < MOE_DROPLESS) return MOE_ERR_INVALID_ARG;
   if (s->overflow != MOE_OVERFLOW_DROP && s->overflow != MOE_OVERFLOW_NEXT_BEST)
@@ -96,7 +97,12 @@ moe_status_t validate_shape(const moe_shape_t* s) {
                      (s->w_dtype == MOE_F32 || s->w_dtype == MOE_BF16 || s->w_dtype == MOE_FP8_E4M3 ||
                       s->w_dtype == MOE_MXFP4);
   if (!known) return MOE_ERR_INVALID_ARG;
-  if (s->top_k != 2 || s->n_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (s->top_k > moe::kMaxTopK || s->n_experts > moe::kMaxExperts || s->n_shared > 1)
+    return MOE_ERR_UNSUPPORTED;
+  if (s->act_dtype == MOE_F32 && s->n_experts > moe::kMaxExpertsF32) return MOE_ERR_UNSUPPORTED;
+  // the fallback round offers a dropped slot of a top-2 token to its 3rd/4th expert
+  if (s->capacity >= 0 && s->overflow == MOE_OVERFLOW_NEXT_BEST && s->top_k != 2)
+    return MOE_ERR_UNSUPPORTED;
   if (s->d_model % 64 != 0 || s->d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (s->d_model > (1 << 16) || s->d_ff > (1 << 18)) return MOE_ERR_UNSUPPORTED;
   const bool combo = (s->act_dtype == MOE_F32 && s->w_dtype == MOE_F32) ||
@@ -148,23 +154,25 @@ size_t down_workspace_bytes(const moe_shape_t& s) {
 
 ForwardLayout forward_layout(const moe_shape_t& s) {
   ForwardLayout L{};
-  const size_t A = (size_t)s.T * s.top_k;                 // assignments = max rows
+  const size_t A = (size_t)s.T * s.top_k;                 // routed assignments
+  const size_t R = (size_t)moe::total_slots(s);           // slots incl. the shared expert = max rows
+  const size_t G = (size_t)moe::expert_groups(s);
   const size_t eb = perm_elem_bytes(s);
   const bool fp8 = s.w_dtype == MOE_FP8_E4M3;
   size_t o = 0;
   L.ids = o;         o += align_up(A * 4);
   L.weights = o;     o += align_up(A * 4);
-  L.next_ids = o;    o += fallback_on(s) ? align_up(A * 4) : 0;
-  L.counts = o;      o += align_up(64 * 4);
-  L.offsets = o;     o += align_up(65 * 4);
-  L.perm_src = o;    o += align_up(A * 4);
-  L.slot_to_row = o; o += align_up(A * 4);
+  L.next_ids = o;    o += fallback_on(s) ? align_up((size_t)s.T * 2 * 4) : 0;
+  L.counts = o;      o += align_up(G * 4);
+  L.offsets = o;     o += align_up((G + 1) * 4);
+  L.perm_src = o;    o += align_up(R * 4);
+  L.slot_to_row = o; o += align_up(R * 4);
   L.drop = o;        o += align_up(A);
-  L.x_perm = o;      o += align_up(A * s.d_model * eb);
-  L.x_scale = o;     o += fp8 ? align_up(A * (s.d_model / 32)) : 0;
-  L.h = o;           o += align_up(A * s.d_ff * eb);
-  L.h_scale = o;     o += fp8 ? align_up(A * (s.d_ff / 32)) : 0;
-  L.y_perm = o;      o += align_up(A * s.d_model * 4);
+  L.x_perm = o;      o += align_up(R * s.d_model * eb);
+  L.x_scale = o;     o += fp8 ? align_up(R * (s.d_model / 32)) : 0;
+  L.h = o;           o += align_up(R * s.d_ff * eb);
+  L.h_scale = o;     o += fp8 ? align_up(R * (s.d_ff / 32)) : 0;
+  L.y_perm = o;      o += align_up(R * s.d_model * 4);
   L.down_ws = o;     o += align_up(down_workspace_bytes(s));
   L.total = o;
   return L;
@@ -242,7 +250,7 @@ moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_ids, const fl
     e = moe::launch_capacity_select(*s, topk_ids, topk_weights, next, drop_mask, st);
     drop_in = drop_mask;
   } else if (drop_mask != nullptr) {
-    e = launch_fill_u8(drop_mask, (int64_t)s->T * 2, 0, st);
+    e = launch_fill_u8(drop_mask, (int64_t)s->T * s->top_k, 0, st);
   }
   if (e == hipSuccess)
     e = moe::launch_permute_index(*s, topk_ids, drop_in, next, expert_counts, expert_offsets,
@@ -343,7 +351,7 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_gate
       e = moe::launch_capacity_select(*s, ids, gw, next, drop, st);
       drop_in = drop;
     } else if (drop_mask_out != nullptr) {
-      e = launch_fill_u8(drop_mask_out, (int64_t)s->T * 2, 0, st);
+      e = launch_fill_u8(drop_mask_out, (int64_t)s->T * s->top_k, 0, st);
     }
   }
   if (e == hipSuccess)

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
   static_assert(!SPLIT || !DUAL, "split runs: single GEMM");
   static_assert(!DUAL || (G::TA / 2) % 16 == 0, "w3 rows start on a swizzle period");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * G::STAGE_BYTES];
-  __shared__ int32_t offs[kMaxExperts + 1];
+  __shared__ int32_t offs[kMaxExpertGroups + 1];
 
   constexpr int HA = WA / 2;                 // dual: w1 (or w3) blocks per wavefront
   constexpr int CH_TILE = DUAL ? G::TA / 2 : G::TA;
@@ -501,18 +501,18 @@ hipError_t launch_prefill(const moe_shape_t& s, const uint16_t* act, const int32
   if constexpr (!DUAL) {
     if (partials != nullptr) {   // split tail: K-runs into partial tiles, then their sum
       hipLaunchKernelGGL((grouped_gemm_bf16_prefill<false, C::BK, C::NS, C::WR, C::WC, C::WA, C::WB, true>),
-                         dim3((unsigned)grid), dim3(G::THREADS), 0, st, act, offsets, s.n_experts, wa,
+                         dim3((unsigned)grid), dim3(G::THREADS), 0, st, act, offsets, expert_groups(s), wa,
                          wb, N, K, out, partials, n_tiles);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(split_fixup_kernel<G::TA>, dim3((unsigned)(grid * kFixupRowGroups)), dim3(256), 0,
-                         st, offsets, s.n_experts, N, K, C::BK, n_tiles, (int)(grid / 8), partials,
+                         st, offsets, expert_groups(s), N, K, C::BK, n_tiles, (int)(grid / 8), partials,
                          static_cast<float*>(out));
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((grouped_gemm_bf16_prefill<DUAL, C::BK, C::NS, C::WR, C::WC, C::WA, C::WB, false>),
-                     dim3((unsigned)grid), dim3(G::THREADS), 0, st, act, offsets, s.n_experts, wa,
+                     dim3((unsigned)grid), dim3(G::THREADS), 0, st, act, offsets, expert_groups(s), wa,
                      wb, N, K, out, nullptr, n_tiles);
   return hipGetLastError();
 }

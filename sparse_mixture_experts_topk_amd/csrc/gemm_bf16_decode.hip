@@ -120,11 +120,11 @@ hipError_t launch_variant(const moe_shape_t& s, const uint16_t* act, const int32
                           const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
                           hipStream_t st) {
   const int tok_tiles = (int)((max_rows_per_expert(s) + 15) / 16);
-  const int64_t groups = (int64_t)s.n_experts * tok_tiles * (N / 16);
+  const int64_t groups = (int64_t)expert_groups(s) * tok_tiles * (N / 16);
   if (groups <= 0) return hipSuccess;   // no expert can hold a row (capacity 0)
   const int64_t blocks = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
   hipLaunchKernelGGL((grouped_gemm_bf16_decode<DUAL, ROWS, MIN_WAVES>), dim3((unsigned)blocks),
-                     dim3(kWavesPerBlock * kWave), 0, st, act, offsets, s.n_experts, wa, wb, N, K,
+                     dim3(kWavesPerBlock * kWave), 0, st, act, offsets, expert_groups(s), wa, wb, N, K,
                      out, tok_tiles);
   return hipGetLastError();
 }

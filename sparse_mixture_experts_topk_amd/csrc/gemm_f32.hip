@@ -104,7 +104,7 @@ hipError_t launch_f32(const moe_shape_t& s, const float* act, const int32_t* off
   const int64_t grid = max_token_tiles(s, F32_TM) * n_tiles;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(grouped_gemm_f32_kernel<DUAL>, dim3((unsigned)grid), dim3(256), 0, st, act,
-                     offsets, s.n_experts, wa, wb, N, K, out, n_tiles);
+                     offsets, expert_groups(s), wa, wb, N, K, out, n_tiles);
   return hipGetLastError();
 }
 

@@ -294,7 +294,7 @@ hipError_t launch_fp8(const moe_shape_t& s, const uint8_t* act, const uint8_t* a
   const int64_t padded = (grid + 7) / 8 * 8;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(grouped_gemm_fp8_prefill<DUAL>, dim3((unsigned)padded), dim3(F8_THREADS), 0,
-                     st, act, act_scale, offsets, s.n_experts, wa, wb, sa, sb, N, K, out,
+                     st, act, act_scale, offsets, expert_groups(s), wa, wb, sa, sb, N, K, out,
                      out_scale, n_tiles, (int)padded);
   return hipGetLastError();
 }

@@ -257,12 +257,12 @@ hipError_t launch_variant(const moe_shape_t& s, const uint16_t* act, const int32
                           const uint8_t* wa, const uint8_t* sa, const uint8_t* wb,
                           const uint8_t* sb, int N, int K, void* out, hipStream_t st) {
   const int tok_tiles = (int)((max_rows_per_expert(s) + 15) / 16);
-  const int64_t groups = (int64_t)s.n_experts * tok_tiles * (N / (16 * RB));
+  const int64_t groups = (int64_t)expert_groups(s) * tok_tiles * (N / (16 * RB));
   if (groups <= 0) return hipSuccess;   // no expert can hold a row (capacity 0)
   constexpr int GPB = kMx4Waves / KS;   // output groups per workgroup
   const int64_t blocks = (groups + GPB - 1) / GPB;
   hipLaunchKernelGGL((grouped_gemm_mxfp4_decode<DUAL, RB, MIN_WAVES, PD, KS>), dim3((unsigned)blocks),
-                     dim3(kMx4Waves * kWave), 0, st, act, offsets, s.n_experts, wa, sa, wb, sb, N,
+                     dim3(kMx4Waves * kWave), 0, st, act, offsets, expert_groups(s), wa, sa, wb, sb, N,
                      K, out, tok_tiles);
   return hipGetLastError();
 }

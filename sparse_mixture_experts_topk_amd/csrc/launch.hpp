@@ -12,12 +12,13 @@
 
 namespace moe {
 
-// Router GEMV + top-2 + two-way softmax (+ 3rd/4th-ranked experts when next_ids != NULL).
+// Router GEMV + top-k + softmax of the kept logits (+ the experts ranked k+1, k+2
+// when next_ids != NULL).
 hipError_t launch_route_topk(const moe_shape_t& s, const void* x, const void* w_gate,
                              const float* bias, int32_t* ids, float* weights, float* logits,
                              int32_t* next_ids, hipStream_t st);
 
-// Capacity selection: writes drop_mask[T*2] (0 kept, 1 dropped); with
+// Capacity selection: writes drop_mask[T*k] (0 kept, 1 dropped); with
 // MOE_OVERFLOW_NEXT_BEST a second round re-offers the dropped assignments to
 // next_ids and marks the ones taken with 2.
 hipError_t launch_capacity_select(const moe_shape_t& s, const int32_t* ids, const float* weights,
@@ -29,7 +30,7 @@ hipError_t launch_permute_index(const moe_shape_t& s, const int32_t* ids, const 
                                 const int32_t* next_ids, int32_t* counts, int32_t* offsets,
                                 int32_t* perm_src, int32_t* slot_to_row, hipStream_t st);
 
-// x_perm[row] = x[perm_src[row] / 2] (fp8: block-quantised codes + E8M0 scales).
+// x_perm[row] = x[token of perm_src[row]] (fp8: block-quantised codes + E8M0 scales).
 hipError_t launch_permute_scatter(const moe_shape_t& s, const void* x, const int32_t* offsets,
                                   const int32_t* perm_src, void* x_perm, uint8_t* x_perm_scale,
                                   hipStream_t st);
@@ -69,8 +70,16 @@ size_t down_workspace_bytes_bf16(const moe_shape_t& s);
 // Whether the fp8 matrix-core path is built in.
 constexpr bool kFp8Available = true;
 
-// Largest n_experts the library accepts.
-constexpr int kMaxExperts = 64;
+// Largest n_experts the library accepts (routed), the largest top_k, and the
+// largest n_experts of the fp32-activation router.
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 8;
+constexpr int kMaxExpertsF32 = 64;
+// Expert groups of the permuted rows: routed experts, then the shared one.
+constexpr int kMaxExpertGroups = kMaxExperts + 1;
+inline int expert_groups(const moe_shape_t& s) { return s.n_experts + s.n_shared; }
+// Slots (assignments) per token, the shared expert's included.
+inline int64_t total_slots(const moe_shape_t& s) { return (int64_t)s.T * (s.top_k + s.n_shared); }
 
 // Compute units of the current device (queried once per device).
 int device_cu_count();
@@ -95,20 +104,28 @@ hipError_t launch_down_mxfp4(const moe_shape_t& s, const uint16_t* h, const int3
                              const uint8_t* w2, const uint8_t* w2_scale, float* y_perm,
                              hipStream_t st);
 
-// Largest number of rows any expert can receive: each token picks an expert at most once.
-inline int64_t max_rows_per_expert(const moe_shape_t& s) {
+// Largest number of rows any routed expert can receive: each token picks an expert at most once.
+inline int64_t max_rows_per_routed_expert(const moe_shape_t& s) {
   int64_t m = s.T;
   if (s.capacity >= 0 && s.capacity < m) m = s.capacity;
   return m;
 }
 
-// Upper bound of sum_e ceil(count_e / rows_per_tile) given sum_e count_e <= T*k.
+// Largest number of rows of any expert group (the shared expert takes all T tokens).
+inline int64_t max_rows_per_expert(const moe_shape_t& s) {
+  return s.n_shared > 0 ? (int64_t)s.T : max_rows_per_routed_expert(s);
+}
+
+// Upper bound of sum_g ceil(count_g / rows_per_tile) over the expert groups given
+// sum_e count_e <= T*k over the routed experts (and <= capacity*E), plus the
+// shared expert's T rows.
 inline int64_t max_token_tiles(const moe_shape_t& s, int rows_per_tile) {
   int64_t total = (int64_t)s.T * s.top_k;
   if (s.capacity >= 0) total = std::min<int64_t>(total, (int64_t)s.capacity * s.n_experts);
   int64_t t = (total + rows_per_tile - 1) / rows_per_tile + s.n_experts;
-  int64_t per_expert = (max_rows_per_expert(s) + rows_per_tile - 1) / rows_per_tile;
-  return std::min<int64_t>(t, per_expert * s.n_experts);
+  int64_t per_expert = (max_rows_per_routed_expert(s) + rows_per_tile - 1) / rows_per_tile;
+  t = std::min<int64_t>(t, per_expert * s.n_experts);
+  return t + (int64_t)s.n_shared * ((s.T + rows_per_tile - 1) / rows_per_tile);
 }
 
 }  // namespace moe

@@ -23,12 +23,22 @@
 //   round left free.  Taken assignments are marked 2.  The round only turns
 //   marks 1 into 2, so "dropped in the first round" (mark != 0) reads the
 //   same in every workgroup while others write.
-// permute_index: one workgroup of 1024 lanes.  Pass 1 counts kept
-//   assignments per expert with LDS atomics (order-free).  Pass 2 walks the
-//   tokens in chunks of 1024; per expert a wavefront ballot + popcount gives
-//   each assignment its rank among earlier tokens of the chunk, and a scan
-//   over the 16 wavefronts places the chunk after the previous ones, so rows
-//   inside an expert follow ascending token order (stable, deterministic).
+// permute_index (top-2, up to 64 experts, no shared expert): one workgroup
+//   of 1024 lanes.  Pass 1 counts kept assignments per expert with LDS
+//   atomics (order-free).  Pass 2 walks the tokens in chunks of 1024; per
+//   expert a wavefront ballot + popcount gives each assignment its rank among
+//   earlier tokens of the chunk, and a scan over the 16 wavefronts places the
+//   chunk after the previous ones, so rows inside an expert follow ascending
+//   token order (stable, deterministic).
+// expert_count + expert_place (any top-k, up to 256 experts, shared expert;
+//   the many-expert form of the DeepSeek-V3 remark on the "Mixtral 8x7B"
+//   interview page): one workgroup per expert.  The first kernel counts the
+//   expert's kept assignments; the second sums the counts of the experts
+//   before it (its offset) and walks the tokens in chunks of 1024, a token
+//   per lane, placing the token's assignment to this expert with a ballot
+//   rank plus a scan over the 16 wavefronts -- ascending token order again.
+//   The shared expert's workgroup writes its T rows (slot T*k + t) after
+//   the routed ones.
 // permute_scatter: one wavefront per permuted row copies x[token] in 16-byte
 //   vectors; for fp8 experts each lane quantises 32-element blocks to e4m3
 //   with a power-of-two (E8M0) block scale.
@@ -38,9 +48,9 @@
 namespace moe {
 namespace {
 
-__device__ __forceinline__ uint64_t capacity_key(const float* w, int i) {
+__device__ __forceinline__ uint64_t capacity_key(const float* w, int i, int k) {
   const uint32_t gbits = __float_as_uint(w[i]);  // gate weights are >= +0: bits are monotone
-  const uint32_t tok = (uint32_t)(i >> 1);
+  const uint32_t tok = (uint32_t)(i / k);
   return ((uint64_t)gbits << 32) | (uint64_t)(0xffffffffu - tok);
 }
 
@@ -48,7 +58,8 @@ __device__ __forceinline__ uint64_t capacity_key(const float* w, int i) {
 // read their keys from global memory in every pass).
 constexpr int kCapKeysInLds = 8192;   // a power of two
 
-// Fallback expert of assignment i = 2 t + s that the capacity round dropped:
+// Fallback expert of assignment i = 2 t + s that the capacity round dropped
+// (the fallback round is defined for top-2 only):
 // the token's 3rd-ranked expert, or its 4th for slot 1 when slot 0 was
 // dropped too (-1 where there is no such expert).
 __device__ __forceinline__ int fallback_expert(const uint8_t* drop, const int32_t* next, int i) {
@@ -56,6 +67,9 @@ __device__ __forceinline__ int fallback_expert(const uint8_t* drop, const int32_
   const int j = ((i & 1) && drop[2 * t] != 0) ? 1 : 0;
   return next[2 * t + j];
 }
+
+// Token of slot index i: t * k + s for routed slots, T * k + t for the shared expert's.
+__device__ __forceinline__ int slot_token(int i, int k, int Tk) { return i < Tk ? i / k : i - Tk; }
 
 // Expert that finally processes assignment i (-1: dropped).
 __device__ __forceinline__ int final_expert(const int32_t* ids, const uint8_t* drop,
@@ -71,7 +85,7 @@ template <bool FALLBACK>
 __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __restrict__ ids,
                                                                const float* __restrict__ w,
                                                                const int32_t* __restrict__ next,
-                                                               int n_assign, int capacity_in,
+                                                               int n_assign, int k, int capacity_in,
                                                                uint8_t* __restrict__ drop) {
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
@@ -125,7 +139,7 @@ __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __
       if (lane == 0) base = atomicAdd(&s_count, (int)__popcll(bal));
       base = __shfl(base, 0);
       const int pos = base + (int)__popcll(bal & ((1ull << lane) - 1));
-      if (m && pos < kCapKeysInLds) keys[pos] = capacity_key(w, i);
+      if (m && pos < kCapKeysInLds) keys[pos] = capacity_key(w, i, k);
     }
   }
   __syncthreads();
@@ -192,7 +206,7 @@ __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __
       __syncthreads();
       for (int i = tid; i < n_assign; i += blockDim.x) {
         if (expert_of(i) != e) continue;
-        const uint64_t key = capacity_key(w, i);
+        const uint64_t key = capacity_key(w, i, k);
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
@@ -227,7 +241,7 @@ __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       const int i = i0 + q * blockDim.x;
-      if (id[q] == e) drop[i] = capacity_key(w, i) >= prefix ? kKept : 1;
+      if (id[q] == e) drop[i] = capacity_key(w, i, k) >= prefix ? kKept : 1;
     }
   }
 }
@@ -307,15 +321,104 @@ __global__ __launch_bounds__(kIndexThreads) void permute_index_kernel(
   }
 }
 
+constexpr int kPlaceThreads = 1024;
+constexpr int kPlaceWaves = kPlaceThreads / kWave;
+
+// Sum over the workgroup of one int per lane (every lane gets the total).
+__device__ __forceinline__ int block_sum(int v, int* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  int total = 0;
+  for (int w = 0; w < kPlaceWaves; ++w) total += red[w];
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kPlaceThreads) void expert_count_kernel(
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ drop,
+    const int32_t* __restrict__ next, int n_assign, int32_t* __restrict__ counts) {
+  __shared__ int red[kPlaceWaves];
+  const int e = blockIdx.x;
+  int mine = 0;
+  for (int i = threadIdx.x; i < n_assign; i += kPlaceThreads)
+    mine += final_expert(ids, drop, next, i) == e ? 1 : 0;
+  const int total = block_sum(mine, red);
+  if (threadIdx.x == 0) counts[e] = total;
+}
+
+// Workgroup e < E: rows of routed expert e; workgroup E: the shared expert.
+__global__ __launch_bounds__(kPlaceThreads) void expert_place_kernel(
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ drop,
+    const int32_t* __restrict__ next, int T, int k, int E, int S, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+    int32_t* __restrict__ slot_to_row) {
+  __shared__ int red[kPlaceWaves];
+  __shared__ int s_wave[kPlaceWaves];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int part = 0;
+  for (int j = tid; j < e && j < E; j += kPlaceThreads) part += counts[j];
+  const int base = block_sum(part, red);
+  const int64_t Tk = (int64_t)T * k;
+  if (e == E) {   // shared expert: every token, after the routed rows
+    for (int t = tid; t < T; t += kPlaceThreads) {
+      perm_src[base + t] = (int32_t)(Tk + t);
+      slot_to_row[Tk + t] = base + t;
+    }
+    if (tid == 0) {
+      counts[E] = T;
+      offsets[E] = base;
+      offsets[E + 1] = base + T;
+    }
+    return;
+  }
+  if (tid == 0) {
+    offsets[e] = base;
+    if (e == E - 1 && S == 0) offsets[E] = base + counts[e];
+  }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int chunk_base = base;
+  for (int c0 = 0; c0 < T; c0 += kPlaceThreads) {
+    const int t = c0 + tid;
+    int slot = -1;
+    if (t < T) {
+      for (int s = 0; s < k; ++s) {
+        const int i = t * k + s;
+        const int fe = final_expert(ids, drop, next, i);
+        if (fe == e) slot = s;
+        else if (fe < 0 && ids[i] == e) slot_to_row[i] = -1;   // dropped: its router expert writes it
+      }
+    }
+    const uint64_t b = __ballot(slot >= 0);
+    if (lane == 0) s_wave[wave] = __popcll(b);
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int w = 0; w < kPlaceWaves; ++w) {
+      before += w < wave ? s_wave[w] : 0;
+      total += s_wave[w];
+    }
+    if (slot >= 0) {
+      const int row = chunk_base + before + __popcll(b & lt_mask);
+      perm_src[row] = t * k + slot;
+      slot_to_row[t * k + slot] = row;
+    }
+    chunk_base += total;
+    __syncthreads();
+  }
+}
+
 // One wavefront per row; 16-byte vectors.
 __global__ __launch_bounds__(256) void permute_scatter_copy_kernel(
-    const uint8_t* __restrict__ x, const int32_t* __restrict__ offsets, int E,
-    const int32_t* __restrict__ perm_src, int row_bytes, uint8_t* __restrict__ x_perm,
+    const uint8_t* __restrict__ x, const int32_t* __restrict__ offsets, int G,
+    const int32_t* __restrict__ perm_src, int k, int Tk, int row_bytes, uint8_t* __restrict__ x_perm,
     int max_rows) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= max_rows || row >= offsets[E]) return;
-  const int tok = perm_src[row] >> 1;
+  if (row >= max_rows || row >= offsets[G]) return;
+  const int tok = slot_token(perm_src[row], k, Tk);
   const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)tok * row_bytes);
   uint4* dst = reinterpret_cast<uint4*>(x_perm + (int64_t)row * row_bytes);
   for (int c = lane; c < row_bytes / 16; c += kWave) dst[c] = src[c];
@@ -357,13 +460,13 @@ __device__ __forceinline__ void quantize_block32_bf16(const uint4* src, uint4* d
 }
 
 __global__ __launch_bounds__(256) void permute_scatter_fp8_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets, int E,
-    const int32_t* __restrict__ perm_src, int d, uint8_t* __restrict__ x_perm,
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets, int G,
+    const int32_t* __restrict__ perm_src, int k, int Tk, int d, uint8_t* __restrict__ x_perm,
     uint8_t* __restrict__ x_scale, int max_rows) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= max_rows || row >= offsets[E]) return;
-  const int tok = perm_src[row] >> 1;
+  if (row >= max_rows || row >= offsets[G]) return;
+  const int tok = slot_token(perm_src[row], k, Tk);
   const int nblk = d / 32;
   for (int b = lane; b < nblk; b += kWave) {
     const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)tok * d + b * 32);
@@ -382,36 +485,48 @@ __global__ void fill_u8_kernel(uint8_t* __restrict__ p, int64_t n, uint8_t v) {
 
 hipError_t launch_capacity_select(const moe_shape_t& s, const int32_t* ids, const float* weights,
                                   const int32_t* next_ids, uint8_t* drop_mask, hipStream_t st) {
+  const int n_assign = s.T * s.top_k;
   hipLaunchKernelGGL(capacity_select_kernel<false>, dim3(s.n_experts), dim3(1024), 0, st, ids,
-                     weights, nullptr, 2 * s.T, s.capacity, drop_mask);
+                     weights, nullptr, n_assign, s.top_k, s.capacity, drop_mask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || s.overflow != MOE_OVERFLOW_NEXT_BEST) return e;
   hipLaunchKernelGGL(capacity_select_kernel<true>, dim3(s.n_experts), dim3(1024), 0, st, ids,
-                     weights, next_ids, 2 * s.T, s.capacity, drop_mask);
+                     weights, next_ids, n_assign, s.top_k, s.capacity, drop_mask);
   return hipGetLastError();
 }
 
 hipError_t launch_permute_index(const moe_shape_t& s, const int32_t* ids, const uint8_t* drop_mask,
                                 const int32_t* next_ids, int32_t* counts, int32_t* offsets,
                                 int32_t* perm_src, int32_t* slot_to_row, hipStream_t st) {
-  hipLaunchKernelGGL(permute_index_kernel, dim3(1), dim3(kIndexThreads), 0, st, ids, drop_mask,
-                     next_ids, s.T, s.n_experts, counts, offsets, perm_src, slot_to_row);
+  if (s.top_k == 2 && s.n_experts <= 64 && s.n_shared == 0) {
+    hipLaunchKernelGGL(permute_index_kernel, dim3(1), dim3(kIndexThreads), 0, st, ids, drop_mask,
+                       next_ids, s.T, s.n_experts, counts, offsets, perm_src, slot_to_row);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(expert_count_kernel, dim3(s.n_experts), dim3(kPlaceThreads), 0, st, ids,
+                     drop_mask, next_ids, s.T * s.top_k, counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(expert_place_kernel, dim3(expert_groups(s)), dim3(kPlaceThreads), 0, st, ids,
+                     drop_mask, next_ids, s.T, s.top_k, s.n_experts, s.n_shared, counts, offsets,
+                     perm_src, slot_to_row);
   return hipGetLastError();
 }
 
 hipError_t launch_permute_scatter(const moe_shape_t& s, const void* x, const int32_t* offsets,
                                   const int32_t* perm_src, void* x_perm, uint8_t* x_perm_scale,
                                   hipStream_t st) {
-  const int max_rows = 2 * s.T;
+  const int max_rows = (int)total_slots(s);
   const int blocks = (max_rows + 3) / 4;
+  const int G = expert_groups(s), k = s.top_k, Tk = s.T * s.top_k;
   if (s.w_dtype == MOE_FP8_E4M3) {
     hipLaunchKernelGGL(permute_scatter_fp8_kernel, dim3(blocks), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(x), offsets, s.n_experts, perm_src, s.d_model,
+                       static_cast<const uint16_t*>(x), offsets, G, perm_src, k, Tk, s.d_model,
                        static_cast<uint8_t*>(x_perm), x_perm_scale, max_rows);
   } else {
     const int es = s.act_dtype == MOE_F32 ? 4 : 2;
     hipLaunchKernelGGL(permute_scatter_copy_kernel, dim3(blocks), dim3(256), 0, st,
-                       static_cast<const uint8_t*>(x), offsets, s.n_experts, perm_src,
+                       static_cast<const uint8_t*>(x), offsets, G, perm_src, k, Tk,
                        s.d_model * es, static_cast<uint8_t*>(x_perm), max_rows);
   }
   return hipGetLastError();

@@ -1,24 +1,78 @@
-// Router GEMV fused with top-2 selection and the two-way softmax.
+// Router GEMV fused with top-k selection and the softmax of the kept logits.
 //
 // Pages: "Mixtral" study notes, MixtralMoE.forward (gate -> topk -> softmax of
 // the kept logits); "Mixtral and Mixture-of-Experts, Explained", gate equation
-// G(x) = Softmax(TopK(x . W_g)) with non-selected logits at -inf, so the kept
-// pair's weights are w0 = 1 / (1 + exp(l1 - l0)) and w1 = 1 - w0.
+// G(x) = Softmax(TopK(x . W_g)) with non-selected logits at -inf, so a kept
+// pair's weights are w0 = 1 / (1 + exp(l1 - l0)) and w1 = 1 - w0, and k kept
+// logits get w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).  Many experts and
+// k up to 8: the DeepSeek-V3 remark on the "Mixtral 8x7B" interview page
+// (256 routed experts, 8 active per token).
+//
+// Selection, both kernels: k rounds of an arg-max (value descending, index
+// ascending) over the experts not yet taken, so slot j holds the j-th largest
+// logit and equal logits go to the lower index; on request two more rounds
+// give the experts ranked k+1 and k+2 (the targets of the overflow fallback).
 //
 // Mapping: one wavefront owns TPW = 64 / EP tokens (EP = n_experts rounded up
 // to 8, 16, 32 or 64).  Each lane strides over d in 16-byte vectors of x and
 // of every router row, accumulating TPW * EP = 64 fp32 partial sums.  A
 // recursive-halving exchange (6 shuffle rounds, 63 exchanges) then leaves lane
 // L holding the full logit of (token L / EP, expert L % EP); the top-2 is a
-// butterfly arg-max inside each EP-lane group, ties going to the lower index.
-// On request the two best experts outside the top-2 (ranks 3 and 4, the
-// targets of the overflow fallback) follow with the same arg-max.
+// butterfly arg-max inside each EP-lane group per selection round.
 // W_g (64 KiB at d = 4096, E = 8) stays L2-resident; x is read once.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace moe {
 namespace {
+
+// Selection rounds at most: k, then ranks k+1 and k+2.
+constexpr int kMaxRounds = kMaxTopK + 2;
+
+// (value, index) a ranks before b: larger value, or equal value and lower index.
+__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+
+// Gate weights of one token from its k kept logits v[0] >= v[1] >= ...:
+// k == 2 keeps the logistic form (w0 + w1 == 1 exactly), otherwise the
+// softmax relative to the largest logit.
+__device__ __forceinline__ void gate_weights(const float (&v)[kMaxRounds], int k, float (&w)[kMaxTopK]) {
+  if (k == 2) {
+    w[0] = 1.0f / (1.0f + expf(v[1] - v[0]));
+    w[1] = 1.0f - w[0];
+    return;
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    w[j] = j < k ? expf(v[j] - v[0]) : 0.f;
+    sum += w[j];
+  }
+  const float inv = 1.0f / sum;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) w[j] *= inv;
+}
+
+// One token's outputs: ids and weights [k], next [2] (-inf marks a rank past
+// n_experts: logits are finite).
+__device__ __forceinline__ void store_token(const float (&v)[kMaxRounds], const int (&id)[kMaxRounds],
+                                            int k, int64_t tok, int32_t* __restrict__ ids,
+                                            float* __restrict__ wout, int32_t* __restrict__ next) {
+  float w[kMaxTopK];
+  gate_weights(v, k, w);
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k) {
+      ids[tok * k + j] = id[j];
+      wout[tok * k + j] = w[j];
+    }
+  if (next != nullptr) {
+#pragma unroll
+    for (int j = 0; j < kMaxRounds; ++j)
+      if (j == k || j == k + 1) next[tok * 2 + (j - k)] = v[j] == -INFINITY ? -1 : id[j];
+  }
+}
 
 template <bool BF16>
 __device__ __forceinline__ void load_vec(const void* base, int64_t off, float* out) {
@@ -37,8 +91,8 @@ __device__ __forceinline__ void load_vec(const void* base, int64_t off, float* o
 template <int EP, bool BF16>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const void* __restrict__ x, const void* __restrict__ wg, const float* __restrict__ bias, int T,
-    int d, int E, int32_t* __restrict__ ids, float* __restrict__ wout, float* __restrict__ logits,
-    int32_t* __restrict__ next) {
+    int d, int E, int k, int32_t* __restrict__ ids, float* __restrict__ wout,
+    float* __restrict__ logits, int32_t* __restrict__ next) {
   constexpr int TPW = kWave / EP;
   constexpr int VEC = BF16 ? 8 : 4;
   const int lane = threadIdx.x & 63;
@@ -49,12 +103,12 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 #pragma unroll
   for (int i = 0; i < TPW * EP; ++i) acc[i] = 0.f;
 
-  for (int k = lane * VEC; k < d; k += kWave * VEC) {
+  for (int kk = lane * VEC; kk < d; kk += kWave * VEC) {
     float xv[TPW][VEC];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       if (tok0 + t < T) {
-        load_vec<BF16>(x, (int64_t)(tok0 + t) * d + k, xv[t]);
+        load_vec<BF16>(x, (int64_t)(tok0 + t) * d + kk, xv[t]);
       } else {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) xv[t][v] = 0.f;
@@ -64,7 +118,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     for (int e = 0; e < EP; ++e) {
       if (e < E) {
         float wv[VEC];
-        load_vec<BF16>(wg, (int64_t)e * d + k, wv);
+        load_vec<BF16>(wg, (int64_t)e * d + kk, wv);
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -94,118 +148,86 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   if (real && bias != nullptr) l += bias[e];
   if (logits != nullptr && real && tok < T) logits[(int64_t)tok * E + e] = l;
 
-  // Top-2 inside each group of EP lanes: (value desc, index asc).
-  float v0 = real ? l : -INFINITY;
-  int i0 = e;
+  // Selection rounds inside each group of EP lanes: butterfly arg-max over the
+  // lanes whose expert is not taken yet; the winner's lane leaves later rounds.
+  const int rounds = k + (next != nullptr ? 2 : 0);
+  bool taken = !real;
+  float v[kMaxRounds];
+  int id[kMaxRounds];
 #pragma unroll
-  for (int o = EP / 2; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(v0, o);
-    const int oi = __shfl_xor(i0, o);
-    if (ov > v0 || (ov == v0 && oi < i0)) { v0 = ov; i0 = oi; }
-  }
-  float v1 = (real && e != i0) ? l : -INFINITY;
-  int i1 = e;
+  for (int j = 0; j < kMaxRounds; ++j) {
+    v[j] = -INFINITY;
+    id[j] = 0;
+    if (j < rounds) {
+      float bv = taken ? -INFINITY : l;
+      int bi = e;
 #pragma unroll
-  for (int o = EP / 2; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(v1, o);
-    const int oi = __shfl_xor(i1, o);
-    if (ov > v1 || (ov == v1 && oi < i1)) { v1 = ov; i1 = oi; }
-  }
-  if (e == 0 && tok < T) {
-    const float w0 = 1.0f / (1.0f + expf(v1 - v0));
-    reinterpret_cast<int2*>(ids)[tok] = make_int2(i0, i1);
-    reinterpret_cast<float2*>(wout)[tok] = make_float2(w0, 1.0f - w0);
-  }
-  if (next != nullptr) {   // ranks 3 and 4: the same arg-max outside the top-2
-    float v2 = (real && e != i0 && e != i1) ? l : -INFINITY;
-    int i2 = e;
-#pragma unroll
-    for (int o = EP / 2; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(v2, o);
-      const int oi = __shfl_xor(i2, o);
-      if (ov > v2 || (ov == v2 && oi < i2)) { v2 = ov; i2 = oi; }
+      for (int o = EP / 2; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      if (bv != -INFINITY && bi == e) taken = true;
+      v[j] = bv;
+      id[j] = bi;
     }
-    float v3 = (real && e != i0 && e != i1 && e != i2) ? l : -INFINITY;
-    int i3 = e;
-#pragma unroll
-    for (int o = EP / 2; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(v3, o);
-      const int oi = __shfl_xor(i3, o);
-      if (ov > v3 || (ov == v3 && oi < i3)) { v3 = ov; i3 = oi; }
-    }
-    // logits are finite, so -inf marks a rank past n_experts
-    if (e == 0 && tok < T)
-      reinterpret_cast<int2*>(next)[tok] = make_int2(v2 == -INFINITY ? -1 : i2, v3 == -INFINITY ? -1 : i3);
   }
+  if (e == 0 && tok < T) store_token(v, id, k, tok, ids, wout, next);
 }
 
 // ---------------------------------------------------------------------------
 // bf16 router on the matrix cores.  A 512-lane workgroup owns 16 tokens; its
-// 8 wavefronts split K, each accumulating D[expert][token] = W_g . x^T with
-// v_mfma_f32_16x16x32_bf16 (A = 16 router rows, B = 16 token rows, zero rows
-// past E / T), for EB blocks of 16 experts.  Partial tiles are summed through
-// LDS in a fixed order; wavefront 0 then holds, per lane, token (lane & 15)
-// and experts 16 eb + 4 (lane >> 4) + r.  Each lane keeps its local top-2
-// and two xor-shuffle merges (16, 32) give the token's top-2 (on request a
-// second such pass outside the top-2 gives ranks 3 and 4).  Exact in the
-// sense that matters: bf16 products are exact in fp32 and accumulate in fp32.
+// 8 wavefronts split K (and, for many experts, the expert blocks: EW groups
+// of EB / EW blocks, each over K / (8 / EW)), each accumulating
+// D[expert][token] = W_g . x^T with v_mfma_f32_16x16x32_bf16 (A = 16 router
+// rows, B = 16 token rows, zero rows past E / T), for EB blocks of 16
+// experts.  Partial tiles are summed through LDS in a fixed order;
+// wavefront 0 then holds, per lane, token (lane & 15) and experts
+// 16 eb + 4 (lane >> 4) + q.  A selection round takes each lane's best
+// expert not yet taken (a 64-bit mask per lane) and two xor-shuffle merges
+// (16, 32) give the token's winner.  Exact in the sense that matters: bf16
+// products are exact in fp32 and accumulate in fp32.
 constexpr int kRouteWaves = 8;
 
-// (value, index) a ranks before b: larger value, or equal value and lower index.
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
-}
-
-// Merge two sorted top-2 lists (v0,i0 >= v1,i1) and (w0,j0 >= w1,j1) into the first.
-// Plain scalars and selects, so everything stays in registers.
-__device__ __forceinline__ void merge2(float& v0, int& i0, float& v1, int& i1, float w0, int j0,
-                                       float w1, int j1) {
-  const bool a_first = better(v0, i0, w0, j0);
-  const float fv = a_first ? v0 : w0;
-  const int fi = a_first ? i0 : j0;
-  // runner-up: best of the loser's head and the winner's second
-  const float cv = a_first ? w0 : v0;
-  const int ci = a_first ? j0 : i0;
-  const float sv2 = a_first ? v1 : w1;
-  const int si2 = a_first ? i1 : j1;
-  const bool c_second = better(cv, ci, sv2, si2);
-  v1 = c_second ? cv : sv2;
-  i1 = c_second ? ci : si2;
-  v0 = fv;
-  i0 = fi;
-}
-
-template <int EB>
+template <int EB, int EW>
 __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias,
-    int T, int d, int E, int32_t* __restrict__ ids, float* __restrict__ wout,
+    int T, int d, int E, int k, int32_t* __restrict__ ids, float* __restrict__ wout,
     float* __restrict__ logits, int32_t* __restrict__ next) {
-  __shared__ f32x4_t part[kRouteWaves - 1][EB][64];
+  static_assert(EB * 4 <= 64, "one bit per expert of a lane in the taken mask");
+  static_assert(EB % EW == 0 && kRouteWaves % EW == 0, "expert groups");
+  constexpr int EBW = EB / EW;                 // expert blocks of one wavefront
+  constexpr int KP = kRouteWaves / EW;         // K parts
+  // EW == 1: wavefront 0 keeps its own part; else every wavefront stores its part
+  constexpr int NPART = EW == 1 ? KP - 1 : KP;
+  __shared__ f32x4_t part[NPART][EB][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ew = wave % EW, kp = wave / EW;
   const int tok0 = blockIdx.x * 16;
   const int r = lane & 15, g = lane >> 4;
   const bool tok_ok = tok0 + r < T;
   const uint16_t* px = x + (int64_t)(tok_ok ? tok0 + r : 0) * d + g * 8;
-  const uint16_t* pw[EB];
-  bool w_ok[EB];
+  const uint16_t* pw[EBW];
+  bool w_ok[EBW];
 #pragma unroll
-  for (int eb = 0; eb < EB; ++eb) {
-    w_ok[eb] = eb * 16 + r < E;
-    pw[eb] = wg + (int64_t)(w_ok[eb] ? eb * 16 + r : 0) * d + g * 8;
+  for (int i = 0; i < EBW; ++i) {
+    const int eb = ew * EBW + i;
+    w_ok[i] = eb * 16 + r < E;
+    pw[i] = wg + (int64_t)(w_ok[i] ? eb * 16 + r : 0) * d + g * 8;
   }
   f32x4_t acc[EB];
 #pragma unroll
   for (int eb = 0; eb < EB; ++eb) acc[eb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nblk = d / 32;
-  const int b0 = wave * nblk / kRouteWaves, b1 = (wave + 1) * nblk / kRouteWaves;
-  // all of a wavefront's K blocks in flight at once at d = 4096 (16 per wavefront)
-  constexpr int U = 16 / EB;
+  const int b0 = kp * nblk / KP, b1 = (kp + 1) * nblk / KP;
+  // 16 K blocks of 16-byte loads per lane in flight
+  constexpr int U = EBW >= 16 ? 1 : 16 / EBW;
   const uint4 z = make_uint4(0, 0, 0, 0);
   for (int b = b0; b < b1; b += U) {
     // Unconditional 16-byte loads from clamped (always valid) addresses, then a
     // select: a conditional load would be split into guarded dword loads.
-    uint4 xa[U], wa[U][EB];
+    uint4 xa[U], wa[U][EBW];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool in = b + u < b1;
@@ -213,106 +235,104 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
       const uint4 xv = *reinterpret_cast<const uint4*>(px + blk * 32);
       xa[u] = (in && tok_ok) ? xv : z;
 #pragma unroll
-      for (int eb = 0; eb < EB; ++eb) {
-        const uint4 wv = *reinterpret_cast<const uint4*>(pw[eb] + blk * 32);
-        wa[u][eb] = (in && w_ok[eb]) ? wv : z;
+      for (int i = 0; i < EBW; ++i) {
+        const uint4 wv = *reinterpret_cast<const uint4*>(pw[i] + blk * 32);
+        wa[u][i] = (in && w_ok[i]) ? wv : z;
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int eb = 0; eb < EB; ++eb)
-        acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][eb]), as_bf16x8(xa[u]),
-                                                           acc[eb], 0, 0, 0);
+      for (int i = 0; i < EBW; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][i]), as_bf16x8(xa[u]),
+                                                          acc[i], 0, 0, 0);
   }
-  if (wave > 0) {
+  if constexpr (EW == 1) {
+    if (wave > 0) {
 #pragma unroll
-    for (int eb = 0; eb < EB; ++eb) part[wave - 1][eb][lane] = acc[eb];
+      for (int eb = 0; eb < EB; ++eb) part[wave - 1][eb][lane] = acc[eb];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 0; w < kRouteWaves - 1; ++w)
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb) acc[eb] += part[w][eb][lane];
+  } else {
+#pragma unroll
+    for (int i = 0; i < EBW; ++i) part[kp][ew * EBW + i][lane] = acc[i];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) {
+      acc[eb] = part[0][eb][lane];
+#pragma unroll
+      for (int w = 1; w < KP; ++w) acc[eb] += part[w][eb][lane];
+    }
   }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int w = 0; w < kRouteWaves - 1; ++w)
-#pragma unroll
-    for (int eb = 0; eb < EB; ++eb) acc[eb] += part[w][eb][lane];
 
   const int tok = tok0 + r;
-  // local top-2 over this lane's experts, visited in increasing index order
-  float v0 = -INFINITY, v1 = -INFINITY;
-  int i0 = 1 << 30, i1 = 1 << 30;
 #pragma unroll
   for (int eb = 0; eb < EB; ++eb) {
     const int ebase = eb * 16 + 4 * g;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = ebase + q;
-      const bool real = e < E;
-      float l = acc[eb][q];
-      if (real && bias != nullptr) l += bias[e];
-      acc[eb][q] = l;
-      const float lv = real ? l : -INFINITY;
-      const int li = real ? e : (1 << 30);
-      const bool top = better(lv, li, v0, i0);
-      const bool sec = !top && better(lv, li, v1, i1);
-      v1 = top ? v0 : (sec ? lv : v1);
-      i1 = top ? i0 : (sec ? li : i1);
-      v0 = top ? lv : v0;
-      i0 = top ? li : i0;
-    }
+    for (int q = 0; q < 4; ++q)
+      if (ebase + q < E && bias != nullptr) acc[eb][q] += bias[ebase + q];
     if (logits != nullptr && tok < T) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (ebase + q < E) logits[(int64_t)tok * E + ebase + q] = acc[eb][q];
     }
   }
+  // taken: bit 4 eb + q = expert 16 eb + 4 g + q of this lane is out (taken or past E)
+  uint64_t taken = 0;
 #pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-    const float w0 = __shfl_xor(v0, o), w1 = __shfl_xor(v1, o);
-    const int j0 = __shfl_xor(i0, o), j1 = __shfl_xor(i1, o);
-    merge2(v0, i0, v1, i1, w0, j0, w1, j1);
-  }
-  if (g == 0 && tok < T) {
-    const float w0 = 1.0f / (1.0f + expf(v1 - v0));
-    reinterpret_cast<int2*>(ids)[tok] = make_int2(i0, i1);
-    reinterpret_cast<float2*>(wout)[tok] = make_float2(w0, 1.0f - w0);
-  }
-  if (next != nullptr) {   // ranks 3 and 4: top-2 of the experts outside the top-2
-    float u0 = -INFINITY, u1 = -INFINITY;
-    int j0 = 1 << 30, j1 = 1 << 30;
+  for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
-    for (int eb = 0; eb < EB; ++eb)
+    for (int q = 0; q < 4; ++q)
+      if (eb * 16 + 4 * g + q >= E) taken |= 1ull << (4 * eb + q);
+  const int rounds = k + (next != nullptr ? 2 : 0);
+  float v[kMaxRounds];
+  int id[kMaxRounds];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = eb * 16 + 4 * g + q;
-        const bool cand = e < E && e != i0 && e != i1;
-        const float lv = cand ? acc[eb][q] : -INFINITY;
-        const int li = cand ? e : (1 << 30);
-        const bool top = better(lv, li, u0, j0);
-        const bool sec = !top && better(lv, li, u1, j1);
-        u1 = top ? u0 : (sec ? lv : u1);
-        j1 = top ? j0 : (sec ? li : j1);
-        u0 = top ? lv : u0;
-        j0 = top ? li : j0;
+  for (int j = 0; j < kMaxRounds; ++j) {
+    v[j] = -INFINITY;
+    id[j] = 0;
+    if (j < rounds) {
+      float bv = -INFINITY;
+      int bi = 1 << 30;
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {       // increasing expert index within the lane
+          const bool cand = ((taken >> (4 * eb + q)) & 1ull) == 0;
+          const float lv = cand ? acc[eb][q] : -INFINITY;
+          const int li = cand ? eb * 16 + 4 * g + q : (1 << 30);
+          const bool win = better(lv, li, bv, bi);
+          bv = win ? lv : bv;
+          bi = win ? li : bi;
+        }
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
       }
-#pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-      const float w0 = __shfl_xor(u0, o), w1 = __shfl_xor(u1, o);
-      const int k0 = __shfl_xor(j0, o), k1 = __shfl_xor(j1, o);
-      merge2(u0, j0, u1, j1, w0, k0, w1, k1);
+      if (bi < E && ((bi >> 2) & 3) == g) taken |= 1ull << (4 * (bi >> 4) + (bi & 3));
+      v[j] = bv;
+      id[j] = bi;
     }
-    // logits are finite, so -inf marks a rank past n_experts
-    if (g == 0 && tok < T)
-      reinterpret_cast<int2*>(next)[tok] = make_int2(u0 == -INFINITY ? -1 : j0, u1 == -INFINITY ? -1 : j1);
   }
+  if (g == 0 && tok < T) store_token(v, id, k, tok, ids, wout, next);
 }
 
-template <int EB>
+template <int EB, int EW>
 hipError_t launch_mfma(const moe_shape_t& s, const void* x, const void* wg, const float* bias,
                        int32_t* ids, float* w, float* logits, int32_t* next, hipStream_t st) {
   const int blocks = (s.T + 15) / 16;
-  hipLaunchKernelGGL((route_topk_mfma_kernel<EB>), dim3(blocks), dim3(kRouteWaves * 64), 0, st,
+  hipLaunchKernelGGL((route_topk_mfma_kernel<EB, EW>), dim3(blocks), dim3(kRouteWaves * 64), 0, st,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), bias, s.T,
-                     s.d_model, s.n_experts, ids, w, logits, next);
+                     s.d_model, s.n_experts, s.top_k, ids, w, logits, next);
   return hipGetLastError();
 }
 
@@ -323,7 +343,7 @@ hipError_t launch_ep(const moe_shape_t& s, const void* x, const void* wg, const 
   const int waves = (s.T + TPW - 1) / TPW;
   const int blocks = (waves + 3) / 4;
   hipLaunchKernelGGL((route_topk_kernel<EP, BF16>), dim3(blocks), dim3(256), 0, st, x, wg, bias,
-                     s.T, s.d_model, s.n_experts, ids, w, logits, next);
+                     s.T, s.d_model, s.n_experts, s.top_k, ids, w, logits, next);
   return hipGetLastError();
 }
 
@@ -342,9 +362,11 @@ hipError_t launch_route_topk(const moe_shape_t& s, const void* x, const void* w_
                              const float* bias, int32_t* ids, float* weights, float* logits,
                              int32_t* next_ids, hipStream_t st) {
   if (s.act_dtype == MOE_BF16) {
-    if (s.n_experts <= 16) return launch_mfma<1>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
-    if (s.n_experts <= 32) return launch_mfma<2>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
-    return launch_mfma<4>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
+    if (s.n_experts <= 16) return launch_mfma<1, 1>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
+    if (s.n_experts <= 32) return launch_mfma<2, 1>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
+    if (s.n_experts <= 64) return launch_mfma<4, 1>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
+    if (s.n_experts <= 128) return launch_mfma<8, 2>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
+    return launch_mfma<16, 4>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
   }
   return launch_dtype<false>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
 }

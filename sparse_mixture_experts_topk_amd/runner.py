@@ -69,17 +69,17 @@ class ForwardBuffers:
 
 
 def alloc_forward(cfg, device="cuda", with_outputs=True) -> ForwardBuffers:
-    T, d, E = cfg.T, cfg.d_model, cfg.n_experts
+    T, d, E, k = cfg.T, cfg.d_model, cfg.n_experts, cfg.top_k
     shape = shape_of(cfg)
     ws = torch.empty(max(1, moe_workspace_bytes(shape, MOE_CALL_FORWARD)), dtype=torch.uint8,
                      device=device)
     y = torch.empty(T, d, dtype=_act_dtype(cfg), device=device)
     if not with_outputs:
         return ForwardBuffers(y, None, None, None, None, None, ws)
-    return ForwardBuffers(y, torch.empty(T, 2, dtype=torch.int32, device=device),
-                          torch.empty(T, 2, dtype=torch.float32, device=device),
-                          torch.empty(E, dtype=torch.int32, device=device),
-                          torch.empty(T * 2, dtype=torch.uint8, device=device),
+    return ForwardBuffers(y, torch.empty(T, k, dtype=torch.int32, device=device),
+                          torch.empty(T, k, dtype=torch.float32, device=device),
+                          torch.empty(E + cfg.n_shared, dtype=torch.int32, device=device),
+                          torch.empty(T * k, dtype=torch.uint8, device=device),
                           torch.empty(T, E, dtype=torch.float32, device=device), ws)
 
 
@@ -97,32 +97,33 @@ def staged(di: DeviceInputs, stream=None) -> dict:
     """The five boundary calls in sequence; returns every intermediate buffer."""
     cfg = di.cfg
     dev = di.x.device
-    T, d, F, E = cfg.T, cfg.d_model, cfg.d_ff, cfg.n_experts
-    A = 2 * T
+    T, d, F, E, k, S = cfg.T, cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, cfg.n_shared
+    A = T * k                  # routed slots
+    R = T * (k + S)            # slots incl. the shared expert = most rows
     shape = shape_of(cfg)
     fp8 = cfg.w_dtype == "fp8_e4m3"
     o = {}
-    o["topk_ids"] = torch.empty(T, 2, dtype=torch.int32, device=dev)
-    o["topk_weights"] = torch.empty(T, 2, dtype=torch.float32, device=dev)
+    o["topk_ids"] = torch.empty(T, k, dtype=torch.int32, device=dev)
+    o["topk_weights"] = torch.empty(T, k, dtype=torch.float32, device=dev)
     o["logits"] = torch.empty(T, E, dtype=torch.float32, device=dev)
     o["next_ids"] = torch.empty(T, 2, dtype=torch.int32, device=dev)
     moe_route_topk(shape, di.x, di.w_gate, di.router_bias, o["topk_ids"], o["topk_weights"],
                    o["logits"], o["next_ids"], stream)
-    o["expert_counts"] = torch.empty(E, dtype=torch.int32, device=dev)
-    o["expert_offsets"] = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    o["perm_src"] = torch.full((A,), -7, dtype=torch.int32, device=dev)
-    o["slot_to_row"] = torch.empty(A, dtype=torch.int32, device=dev)
+    o["expert_counts"] = torch.empty(E + S, dtype=torch.int32, device=dev)
+    o["expert_offsets"] = torch.empty(E + S + 1, dtype=torch.int32, device=dev)
+    o["perm_src"] = torch.full((R,), -7, dtype=torch.int32, device=dev)
+    o["slot_to_row"] = torch.empty(R, dtype=torch.int32, device=dev)
     o["drop_mask"] = torch.empty(A, dtype=torch.uint8, device=dev)
-    o["x_perm"] = torch.empty(A, d, dtype=_perm_dtype(cfg), device=dev)
-    o["x_perm_scale"] = torch.empty(A, d // 32, dtype=torch.uint8, device=dev) if fp8 else None
+    o["x_perm"] = torch.empty(R, d, dtype=_perm_dtype(cfg), device=dev)
+    o["x_perm_scale"] = torch.empty(R, d // 32, dtype=torch.uint8, device=dev) if fp8 else None
     moe_permute(shape, o["topk_ids"], o["topk_weights"], o["next_ids"], di.x, o["expert_counts"],
                 o["expert_offsets"], o["perm_src"], o["slot_to_row"], o["drop_mask"], o["x_perm"],
                 o["x_perm_scale"], None, stream)
-    o["h"] = torch.empty(A, F, dtype=_perm_dtype(cfg), device=dev)
-    o["h_scale"] = torch.empty(A, F // 32, dtype=torch.uint8, device=dev) if fp8 else None
+    o["h"] = torch.empty(R, F, dtype=_perm_dtype(cfg), device=dev)
+    o["h_scale"] = torch.empty(R, F // 32, dtype=torch.uint8, device=dev) if fp8 else None
     moe_expert_gemm_gate_up(shape, o["x_perm"], o["x_perm_scale"], o["expert_offsets"], di.w1,
                             di.w3, di.w1_scale, di.w3_scale, o["h"], o["h_scale"], None, stream)
-    o["y_perm"] = torch.empty(A, d, dtype=torch.float32, device=dev)
+    o["y_perm"] = torch.empty(R, d, dtype=torch.float32, device=dev)
     down_ws = moe_workspace_bytes(shape, MOE_CALL_DOWN)
     o["down_ws"] = torch.empty(down_ws, dtype=torch.uint8, device=dev) if down_ws else None
     moe_expert_gemm_down(shape, o["h"], o["h_scale"], o["expert_offsets"], di.w2, di.w2_scale,

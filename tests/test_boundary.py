@@ -60,7 +60,17 @@ def S(**kw):
     (dict(), 0),
     (dict(T=-1), 1), (dict(T=(1 << 24) + 1), 1), (dict(n_experts=1), 1), (dict(top_k=0), 1),
     (dict(d_model=0), 1), (dict(capacity=-2), 1), (dict(act_dtype=7), 1), (dict(w_dtype=9), 1),
-    (dict(top_k=3), 2), (dict(n_experts=65), 2), (dict(d_model=100), 2), (dict(d_ff=4000), 2),
+    (dict(d_model=100), 2), (dict(d_ff=4000), 2),
+    # general top-k, many experts, a shared expert
+    (dict(top_k=1), 0), (dict(top_k=3), 0), (dict(n_experts=256, top_k=8), 0),
+    (dict(n_experts=256, top_k=8, n_shared=1), 0), (dict(n_experts=65), 0),
+    (dict(n_experts=257), 2), (dict(n_experts=16, top_k=9), 2), (dict(top_k=9), 1),
+    (dict(n_shared=2), 2), (dict(n_shared=-1), 1),
+    (dict(act_dtype="f32", w_dtype="f32", n_experts=64, top_k=5), 0),
+    (dict(act_dtype="f32", w_dtype="f32", n_experts=65), 2),
+    (dict(top_k=3, capacity=10, overflow="next_best"), 2), (dict(top_k=3, overflow="next_best"), 0),
+    (dict(w_dtype="mxfp4", T=64, n_shared=1, capacity=8), 0),
+    (dict(w_dtype="mxfp4", T=65, n_shared=1, capacity=8), 2),
     (dict(act_dtype="f32", w_dtype="bf16"), 2), (dict(act_dtype="bf16", w_dtype="f32"), 2),
     (dict(act_dtype="f32", w_dtype="f32"), 0), (dict(capacity=0), 0), (dict(T=0), 0),
     (dict(w_dtype="fp8_e4m3"), 0), (dict(w_dtype="fp8_e4m3", d_model=4160), 2),
@@ -92,6 +102,19 @@ def test_workspace_sizes():
     with pytest.raises(moe.MoEError):
         moe.moe_workspace_bytes(S(T=-5))
     assert _status("moe_workspace_bytes", ctypes.byref(s), 0, None) == 1
+
+
+def test_workspace_covers_every_slot_with_a_shared_expert():
+    # 8192 tokens x (8 routed + 1 shared) slots: x_perm, h (bf16) and y_perm (fp32) rows
+    s = S(T=8192, d_model=4096, d_ff=2048, n_experts=256, top_k=8, n_shared=1)
+    R = 8192 * 9
+    assert moe.moe_workspace_bytes(s) >= R * (4096 * 2 + 2048 * 2 + 4096 * 4)
+    s0 = S(T=8192, d_model=4096, d_ff=2048, n_experts=256, top_k=8)
+    diff = moe.moe_workspace_bytes(s) - moe.moe_workspace_bytes(s0)
+    assert diff >= 8192 * (4096 * 2 + 2048 * 2 + 4096 * 4)
+    # the shared expert takes every token: > 64 rows per expert means the tiled bf16 path
+    assert moe.moe_workspace_bytes(S(T=100, capacity=8, n_shared=1), moe.MOE_CALL_DOWN) > 0
+    assert moe.moe_workspace_bytes(S(T=100, capacity=8), moe.MOE_CALL_DOWN) == 0
 
 
 def test_down_workspace_size_and_requirement():
@@ -153,7 +176,7 @@ def test_calls_reject_null_and_misaligned_pointers_without_device_work():
 
 
 def test_unsupported_shapes_rejected_by_every_call():
-    bad = ctypes.byref(S(top_k=4))
+    bad = ctypes.byref(S(n_experts=300, top_k=4))
     dummy = 1 << 20
     assert _status("moe_route_topk", bad, dummy, dummy, None, dummy, dummy, None, None, None) == 2
     assert _status("moe_combine", bad, dummy, dummy, dummy, dummy, None) == 2

@@ -13,7 +13,7 @@ import oracle
 import sparse_mixture_experts_topk_amd as moe
 from sparse_mixture_experts_topk_amd import runner, synthetic
 from parity import (adjusted_oracle, assert_close, cached_inputs, check_next, check_permutation,
-                    check_routing, rel_errors, sample_tokens, to_np, tol_key)
+                    check_routing, rel_errors, sample_tokens, to_np, token_of_slot, tol_key)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,12 +42,13 @@ def mid_cfg(name, **kw):
 def run_staged_and_check(cfg, inputs=None, tokens=None, check_h=True):
     inputs = inputs if inputs is not None else synthetic.make_inputs(cfg)
     say(f"staged {cfg.name} T={cfg.T} d={cfg.d_model} F={cfg.d_ff} E={cfg.n_experts} "
-        f"cap={cfg.capacity} overflow={cfg.overflow} {cfg.act_dtype}/{cfg.w_dtype}")
+        f"k={cfg.top_k} shared={cfg.n_shared} cap={cfg.capacity} overflow={cfg.overflow} "
+        f"{cfg.act_dtype}/{cfg.w_dtype}")
     di = runner.DeviceInputs.from_host(inputs)
     st = runner.staged(di)
     torch.cuda.synchronize()
     gpu_ids = to_np(st["topk_ids"])
-    marks = to_np(st["drop_mask"]).reshape(-1, 2)
+    marks = to_np(st["drop_mask"]).reshape(-1, cfg.top_k)
     fallback = cfg.capacity >= 0 and cfg.overflow == "next_best"
     gpu_next = to_np(st["next_ids"]) if fallback else None
     gpu_keep = (marks == 0) if fallback else ~marks.astype(bool)
@@ -60,16 +61,16 @@ def run_staged_and_check(cfg, inputs=None, tokens=None, check_h=True):
     check_next(base, to_np(st["next_ids"]))
     check_permutation(res, st)
     n = int(res.perm.offsets[-1])
-    rows = np.arange(n) if tokens is None else np.flatnonzero(
-        np.isin(res.perm.perm_src // 2, np.asarray(tokens)))
+    row_tok = token_of_slot(res.perm.perm_src, cfg.T, cfg.top_k)
+    rows = np.arange(n) if tokens is None else np.flatnonzero(np.isin(row_tok, np.asarray(tokens)))
     # x_perm is a copy of the token rows (bit-exact)
     if cfg.w_dtype != "fp8_e4m3":
         xs = st["x_perm"][torch.from_numpy(rows).cuda()].cpu()
-        src = inputs.x[torch.from_numpy(res.perm.perm_src[rows] // 2)]
+        src = inputs.x[torch.from_numpy(row_tok[rows])]
         assert torch.equal(xs, src), "x_perm is not an exact copy of x"
     else:
         # fp8: x_perm holds block-quantised codes; they must equal the oracle's exactly
-        codes, ex, _ = oracle.fp8.block_quantize(oracle.to_f64(inputs.x)[res.perm.perm_src[rows] // 2])
+        codes, ex, _ = oracle.fp8.block_quantize(oracle.to_f64(inputs.x)[row_tok[rows]])
         idx = torch.from_numpy(rows).cuda()
         assert np.array_equal(to_np(st["x_perm"][idx]), codes), "fp8 x codes differ"
         assert np.array_equal(to_np(st["x_perm_scale"][idx]).astype(np.int64) - 127, ex), "x scales differ"
@@ -437,4 +438,170 @@ def test_longctx_fp8_config_sampled():
     inp = cached_inputs("longctx_fp8")
     base = oracle.forward(inp, tokens=[])
     toks = sample_tokens(base, n_random=16)
+    run_staged_and_check(cfg, inputs=inp, tokens=toks, check_h=True)
+
+
+# ------------------------------------- general top-k, many experts, shared ---
+
+def fg_cfg(name, **kw):
+    base = dict(name=name, T=300, d_model=512, d_ff=256, n_experts=64, top_k=8, n_shared=1,
+                act_dtype="bf16", w_dtype="bf16", x_std=1.0, wg_std=512 ** -0.5, w13_std=0.05,
+                w2_std=0.05, seed=41)
+    base.update(kw)
+    return synthetic.MoEConfig(**base)
+
+
+@pytest.mark.parametrize("E,k", [(256, 8), (100, 5), (64, 1), (17, 7), (8, 8), (129, 2), (33, 3)])
+def test_route_general_topk(E, k):
+    cfg = synthetic.MoEConfig(name=f"route_E{E}_k{k}", T=333, d_model=256, d_ff=64, n_experts=E,
+                              top_k=k, wg_std=256 ** -0.5, seed=42)
+    inp = synthetic.make_inputs(cfg, with_weights=False)
+    say(f"route E={E} k={k} T=333 d=256 bf16 (+ ranks k+1, k+2)")
+    shape = moe.shape_of(cfg)
+    ids = torch.empty(cfg.T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(cfg.T, k, dtype=torch.float32, device="cuda")
+    lg = torch.empty(cfg.T, E, dtype=torch.float32, device="cuda")
+    nx = torch.empty(cfg.T, 2, dtype=torch.int32, device="cuda")
+    moe.moe_route_topk(shape, inp.x.cuda(), inp.w_gate.cuda(), None, ids, w, lg, nx)
+    torch.cuda.synchronize()
+    res = oracle.forward(inp, tokens=[])
+    check_routing(res, to_np(ids), to_np(w), to_np(lg), 3e-4)
+    check_next(res, to_np(nx))
+    if k == 1:
+        assert np.all(to_np(w) == 1.0)
+
+
+@pytest.mark.parametrize("E,k", [(64, 5), (40, 1), (3, 3)])
+def test_route_general_topk_fp32(E, k):
+    cfg = synthetic.MoEConfig(name=f"route32_E{E}_k{k}", T=257, d_model=128, d_ff=64, n_experts=E,
+                              top_k=k, act_dtype="f32", w_dtype="f32", wg_std=128 ** -0.5, seed=43)
+    inp = synthetic.make_inputs(cfg, with_weights=False)
+    say(f"route fp32 E={E} k={k} T=257 d=128")
+    shape = moe.shape_of(cfg)
+    ids = torch.empty(cfg.T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(cfg.T, k, dtype=torch.float32, device="cuda")
+    lg = torch.empty(cfg.T, E, dtype=torch.float32, device="cuda")
+    nx = torch.empty(cfg.T, 2, dtype=torch.int32, device="cuda")
+    moe.moe_route_topk(shape, inp.x.cuda(), inp.w_gate.cuda(), None, ids, w, lg, nx)
+    torch.cuda.synchronize()
+    res = oracle.forward(inp, tokens=[])
+    check_routing(res, to_np(ids), to_np(w), to_np(lg), 1e-5)
+    check_next(res, to_np(nx))
+
+
+def test_route_general_topk_ties():
+    """Duplicated router rows give exactly equal logits: the lower index always ranks first."""
+    say("route E=256 k=8 with duplicated router rows (exact ties)")
+    cfg = synthetic.MoEConfig(name="ties_k8", T=200, d_model=128, d_ff=64, n_experts=256, top_k=8,
+                              wg_std=128 ** -0.5, seed=44)
+    inp = synthetic.make_inputs(cfg, with_weights=False)
+    wg = inp.w_gate.clone()
+    for e in (40, 77, 200, 255):
+        wg[e] = wg[13]
+    inp.w_gate = wg
+    ids = torch.empty(cfg.T, 8, dtype=torch.int32, device="cuda")
+    w = torch.empty(cfg.T, 8, dtype=torch.float32, device="cuda")
+    moe.moe_route_topk(moe.shape_of(cfg), inp.x.cuda(), wg.cuda(), None, ids, w, None)
+    torch.cuda.synchronize()
+    g = to_np(ids)
+    res = oracle.forward(inp, tokens=[])
+    assert np.array_equal(g, res.routing.ids)
+    # wherever several of the tied experts are picked they appear consecutively, 13 first
+    for row in g:
+        tied = [e for e in row if e in (13, 40, 77, 200, 255)]
+        assert tied == sorted(tied)
+    # all rows equal: experts 0..7 with weights 1/8
+    wg[:] = wg[0]
+    moe.moe_route_topk(moe.shape_of(cfg), inp.x.cuda(), wg.cuda(), None, ids, w, None)
+    torch.cuda.synchronize()
+    assert np.all(to_np(ids) == np.arange(8)) and np.all(to_np(w) == np.float32(0.125))
+
+
+def test_finegrained_mid_prefill_path():
+    # 64 experts x ~37 rows and a 300-row shared expert: the tiled bf16 path (> 64 rows)
+    run_staged_and_check(fg_cfg("fg_mid"))
+
+
+def test_finegrained_256_experts_prefill_path():
+    # 257 expert groups in the tiled kernel's LDS offset table
+    st, res, _ = run_staged_and_check(fg_cfg("fg_e256", T=500, d_model=256, n_experts=256, seed=45))
+    assert to_np(st["expert_counts"])[256] == 500 and np.count_nonzero(res.perm.counts[:256]) > 200
+
+
+def test_finegrained_decode_path():
+    run_staged_and_check(fg_cfg("fg_decode", T=40, n_experts=128, top_k=6, seed=46))
+    run_staged_and_check(fg_cfg("fg_t1", T=1, n_experts=256, seed=47))
+
+
+def test_general_topk_without_shared_and_edge_k():
+    run_staged_and_check(fg_cfg("fg_k1", T=200, n_experts=16, top_k=1, n_shared=0, seed=48))
+    run_staged_and_check(fg_cfg("fg_kE", T=120, n_experts=8, top_k=8, n_shared=0, seed=49))
+    run_staged_and_check(fg_cfg("fg_e2s", T=150, n_experts=2, top_k=2, n_shared=1, seed=50))
+
+
+def test_general_topk_capacity_with_shared():
+    T = 600
+    # capacity below the mean load (600 * 3 / 16 = 112.5) so that every expert drops
+    cfg = fg_cfg("fg_cap", T=T, n_experts=16, top_k=3, capacity=100, seed=51)
+    st, res, _ = run_staged_and_check(cfg)
+    assert (~res.keep).sum() > 0 and res.perm.counts[16] == T
+    # capacity 0: only the shared expert contributes
+    st, res, _ = run_staged_and_check(fg_cfg("fg_cap0", T=100, n_experts=16, top_k=4, capacity=0,
+                                             seed=52))
+    assert to_np(st["drop_mask"]).all() and to_np(st["expert_counts"]).tolist() == [0] * 16 + [100]
+
+
+def test_general_topk_fp32_fp8_mxfp4():
+    run_staged_and_check(fg_cfg("fg_f32", T=96, d_model=128, d_ff=128, n_experts=32, top_k=4,
+                                act_dtype="f32", w_dtype="f32", wg_std=128 ** -0.5, seed=53))
+    run_staged_and_check(fg_cfg("fg_fp8", T=300, n_experts=32, top_k=4, d_ff=384,
+                                w_dtype="fp8_e4m3", seed=54))
+    run_staged_and_check(fg_cfg("fg_mx4", T=16, n_experts=64, top_k=8, d_ff=512, w_dtype="mxfp4",
+                                seed=55))
+
+
+def test_general_topk_forward_matches_staged():
+    for cfg in (fg_cfg("fg_fwd", T=260, n_experts=64, top_k=8, capacity=40, seed=56),
+                fg_cfg("fg_fwd_dec", T=24, n_experts=256, top_k=8, seed=57)):
+        inp = synthetic.make_inputs(cfg)
+        say(f"moe_forward vs staged: {cfg.name}")
+        di = runner.DeviceInputs.from_host(inp)
+        st = runner.staged(di)
+        b = runner.forward(di)
+        b2 = runner.forward(di)
+        torch.cuda.synchronize()
+        assert torch.equal(st["y"], b.y) and torch.equal(b.y, b2.y)
+        assert torch.equal(st["topk_ids"], b.topk_ids) and torch.equal(st["expert_counts"], b.expert_counts)
+
+
+def test_combine_general_topk_isolated():
+    cfg = fg_cfg("fg_combine", T=200, n_experts=32, top_k=5, capacity=30, seed=58)
+    inp = synthetic.make_inputs(cfg)
+    say("combine in isolation (k=5, shared, capacity)")
+    st = runner.staged(runner.DeviceInputs.from_host(inp))
+    torch.cuda.synchronize()
+    yp = to_np(st["y_perm"])
+    s2r = to_np(st["slot_to_row"])
+    g = to_np(st["topk_weights"]).astype(np.float64)
+    T, k = cfg.T, cfg.top_k
+    ref = np.zeros((T, cfg.d_model))
+    for s_ in range(k):
+        rr = s2r[:T * k].reshape(T, k)[:, s_]
+        ok = rr >= 0
+        ref[ok] += g[ok, s_, None] * yp[rr[ok]]
+    ref += yp[s2r[T * k:]]
+    got = to_np(st["y"].float())
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+
+
+def test_finegrained_decode_config_full():
+    run_staged_and_check(synthetic.CONFIGS["finegrained_decode_bf16"],
+                         inputs=cached_inputs("finegrained_decode_bf16"))
+
+
+def test_finegrained_prefill_config_sampled():
+    cfg = synthetic.CONFIGS["finegrained_prefill_bf16"]
+    inp = cached_inputs("finegrained_prefill_bf16")
+    base = oracle.forward(inp, tokens=[])
+    toks = sample_tokens(base, n_random=12, edge_groups=12)
     run_staged_and_check(cfg, inputs=inp, tokens=toks, check_h=True)
