@@ -167,7 +167,8 @@ def main():
         d = copies[i % len(copies)]
         fallback = cfg.capacity >= 0 and cfg.overflow == "next_best"
         moe.moe_route_topk(shape, d.x, d.w_gate, d.router_bias, st["topk_ids"],
-                           st["topk_weights"], None, st["next_ids"] if fallback else None, stream)
+                           st["topk_weights"], None, st["next_ids"] if fallback else None,
+                           st["route_ws"], stream)
         moe.moe_permute(shape, st["topk_ids"], st["topk_weights"],
                         st["next_ids"] if fallback else None, d.x, st["expert_counts"],
                         st["expert_offsets"], st["perm_src"], st["slot_to_row"],

@@ -129,7 +129,7 @@ typedef struct {
 
 /* Which call a workspace is sized for. */
 typedef enum { MOE_CALL_PERMUTE = 0, MOE_CALL_GATE_UP = 1, MOE_CALL_DOWN = 2,
-               MOE_CALL_FORWARD = 3 } moe_call_t;
+               MOE_CALL_FORWARD = 3, MOE_CALL_ROUTE = 4 } moe_call_t;
 
 /* Human-readable name of a status.  Never NULL. */
 const char* moe_status_string(moe_status_t status);
@@ -160,10 +160,17 @@ moe_status_t moe_workspace_bytes(const moe_shape_t* shape, moe_call_t call, size
  *                each token (same order: logit descending, ties -> lower index),
  *                -1 where n_experts is too small.  moe_permute needs them for
  *                MOE_OVERFLOW_NEXT_BEST.
- * Logits accumulate in fp32.  No workspace. */
+ * Logits accumulate in fp32.
+ * Workspace: moe_workspace_bytes(MOE_CALL_ROUTE) bytes, 16-byte aligned: T*E*4
+ * (an fp32 logit buffer) for bf16 shapes with more than 64 experts, whose
+ * router runs as a logits kernel over a token x expert grid followed by a
+ * selection kernel; 0 otherwise.  When `logits` is given it serves as that
+ * buffer and the workspace may be NULL.  Too small or NULL when needed ->
+ * MOE_ERR_WORKSPACE. */
 moe_status_t moe_route_topk(const moe_shape_t* shape, const void* x, const void* w_gate,
                             const float* router_bias, int32_t* topk_ids, float* topk_weights,
-                            float* logits, int32_t* next_ids, void* stream);
+                            float* logits, int32_t* next_ids, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* Capacity selection (when shape->capacity >= 0) and grouping of tokens by expert.
  * Pages: "How Mixtral 8x7B uses mixture of experts", sections "Routing without

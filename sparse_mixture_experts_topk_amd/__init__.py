@@ -15,14 +15,14 @@ import torch
 
 from . import _lib
 from ._lib import (MOE_BF16, MOE_CALL_DOWN, MOE_CALL_FORWARD, MOE_CALL_GATE_UP,
-                   MOE_CALL_PERMUTE, MOE_DROPLESS, MOE_F32, MOE_FP8_E4M3, MOE_MXFP4, MOE_OVERFLOW_DROP,
+                   MOE_CALL_PERMUTE, MOE_CALL_ROUTE, MOE_DROPLESS, MOE_F32, MOE_FP8_E4M3, MOE_MXFP4, MOE_OVERFLOW_DROP,
                    MOE_OVERFLOW_NEXT_BEST, MoeShape)
 
 __all__ = ["MoEError", "MoeShape", "make_shape", "moe_status_string", "moe_version",
            "moe_workspace_bytes", "moe_route_topk", "moe_permute", "moe_expert_gemm_gate_up",
            "moe_expert_gemm_down", "moe_combine", "moe_forward", "MOE_F32", "MOE_BF16",
            "MOE_FP8_E4M3", "MOE_MXFP4", "MOE_DROPLESS", "MOE_CALL_PERMUTE", "MOE_CALL_GATE_UP",
-           "MOE_CALL_DOWN", "MOE_CALL_FORWARD", "MOE_OVERFLOW_DROP", "MOE_OVERFLOW_NEXT_BEST"]
+           "MOE_CALL_DOWN", "MOE_CALL_FORWARD", "MOE_CALL_ROUTE", "MOE_OVERFLOW_DROP", "MOE_OVERFLOW_NEXT_BEST"]
 
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3, "mxfp4": MOE_MXFP4}
 _OVF = {"drop": MOE_OVERFLOW_DROP, "next_best": MOE_OVERFLOW_NEXT_BEST}
@@ -90,10 +90,11 @@ def moe_workspace_bytes(shape: MoeShape, call: int = MOE_CALL_FORWARD) -> int:
 
 
 def moe_route_topk(shape, x, w_gate, router_bias, topk_ids, topk_weights, logits=None,
-                   next_ids=None, stream=None):
+                   next_ids=None, workspace=None, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("moe_route_topk", _lib.load().moe_route_topk(
         ctypes.byref(shape), _p(x), _p(w_gate), _p(router_bias), _p(topk_ids), _p(topk_weights),
-        _p(logits), _p(next_ids), _stream(stream)))
+        _p(logits), _p(next_ids), _p(workspace), ws_bytes, _stream(stream)))
 
 
 def moe_permute(shape, topk_ids, topk_weights, next_ids, x, expert_counts, expert_offsets,

@@ -10,7 +10,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 MOE_DROPLESS = -1
 MOE_OVERFLOW_DROP, MOE_OVERFLOW_NEXT_BEST = 0, 1
-MOE_CALL_PERMUTE, MOE_CALL_GATE_UP, MOE_CALL_DOWN, MOE_CALL_FORWARD = range(4)
+MOE_CALL_PERMUTE, MOE_CALL_GATE_UP, MOE_CALL_DOWN, MOE_CALL_FORWARD, MOE_CALL_ROUTE = range(5)
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_bytes", "moe_route_topk",
@@ -35,7 +35,7 @@ _SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [I32]),
     "moe_version": (ctypes.c_char_p, []),
     "moe_workspace_bytes": (I32, [SHAPE, I32, ctypes.POINTER(SZ)]),
-    "moe_route_topk": (I32, [SHAPE, P, P, P, P, P, P, P, P]),
+    "moe_route_topk": (I32, [SHAPE, P, P, P, P, P, P, P, P, SZ, P]),
     "moe_permute": (I32, [SHAPE, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
     "moe_expert_gemm_gate_up": (I32, [SHAPE, P, P, P, P, P, P, P, P, P, P, SZ, P]),
     "moe_expert_gemm_down": (I32, [SHAPE, P, P, P, P, P, P, P, SZ, P]),

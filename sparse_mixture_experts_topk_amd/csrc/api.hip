@@ -137,7 +137,7 @@ moe_status_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 // Workspace layout of moe_forward (each region 256-byte aligned).
 struct ForwardLayout {
-  size_t ids, weights, next_ids, counts, offsets, perm_src, slot_to_row, drop, x_perm, x_scale, h,
+  size_t route_logits, ids, weights, next_ids, counts, offsets, perm_src, slot_to_row, drop, x_perm, x_scale, h,
       h_scale, y_perm, down_ws, total;
 };
 
@@ -160,6 +160,7 @@ ForwardLayout forward_layout(const moe_shape_t& s) {
   const size_t eb = perm_elem_bytes(s);
   const bool fp8 = s.w_dtype == MOE_FP8_E4M3;
   size_t o = 0;
+  L.route_logits = o; o += align_up(moe::route_workspace_bytes(s));
   L.ids = o;         o += align_up(A * 4);
   L.weights = o;     o += align_up(A * 4);
   L.next_ids = o;    o += fallback_on(s) ? align_up((size_t)s.T * 2 * 4) : 0;
@@ -207,20 +208,27 @@ moe_status_t moe_workspace_bytes(const moe_shape_t* s, moe_call_t call, size_t* 
     case MOE_CALL_GATE_UP: *bytes = 0; return MOE_OK;
     case MOE_CALL_DOWN: *bytes = down_workspace_bytes(*s); return MOE_OK;
     case MOE_CALL_FORWARD: *bytes = forward_layout(*s).total; return MOE_OK;
+    case MOE_CALL_ROUTE: *bytes = moe::route_workspace_bytes(*s); return MOE_OK;
   }
   return MOE_ERR_INVALID_ARG;
 }
 
 moe_status_t moe_route_topk(const moe_shape_t* s, const void* x, const void* w_gate,
                             const float* router_bias, int32_t* topk_ids, float* topk_weights,
-                            float* logits, int32_t* next_ids, void* stream) {
+                            float* logits, int32_t* next_ids, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   moe_status_t v = validate_shape(s);
   if (v != MOE_OK) return v;
   if (s->T == 0) return MOE_OK;
   if ((v = check_ptrs({x, w_gate, topk_ids, topk_weights}, {router_bias, logits, next_ids})) != MOE_OK)
     return v;
+  const size_t need = moe::route_workspace_bytes(*s);
+  if (need > 0 && logits == nullptr &&
+      (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_route_topk(*s, x, w_gate, router_bias, topk_ids, topk_weights, logits,
-                                         next_ids, static_cast<hipStream_t>(stream)));
+                                         next_ids, need > 0 ? workspace : nullptr,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_ids, const float* topk_weights,
@@ -344,7 +352,8 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_gate
   float* y_perm = at<float>(workspace, L.y_perm);
   int32_t* next = fallback_on(*s) ? at<int32_t>(workspace, L.next_ids) : nullptr;
 
-  hipError_t e = moe::launch_route_topk(*s, x, w_gate, router_bias, ids, gw, logits_out, next, st);
+  hipError_t e = moe::launch_route_topk(*s, x, w_gate, router_bias, ids, gw, logits_out, next,
+                                       at<void>(workspace, L.route_logits), st);
   const uint8_t* drop_in = nullptr;
   if (e == hipSuccess) {
     if (s->capacity >= 0) {

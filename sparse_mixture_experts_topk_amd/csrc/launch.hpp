@@ -14,9 +14,12 @@ namespace moe {
 
 // Router GEMV + top-k + softmax of the kept logits (+ the experts ranked k+1, k+2
 // when next_ids != NULL).
+// bf16 with more than 64 experts: logits to an fp32 [T, E] buffer (`logits`
+// when given, else `workspace` of route_workspace_bytes(s)), then selection.
 hipError_t launch_route_topk(const moe_shape_t& s, const void* x, const void* w_gate,
                              const float* bias, int32_t* ids, float* weights, float* logits,
-                             int32_t* next_ids, hipStream_t st);
+                             int32_t* next_ids, void* workspace, hipStream_t st);
+size_t route_workspace_bytes(const moe_shape_t& s);
 
 // Capacity selection: writes drop_mask[T*k] (0 kept, 1 dropped); with
 // MOE_OVERFLOW_NEXT_BEST a second round re-offers the dropped assignments to
@@ -80,6 +83,8 @@ constexpr int kMaxExpertGroups = kMaxExperts + 1;
 inline int expert_groups(const moe_shape_t& s) { return s.n_experts + s.n_shared; }
 // Slots (assignments) per token, the shared expert's included.
 inline int64_t total_slots(const moe_shape_t& s) { return (int64_t)s.T * (s.top_k + s.n_shared); }
+// The router runs as logits + selection (two kernels) rather than one fused kernel.
+inline bool route_two_pass(const moe_shape_t& s) { return s.act_dtype == MOE_BF16 && s.n_experts > 64; }
 
 // Compute units of the current device (queried once per device).
 int device_cu_count();

@@ -8,7 +8,10 @@
 // k up to 8: the DeepSeek-V3 remark on the "Mixtral 8x7B" interview page
 // (256 routed experts, 8 active per token).
 //
-// Selection, both kernels: k rounds of an arg-max (value descending, index
+// Up to 64 experts the router is one fused kernel (below); more experts
+// (bf16) take two: logits over a token x expert grid, then selection.
+//
+// Selection, every kernel: k rounds of an arg-max (value descending, index
 // ascending) over the experts not yet taken, so slot j holds the j-th largest
 // logit and equal logits go to the lower index; on request two more rounds
 // give the experts ranked k+1 and k+2 (the targets of the overflow fallback).
@@ -177,11 +180,10 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 
 // ---------------------------------------------------------------------------
 // bf16 router on the matrix cores.  A 512-lane workgroup owns 16 tokens; its
-// 8 wavefronts split K (and, for many experts, the expert blocks: EW groups
-// of EB / EW blocks, each over K / (8 / EW)), each accumulating
-// D[expert][token] = W_g . x^T with v_mfma_f32_16x16x32_bf16 (A = 16 router
-// rows, B = 16 token rows, zero rows past E / T), for EB blocks of 16
-// experts.  Partial tiles are summed through LDS in a fixed order;
+// 8 wavefronts split K, each accumulating D[expert][token] = W_g . x^T with
+// v_mfma_f32_16x16x32_bf16 (A = 16 router rows, B = 16 token rows, zero rows
+// past E / T), for EB blocks of 16 experts (E <= 64).  Partial tiles are
+// summed through LDS in a fixed order;
 // wavefront 0 then holds, per lane, token (lane & 15) and experts
 // 16 eb + 4 (lane >> 4) + q.  A selection round takes each lane's best
 // expert not yet taken (a 64-bit mask per lane) and two xor-shuffle merges
@@ -189,45 +191,38 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 // products are exact in fp32 and accumulate in fp32.
 constexpr int kRouteWaves = 8;
 
-template <int EB, int EW>
+template <int EB>
 __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* __restrict__ ids, float* __restrict__ wout,
     float* __restrict__ logits, int32_t* __restrict__ next) {
   static_assert(EB * 4 <= 64, "one bit per expert of a lane in the taken mask");
-  static_assert(EB % EW == 0 && kRouteWaves % EW == 0, "expert groups");
-  constexpr int EBW = EB / EW;                 // expert blocks of one wavefront
-  constexpr int KP = kRouteWaves / EW;         // K parts
-  // EW == 1: wavefront 0 keeps its own part; else every wavefront stores its part
-  constexpr int NPART = EW == 1 ? KP - 1 : KP;
-  __shared__ f32x4_t part[NPART][EB][64];
+  __shared__ f32x4_t part[kRouteWaves - 1][EB][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ew = wave % EW, kp = wave / EW;
   const int tok0 = blockIdx.x * 16;
   const int r = lane & 15, g = lane >> 4;
   const bool tok_ok = tok0 + r < T;
   const uint16_t* px = x + (int64_t)(tok_ok ? tok0 + r : 0) * d + g * 8;
-  const uint16_t* pw[EBW];
-  bool w_ok[EBW];
+  const uint16_t* pw[EB];
+  bool w_ok[EB];
 #pragma unroll
-  for (int i = 0; i < EBW; ++i) {
-    const int eb = ew * EBW + i;
-    w_ok[i] = eb * 16 + r < E;
-    pw[i] = wg + (int64_t)(w_ok[i] ? eb * 16 + r : 0) * d + g * 8;
+  for (int eb = 0; eb < EB; ++eb) {
+    w_ok[eb] = eb * 16 + r < E;
+    pw[eb] = wg + (int64_t)(w_ok[eb] ? eb * 16 + r : 0) * d + g * 8;
   }
   f32x4_t acc[EB];
 #pragma unroll
   for (int eb = 0; eb < EB; ++eb) acc[eb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nblk = d / 32;
-  const int b0 = kp * nblk / KP, b1 = (kp + 1) * nblk / KP;
-  // 16 K blocks of 16-byte loads per lane in flight
-  constexpr int U = EBW >= 16 ? 1 : 16 / EBW;
+  const int b0 = wave * nblk / kRouteWaves, b1 = (wave + 1) * nblk / kRouteWaves;
+  // all of a wavefront's K blocks in flight at once at d = 4096 (16 per wavefront)
+  constexpr int U = 16 / EB;
   const uint4 z = make_uint4(0, 0, 0, 0);
   for (int b = b0; b < b1; b += U) {
     // Unconditional 16-byte loads from clamped (always valid) addresses, then a
     // select: a conditional load would be split into guarded dword loads.
-    uint4 xa[U], wa[U][EBW];
+    uint4 xa[U], wa[U][EB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool in = b + u < b1;
@@ -235,41 +230,28 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
       const uint4 xv = *reinterpret_cast<const uint4*>(px + blk * 32);
       xa[u] = (in && tok_ok) ? xv : z;
 #pragma unroll
-      for (int i = 0; i < EBW; ++i) {
-        const uint4 wv = *reinterpret_cast<const uint4*>(pw[i] + blk * 32);
-        wa[u][i] = (in && w_ok[i]) ? wv : z;
+      for (int eb = 0; eb < EB; ++eb) {
+        const uint4 wv = *reinterpret_cast<const uint4*>(pw[eb] + blk * 32);
+        wa[u][eb] = (in && w_ok[eb]) ? wv : z;
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int i = 0; i < EBW; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][i]), as_bf16x8(xa[u]),
-                                                          acc[i], 0, 0, 0);
+      for (int eb = 0; eb < EB; ++eb)
+        acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][eb]), as_bf16x8(xa[u]),
+                                                           acc[eb], 0, 0, 0);
   }
-  if constexpr (EW == 1) {
-    if (wave > 0) {
+  if (wave > 0) {
 #pragma unroll
-      for (int eb = 0; eb < EB; ++eb) part[wave - 1][eb][lane] = acc[eb];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int w = 0; w < kRouteWaves - 1; ++w)
-#pragma unroll
-      for (int eb = 0; eb < EB; ++eb) acc[eb] += part[w][eb][lane];
-  } else {
-#pragma unroll
-    for (int i = 0; i < EBW; ++i) part[kp][ew * EBW + i][lane] = acc[i];
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int eb = 0; eb < EB; ++eb) {
-      acc[eb] = part[0][eb][lane];
-#pragma unroll
-      for (int w = 1; w < KP; ++w) acc[eb] += part[w][eb][lane];
-    }
+    for (int eb = 0; eb < EB; ++eb) part[wave - 1][eb][lane] = acc[eb];
   }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kRouteWaves - 1; ++w)
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) acc[eb] += part[w][eb][lane];
 
   const int tok = tok0 + r;
 #pragma unroll
@@ -326,11 +308,177 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
   if (g == 0 && tok < T) store_token(v, id, k, tok, ids, wout, next);
 }
 
-template <int EB, int EW>
+// ---------------------------------------------------------------------------
+// Many experts (E > 64, bf16): logits, then selection, in two kernels.
+//
+// route_logits: one workgroup of 4 wavefronts per tile of 16 TM tokens x
+// 16 EN experts; the wavefronts split K and sum their partial tiles through
+// LDS in a fixed order.  The grid spans tokens and experts, so at decode
+// (one token tile) the router matrix is read by E / (16 EN) workgroups in
+// parallel instead of one.  Logits (+ bias) go to an fp32 [T, E] buffer.
+// route_select: one wavefront per token; lane l holds experts l + 64 j; a
+// selection round is a local arg-max then a 6-step butterfly over the lanes.
+constexpr int kLogitWaves = 4;
+
+template <int TM, int EN>
+__global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias,
+    int T, int d, int E, float* __restrict__ logits) {
+  __shared__ f32x4_t part[kLogitWaves - 1][TM * EN][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok0 = blockIdx.x * 16 * TM, e0 = blockIdx.y * 16 * EN;
+  const int r = lane & 15, g = lane >> 4;
+  const uint16_t* px[TM];
+  const uint16_t* pw[EN];
+  bool x_ok[TM], w_ok[EN];
+#pragma unroll
+  for (int m = 0; m < TM; ++m) {
+    x_ok[m] = tok0 + 16 * m + r < T;
+    px[m] = x + (int64_t)(x_ok[m] ? tok0 + 16 * m + r : 0) * d + g * 8;
+  }
+#pragma unroll
+  for (int n = 0; n < EN; ++n) {
+    w_ok[n] = e0 + 16 * n + r < E;
+    pw[n] = wg + (int64_t)(w_ok[n] ? e0 + 16 * n + r : 0) * d + g * 8;
+  }
+  f32x4_t acc[TM][EN];
+#pragma unroll
+  for (int m = 0; m < TM; ++m)
+#pragma unroll
+    for (int n = 0; n < EN; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nblk = d / 32;
+  const int b0 = wave * nblk / kLogitWaves, b1 = (wave + 1) * nblk / kLogitWaves;
+  constexpr int U = 16 / (TM + EN) > 0 ? 16 / (TM + EN) : 1;   // 16-byte loads in flight per lane
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  for (int b = b0; b < b1; b += U) {
+    uint4 xa[U][TM], wa[U][EN];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = b + u < b1;
+      const int blk = in ? b + u : b0;
+#pragma unroll
+      for (int m = 0; m < TM; ++m) {
+        const uint4 v = *reinterpret_cast<const uint4*>(px[m] + blk * 32);
+        xa[u][m] = (in && x_ok[m]) ? v : z;
+      }
+#pragma unroll
+      for (int n = 0; n < EN; ++n) {
+        const uint4 v = *reinterpret_cast<const uint4*>(pw[n] + blk * 32);
+        wa[u][n] = (in && w_ok[n]) ? v : z;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int m = 0; m < TM; ++m)
+#pragma unroll
+        for (int n = 0; n < EN; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][n]), as_bf16x8(xa[u][m]),
+                                                               acc[m][n], 0, 0, 0);
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int m = 0; m < TM; ++m)
+#pragma unroll
+      for (int n = 0; n < EN; ++n) part[wave - 1][m * EN + n][lane] = acc[m][n];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int m = 0; m < TM; ++m) {
+    const int tok = tok0 + 16 * m + r;
+#pragma unroll
+    for (int n = 0; n < EN; ++n) {
+#pragma unroll
+      for (int w = 0; w < kLogitWaves - 1; ++w) acc[m][n] += part[w][m * EN + n][lane];
+      // lane (r, g) holds token r and experts 4 g + q of the 16 x 16 tile
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = e0 + 16 * n + 4 * g + q;
+        if (tok < T && e < E) logits[(int64_t)tok * E + e] = acc[m][n][q] + (bias != nullptr ? bias[e] : 0.f);
+      }
+    }
+  }
+}
+
+constexpr int kSelectTokensPerBlock = 4;
+
+__global__ __launch_bounds__(kSelectTokensPerBlock * 64) void route_select_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ wout, int32_t* __restrict__ next) {
+  constexpr int J = kMaxExperts / kWave;       // logits per lane
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * kSelectTokensPerBlock + (threadIdx.x >> 6);
+  if (tok >= T) return;   // whole wavefront leaves; the kernel has no barrier
+  float l[J];
+  uint32_t taken = 0;      // bit j: expert lane + 64 j is out (taken or past E)
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = lane + kWave * j;
+    l[j] = e < E ? logits[(int64_t)tok * E + e] : -INFINITY;
+    if (e >= E) taken |= 1u << j;
+  }
+  const int rounds = k + (next != nullptr ? 2 : 0);
+  float v[kMaxRounds];
+  int id[kMaxRounds];
+#pragma unroll
+  for (int jr = 0; jr < kMaxRounds; ++jr) {
+    v[jr] = -INFINITY;
+    id[jr] = 0;
+    if (jr < rounds) {
+      float bv = -INFINITY;
+      int bi = 1 << 30;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {          // increasing expert index within the lane
+        const bool cand = ((taken >> j) & 1u) == 0;
+        const float lv = cand ? l[j] : -INFINITY;
+        const int li = cand ? lane + kWave * j : (1 << 30);
+        const bool win = better(lv, li, bv, bi);
+        bv = win ? lv : bv;
+        bi = win ? li : bi;
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      if (bi < E && (bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+      v[jr] = bv;
+      id[jr] = bi;
+    }
+  }
+  if (lane == 0) store_token(v, id, k, tok, ids, wout, next);
+}
+
+template <int TM, int EN>
+hipError_t launch_logits(const moe_shape_t& s, const void* x, const void* wg, const float* bias,
+                         float* logits, hipStream_t st) {
+  const dim3 grid((unsigned)((s.T + 16 * TM - 1) / (16 * TM)), (unsigned)((s.n_experts + 16 * EN - 1) / (16 * EN)));
+  hipLaunchKernelGGL((route_logits_kernel<TM, EN>), grid, dim3(kLogitWaves * 64), 0, st,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), bias, s.T,
+                     s.d_model, s.n_experts, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_two_pass(const moe_shape_t& s, const void* x, const void* wg, const float* bias,
+                           int32_t* ids, float* w, float* logits, int32_t* next, hipStream_t st) {
+  // one token tile: spread the router matrix over as many workgroups as possible
+  hipError_t e = s.T <= 16 ? launch_logits<1, 1>(s, x, wg, bias, logits, st)
+                           : launch_logits<4, 4>(s, x, wg, bias, logits, st);
+  if (e != hipSuccess) return e;
+  const int blocks = (s.T + kSelectTokensPerBlock - 1) / kSelectTokensPerBlock;
+  hipLaunchKernelGGL(route_select_kernel, dim3(blocks), dim3(kSelectTokensPerBlock * 64), 0, st,
+                     logits, s.T, s.n_experts, s.top_k, ids, w, next);
+  return hipGetLastError();
+}
+
+template <int EB>
 hipError_t launch_mfma(const moe_shape_t& s, const void* x, const void* wg, const float* bias,
                        int32_t* ids, float* w, float* logits, int32_t* next, hipStream_t st) {
   const int blocks = (s.T + 15) / 16;
-  hipLaunchKernelGGL((route_topk_mfma_kernel<EB, EW>), dim3(blocks), dim3(kRouteWaves * 64), 0, st,
+  hipLaunchKernelGGL((route_topk_mfma_kernel<EB>), dim3(blocks), dim3(kRouteWaves * 64), 0, st,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), bias, s.T,
                      s.d_model, s.n_experts, s.top_k, ids, w, logits, next);
   return hipGetLastError();
@@ -358,15 +506,20 @@ hipError_t launch_dtype(const moe_shape_t& s, const void* x, const void* wg, con
 
 }  // namespace
 
+size_t route_workspace_bytes(const moe_shape_t& s) {
+  return route_two_pass(s) ? (size_t)s.T * s.n_experts * 4 : 0;
+}
+
 hipError_t launch_route_topk(const moe_shape_t& s, const void* x, const void* w_gate,
                              const float* bias, int32_t* ids, float* weights, float* logits,
-                             int32_t* next_ids, hipStream_t st) {
+                             int32_t* next_ids, void* workspace, hipStream_t st) {
+  if (route_two_pass(s))
+    return launch_two_pass(s, x, w_gate, bias, ids, weights,
+                           logits != nullptr ? logits : static_cast<float*>(workspace), next_ids, st);
   if (s.act_dtype == MOE_BF16) {
-    if (s.n_experts <= 16) return launch_mfma<1, 1>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
-    if (s.n_experts <= 32) return launch_mfma<2, 1>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
-    if (s.n_experts <= 64) return launch_mfma<4, 1>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
-    if (s.n_experts <= 128) return launch_mfma<8, 2>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
-    return launch_mfma<16, 4>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
+    if (s.n_experts <= 16) return launch_mfma<1>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
+    if (s.n_experts <= 32) return launch_mfma<2>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
+    return launch_mfma<4>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
   }
   return launch_dtype<false>(s, x, w_gate, bias, ids, weights, logits, next_ids, st);
 }

@@ -13,7 +13,7 @@ import torch
 
 from . import (moe_combine, moe_expert_gemm_down, moe_expert_gemm_gate_up, moe_forward,
                moe_permute, moe_route_topk, moe_workspace_bytes, shape_of, MOE_CALL_DOWN,
-               MOE_CALL_FORWARD)
+               MOE_CALL_FORWARD, MOE_CALL_ROUTE)
 
 
 def _dev(t: Optional[torch.Tensor], device) -> Optional[torch.Tensor]:
@@ -107,8 +107,10 @@ def staged(di: DeviceInputs, stream=None) -> dict:
     o["topk_weights"] = torch.empty(T, k, dtype=torch.float32, device=dev)
     o["logits"] = torch.empty(T, E, dtype=torch.float32, device=dev)
     o["next_ids"] = torch.empty(T, 2, dtype=torch.int32, device=dev)
+    route_ws = moe_workspace_bytes(shape, MOE_CALL_ROUTE)   # used when no logits buffer is passed
+    o["route_ws"] = torch.empty(route_ws, dtype=torch.uint8, device=dev) if route_ws else None
     moe_route_topk(shape, di.x, di.w_gate, di.router_bias, o["topk_ids"], o["topk_weights"],
-                   o["logits"], o["next_ids"], stream)
+                   o["logits"], o["next_ids"], None, stream)
     o["expert_counts"] = torch.empty(E + S, dtype=torch.int32, device=dev)
     o["expert_offsets"] = torch.empty(E + S + 1, dtype=torch.int32, device=dev)
     o["perm_src"] = torch.full((R,), -7, dtype=torch.int32, device=dev)

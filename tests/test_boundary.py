@@ -117,6 +117,22 @@ def test_workspace_covers_every_slot_with_a_shared_expert():
     assert moe.moe_workspace_bytes(S(T=100, capacity=8), moe.MOE_CALL_DOWN) == 0
 
 
+def test_route_workspace_for_many_experts():
+    # bf16 with more than 64 experts: an fp32 [T, E] logit buffer unless `logits` is passed
+    s = S(T=16, n_experts=256, top_k=8, n_shared=1)
+    assert moe.moe_workspace_bytes(s, moe.MOE_CALL_ROUTE) == 16 * 256 * 4
+    assert moe.moe_workspace_bytes(S(T=16), moe.MOE_CALL_ROUTE) == 0
+    assert moe.moe_workspace_bytes(S(T=16, n_experts=64), moe.MOE_CALL_ROUTE) == 0
+    assert moe.moe_workspace_bytes(s) >= moe.moe_workspace_bytes(S(T=16, n_experts=256, top_k=8)) + 16 * 4096 * 2
+    dummy = 1 << 20
+    b = ctypes.byref(s)
+    assert _status("moe_route_topk", b, dummy, dummy, None, dummy, dummy, None, None, None, 0, None) == 3
+    assert _status("moe_route_topk", b, dummy, dummy, None, dummy, dummy, None, None, dummy,
+                   16 * 256 * 4 - 1, None) == 3
+    assert _status("moe_route_topk", b, dummy, dummy, None, dummy, dummy, None, None, dummy + 8,
+                   16 * 256 * 4, None) == 3
+
+
 def test_down_workspace_size_and_requirement():
     # many rows per expert (bf16): fp32 partial tiles for the split tail work
     big = S(T=8192)
@@ -143,9 +159,9 @@ def test_down_workspace_size_and_requirement():
 def test_calls_reject_null_and_misaligned_pointers_without_device_work():
     s = ctypes.byref(S())
     dummy = 1 << 20  # never dereferenced: validation fails first
-    assert _status("moe_route_topk", s, None, dummy, None, dummy, dummy, None, None, None) == 1
-    assert _status("moe_route_topk", s, dummy + 2, dummy, None, dummy, dummy, None, None, None) == 1
-    assert _status("moe_route_topk", s, dummy, dummy, None, dummy, dummy, None, dummy + 4, None) == 1
+    assert _status("moe_route_topk", s, None, dummy, None, dummy, dummy, None, None, None, 0, None) == 1
+    assert _status("moe_route_topk", s, dummy + 2, dummy, None, dummy, dummy, None, None, None, 0, None) == 1
+    assert _status("moe_route_topk", s, dummy, dummy, None, dummy, dummy, None, dummy + 4, None, 0, None) == 1
     assert _status("moe_combine", s, None, dummy, dummy, dummy, None) == 1
     assert _status("moe_expert_gemm_gate_up", s, dummy, None, None, dummy, dummy, None, None,
                    dummy, None, None, 0, None) == 1
@@ -178,14 +194,14 @@ def test_calls_reject_null_and_misaligned_pointers_without_device_work():
 def test_unsupported_shapes_rejected_by_every_call():
     bad = ctypes.byref(S(n_experts=300, top_k=4))
     dummy = 1 << 20
-    assert _status("moe_route_topk", bad, dummy, dummy, None, dummy, dummy, None, None, None) == 2
+    assert _status("moe_route_topk", bad, dummy, dummy, None, dummy, dummy, None, None, None, 0, None) == 2
     assert _status("moe_combine", bad, dummy, dummy, dummy, dummy, None) == 2
 
 
 def test_empty_input_is_a_no_op():
     s = ctypes.byref(S(T=0))
     # all pointers NULL: T == 0 returns before any pointer check or launch
-    assert _status("moe_route_topk", s, None, None, None, None, None, None, None, None) == 0
+    assert _status("moe_route_topk", s, None, None, None, None, None, None, None, None, 0, None) == 0
     assert _status("moe_forward", s, *([None] * 15), None, 0, None) == 0
     assert _status("moe_combine", s, None, None, None, None, None) == 0
 

@@ -501,7 +501,9 @@ def test_route_general_topk_ties():
     inp.w_gate = wg
     ids = torch.empty(cfg.T, 8, dtype=torch.int32, device="cuda")
     w = torch.empty(cfg.T, 8, dtype=torch.float32, device="cuda")
-    moe.moe_route_topk(moe.shape_of(cfg), inp.x.cuda(), wg.cuda(), None, ids, w, None)
+    ws = torch.empty(moe.moe_workspace_bytes(moe.shape_of(cfg), moe.MOE_CALL_ROUTE), dtype=torch.uint8,
+                     device="cuda")
+    moe.moe_route_topk(moe.shape_of(cfg), inp.x.cuda(), wg.cuda(), None, ids, w, None, None, ws)
     torch.cuda.synchronize()
     g = to_np(ids)
     res = oracle.forward(inp, tokens=[])
@@ -512,7 +514,7 @@ def test_route_general_topk_ties():
         assert tied == sorted(tied)
     # all rows equal: experts 0..7 with weights 1/8
     wg[:] = wg[0]
-    moe.moe_route_topk(moe.shape_of(cfg), inp.x.cuda(), wg.cuda(), None, ids, w, None)
+    moe.moe_route_topk(moe.shape_of(cfg), inp.x.cuda(), wg.cuda(), None, ids, w, None, None, ws)
     torch.cuda.synchronize()
     assert np.all(to_np(ids) == np.arange(8)) and np.all(to_np(w) == np.float32(0.125))
 
@@ -570,7 +572,10 @@ def test_general_topk_forward_matches_staged():
         b = runner.forward(di)
         b2 = runner.forward(di)
         torch.cuda.synchronize()
-        assert torch.equal(st["y"], b.y) and torch.equal(b.y, b2.y)
+        # no optional outputs: the router's logit buffer then lives in the workspace
+        b3 = runner.forward(di, runner.alloc_forward(cfg, with_outputs=False))
+        torch.cuda.synchronize()
+        assert torch.equal(st["y"], b.y) and torch.equal(b.y, b2.y) and torch.equal(b.y, b3.y)
         assert torch.equal(st["topk_ids"], b.topk_ids) and torch.equal(st["expert_counts"], b.expert_counts)
 
 
