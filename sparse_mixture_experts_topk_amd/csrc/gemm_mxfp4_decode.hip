@@ -15,10 +15,13 @@
 // exactly (every E2M1 value times 2^e is a bf16 value), so the matrix cores
 // (v_mfma_f32_16x16x32_bf16) see the exact dequantised weights.
 //
-// A wavefront owns RB blocks of 16 output channels (dual: the same channels
-// of w1 and w3) of one expert against one tile of up to 16 of its tokens, and
-// streams its part of K (KS wavefronts of a workgroup split K) in stages of
-// 256 elements (128 bytes per row), PD stages ahead.  Weights
+// An output group is RB blocks of 16 output channels (dual: the same channels
+// of w1 and w3) of one expert against one tile of up to 16 of its tokens; the
+// KS wavefronts of a workgroup split its K range.  The launch is persistent:
+// each wavefront works through a sequence of groups and streams its part of
+// K of each in stages of 256 elements (128 bytes per row), PD stages ahead
+// without a break between groups (so no wavefront is a short stream that
+// starts and drains on its own).  Weights
 // are read in a wide pattern (8 rows x 128 contiguous bytes per load
 // instruction, non-temporal), written to the wavefront's own LDS tile
 // (16-byte chunks XOR-swizzled by row) and read back one 16-byte chunk --
@@ -57,65 +60,103 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, float scale) {
   return as_bf16x8(u);
 }
 
-// KS wavefronts of a workgroup share one output group and split its K range
-// (more wavefronts in flight for a long K); their partial sums are added
-// through LDS in K order, so the result does not depend on timing.
+// Persistent form.  The grid is the resident capacity; workgroup b takes
+// rounds r = 0, 1, ... of GPW output groups (the KS wavefronts of a group
+// split its K range), groups numbered over the experts' token tiles only, so
+// no workgroup streams an empty expert.  Each wavefront's weight loads form
+// one stream across its groups: the ring keeps PD stages in flight through
+// group boundaries.  KS must divide the stage count K / 256.
 template <bool DUAL, int RB, int MIN_WAVES, int PD, int KS>
 __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxfp4_decode(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
     const uint8_t* __restrict__ wa, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ wb,
-    const uint8_t* __restrict__ sb, int N, int K, void* __restrict__ out, int tok_tiles) {
+    const uint8_t* __restrict__ sb, int N, int K, void* __restrict__ out) {
   constexpr int NM = DUAL ? 2 : 1;
   constexpr int CH = 16 * RB;                       // output channels per wavefront
+  constexpr int GPW = kMx4Waves / KS;               // output groups per workgroup round
+  constexpr int PART = NM * RB * 64 * 4;            // fp32 partial sums per wavefront
   __shared__ __attribute__((aligned(16))) uint8_t lds[kMx4Waves][NM][RB][16 * kMx4RowBytes];
-
+  __shared__ __attribute__((aligned(16))) float parts[kMx4Waves][PART];
+  __shared__ int32_t s_offs[kMaxExpertGroups + 1];
   static_assert(kMx4Waves % KS == 0, "K split");
-  // wavefront index and everything derived from it are uniform: kept in
-  // scalar registers (the token descriptor must be, or every buffer load
-  // would become a loop over the lanes' distinct descriptors)
+
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kpart = w % KS;
-  const int groups = N / CH;
-  const int gid = blockIdx.x * (kMx4Waves / KS) + w / KS;
-  const int cg = gid % groups;
-  const int rest = gid / groups;
-  const int tt = rest % tok_tiles;
-  const int e = rest / tok_tiles;
-  int row0 = 0, rows = 0;
-  if (e < E) {
-    row0 = __builtin_amdgcn_readfirstlane(offsets[e] + tt * 16);
-    rows = __builtin_amdgcn_readfirstlane(min(16, offsets[e + 1] - row0));
-  }
-  // the KS wavefronts of a group share this flag; a workgroup only returns as a whole
-  const bool active = rows > 0;
-  if constexpr (KS == 1) {
-    if (!active) return;
-  } else {
-    if (__syncthreads_or(active) == 0) return;
-  }
+  const int kpart = w % KS, slot = w / KS;
+  for (int i = threadIdx.x; i <= E; i += kMx4Waves * kWave) s_offs[i] = offsets[i];
+  __syncthreads();
+  const int CGN = N / CH;
+  int A = 0;                                        // output groups over all token tiles
+  for (int e = 0; e < E; ++e)
+    A += (__builtin_amdgcn_readfirstlane(s_offs[e + 1] - s_offs[e]) + 15) / 16 * CGN;
+  const int per_round = gridDim.x * GPW;
+  const int first = blockIdx.x * GPW;
+  if (first >= A) return;                           // uniform over the workgroup
+  const int R = (A - first + per_round - 1) / per_round;
+
+  struct Grp { int e, cg, row0, rows; };            // rows == 0: no group (loads stay valid)
+  auto locate = [&](int rd) __attribute__((always_inline)) -> Grp {
+    int a = rd * per_round + first + slot;
+    Grp gp{0, 0, 0, 0};
+    if (a >= A) return gp;
+    for (int e = 0; e < E; ++e) {
+      const int cnt = __builtin_amdgcn_readfirstlane(s_offs[e + 1] - s_offs[e]);
+      const int t = (cnt + 15) / 16 * CGN;
+      if (a < t) {
+        const int tt = a / CGN;
+        gp.e = e;
+        gp.cg = a - tt * CGN;
+        gp.row0 = __builtin_amdgcn_readfirstlane(s_offs[e]) + tt * 16;
+        gp.rows = min(16, cnt - tt * 16);
+        break;
+      }
+      a -= t;
+    }
+    return gp;
+  };
 
   const int64_t kb = K / 2;                         // bytes per weight row
   const int nblk = K / 32;                          // scale bytes per weight row
-  // wide loader: lane -> row lrow (+ 8 for the second instruction), 16-byte chunk lch
   const int lrow = lane >> 3, lch = lane & 7;
-  const uint8_t* pw[NM];
-  const uint8_t* ps[NM];
-  pw[0] = wa + ((int64_t)e * N + cg * CH) * kb;
-  ps[0] = sa + ((int64_t)e * N + cg * CH) * nblk;
-  if constexpr (DUAL) {
-    pw[1] = wb + ((int64_t)e * N + cg * CH) * kb;
-    ps[1] = sb + ((int64_t)e * N + cg * CH) * nblk;
-  }
-  // matrix-core operands: lane (r, g) = row / token r, element group g.  The
-  // token operand is read through a buffer descriptor bounded to the tile's
-  // rows: lanes of rows past the tile get an out-of-range offset, load zeros
-  // and fetch nothing (at decode most of the 16 rows are empty, and every
-  // weight byte here meets four token bytes).
-  const int r = lane & 15, g = lane >> 4;
-  const __amdgpu_buffer_rsrc_t xrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(act) + (int64_t)row0 * K, 0,
-                                        rows * K * 2, 0x00020000);
-  const int xoff = r < rows ? (r * K + g * 32) * 2 : 0x7ff00000;
+  const int tr = lane & 15, g = lane >> 4;
+  const int nsp = K / kMx4StageK / KS;              // stages per K part
+  const int st_begin = kpart * nsp;
+  const int S = R * nsp;                            // stages of this wavefront's stream
+
+  struct WOps {
+    uint4 w[NM][RB][2];
+    uint2 s[NM][RB];
+  };
+  // load cursor
+  int lr = 0, lst = st_begin;
+  Grp lg = locate(0);
+  auto load_weights = [&](WOps& o) __attribute__((always_inline)) {
+    const int64_t wrow0 = (int64_t)lg.e * N + lg.cg * CH;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const uint8_t* pw = (m == 0 ? wa : wb) + wrow0 * kb;
+      const uint8_t* ps = (m == 0 ? sa : sb) + wrow0 * nblk;
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          o.w[m][b][i] = load_stream16(pw + (int64_t)(b * 16 + i * 8 + lrow) * kb + lst * kMx4RowBytes + lch * 16);
+        o.s[m][b] = *reinterpret_cast<const uint2*>(ps + (int64_t)(b * 16 + tr) * nblk + lst * 8);
+      }
+    }
+    if (++lst == st_begin + nsp) {                  // past the stream's end: reload its last group
+      lst = st_begin;
+      if (lr + 1 < R) lg = locate(++lr);
+    }
+  };
+  // compute cursor
+  int cr = 0, cst = st_begin;
+  Grp cgp = locate(0);
+  auto token_rsrc = [&]() __attribute__((always_inline)) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(act) + (int64_t)cgp.row0 * K, 0,
+                                             cgp.rows * K * 2, 0x00020000);
+  };
+  __amdgpu_buffer_rsrc_t xrs = token_rsrc();
+  const int xoff_in = (tr * K + g * 32) * 2;
 
   f32x4_t acc[NM][RB];
 #pragma unroll
@@ -123,47 +164,64 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
 #pragma unroll
     for (int b = 0; b < RB; ++b) acc[m][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Stage st's weight chunks (2 wide loads per 16-row block) and this lane's
-  // 8 scale bytes of row r (blocks 8 st .. 8 st + 7).
-  struct WOps {
-    uint4 w[NM][RB][2];
-    uint2 s[NM][RB];
-  };
-  auto load_weights = [&](int st, WOps& o) __attribute__((always_inline)) {
+  // End of a group: partial sums of its KS wavefronts through LDS in K order,
+  // the first wavefront stores, every wavefront moves to its next group.
+  auto finish = [&]() __attribute__((always_inline)) {
+    if constexpr (KS > 1) {
+      __syncthreads();                              // the previous group's partials are read
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+          *reinterpret_cast<f32x4_t*>(&parts[w][((m * RB + b) * 64 + lane) * 4]) = acc[m][b];
+      __syncthreads();
+      if (kpart == 0) {
+#pragma unroll
+        for (int k = 1; k < KS; ++k)
+#pragma unroll
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+              acc[m][b] += *reinterpret_cast<const f32x4_t*>(&parts[w + k][((m * RB + b) * 64 + lane) * 4]);
+      }
+    }
+    if (kpart == 0 && tr < cgp.rows) {
+      const int64_t orow = cgp.row0 + tr;
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const int c = cgp.cg * CH + b * 16 + g * 4;
+        if constexpr (DUAL) {
+          float hv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hv[i] = swiglu_fast(acc[0][b][i], acc[1][b][i]);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow * N + c) =
+              make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+        } else {
+          *reinterpret_cast<float4*>(static_cast<float*>(out) + orow * N + c) =
+              make_float4(acc[0][b][0], acc[0][b][1], acc[0][b][2], acc[0][b][3]);
+        }
+      }
+    }
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int b = 0; b < RB; ++b) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          o.w[m][b][i] = load_stream16(pw[m] + (int64_t)(b * 16 + i * 8 + lrow) * kb +
-                                       st * kMx4RowBytes + lch * 16);
-        o.s[m][b] = *reinterpret_cast<const uint2*>(ps[m] + (int64_t)(b * 16 + r) * nblk + st * 8);
-      }
+      for (int b = 0; b < RB; ++b) acc[m][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    cst = st_begin;
+    if (cr + 1 < R) {
+      cgp = locate(++cr);
+      xrs = token_rsrc();
+    }
   };
-  // One stage:
-  //  1. the token operand of instruction (j, q): 8 bf16 at element
-  //     32 (4 j + g) + 8 q of the stage (zeros for rows past the tile);
-  //  2. this stage's weights (loaded PD stages earlier) to the wavefront-private
-  //     LDS tile (LDS operations of one wavefront execute in order);
-  //  3. the weights of stage st + PD into `nxt`, the slot stage st - 1 used:
-  //     issued after the token loads, so waiting for the tokens leaves them in
-  //     flight.  Unconditional (past the end they reload the last stage): a
-  //     branch would make the compiler's wait counts assume they may be absent;
-  //  4. read back, dequantise, multiply.
-  // The PD + 1 weight sets rotate without copies, so no register move waits
-  // for a load in flight.
-  const int nst_all = K / kMx4StageK;
-  const int st_begin = nst_all * kpart / KS, st_end = nst_all * (kpart + 1) / KS;
-  const int nst = st_end;                           // stages are numbered globally
-  auto stage = [&](int st, WOps& cur, WOps& nxt) __attribute__((always_inline)) {
+
+  auto stage = [&](WOps& cur, WOps& nxt) __attribute__((always_inline)) {
+    const int xoff = tr < cgp.rows ? xoff_in : 0x7ff00000;
     uint4 x[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         x[j][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                      xrs, xoff, (st * kMx4StageK + j * 128 + q * 8) * 2, 0));
+                      xrs, xoff, (cst * kMx4StageK + j * 128 + q * 8) * 2, 0));
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -174,7 +232,7 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
           *reinterpret_cast<uint4*>(&lds[w][m][b][row * kMx4RowBytes + ((lch ^ lds_swizzle_key(row)) & 7) * 16]) =
               cur.w[m][b][i];
         }
-    load_weights(min(st + PD, nst - 1), nxt);
+    load_weights(nxt);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int chunk = 4 * j + g;
@@ -183,7 +241,7 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
           const uint4 c = *reinterpret_cast<const uint4*>(
-              &lds[w][m][b][r * kMx4RowBytes + ((chunk ^ lds_swizzle_key(r)) & 7) * 16]);
+              &lds[w][m][b][tr * kMx4RowBytes + ((chunk ^ lds_swizzle_key(tr)) & 7) * 16]);
           const uint32_t sbyte = ((j ? cur.s[m][b].y : cur.s[m][b].x) >> (8 * g)) & 255u;
           const float scale = e8m0_to_f32(sbyte);
           const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
@@ -193,78 +251,46 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
                                                                  as_bf16x8(x[j][q]), acc[m][b], 0, 0, 0);
         }
     }
+    if (++cst == st_begin + nsp) finish();
   };
-  if (active && st_end > st_begin) {          // a K part can be empty when K is short
-    WOps ring[PD + 1];
-#pragma unroll
-    for (int i = 0; i < PD; ++i) load_weights(min(st_begin + i, nst - 1), ring[i]);
-    // full rounds of PD + 1 stages, then the remaining stages one by one
-    const int nfull = st_begin + (st_end - st_begin) / (PD + 1) * (PD + 1);
-    for (int st0 = st_begin; st0 < nfull; st0 += PD + 1) {
-#pragma unroll
-      for (int u = 0; u <= PD; ++u) stage(st0 + u, ring[u], ring[(u + PD) % (PD + 1)]);
-    }
-#pragma unroll
-    for (int u = 0; u < PD; ++u)
-      if (nfull + u < nst) stage(nfull + u, ring[u], ring[(u + PD) % (PD + 1)]);
-  }
-  if constexpr (KS > 1) {
-    // partial sums through LDS: each wavefront's own tile region holds its
-    // 16x16 accumulators; the group's first wavefront adds the others in K order
-    static_assert(NM * RB * 16 * 16 * 4 <= NM * RB * 16 * kMx4RowBytes, "partials fit the LDS tile");
-    float* part = reinterpret_cast<float*>(&lds[w][0][0][0]);
-    __syncthreads();                                // every wavefront is done with its LDS tile
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int b = 0; b < RB; ++b)
-        *reinterpret_cast<f32x4_t*>(&part[((m * RB + b) * 64 + lane) * 4]) = acc[m][b];
-    __syncthreads();
-    if (kpart != 0 || !active) return;
-#pragma unroll
-    for (int k = 1; k < KS; ++k) {
-      const float* other = reinterpret_cast<const float*>(&lds[w + k][0][0][0]);
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int b = 0; b < RB; ++b)
-          acc[m][b] += *reinterpret_cast<const f32x4_t*>(&other[((m * RB + b) * 64 + lane) * 4]);
-    }
-  }
 
-  // 16x16 accumulators: lane holds token column (lane & 15), channels 4 (lane >> 4) + 0..3.
-  const int tcol = lane & 15;
-  if (tcol >= rows) return;
-  const int64_t orow = row0 + tcol;
+  WOps ring[PD + 1];
 #pragma unroll
-  for (int b = 0; b < RB; ++b) {
-    const int c = cg * CH + b * 16 + (lane >> 4) * 4;
-    if constexpr (DUAL) {
-      float hv[4];
+  for (int i = 0; i < PD; ++i) load_weights(ring[i]);
+  const int nfull = S / (PD + 1) * (PD + 1);
+  for (int p0 = 0; p0 < nfull; p0 += PD + 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hv[i] = swiglu_fast(acc[0][b][i], acc[1][b][i]);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow * N + c) =
-          make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
-    } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(out) + orow * N + c) =
-          make_float4(acc[0][b][0], acc[0][b][1], acc[0][b][2], acc[0][b][3]);
-    }
+    for (int u = 0; u <= PD; ++u) stage(ring[u], ring[(u + PD) % (PD + 1)]);
   }
+#pragma unroll
+  for (int u = 0; u < PD; ++u)
+    if (nfull + u < S) stage(ring[u], ring[(u + PD) % (PD + 1)]);
 }
 
+// Workgroups per CU = MIN_WAVES wavefronts per SIMD; KS is the largest of 4, 2, 1
+// that divides the stage count.
 template <bool DUAL, int RB, int MIN_WAVES, int PD, int KS>
+hipError_t launch_ks(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
+                     const uint8_t* wa, const uint8_t* sa, const uint8_t* wb, const uint8_t* sb,
+                     int N, int K, void* out, hipStream_t st) {
+  constexpr int kWgPerCu = MIN_WAVES * 4 / kMx4Waves;
+  static_assert(kWgPerCu >= 1, "resident workgroups");
+  const int64_t grid = (int64_t)device_cu_count() * kWgPerCu;
+  hipLaunchKernelGGL((grouped_gemm_mxfp4_decode<DUAL, RB, MIN_WAVES, PD, KS>), dim3((unsigned)grid),
+                     dim3(kMx4Waves * kWave), 0, st, act, offsets, expert_groups(s), wa, sa, wb, sb, N,
+                     K, out);
+  return hipGetLastError();
+}
+
+template <bool DUAL, int RB, int MIN_WAVES, int PD>
 hipError_t launch_variant(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                           const uint8_t* wa, const uint8_t* sa, const uint8_t* wb,
                           const uint8_t* sb, int N, int K, void* out, hipStream_t st) {
-  const int tok_tiles = (int)((max_rows_per_expert(s) + 15) / 16);
-  const int64_t groups = (int64_t)expert_groups(s) * tok_tiles * (N / (16 * RB));
-  if (groups <= 0) return hipSuccess;   // no expert can hold a row (capacity 0)
-  constexpr int GPB = kMx4Waves / KS;   // output groups per workgroup
-  const int64_t blocks = (groups + GPB - 1) / GPB;
-  hipLaunchKernelGGL((grouped_gemm_mxfp4_decode<DUAL, RB, MIN_WAVES, PD, KS>), dim3((unsigned)blocks),
-                     dim3(kMx4Waves * kWave), 0, st, act, offsets, expert_groups(s), wa, sa, wb, sb, N,
-                     K, out, tok_tiles);
-  return hipGetLastError();
+  if (max_rows_per_expert(s) <= 0) return hipSuccess;   // no expert can hold a row (capacity 0)
+  const int nst = K / kMx4StageK;
+  if (nst % 4 == 0) return launch_ks<DUAL, RB, MIN_WAVES, PD, 4>(s, act, offsets, wa, sa, wb, sb, N, K, out, st);
+  if (nst % 2 == 0) return launch_ks<DUAL, RB, MIN_WAVES, PD, 2>(s, act, offsets, wa, sa, wb, sb, N, K, out, st);
+  return launch_ks<DUAL, RB, MIN_WAVES, PD, 1>(s, act, offsets, wa, sa, wb, sb, N, K, out, st);
 }
 
 }  // namespace
@@ -274,17 +300,18 @@ hipError_t launch_gate_up_mxfp4(const moe_shape_t& s, const uint16_t* x_perm,
                                 const uint8_t* w3, const uint8_t* w3_scale, uint16_t* h,
                                 hipStream_t st) {
   // Measured at the Mixtral decode shape (4 rows per expert): 32 channels per
-  // wavefront and K split in two streams 4.8 TB/s; 16 channels, no split, 4.3.
-  return launch_variant<true, 2, 2, 2, 2>(s, x_perm, offsets, w1, w1_scale, w3, w3_scale, s.d_ff,
-                                    s.d_model, h, st);
+  // wavefront, K split in four, one stage ahead, three workgroups per CU:
+  // 5.4 TB/s (the one-group-per-workgroup form streamed 4.8).
+  return launch_variant<true, 2, 3, 1>(s, x_perm, offsets, w1, w1_scale, w3, w3_scale, s.d_ff,
+                                       s.d_model, h, st);
 }
 
 hipError_t launch_down_mxfp4(const moe_shape_t& s, const uint16_t* h, const int32_t* offsets,
                              const uint8_t* w2, const uint8_t* w2_scale, float* y_perm,
                              hipStream_t st) {
-  // 64 channels per wavefront, K (14336) split in four: 4.7 TB/s; 16, no split: 3.7.
-  return launch_variant<false, 4, 2, 2, 4>(s, h, offsets, w2, w2_scale, nullptr, nullptr, s.d_model,
-                                     s.d_ff, y_perm, st);
+  // 64 channels per wavefront, K (14336) split in four, two stages ahead: 4.8 TB/s.
+  return launch_variant<false, 4, 2, 2>(s, h, offsets, w2, w2_scale, nullptr, nullptr, s.d_model,
+                                        s.d_ff, y_perm, st);
 }
 
 }  // namespace moe
