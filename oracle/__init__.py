@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the sparse top-2 MoE layer -- TEST INFRASTRUCTURE ONLY.
+"""fp64 CPU oracle of the sparse top-k MoE layer -- TEST INFRASTRUCTURE ONLY.
 
 Only tests/, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline leg
 may import this package.  It shares no code with the HIP path

@@ -1,4 +1,5 @@
-"""Plain fp64 CPU oracle of the sparse top-2 MoE feed-forward layer.
+"""Plain fp64 CPU oracle of the sparse top-k MoE feed-forward layer (top-2 Mixtral form
+and the general form of step 8).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares
@@ -106,9 +107,9 @@ class Routing:
     G: np.ndarray          # [T, k] float64 gate weights
     gap12: np.ndarray      # [T] smallest gap between consecutive ranks 1..k (slot order)
     gap23: np.ndarray      # [T] logit(k-th) - logit(k+1-th): the selected set (inf when E == k)
-    next_ids: np.ndarray   # [T, 2] int64: 3rd- and 4th-ranked experts (-1 when E is smaller)
-    gap34: np.ndarray      # [T] logit(3rd) - logit(4th)  (inf when absent)
-    gap45: np.ndarray      # [T] logit(4th) - logit(5th)  (inf when absent)
+    next_ids: np.ndarray   # [T, 2] int64: experts ranked k+1 and k+2 (-1 when E is smaller)
+    gap34: np.ndarray      # [T] logit(k+1-th) - logit(k+2-th)  (inf when absent)
+    gap45: np.ndarray      # [T] logit(k+2-th) - logit(k+3-th)  (inf when absent)
 
 
 def topk_gate(logits: np.ndarray, k: int = 2) -> Routing:

@@ -79,7 +79,7 @@ __device__ __forceinline__ int final_expert(const int32_t* ids, const uint8_t* d
   return m == 0 ? ids[i] : m == 2 ? fallback_expert(drop, next, i) : -1;
 }
 
-// FALLBACK = false: the capacity round over the top-2 assignments (marks 0/1).
+// FALLBACK = false: the capacity round over the top-k assignments (marks 0/1).
 // FALLBACK = true: the fallback round over the assignments the first marked 1.
 template <bool FALLBACK>
 __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __restrict__ ids,

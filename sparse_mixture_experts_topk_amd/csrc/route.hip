@@ -20,8 +20,8 @@
 // to 8, 16, 32 or 64).  Each lane strides over d in 16-byte vectors of x and
 // of every router row, accumulating TPW * EP = 64 fp32 partial sums.  A
 // recursive-halving exchange (6 shuffle rounds, 63 exchanges) then leaves lane
-// L holding the full logit of (token L / EP, expert L % EP); the top-2 is a
-// butterfly arg-max inside each EP-lane group per selection round.
+// L holding the full logit of (token L / EP, expert L % EP); each selection
+// round is a butterfly arg-max inside the EP-lane group.
 // W_g (64 KiB at d = 4096, E = 8) stays L2-resident; x is read once.
 #include "device_common.hpp"
 #include "launch.hpp"
