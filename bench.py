@@ -34,21 +34,21 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8_e4m3": 5000.0, "f32": 157.3}   # dense matri
 DEFAULTS = {"decode_bf16": (200, 20), "prefill_bf16": (20, 3), "skewed_capacity_bf16": (20, 3),
             "longctx_fp8": (10, 3), "tiny_fp32": (200, 20), "finegrained_decode_bf16": (100, 10),
             "finegrained_prefill_bf16": (10, 3)}
-KERNEL_SOURCES = ("sparse_mixture_experts_topk_amd/csrc/gemm_bf16.hip",
-                  "sparse_mixture_experts_topk_amd/csrc/gemm_bf16_decode.hip",
-                  "sparse_mixture_experts_topk_amd/csrc/lds_stream.hpp",
-                  "sparse_mixture_experts_topk_amd/csrc/device_common.hpp",
-                  "sparse_mixture_experts_topk_amd/csrc/gemm_fp8.hip",
-                  "sparse_mixture_experts_topk_amd/csrc/gemm_f32.hip")
+# Sources of the dominant (gate/up) kernel of each weight dtype: a committed
+# traffic measurement counts only while the hash of these files is unchanged.
+_CSRC = "sparse_mixture_experts_topk_amd/csrc/"
+KERNEL_SOURCES = {
+    "bf16": (_CSRC + "gemm_bf16.hip", _CSRC + "gemm_bf16_decode.hip", _CSRC + "lds_stream.hpp",
+             _CSRC + "device_common.hpp"),
+    "fp8_e4m3": (_CSRC + "gemm_fp8.hip", _CSRC + "device_common.hpp"),
+    "mxfp4": (_CSRC + "gemm_mxfp4_decode.hip", _CSRC + "lds_stream.hpp", _CSRC + "device_common.hpp"),
+    "f32": (_CSRC + "gemm_f32.hip", _CSRC + "device_common.hpp"),
+}
 
 
-# MXFP4 workloads also run the 4-bit weight-streaming kernels.
-MXFP4_SOURCES = KERNEL_SOURCES + ("sparse_mixture_experts_topk_amd/csrc/gemm_mxfp4_decode.hip",)
-
-
-def kernel_source_sha(cfg=None) -> str:
+def kernel_source_sha(cfg) -> str:
     h = hashlib.sha256()
-    for p in (MXFP4_SOURCES if cfg is not None and cfg.w_dtype == "mxfp4" else KERNEL_SOURCES):
+    for p in KERNEL_SOURCES[cfg.w_dtype]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

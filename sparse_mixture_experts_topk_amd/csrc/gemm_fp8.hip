@@ -65,6 +65,7 @@ constexpr int F8_ROWS = 256;
 constexpr int F8_BK = 128;                    // K per stage: 128 fp8 = 128 bytes per row
 constexpr int F8_TILE_BYTES = F8_ROWS * F8_BK;
 constexpr int F8_THREADS = 256;
+constexpr int kF8GroupN = 8;                  // channel tiles per group of the tile order
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ lds_swizzle_key(row)) << 4);
@@ -83,6 +84,20 @@ __global__ __launch_bounds__(F8_THREADS, 1) void grouped_gemm_fp8_prefill(
   int e, r0, r1, mt, nt;
   const int tile = xcd_remap(blockIdx.x, grid_padded);
   if (!locate_tile(offsets, E, F8_ROWS, n_tiles, tile, e, r0, r1, mt, nt)) return;
+  {
+    // Order of an expert's tiles: groups of kF8GroupN channel tiles, channel
+    // tile fastest inside a group, so the tiles one XCD runs at a time (its 32
+    // consecutive ones) are 8 channel tiles x 4 token tiles, each weight and
+    // token slice fetched into its L2 once for several of them.
+    const int mtc = (r1 - r0 + F8_ROWS - 1) / F8_ROWS;
+    const int l = nt * mtc + mt;                      // tile index inside the expert
+    const int gi = l / (mtc * kF8GroupN);
+    const int nt0 = gi * kF8GroupN;
+    const int gsz = min(kF8GroupN, n_tiles - nt0);
+    const int idx = l - gi * mtc * kF8GroupN;
+    nt = nt0 + idx % gsz;
+    mt = idx / gsz;
+  }
   const int tok0 = r0 + mt * F8_ROWS;
   const int tok_rows = min(F8_ROWS, r1 - tok0);
   const int ch0 = nt * CH_TILE;
