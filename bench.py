@@ -39,8 +39,9 @@ DEFAULTS = {"decode_bf16": (200, 20), "prefill_bf16": (20, 3), "skewed_capacity_
 _CSRC = "sparse_mixture_experts_topk_amd/csrc/"
 KERNEL_SOURCES = {
     "bf16": (_CSRC + "gemm_bf16.hip", _CSRC + "gemm_bf16_decode.hip", _CSRC + "lds_stream.hpp",
-             _CSRC + "device_common.hpp"),
-    "fp8_e4m3": (_CSRC + "gemm_fp8.hip", _CSRC + "device_common.hpp"),
+             _CSRC + "persistent_tiles.hpp", _CSRC + "device_common.hpp"),
+    "fp8_e4m3": (_CSRC + "gemm_fp8.hip", _CSRC + "lds_stream.hpp", _CSRC + "persistent_tiles.hpp",
+                 _CSRC + "device_common.hpp"),
     "mxfp4": (_CSRC + "gemm_mxfp4_decode.hip", _CSRC + "lds_stream.hpp", _CSRC + "device_common.hpp"),
     "f32": (_CSRC + "gemm_f32.hip", _CSRC + "device_common.hpp"),
 }

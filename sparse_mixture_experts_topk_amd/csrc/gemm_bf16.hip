@@ -33,6 +33,7 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "lds_stream.hpp"
+#include "persistent_tiles.hpp"
 
 namespace moe {
 
@@ -73,38 +74,6 @@ struct TileGeom {
   __device__ static __forceinline__ int key(int row) { return (row / (16 / CPR)) & (CPR - 1); }
 };
 
-// Work split of a persistent launch.  The expert-major tile list (token
-// tiles fastest) is cut into 8 contiguous shares, one per XCD; the `slots`
-// workgroups of XCD x (blockIdx = slot * 8 + x) take its full tiles in
-// rounds: tiles share_begin + slot + i * slots, i < R.  The share's last
-// `tail` < slots tiles are either taken whole by the first `tail` slots
-// (data-parallel), or (split) cut along K into `slots` near-equal runs of P
-// slices, one per workgroup, each covering parts of at most two tiles; the
-// parts are written as fp32 partial tiles and summed by a second kernel in
-// K order, which keeps the result independent of timing.
-struct TileSplit {
-  int share_begin, R, tail, P;
-
-  __device__ static int total_tiles(const int32_t* offs, int E, int n_tiles) {
-    int total = 0;
-    for (int e = 0; e < E; ++e)
-      total += (__builtin_amdgcn_readfirstlane(offs[e + 1]) -
-                __builtin_amdgcn_readfirstlane(offs[e]) + PF_ROWS - 1) / PF_ROWS;
-    return total * n_tiles;
-  }
-  __device__ static TileSplit of(int total, int xcd, int slots, int KT) {
-    TileSplit t;
-    const int per_xcd = (total + 7) >> 3;
-    t.share_begin = xcd * per_xcd;
-    const int len = max(0, min(t.share_begin + per_xcd, total) - t.share_begin);
-    t.R = len / slots;
-    t.tail = len - t.R * slots;
-    t.P = (t.tail * KT + slots - 1) / slots;
-    return t;
-  }
-};
-
-constexpr int kMaxPersistentGroups = 256;
 
 // Tile: TA weight rows x 256 tokens.  The dual (gate/up) kernel's weight rows
 // are TA / 2 rows of w1 followed by the same TA / 2 rows of w3, and a
@@ -155,7 +124,7 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
   const int KT = K / BK;
   const int slots = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const TileSplit sp = TileSplit::of(TileSplit::total_tiles(offs, E, n_tiles), xcd, slots, KT);
+  const TileSplit sp = TileSplit::of(TileSplit::total_tiles(offs, E, n_tiles, PF_ROWS), xcd, slots, KT);
   // this workgroup's items: whole tiles, then (split) up to two K-runs of tail tiles
   const int n_whole = sp.R + ((!SPLIT && slot < sp.tail) ? 1 : 0);
   const int run0 = slot * sp.P, run1 = min(run0 + sp.P, sp.tail * KT);
@@ -439,7 +408,7 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(const int32_t* __restr
   const int rg = blockIdx.x % kFixupRowGroups;
   const int xcd = (blockIdx.x / kFixupRowGroups) & 7, j = blockIdx.x / kFixupRowGroups >> 3;
   const int KT = K / BK;
-  const TileSplit sp = TileSplit::of(TileSplit::total_tiles(offsets, E, n_tiles), xcd, slots, KT);
+  const TileSplit sp = TileSplit::of(TileSplit::total_tiles(offsets, E, n_tiles, PF_ROWS), xcd, slots, KT);
   if (j >= sp.tail) return;
   int e, r0, r1, mt, nt;
   locate_tile(offsets, E, PF_ROWS, n_tiles, sp.share_begin + sp.R * slots + j, e, r0, r1, mt, nt);
@@ -479,13 +448,6 @@ template <bool DUAL>
 using PrefillGeom = TileGeom<PrefillCfg<DUAL>::BK, PrefillCfg<DUAL>::WR, PrefillCfg<DUAL>::WC, PrefillCfg<DUAL>::WA,
                              PrefillCfg<DUAL>::WB>;
 constexpr int64_t kPartialTileBytes = (int64_t)PF_ROWS * PrefillGeom<false>::TA * 4;
-
-// Workgroups of the persistent launch: one per CU, at most kMaxPersistentGroups,
-// a multiple of the 8 XCDs, and no more than there are tiles.
-int64_t persistent_grid(int64_t max_tiles) {
-  const int64_t cus = std::min<int64_t>(device_cu_count(), kMaxPersistentGroups);
-  return std::max<int64_t>(8, std::min<int64_t>((max_tiles + 7) / 8 * 8, cus / 8 * 8));
-}
 
 template <bool DUAL>
 hipError_t launch_prefill(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,

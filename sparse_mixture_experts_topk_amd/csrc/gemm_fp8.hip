@@ -13,42 +13,21 @@
 // lane half h holds the h-th 16-element half of each of the two blocks and
 // supplies the scale of block h: the token operand's block scales are
 // applied in hardware with no extra VALU work.  The weight operand's scale
-// is 1 (E8M0 127) and its per-channel fp32 scale is applied in the epilogue.  The gate/up epilogue forms h = silu(g) * u in
-// fp32 and block-quantises it per (token, 32 channels): the amax of a block
-// lives in two lanes (16 channels each) and is completed with one lane swap.
+// is 1 (E8M0 127) and its per-channel fp32 scale is applied in the epilogue.
+// The gate/up epilogue forms h = silu(g) * u in fp32 and block-quantises it
+// per (token, 32 channels): the amax of a block lives in two lanes (16
+// channels each) and is completed with one lane swap.
 //
-// Tile structure follows the bf16 prefill kernel: 256 lanes, 256 weight rows
-// (dual: 128 w1 + the same 128 w3) x 256 token rows, K staged 128 at a time
-// (128 bytes per LDS row, 16-byte chunks XOR-swizzled by row), buffer-
-// resource loads bounded to the valid rows, the next slice fetched into
-// registers during the current one, fragment reads one substep ahead, one
-// barrier per slice, XCD-aware grouped tile schedule.
+// The kernel below runs the bf16 prefill kernel's pipeline (persistent
+// workgroups, one load stream through a ring of LDS stages filled by loads
+// that write LDS directly, 384 x 256 tiles, 8 wavefronts) on fp8 operands.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "lds_stream.hpp"
+#include "persistent_tiles.hpp"
 
 namespace moe {
 namespace {
-
-constexpr int kBufferFlags = 0x00020000;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kBufferFlags);
-}
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-}
-
-__device__ __forceinline__ float swiglu_fast(float g, float u) {
-  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
-  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
-}
 
 // E8M0 exponent of a block: ceil(log2(fp32(amax / 448))) clamped to [-127, 127];
 // 0 for an all-zero block.
@@ -61,256 +40,340 @@ __device__ __forceinline__ int block_exponent(float amax) {
   return man == 0 ? ex - 127 : ex - 126;
 }
 
-constexpr int F8_ROWS = 256;
-constexpr int F8_BK = 128;                    // K per stage: 128 fp8 = 128 bytes per row
-constexpr int F8_TILE_BYTES = F8_ROWS * F8_BK;
-constexpr int F8_THREADS = 256;
-constexpr int kF8GroupN = 8;                  // channel tiles per group of the tile order
-
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ lds_swizzle_key(row)) << 4);
-}
+// ---------------------------------------------------------------------------
+// Persistent tile kernel: the bf16 prefill kernel's pipeline with fp8 operands.
+//
+// 512 lanes (two wavefronts per SIMD), a 384 x 256 tile (weights x tokens;
+// gate/up: 192 rows of w1 and the same 192 of w3).  K advances 64 at a time:
+// a slice row is 64 fp8 bytes, so an LDS stage holds 24 + 16 KiB as in the
+// bf16 kernel and is filled the same way, by buffer loads that write LDS
+// directly, two slices in flight while one is multiplied.  One
+// v_mfma_scale_f32_32x32x64_f8f6f4 per block pair covers a slice.  The token
+// operand's E8M0 scales come as dwords (four bytes per token row = the two
+// blocks of two consecutive slices) by the same kind of load into a two-slot
+// LDS ring: wavefronts 0..3 issue one on every even slice.  The wait for a
+// slice allows the five weight and token loads of the slice after it to be
+// pending; when that slice also carries a scale load the wait is one load
+// stricter than needed, never looser.  Each wavefront owns 6 x 2 accumulator blocks (192 fp32 per lane);
+// a slice's 12 matrix instructions run in two halves of 3 weight blocks:
+// the first carries the slice loads, the second follows the wait and the
+// barrier and reads the next slice's first fragments.  Weight fragments are
+// double-buffered one block ahead.  Tiles are scheduled as in the bf16
+// kernel (persistent workgroups, one load stream across tiles).
+constexpr int F8T_BK = 64;                          // K (bytes) per slice
+constexpr int F8T_NS = 3;                           // LDS ring stages
+constexpr int F8T_WR = 2, F8T_WC = 4, F8T_WA = 6, F8T_WB = 2;
+constexpr int F8T_NW = F8T_WR * F8T_WC;
+constexpr int F8T_THREADS = 64 * F8T_NW;
+constexpr int F8T_TA = 32 * F8T_WR * F8T_WA;        // 384 weight rows
+constexpr int F8T_TB = 32 * F8T_WC * F8T_WB;        // 256 token rows
+constexpr int F8T_CPR = F8T_BK / 16;                // 16-byte chunks per row slice
+constexpr int F8T_RPI = 64 / F8T_CPR;               // rows per 1 KiB load instruction
+constexpr int F8T_JA = F8T_TA / F8T_RPI / F8T_NW;   // weight loads per wavefront per slice
+constexpr int F8T_JB = F8T_TB / F8T_RPI / F8T_NW;   // token loads per wavefront per slice
+constexpr int F8T_DMA = F8T_JA + F8T_JB;            // weight and token loads per slice
+constexpr int F8T_OPA = F8T_TA * F8T_BK;
+constexpr int F8T_STAGE = (F8T_TA + F8T_TB) * F8T_BK;
+constexpr int F8T_SCW = F8T_TB / 64;                // wavefronts that load scales
+constexpr int F8T_SLOTS = 3 * F8T_WB;               // load slots of a slice (the first half's instructions)
+constexpr int F8T_OOB = 0x7ff00000;                 // offset past every descriptor
+constexpr int kF8GroupN = 8;                        // channel tiles per group of the tile order
+static_assert(F8T_JA * F8T_RPI * F8T_NW == F8T_TA && F8T_JB * F8T_RPI * F8T_NW == F8T_TB, "whole loads");
+static_assert(F8T_DMA + 1 <= F8T_SLOTS, "one load slot per matrix instruction of the first half");
+static_assert((F8T_NW * F8T_RPI) % 16 == 0, "loads of a wavefront are whole swizzle periods apart");
 
 template <bool DUAL>
-__global__ __launch_bounds__(F8_THREADS, 1) void grouped_gemm_fp8_prefill(
+__global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
     const uint8_t* __restrict__ act, const uint8_t* __restrict__ act_scale,
     const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ wa,
     const uint8_t* __restrict__ wb, const float* __restrict__ sa, const float* __restrict__ sb,
-    int N, int K, void* __restrict__ out, uint8_t* __restrict__ out_scale, int n_tiles,
-    int grid_padded) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][F8_TILE_BYTES];
-
-  constexpr int CH_TILE = DUAL ? 128 : 256;
-  int e, r0, r1, mt, nt;
-  const int tile = xcd_remap(blockIdx.x, grid_padded);
-  if (!locate_tile(offsets, E, F8_ROWS, n_tiles, tile, e, r0, r1, mt, nt)) return;
-  {
-    // Order of an expert's tiles: groups of kF8GroupN channel tiles, channel
-    // tile fastest inside a group, so the tiles one XCD runs at a time (its 32
-    // consecutive ones) are 8 channel tiles x 4 token tiles, each weight and
-    // token slice fetched into its L2 once for several of them.
-    const int mtc = (r1 - r0 + F8_ROWS - 1) / F8_ROWS;
-    const int l = nt * mtc + mt;                      // tile index inside the expert
-    const int gi = l / (mtc * kF8GroupN);
-    const int nt0 = gi * kF8GroupN;
-    const int gsz = min(kF8GroupN, n_tiles - nt0);
-    const int idx = l - gi * mtc * kF8GroupN;
-    nt = nt0 + idx % gsz;
-    mt = idx / gsz;
-  }
-  const int tok0 = r0 + mt * F8_ROWS;
-  const int tok_rows = min(F8_ROWS, r1 - tok0);
-  const int ch0 = nt * CH_TILE;
-
+    int N, int K, void* __restrict__ out, uint8_t* __restrict__ out_scale, int n_tiles) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[F8T_NS * F8T_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint32_t scs[2][F8T_TB];   // scale slots of slice pairs
+  __shared__ int32_t offs[kMaxExpertGroups + 1];
+  constexpr int WA = F8T_WA, WB = F8T_WB, NS = F8T_NS;
+  constexpr int HA = WA / 2;                        // dual: w1 (or w3) blocks per wavefront
+  constexpr int CH_TILE = DUAL ? F8T_TA / 2 : F8T_TA;
+  constexpr int kOne = 0x7f7f7f7f;                  // E8M0 127 = 1.0: the weight operand's scale
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
-
-  const int lrow = tid >> 3, lchunk = tid & 7;
-  const int64_t rowbytes = K;
-  const int nblk = K / 32;                    // scale blocks per row
-  const __amdgpu_buffer_rsrc_t rs_t = make_rsrc(act + (int64_t)tok0 * K, tok_rows * rowbytes);
-  const __amdgpu_buffer_rsrc_t rs_ts = make_rsrc(act_scale + (int64_t)tok0 * nblk,
-                                                 (int64_t)tok_rows * nblk);
-  const __amdgpu_buffer_rsrc_t rs_w0 =
-      make_rsrc(wa + ((int64_t)e * N + ch0) * K, (int64_t)(N - ch0) * rowbytes);
-  const __amdgpu_buffer_rsrc_t rs_w1 =
-      DUAL ? make_rsrc(wb + ((int64_t)e * N + ch0) * K, (int64_t)(N - ch0) * rowbytes) : rs_w0;
-  int voff_w[8], voff_t[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int wrow = (DUAL ? (j & 3) * 32 : j * 32) + lrow;
-    voff_w[j] = (int)(wrow * rowbytes) + lchunk * 16;
-    voff_t[j] = (int)((j * 32 + lrow) * rowbytes) + lchunk * 16;
-  }
-  const int st_off = swz(lrow, lchunk);
-
-  uint4 rw[8], rt[8];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      rw[j] = buf_load16((DUAL && j >= 4) ? rs_w1 : rs_w0, voff_w[j], k0);
-      rt[j] = buf_load16(rs_t, voff_t[j], k0);
-    }
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / F8T_WC, wc = wave % F8T_WC;
+  // lane index the compiler cannot keep in a register through the K loop
+  auto lane_now = [&]() __attribute__((always_inline)) {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      *reinterpret_cast<uint4*>(&smem[buf][0][st_off + j * 32 * 128]) = rw[j];
-      *reinterpret_cast<uint4*>(&smem[buf][1][st_off + j * 32 * 128]) = rt[j];
-    }
-  };
+  auto key = [](int row) { return (row / (16 / F8T_CPR)) & (F8T_CPR - 1); };
 
-  // fragment addressing.  The scale a lane supplies covers bytes 16 h .. 16 h + 15
-  // of BOTH lanes of its row (h = its lane half), so a 32-element scale block
-  // is split across the halves: for MFMA step s, lane half fg holds 16-byte
-  // chunk 4 s + fg (block 2 s) in its low half and chunk 4 s + 2 + fg
-  // (block 2 s + 1) in its high half, and supplies the scale of block 2 s + fg.
-  const int fi = lane & 31, fg = lane >> 5;
-  int frag_off[2][2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-      frag_off[s][c] = fi * 128 + (((4 * s + 2 * c + fg) ^ lds_swizzle_key(fi)) << 4);
-  int arow[4], brow[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    if constexpr (DUAL) arow[a] = (a >> 1) * 128 + wr * 64 + (a & 1) * 32;
-    else arow[a] = wr * 128 + a * 32;
-    brow[a] = wc * 128 + a * 32;
-  }
-  // token-operand scales: 4 E8M0 bytes (blocks 4 kt .. 4 kt + 3) per token row per slice;
-  // shifted so that the byte of this lane's half sits at position 2 s
-  int voff_sc[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) voff_sc[b] = (brow[b] + fi) * nblk;
-  const int sc_shift = 8 * fg;
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-
-  auto read_frags = [&](int buf, int s, i32x8_t* fa, i32x8_t* fb) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(&smem[buf][0][arow[a] * 128 + frag_off[s][0]]);
-      const uint4 hi = *reinterpret_cast<const uint4*>(&smem[buf][0][arow[a] * 128 + frag_off[s][1]]);
-      fa[a] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(&smem[buf][1][brow[b] * 128 + frag_off[s][0]]);
-      const uint4 hi = *reinterpret_cast<const uint4*>(&smem[buf][1][brow[b] * 128 + frag_off[s][1]]);
-      fb[b] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-  };
-  constexpr int kOne = 0x7f7f7f7f;            // E8M0 127 = 1.0 in every byte
-  auto mfmas = [&](const i32x8_t* fa, const i32x8_t* fb, const int* sc, int s) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (s == 0)
-          acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[a], fb[b], acc[a][b], 0, 0,
-                                                                      0, kOne, 0, sc[b]);
-        else
-          acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[a], fb[b], acc[a][b], 0, 0,
-                                                                      0, kOne, 2, sc[b]);
-      }
-  };
-
-  const int KT = K / F8_BK;
-  gload(0);
-  sstore(0);
-  int sc_cur[4], sc_next[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) sc_cur[b] = (int)(buf_load4(rs_ts, voff_sc[b], 0) >> sc_shift);
+  if (tid <= E) offs[tid] = offsets[tid];
   __syncthreads();
-  i32x8_t fa0[4], fb0[4], fa1[4], fb1[4];
-  read_frags(0, 0, fa0, fb0);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    gload((kt + 1) * F8_BK);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) sc_next[b] = (int)buf_load4(rs_ts, voff_sc[b], (kt + 1) * 4);
-    read_frags(buf, 1, fa1, fb1);
-    mfmas(fa0, fb0, sc_cur, 0);
-    sstore(buf ^ 1);
-    mfmas(fa1, fb1, sc_cur, 1);
-    // step 0: 16 MFMA with 16 global + 4 scale reads and 16 fragment reads
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
-    }
-    // step 1: 16 MFMA with the 16 LDS writes of the next slice
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    __syncthreads();
-    read_frags(buf ^ 1, 0, fa0, fb0);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) sc_cur[b] = sc_next[b] >> sc_shift;
-  }
+  const int KT = K / F8T_BK;                        // even: K is a multiple of 128
+  const int slots = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const TileSplit sp = TileSplit::of(TileSplit::total_tiles(offs, E, n_tiles, F8T_TB), xcd, slots, KT);
+  const int n_items = sp.R + (slot < sp.tail ? 1 : 0);
+  if (n_items == 0) return;
 
-  // ---- epilogue: lane = token (fi), registers = channels ----
+  struct Tile { int e, tok0, tok_rows, ch0; };
+  auto tile_of = [&](int i) __attribute__((always_inline)) -> Tile {
+    int e, r0, r1, mt, nt;
+    locate_tile(offs, E, F8T_TB, n_tiles, sp.share_begin + slot + i * slots, e, r0, r1, mt, nt);
+    {
+      // an expert's tiles in groups of kF8GroupN channel tiles, channel tile
+      // fastest: the tiles an XCD's workgroups run at a time share weight and
+      // token slices in its L2
+      const int mtc = (r1 - r0 + F8T_TB - 1) / F8T_TB;
+      const int l = nt * mtc + mt;
+      const int gi = l / (mtc * kF8GroupN);
+      const int nt0 = gi * kF8GroupN;
+      const int gsz = min(kF8GroupN, n_tiles - nt0);
+      const int idx = l - gi * mtc * kF8GroupN;
+      nt = nt0 + idx % gsz;
+      mt = idx / gsz;
+    }
+    Tile t;
+    t.e = __builtin_amdgcn_readfirstlane(e);
+    t.tok0 = __builtin_amdgcn_readfirstlane(r0 + mt * F8T_TB);
+    t.tok_rows = __builtin_amdgcn_readfirstlane(min(F8T_TB, r1 - t.tok0));
+    t.ch0 = __builtin_amdgcn_readfirstlane(nt * CH_TILE);
+    return t;
+  };
+
+  // ---- global -> LDS loads (as in the bf16 kernel, one byte per element) ----
+  const int64_t rowbytes = K;
+  const int nblk = K / 32;                          // scale bytes per token row
+  auto voff_base = [&]() __attribute__((always_inline)) {
+    const int l = lane_now();
+    const int r = wave * F8T_RPI + l / F8T_CPR;
+    return (int)(r * rowbytes) + (((l % F8T_CPR) ^ key(r)) << 4);
+  };
+  const int vstep = F8T_NW * F8T_RPI * (int)rowbytes;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+  const uint32_t sc_base = (uint32_t)(uintptr_t)&scs[0][0];
+
+  i32x4_t d_tok, d_w0, d_w1, d_sc;
+  int li = 0, lkt = 0;
+  auto load_tile = [&]() __attribute__((always_inline)) {
+    if (li < n_items) {
+      const Tile t = tile_of(li);
+      lkt = 0;
+      d_tok = make_desc(act + (int64_t)t.tok0 * K, t.tok_rows * rowbytes);
+      d_sc = make_desc(act_scale + (int64_t)t.tok0 * nblk, (int64_t)t.tok_rows * nblk);
+      d_w0 = make_desc(wa + ((int64_t)t.e * N + t.ch0) * K, (int64_t)(N - t.ch0) * rowbytes);
+      d_w1 = DUAL ? make_desc(wb + ((int64_t)t.e * N + t.ch0 - F8T_TA / 2) * K,
+                              (int64_t)(N - t.ch0 + F8T_TA / 2) * rowbytes)
+                  : d_w0;
+    }
+  };
+  load_tile();
+  // Load j of the cursor's slice (stream slice ls): JA weight blocks, JB
+  // token blocks, then (wavefronts w < F8T_SCW, even slices) the scale dword
+  // of token row 64 w + lane: the bytes of slices ls and ls + 1.
+  auto dma = [&](int ls, int j, int vb) __attribute__((always_inline)) {
+    const bool live = li < n_items;
+    const int soff = live ? lkt * F8T_BK : F8T_OOB;
+    const uint32_t sb = lds_base + (uint32_t)((ls % NS) * F8T_STAGE);
+    if (j < F8T_JA) {
+      const int blk = F8T_NW * j + wave;
+      const bool w3 = DUAL && blk * F8T_RPI >= F8T_TA / 2;
+      dma_to_lds(w3 ? d_w1 : d_w0, vb + j * vstep, soff, __builtin_amdgcn_readfirstlane(sb + blk * 1024));
+    } else if (j < F8T_JA + F8T_JB) {
+      const int q = j - F8T_JA;
+      dma_to_lds(d_tok, vb + q * vstep, soff,
+                 __builtin_amdgcn_readfirstlane(sb + F8T_OPA + (F8T_NW * q + wave) * 1024));
+    } else if (live && (ls & 1) == 0 && wave < F8T_SCW) {
+      const uint32_t dst = sc_base + (uint32_t)(((ls >> 1) & 1) * F8T_TB * 4 + wave * 256);
+      dma4_to_lds(d_sc, (wave * 64 + lane_now()) * nblk, (lkt >> 1) * 4, __builtin_amdgcn_readfirstlane(dst));
+    }
+  };
+  auto advance_load = [&]() __attribute__((always_inline)) {
+    if (++lkt == KT) {
+      ++li;
+      load_tile();
+    }
+  };
+
+  // ---- fragments (v_mfma_scale_f32_32x32x64_f8f6f4: lane (fi, fg) holds row
+  //      fi, chunk fg in its low and chunk 2 + fg in its high 16 bytes, and
+  //      supplies the scale of block fg of the slice) ----
+  int arow[WA], bfrow[WB];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int tl = wc * 128 + b * 32 + fi;
-    const bool tok_in = tl < tok_rows;
-    const int64_t orow = tok0 + tl;
-    if constexpr (DUAL) {
+  for (int a = 0; a < WA; ++a) {
+    if constexpr (DUAL) arow[a] = (a / HA) * (F8T_TA / 2) + wr * (HA * 32) + (a % HA) * 32;
+    else arow[a] = wr * (WA * 32) + a * 32;
+  }
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int cbase = ch0 + wr * 64 + a * 32;      // one 32-channel quantisation block
-        float hv[16];
-        float amax = 0.f;
+  for (int b = 0; b < WB; ++b) bfrow[b] = wc * (WB * 32) + b * 32;
+  auto read_frag = [&](int g, int f) __attribute__((always_inline)) -> i32x8_t {
+    const int l = lane_now(), fi = l & 31, fg = l >> 5;
+    const int row = f < WA ? arow[f] + fi : bfrow[f - WA] + fi;
+    const int base = (g % NS) * F8T_STAGE + (f < WA ? 0 : F8T_OPA) + row * F8T_BK;
+    const uint4 lo = *reinterpret_cast<const uint4*>(&smem[base + ((fg ^ key(fi)) << 4)]);
+    const uint4 hi = *reinterpret_cast<const uint4*>(&smem[base + (((2 + fg) ^ key(fi)) << 4)]);
+    return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  // the E8M0 byte of this lane's token row and block for slice g, in the low byte
+  auto read_scale = [&](int g, int b) __attribute__((always_inline)) -> int {
+    const int l = lane_now(), fi = l & 31, fg = l >> 5;
+    const uint32_t w = scs[(g >> 1) & 1][bfrow[b] + fi];
+    return (int)(w >> (8 * ((g & 1) * 2 + fg)));
+  };
+
+  f32x16_t acc[WA][WB];
+  i32x8_t fa[2], fb[WB];
+  int sc[WB];
+
+  // Half h of slice g: weight blocks a = 3 h .. 3 h + 2 against both token
+  // blocks.  Before the instructions of block a, block a + 1's fragment is
+  // read into the other buffer.  With `loads`, the six loads of stream slice
+  // ls ride along; with `reads` (second half), the next slice gn's token
+  // fragments, scales and first weight fragment are read after their last use.
+  auto half = [&](int h, int g, bool loads, int ls, bool reads, int gn) __attribute__((always_inline)) {
+    const int vb = loads ? voff_base() : 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = cbase + q * 8 + fg * 4;
-          const bool cin = c < N;
-          const float4 s1 = cin ? *reinterpret_cast<const float4*>(sa + (int64_t)e * N + c) : make_float4(0, 0, 0, 0);
-          const float4 s3 = cin ? *reinterpret_cast<const float4*>(sb + (int64_t)e * N + c) : make_float4(0, 0, 0, 0);
-          const float w1s[4] = {s1.x, s1.y, s1.z, s1.w}, w3s[4] = {s3.x, s3.y, s3.z, s3.w};
+    for (int ai = 0; ai < 3; ++ai) {
+      const int a = 3 * h + ai;
+      if (a + 1 < WA) fa[(a + 1) & 1] = read_frag(g, a + 1);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float v = swiglu_fast(acc[a][b][q * 4 + r] * w1s[r], acc[a + 2][b][q * 4 + r] * w3s[r]);
-            hv[q * 4 + r] = v;
-            amax = fmaxf(amax, fabsf(v));
-          }
+      for (int b = 0; b < WB; ++b) {
+        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[a & 1], fb[b], acc[a][b], 0, 0, 0,
+                                                                     kOne, 0, sc[b]);
+        if (loads && ai * WB + b <= F8T_DMA) dma(ls, ai * WB + b, vb);
+        if (reads && a == WA - 1) {
+          fb[b] = read_frag(gn, WA + b);
+          sc[b] = read_scale(gn, b);
         }
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const int ex = block_exponent(amax);
-        const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);
-        if (tok_in && cbase < N) {
-          uint8_t* hrow = static_cast<uint8_t*>(out) + orow * N;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (reads) fa[0] = read_frag(gn, 0);
+  };
+
+  // One slice: the first half with the loads of slice g + NS - 1 (into the
+  // stage slice g - 1 used); wait for this wavefront's loads of slice g + 1,
+  // finish its LDS reads, barrier; the second half.
+  auto iteration = [&](int g, bool last) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    half(0, g, true, g + NS - 1, false, 0);
+    advance_load();
+    wait_vmcnt<F8T_DMA * (NS - 2)>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    half(1, g, false, 0, !last, g + 1);
+  };
+
+  // Results: lane = token (fi), registers = channels; stores through
+  // descriptors bounded to the tile's rows, columns past N get an offset
+  // beyond them.
+  auto epilogue = [&](const Tile& t) __attribute__((always_inline)) {
+    int fi = lane & 31, fg = lane >> 5;
+    asm volatile("" : "+v"(fi), "+v"(fg));
+    if constexpr (DUAL) {
+      const i32x4_t ro = make_desc(static_cast<uint8_t*>(out) + (int64_t)t.tok0 * N, (int64_t)t.tok_rows * N);
+      const i32x4_t rs = make_desc(out_scale + (int64_t)t.tok0 * (N / 32), (int64_t)t.tok_rows * (N / 32));
+#pragma unroll
+      for (int b = 0; b < WB; ++b) {
+        const int tl = wc * (WB * 32) + b * 32 + fi;
+#pragma unroll
+        for (int a = 0; a < HA; ++a) {
+          const int cbase = t.ch0 + wr * (HA * 32) + a * 32;      // one 32-channel quantisation block
+          const bool cin = cbase < N;
+          float hv[16];
+          float amax = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = cin ? cbase + q * 8 + fg * 4 : 0;
+            const float4 s1 = *reinterpret_cast<const float4*>(sa + (int64_t)t.e * N + c);
+            const float4 s3 = *reinterpret_cast<const float4*>(sb + (int64_t)t.e * N + c);
+            const float w1s[4] = {s1.x, s1.y, s1.z, s1.w}, w3s[4] = {s3.x, s3.y, s3.z, s3.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float v = swiglu_fast(acc[a][b][q * 4 + r] * w1s[r], acc[a + HA][b][q * 4 + r] * w3s[r]);
+              hv[q * 4 + r] = v;
+              amax = fmaxf(amax, fabsf(v));
+            }
+          }
+          amax = fmaxf(amax, __shfl_xor(amax, 32));   // the block's other 16 channels
+          const int ex = block_exponent(amax);
+          const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             int packed = 0;
             packed = __builtin_amdgcn_cvt_pk_fp8_f32(hv[q * 4 + 0] * inv, hv[q * 4 + 1] * inv, packed, false);
             packed = __builtin_amdgcn_cvt_pk_fp8_f32(hv[q * 4 + 2] * inv, hv[q * 4 + 3] * inv, packed, true);
-            *reinterpret_cast<int*>(hrow + cbase + q * 8 + fg * 4) = packed;
+            store_b32(ro, cin ? tl * N + cbase + q * 8 + fg * 4 : 0x7fffffff, (uint32_t)packed);
           }
-          if (fg == 0) out_scale[orow * (N / 32) + cbase / 32] = (uint8_t)(ex + 127);
+          store_b8(rs, (cin && fg == 0) ? tl * (N / 32) + cbase / 32 : 0x7fffffff, (uint32_t)(ex + 127));
+          __builtin_amdgcn_sched_barrier(0);
+          acc[a][b] = acc[a + HA][b] = f32x16_t{};   // the next tile starts from zero
         }
       }
     } else {
+      const i32x4_t ro = make_desc(static_cast<float*>(out) + (int64_t)t.tok0 * N, (int64_t)t.tok_rows * N * 4);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int b = 0; b < WB; ++b) {
+        const int tl = wc * (WB * 32) + b * 32 + fi;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = ch0 + wr * 128 + a * 32 + q * 8 + fg * 4;
-          if (tok_in && c < N) {
-            const float4 s2 = *reinterpret_cast<const float4*>(sa + (int64_t)e * N + c);
-            *reinterpret_cast<float4*>(static_cast<float*>(out) + orow * N + c) =
-                make_float4(acc[a][b][q * 4 + 0] * s2.x, acc[a][b][q * 4 + 1] * s2.y,
-                            acc[a][b][q * 4 + 2] * s2.z, acc[a][b][q * 4 + 3] * s2.w);
+        for (int a = 0; a < WA; ++a)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = t.ch0 + wr * (WA * 32) + a * 32 + q * 8 + fg * 4;
+            const bool cin = c < N;
+            const float4 s2 = *reinterpret_cast<const float4*>(sa + (int64_t)t.e * N + (cin ? c : 0));
+            const u32x4_t v = {__float_as_uint(acc[a][b][q * 4 + 0] * s2.x), __float_as_uint(acc[a][b][q * 4 + 1] * s2.y),
+                               __float_as_uint(acc[a][b][q * 4 + 2] * s2.z), __float_as_uint(acc[a][b][q * 4 + 3] * s2.w)};
+            store_b128(ro, cin ? (tl * N + c) * 4 : 0x7fffffff, v);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q == 3) acc[a][b] = f32x16_t{};
           }
-        }
+      }
     }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) {
+    const int vb = voff_base();
+#pragma unroll
+    for (int j = 0; j <= F8T_DMA; ++j) dma(s, j, vb);
+    advance_load();
   }
+  wait_vmcnt<F8T_DMA * (NS - 2)>();
+  __builtin_amdgcn_s_barrier();
+
+#pragma unroll
+  for (int a = 0; a < WA; ++a)
+#pragma unroll
+    for (int b = 0; b < WB; ++b) acc[a][b] = f32x16_t{};
+  int g = 0;                      // stream index of the slice being multiplied
+  for (int ci = 0; ci < n_items; ++ci) {
+    const Tile t = tile_of(ci);
+    fa[0] = read_frag(g, 0);
+#pragma unroll
+    for (int b = 0; b < WB; ++b) {
+      fb[b] = read_frag(g, WA + b);
+      sc[b] = read_scale(g, b);
+    }
+    for (int kt = 0; kt < KT - 1; ++kt) iteration(g++, false);
+    iteration(g++, true);
+    epilogue(t);
+  }
+  wait_vmcnt<0>();   // the loads past the end land before the workgroup's LDS is released
 }
 
 template <bool DUAL>
-hipError_t launch_fp8(const moe_shape_t& s, const uint8_t* act, const uint8_t* act_scale,
-                      const int32_t* offsets, const uint8_t* wa, const uint8_t* wb, const float* sa,
-                      const float* sb, int N, int K, void* out, uint8_t* out_scale, hipStream_t st) {
-  constexpr int CH_TILE = DUAL ? 128 : 256;
+hipError_t launch_fp8_tiles(const moe_shape_t& s, const uint8_t* act, const uint8_t* act_scale,
+                            const int32_t* offsets, const uint8_t* wa, const uint8_t* wb,
+                            const float* sa, const float* sb, int N, int K, void* out,
+                            uint8_t* out_scale, hipStream_t st) {
+  constexpr int CH_TILE = DUAL ? F8T_TA / 2 : F8T_TA;
   const int n_tiles = (N + CH_TILE - 1) / CH_TILE;
-  const int64_t grid = max_token_tiles(s, F8_ROWS) * n_tiles;
-  const int64_t padded = (grid + 7) / 8 * 8;
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_gemm_fp8_prefill<DUAL>, dim3((unsigned)padded), dim3(F8_THREADS), 0,
-                     st, act, act_scale, offsets, expert_groups(s), wa, wb, sa, sb, N, K, out,
-                     out_scale, n_tiles, (int)padded);
+  const int64_t max_tiles = max_token_tiles(s, F8T_TB) * n_tiles;
+  if (max_tiles <= 0) return hipSuccess;
+  const int64_t grid = persistent_grid(max_tiles);
+  hipLaunchKernelGGL(grouped_gemm_fp8_tiles<DUAL>, dim3((unsigned)grid), dim3(F8T_THREADS), 0, st, act,
+                     act_scale, offsets, expert_groups(s), wa, wb, sa, sb, N, K, out, out_scale, n_tiles);
   return hipGetLastError();
 }
 
@@ -320,15 +383,15 @@ hipError_t launch_gate_up_fp8(const moe_shape_t& s, const uint8_t* x_perm, const
                               const int32_t* offsets, const uint8_t* w1, const uint8_t* w3,
                               const float* w1_scale, const float* w3_scale, uint8_t* h,
                               uint8_t* h_scale, hipStream_t st) {
-  return launch_fp8<true>(s, x_perm, x_scale, offsets, w1, w3, w1_scale, w3_scale, s.d_ff,
-                          s.d_model, h, h_scale, st);
+  return launch_fp8_tiles<true>(s, x_perm, x_scale, offsets, w1, w3, w1_scale, w3_scale, s.d_ff,
+                                s.d_model, h, h_scale, st);
 }
 
 hipError_t launch_down_fp8(const moe_shape_t& s, const uint8_t* h, const uint8_t* h_scale,
                            const int32_t* offsets, const uint8_t* w2, const float* w2_scale,
                            float* y_perm, hipStream_t st) {
-  return launch_fp8<false>(s, h, h_scale, offsets, w2, nullptr, w2_scale, nullptr, s.d_model,
-                           s.d_ff, y_perm, nullptr, st);
+  return launch_fp8_tiles<false>(s, h, h_scale, offsets, w2, nullptr, w2_scale, nullptr, s.d_model,
+                                 s.d_ff, y_perm, nullptr, st);
 }
 
 }  // namespace moe
