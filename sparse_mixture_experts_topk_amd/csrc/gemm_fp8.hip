@@ -49,12 +49,14 @@ __device__ __forceinline__ int block_exponent(float amax) {
 // bf16 kernel and is filled the same way, by buffer loads that write LDS
 // directly, two slices in flight while one is multiplied.  One
 // v_mfma_scale_f32_32x32x64_f8f6f4 per block pair covers a slice.  The token
-// operand's E8M0 scales come as dwords (four bytes per token row = the two
-// blocks of two consecutive slices) by the same kind of load into a two-slot
-// LDS ring: wavefronts 0..3 issue one on every even slice.  The wait for a
-// slice allows the five weight and token loads of the slice after it to be
-// pending; when that slice also carries a scale load the wait is one load
-// stricter than needed, never looser.  Each wavefront owns 6 x 2 accumulator blocks (192 fp32 per lane);
+// operand's E8M0 scales (one byte per row and 32-element block) come by the
+// same kind of load, 64 bytes of every token row at once -- the scales of 32
+// slices -- into one of two LDS slots, at the first slice of each group of
+// 32: lanes run along a row so that a dword load touches 4 rows, not 64
+// (the scale loads of a row-per-lane layout made the tile's load requests
+// 1.4x as many).  The wait for a slice allows the five weight and token loads
+// of the slice after it to be pending; when that slice also carries scale
+// loads the wait is stricter than needed, never looser.  Each wavefront owns 6 x 2 accumulator blocks (192 fp32 per lane);
 // a slice's 12 matrix instructions run in two halves of 3 weight blocks:
 // the first carries the slice loads, the second follows the wait and the
 // barrier and reads the next slice's first fragments.  Weight fragments are
@@ -74,7 +76,8 @@ constexpr int F8T_JB = F8T_TB / F8T_RPI / F8T_NW;   // token loads per wavefront
 constexpr int F8T_DMA = F8T_JA + F8T_JB;            // weight and token loads per slice
 constexpr int F8T_OPA = F8T_TA * F8T_BK;
 constexpr int F8T_STAGE = (F8T_TA + F8T_TB) * F8T_BK;
-constexpr int F8T_SCW = F8T_TB / 64;                // wavefronts that load scales
+constexpr int F8T_SCG = 32;                         // slices per scale group (64 bytes per row)
+constexpr int F8T_SCQ = F8T_TB / 4 / F8T_NW;        // scale loads per wavefront per group (4 rows each)
 constexpr int F8T_SLOTS = 3 * F8T_WB;               // load slots of a slice (the first half's instructions)
 constexpr int F8T_OOB = 0x7ff00000;                 // offset past every descriptor
 constexpr int kF8GroupN = 8;                        // channel tiles per group of the tile order
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
     const uint8_t* __restrict__ wb, const float* __restrict__ sa, const float* __restrict__ sb,
     int N, int K, void* __restrict__ out, uint8_t* __restrict__ out_scale, int n_tiles) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[F8T_NS * F8T_STAGE];
-  __shared__ __attribute__((aligned(1024))) uint32_t scs[2][F8T_TB];   // scale slots of slice pairs
+  __shared__ __attribute__((aligned(1024))) uint32_t scs[2][F8T_TB * 16];   // [slot][row][16 dwords]
   __shared__ int32_t offs[kMaxExpertGroups + 1];
   constexpr int WA = F8T_WA, WB = F8T_WB, NS = F8T_NS;
   constexpr int HA = WA / 2;                        // dual: w1 (or w3) blocks per wavefront
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
   const uint32_t sc_base = (uint32_t)(uintptr_t)&scs[0][0];
 
   i32x4_t d_tok, d_w0, d_w1, d_sc;
-  int li = 0, lkt = 0;
+  int li = 0, lkt = 0, lgrp = 0;                   // lgrp: scale groups loaded so far
   auto load_tile = [&]() __attribute__((always_inline)) {
     if (li < n_items) {
       const Tile t = tile_of(li);
@@ -168,8 +171,9 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
   };
   load_tile();
   // Load j of the cursor's slice (stream slice ls): JA weight blocks, JB
-  // token blocks, then (wavefronts w < F8T_SCW, even slices) the scale dword
-  // of token row 64 w + lane: the bytes of slices ls and ls + 1.
+  // token blocks, then, at the first slice of a scale group, this
+  // wavefront's F8T_SCQ scale loads (load q: rows 4 q .. 4 q + 3, lane l
+  // the dword l % 16 of row 4 q + l / 16).
   auto dma = [&](int ls, int j, int vb) __attribute__((always_inline)) {
     const bool live = li < n_items;
     const int soff = live ? lkt * F8T_BK : F8T_OOB;
@@ -182,9 +186,16 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
       const int q = j - F8T_JA;
       dma_to_lds(d_tok, vb + q * vstep, soff,
                  __builtin_amdgcn_readfirstlane(sb + F8T_OPA + (F8T_NW * q + wave) * 1024));
-    } else if (live && (ls & 1) == 0 && wave < F8T_SCW) {
-      const uint32_t dst = sc_base + (uint32_t)(((ls >> 1) & 1) * F8T_TB * 4 + wave * 256);
-      dma4_to_lds(d_sc, (wave * 64 + lane_now()) * nblk, (lkt >> 1) * 4, __builtin_amdgcn_readfirstlane(dst));
+    } else if (live && lkt % F8T_SCG == 0) {
+      const uint32_t slot = sc_base + (uint32_t)((lgrp & 1) * F8T_TB * 64);
+      const int l = lane_now();
+#pragma unroll
+      for (int i = 0; i < F8T_SCQ; ++i) {
+        const int q = wave * F8T_SCQ + i;
+        dma4_to_lds(d_sc, (4 * q + l / 16) * nblk + (l % 16) * 4, (lkt / F8T_SCG) * 64,
+                    __builtin_amdgcn_readfirstlane(slot + q * 256));
+      }
+      ++lgrp;
     }
   };
   auto advance_load = [&]() __attribute__((always_inline)) {
@@ -213,11 +224,19 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
     const uint4 hi = *reinterpret_cast<const uint4*>(&smem[base + (((2 + fg) ^ key(fi)) << 4)]);
     return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
-  // the E8M0 byte of this lane's token row and block for slice g, in the low byte
-  auto read_scale = [&](int g, int b) __attribute__((always_inline)) -> int {
+  // The E8M0 byte of this lane's token row and block for tile slice kt (scale
+  // slot cs), in the low byte.
+  int cgrp = 0;                                     // scale groups read so far
+  auto read_scale = [&](int cs, int kt, int b) __attribute__((always_inline)) -> int {
     const int l = lane_now(), fi = l & 31, fg = l >> 5;
-    const uint32_t w = scs[(g >> 1) & 1][bfrow[b] + fi];
-    return (int)(w >> (8 * ((g & 1) * 2 + fg)));
+    const uint32_t w = scs[cs][(bfrow[b] + fi) * 16 + (kt % F8T_SCG) / 2];
+    return (int)(w >> (8 * ((kt & 1) * 2 + fg)));
+  };
+  // slot of tile slice kt's scales (a new group starts every F8T_SCG slices)
+  int cslot = 0;
+  auto scale_slot = [&](int kt) __attribute__((always_inline)) {
+    if (kt % F8T_SCG == 0) cslot = cgrp++ & 1;
+    return cslot;
   };
 
   f32x16_t acc[WA][WB];
@@ -229,7 +248,8 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
   // read into the other buffer.  With `loads`, the six loads of stream slice
   // ls ride along; with `reads` (second half), the next slice gn's token
   // fragments, scales and first weight fragment are read after their last use.
-  auto half = [&](int h, int g, bool loads, int ls, bool reads, int gn) __attribute__((always_inline)) {
+  auto half = [&](int h, int g, bool loads, int ls, bool reads, int gn, int ktn) __attribute__((always_inline)) {
+    const int cs = reads ? scale_slot(ktn) : 0;
     const int vb = loads ? voff_base() : 0;
 #pragma unroll
     for (int ai = 0; ai < 3; ++ai) {
@@ -242,7 +262,7 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
         if (loads && ai * WB + b <= F8T_DMA) dma(ls, ai * WB + b, vb);
         if (reads && a == WA - 1) {
           fb[b] = read_frag(gn, WA + b);
-          sc[b] = read_scale(gn, b);
+          sc[b] = read_scale(cs, ktn, b);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -253,15 +273,15 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
   // One slice: the first half with the loads of slice g + NS - 1 (into the
   // stage slice g - 1 used); wait for this wavefront's loads of slice g + 1,
   // finish its LDS reads, barrier; the second half.
-  auto iteration = [&](int g, bool last) __attribute__((always_inline)) {
+  auto iteration = [&](int g, int kt, bool last) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    half(0, g, true, g + NS - 1, false, 0);
+    half(0, g, true, g + NS - 1, false, 0, 0);
     advance_load();
     wait_vmcnt<F8T_DMA * (NS - 2)>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    half(1, g, false, 0, !last, g + 1);
+    half(1, g, false, 0, !last, g + 1, kt + 1);
   };
 
   // Results: lane = token (fi), registers = channels; stores through
@@ -350,13 +370,14 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
   for (int ci = 0; ci < n_items; ++ci) {
     const Tile t = tile_of(ci);
     fa[0] = read_frag(g, 0);
+    const int cs = scale_slot(0);
 #pragma unroll
     for (int b = 0; b < WB; ++b) {
       fb[b] = read_frag(g, WA + b);
-      sc[b] = read_scale(g, b);
+      sc[b] = read_scale(cs, 0, b);
     }
-    for (int kt = 0; kt < KT - 1; ++kt) iteration(g++, false);
-    iteration(g++, true);
+    for (int kt = 0; kt < KT - 1; ++kt) iteration(g++, kt, false);
+    iteration(g++, KT - 1, true);
     epilogue(t);
   }
   wait_vmcnt<0>();   // the loads past the end land before the workgroup's LDS is released
