@@ -98,6 +98,7 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
   static_assert(!DUAL || (G::TA / 2) % 16 == 0, "w3 rows start on a swizzle period");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * G::STAGE_BYTES];
   __shared__ int32_t offs[kMaxExpertGroups + 1];
+  __shared__ int32_t tpre[kMaxExpertGroups + 1];
 
   constexpr int HA = WA / 2;                 // dual: w1 (or w3) blocks per wavefront
   constexpr int CH_TILE = DUAL ? G::TA / 2 : G::TA;
@@ -116,15 +117,17 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
     return l;
   };
 
-  // Expert offsets go to LDS once, so that locating a tile in the middle of
-  // the load stream issues no vector-memory read (the stream's waits count
-  // its own loads).
+  // Expert offsets and their token-tile prefix go to LDS once, so that
+  // locating a tile in the middle of the load stream issues no vector-memory
+  // read (the stream's waits count its own loads).
   if (tid <= E) offs[tid] = offsets[tid];
+  __syncthreads();
+  if (wave == 0) build_tile_prefix(offs, E, PF_ROWS, tpre, lane);
   __syncthreads();
   const int KT = K / BK;
   const int slots = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const TileSplit sp = TileSplit::of(TileSplit::total_tiles(offs, E, n_tiles, PF_ROWS), xcd, slots, KT);
+  const TileSplit sp = TileSplit::of(__builtin_amdgcn_readfirstlane(tpre[E]) * n_tiles, xcd, slots, KT);
   // this workgroup's items: whole tiles, then (split) up to two K-runs of tail tiles
   const int n_whole = sp.R + ((!SPLIT && slot < sp.tail) ? 1 : 0);
   const int run0 = slot * sp.P, run1 = min(run0 + sp.P, sp.tail * KT);
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
       part = (int)blockIdx.x * 2 + (i - n_whole);
     }
     int e, r0, r1, mt, nt;
-    locate_tile(offs, E, PF_ROWS, n_tiles, t_idx, e, r0, r1, mt, nt);
+    find_tile(offs, tpre, E, n_tiles, t_idx, e, r0, r1, mt, nt);
     Tile t;   // uniform values, kept in scalar registers
     t.e = __builtin_amdgcn_readfirstlane(e);
     t.tok0 = __builtin_amdgcn_readfirstlane(r0 + mt * PF_ROWS);
@@ -405,13 +408,19 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(const int32_t* __restr
                                                           const float* __restrict__ partials,
                                                           float* __restrict__ y) {
   constexpr int CPL = CH / 64;
+  __shared__ int32_t offs[kMaxExpertGroups + 1];
+  __shared__ int32_t tpre[kMaxExpertGroups + 1];
+  for (int i = threadIdx.x; i <= E; i += 256) offs[i] = offsets[i];
+  __syncthreads();
+  if (threadIdx.x < 64) build_tile_prefix(offs, E, PF_ROWS, tpre, threadIdx.x);
+  __syncthreads();
   const int rg = blockIdx.x % kFixupRowGroups;
   const int xcd = (blockIdx.x / kFixupRowGroups) & 7, j = blockIdx.x / kFixupRowGroups >> 3;
   const int KT = K / BK;
-  const TileSplit sp = TileSplit::of(TileSplit::total_tiles(offsets, E, n_tiles, PF_ROWS), xcd, slots, KT);
+  const TileSplit sp = TileSplit::of(__builtin_amdgcn_readfirstlane(tpre[E]) * n_tiles, xcd, slots, KT);
   if (j >= sp.tail) return;
   int e, r0, r1, mt, nt;
-  locate_tile(offsets, E, PF_ROWS, n_tiles, sp.share_begin + sp.R * slots + j, e, r0, r1, mt, nt);
+  find_tile(offs, tpre, E, n_tiles, sp.share_begin + sp.R * slots + j, e, r0, r1, mt, nt);
   const int tok0 = r0 + mt * PF_ROWS, tok_rows = min(PF_ROWS, r1 - tok0), ch0 = nt * CH;
   const int r = rg * 16 + (threadIdx.x >> 4);
   if (r >= tok_rows) return;

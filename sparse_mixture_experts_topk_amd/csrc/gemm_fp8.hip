@@ -94,6 +94,7 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
   __shared__ __attribute__((aligned(1024))) uint8_t smem[F8T_NS * F8T_STAGE];
   __shared__ __attribute__((aligned(1024))) uint32_t scs[2][F8T_TB * 16];   // [slot][row][16 dwords]
   __shared__ int32_t offs[kMaxExpertGroups + 1];
+  __shared__ int32_t tpre[kMaxExpertGroups + 1];
   constexpr int WA = F8T_WA, WB = F8T_WB, NS = F8T_NS;
   constexpr int HA = WA / 2;                        // dual: w1 (or w3) blocks per wavefront
   constexpr int CH_TILE = DUAL ? F8T_TA / 2 : F8T_TA;
@@ -111,17 +112,19 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
 
   if (tid <= E) offs[tid] = offsets[tid];
   __syncthreads();
+  if (wave == 0) build_tile_prefix(offs, E, F8T_TB, tpre, lane);
+  __syncthreads();
   const int KT = K / F8T_BK;                        // even: K is a multiple of 128
   const int slots = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const TileSplit sp = TileSplit::of(TileSplit::total_tiles(offs, E, n_tiles, F8T_TB), xcd, slots, KT);
+  const TileSplit sp = TileSplit::of(__builtin_amdgcn_readfirstlane(tpre[E]) * n_tiles, xcd, slots, KT);
   const int n_items = sp.R + (slot < sp.tail ? 1 : 0);
   if (n_items == 0) return;
 
   struct Tile { int e, tok0, tok_rows, ch0; };
   auto tile_of = [&](int i) __attribute__((always_inline)) -> Tile {
     int e, r0, r1, mt, nt;
-    locate_tile(offs, E, F8T_TB, n_tiles, sp.share_begin + slot + i * slots, e, r0, r1, mt, nt);
+    find_tile(offs, tpre, E, n_tiles, sp.share_begin + slot + i * slots, e, r0, r1, mt, nt);
     {
       // an expert's tiles in groups of kF8GroupN channel tiles, channel tile
       // fastest: the tiles an XCD's workgroups run at a time share weight and

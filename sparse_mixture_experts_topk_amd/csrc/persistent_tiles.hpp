@@ -17,14 +17,6 @@ namespace moe {
 struct TileSplit {
   int share_begin, R, tail, P;
 
-  // Tiles of `rows` tokens x n_tiles channel tiles over every expert group.
-  __device__ static int total_tiles(const int32_t* offs, int E, int n_tiles, int rows) {
-    int total = 0;
-    for (int e = 0; e < E; ++e)
-      total += (__builtin_amdgcn_readfirstlane(offs[e + 1]) -
-                __builtin_amdgcn_readfirstlane(offs[e]) + rows - 1) / rows;
-    return total * n_tiles;
-  }
   __device__ static TileSplit of(int total, int xcd, int slots, int KT) {
     TileSplit t;
     const int per_xcd = (total + 7) >> 3;
@@ -36,6 +28,51 @@ struct TileSplit {
     return t;
   }
 };
+
+// Cumulative token tiles of the expert groups: pre[e] = the sum over e' < e
+// of ceil(rows of e' / rows_per_tile), for e = 0 .. E (so pre[E] is the
+// number of token tiles).  Built in LDS from the group offsets (in LDS) by
+// one wavefront, 64 groups per step with a wavefront prefix sum; the caller
+// synchronises before reading it.
+__device__ inline void build_tile_prefix(const int32_t* offs, int E, int rows_per_tile, int32_t* pre,
+                                         int lane) {
+  int carry = 0;
+  for (int base = 0; base <= E; base += 64) {
+    const int e = base + lane;
+    const int m = e < E ? (offs[e + 1] - offs[e] + rows_per_tile - 1) / rows_per_tile : 0;
+    int v = m;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int u = __shfl_up(v, d);
+      if (lane >= d) v += u;
+    }
+    if (e <= E) pre[e] = carry + v - m;
+    carry += __shfl(v, 63);
+  }
+}
+
+// Tile t of the expert-major tile list (token tiles fastest, n_tiles channel
+// tiles per token tile), t < pre[E] * n_tiles: its group e (a binary search
+// of the prefix for the last group whose first tile is <= t, which is never
+// empty), the group's rows [r0, r1), and its token tile m and channel tile n.
+// Every argument and result is uniform.
+__device__ inline void find_tile(const int32_t* offs, const int32_t* pre, int E, int n_tiles, int t, int& e,
+                                 int& r0, int& r1, int& m, int& n) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (__builtin_amdgcn_readfirstlane(pre[mid]) * n_tiles <= t) lo = mid;
+    else hi = mid;
+  }
+  e = lo;
+  const int p0 = __builtin_amdgcn_readfirstlane(pre[lo]);
+  const int mt = __builtin_amdgcn_readfirstlane(pre[lo + 1]) - p0;
+  const int l = t - p0 * n_tiles;
+  r0 = __builtin_amdgcn_readfirstlane(offs[lo]);
+  r1 = __builtin_amdgcn_readfirstlane(offs[lo + 1]);
+  m = l % mt;
+  n = l / mt;
+}
 
 constexpr int kMaxPersistentGroups = 256;
 
