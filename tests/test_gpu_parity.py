@@ -610,3 +610,38 @@ def test_finegrained_prefill_config_sampled():
     base = oracle.forward(inp, tokens=[])
     toks = sample_tokens(base, n_random=12, edge_groups=12)
     run_staged_and_check(cfg, inputs=inp, tokens=toks, check_h=True)
+
+
+def sweep_cfg(seed):
+    """A seeded random shape of the whole layer: expert count, top-k, shared expert, batch (the
+    weight-streaming and the tiled paths), widths, capacity and overflow, and weight dtype, drawn
+    within what the library supports."""
+    rng = np.random.default_rng(1000 + seed)
+    E = int(rng.choice([2, 3, 8, 13, 40, 64, 65, 100, 256]))
+    k = int(rng.integers(1, min(8, E) + 1))
+    S = int(rng.integers(0, 2))
+    w = str(rng.choice(["bf16", "bf16", "fp8_e4m3", "mxfp4"]))
+    unit = {"bf16": 64, "fp8_e4m3": 128, "mxfp4": 256}[w]
+    d = unit * int(rng.integers(1, 512 // unit + 1))
+    F = unit * int(rng.integers(1, max(1, 448 // unit) + 1))
+    T = int(rng.choice([1, 7, 33, 64] if w == "mxfp4" else [1, 7, 33, 64, 200, 700, 1100]))
+    cap, overflow = -1, "drop"
+    if rng.random() < 0.4:
+        cap = int(rng.integers(0, 2 * T * k // E + 2))
+        if k == 2 and rng.random() < 0.5:
+            overflow = "next_best"
+    return synthetic.MoEConfig(name=f"sweep{seed}", T=T, d_model=d, d_ff=F, n_experts=E, top_k=k,
+                               n_shared=S, capacity=cap, overflow=overflow, act_dtype="bf16",
+                               w_dtype=w, x_std=1.0, wg_std=d ** -0.5, w13_std=0.05, w2_std=0.05,
+                               seed=2000 + seed)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shape_sweep(seed):
+    cfg = sweep_cfg(seed)
+    st, res, _ = run_staged_and_check(cfg)
+    # the staged path and the fused call agree bit for bit on the same shape
+    di = runner.DeviceInputs.from_host(synthetic.make_inputs(cfg))
+    y = runner.forward(di).y
+    torch.cuda.synchronize()
+    assert torch.equal(y, st["y"]), "fused forward differs from the staged calls"
