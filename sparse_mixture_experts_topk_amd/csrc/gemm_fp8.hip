@@ -56,12 +56,14 @@ __device__ __forceinline__ int block_exponent(float amax) {
 // (the scale loads of a row-per-lane layout made the tile's load requests
 // 1.4x as many).  The wait for a slice allows the five weight and token loads
 // of the slice after it to be pending; when that slice also carries scale
-// loads the wait is stricter than needed, never looser.  Each wavefront owns 6 x 2 accumulator blocks (192 fp32 per lane);
-// a slice's 12 matrix instructions run in two halves of 3 weight blocks:
-// the first carries the slice loads, the second follows the wait and the
-// barrier and reads the next slice's first fragments.  Weight fragments are
-// double-buffered one block ahead.  Tiles are scheduled as in the bf16
-// kernel (persistent workgroups, one load stream across tiles).
+// loads (or, in a tile's first slice, its weight scales) the wait is
+// stricter than needed, never looser.  Each wavefront owns 6 x 2
+// accumulator blocks (192 fp32 per lane); a slice's 12 matrix instructions
+// run in two halves of 3 weight blocks: the first carries the slice loads,
+// the second follows the wait and the barrier and reads the next slice's
+// first fragments.  Weight fragments are double-buffered one block ahead.
+// Tiles are scheduled as in the bf16 kernel (persistent workgroups, one load
+// stream across tiles).
 constexpr int F8T_BK = 64;                          // K (bytes) per slice
 constexpr int F8T_NS = 3;                           // LDS ring stages
 constexpr int F8T_WR = 2, F8T_WC = 4, F8T_WA = 6, F8T_WB = 2;
@@ -95,6 +97,9 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
   __shared__ __attribute__((aligned(1024))) uint32_t scs[2][F8T_TB * 16];   // [slot][row][16 dwords]
   __shared__ int32_t offs[kMaxExpertGroups + 1];
   __shared__ int32_t tpre[kMaxExpertGroups + 1];
+  // per-channel weight scales of the tile (gate/up: 192 of w1, then the same
+  // 192 of w3), one slot per tile in a ring of 3
+  __shared__ __attribute__((aligned(16))) float wsc[3][F8T_TA];
   constexpr int WA = F8T_WA, WB = F8T_WB, NS = F8T_NS;
   constexpr int HA = WA / 2;                        // dual: w1 (or w3) blocks per wavefront
   constexpr int CH_TILE = DUAL ? F8T_TA / 2 : F8T_TA;
@@ -157,6 +162,7 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
   const int vstep = F8T_NW * F8T_RPI * (int)rowbytes;
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
   const uint32_t sc_base = (uint32_t)(uintptr_t)&scs[0][0];
+  const uint32_t wsc_base = (uint32_t)(uintptr_t)&wsc[0][0];
 
   i32x4_t d_tok, d_w0, d_w1, d_sc;
   int li = 0, lkt = 0, lgrp = 0;                   // lgrp: scale groups loaded so far
@@ -180,25 +186,39 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
   auto dma = [&](int ls, int j, int vb) __attribute__((always_inline)) {
     const bool live = li < n_items;
     const int soff = live ? lkt * F8T_BK : F8T_OOB;
-    const uint32_t sb = lds_base + (uint32_t)((ls % NS) * F8T_STAGE);
+    const uint32_t stg = lds_base + (uint32_t)((ls % NS) * F8T_STAGE);
     if (j < F8T_JA) {
       const int blk = F8T_NW * j + wave;
       const bool w3 = DUAL && blk * F8T_RPI >= F8T_TA / 2;
-      dma_to_lds(w3 ? d_w1 : d_w0, vb + j * vstep, soff, __builtin_amdgcn_readfirstlane(sb + blk * 1024));
+      dma_to_lds(w3 ? d_w1 : d_w0, vb + j * vstep, soff, __builtin_amdgcn_readfirstlane(stg + blk * 1024));
     } else if (j < F8T_JA + F8T_JB) {
       const int q = j - F8T_JA;
       dma_to_lds(d_tok, vb + q * vstep, soff,
-                 __builtin_amdgcn_readfirstlane(sb + F8T_OPA + (F8T_NW * q + wave) * 1024));
-    } else if (live && lkt % F8T_SCG == 0) {
-      const uint32_t slot = sc_base + (uint32_t)((lgrp & 1) * F8T_TB * 64);
-      const int l = lane_now();
+                 __builtin_amdgcn_readfirstlane(stg + F8T_OPA + (F8T_NW * q + wave) * 1024));
+    } else {
+      if (live && lkt % F8T_SCG == 0) {
+        const uint32_t slot = sc_base + (uint32_t)((lgrp & 1) * F8T_TB * 64);
+        const int l = lane_now();
 #pragma unroll
-      for (int i = 0; i < F8T_SCQ; ++i) {
-        const int q = wave * F8T_SCQ + i;
-        dma4_to_lds(d_sc, (4 * q + l / 16) * nblk + (l % 16) * 4, (lkt / F8T_SCG) * 64,
-                    __builtin_amdgcn_readfirstlane(slot + q * 256));
+        for (int i = 0; i < F8T_SCQ; ++i) {
+          const int q = wave * F8T_SCQ + i;
+          dma4_to_lds(d_sc, (4 * q + l / 16) * nblk + (l % 16) * 4, (lkt / F8T_SCG) * 64,
+                      __builtin_amdgcn_readfirstlane(slot + q * 256));
+        }
+        ++lgrp;
       }
-      ++lgrp;
+      // With the tile's first slice, its weight scales: wavefront w < 6 brings
+      // 64 of them into slot li % 3 (channels past N read as zero), so that
+      // the epilogue reads LDS and issues no vector-memory load, which would
+      // have to wait for every load of the next slices issued before it.
+      if (live && lkt == 0 && wave < F8T_TA / 64) {
+        const Tile t = tile_of(li);
+        constexpr int HW = DUAL ? F8T_TA / 128 : F8T_TA / 64;   // wavefronts per scale array
+        const float* src = (DUAL && wave >= HW) ? sb : sa;
+        const i32x4_t d = make_desc(src + (int64_t)t.e * N + t.ch0, (int64_t)(N - t.ch0) * 4);
+        dma4_to_lds(d, ((wave % HW) * 64 + lane_now()) * 4, 0,
+                    __builtin_amdgcn_readfirstlane(wsc_base + (uint32_t)((li % 3) * F8T_TA * 4 + wave * 256)));
+      }
     }
   };
   auto advance_load = [&]() __attribute__((always_inline)) {
@@ -290,7 +310,7 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
   // Results: lane = token (fi), registers = channels; stores through
   // descriptors bounded to the tile's rows, columns past N get an offset
   // beyond them.
-  auto epilogue = [&](const Tile& t) __attribute__((always_inline)) {
+  auto epilogue = [&](const Tile& t, int ws) __attribute__((always_inline)) {
     int fi = lane & 31, fg = lane >> 5;
     asm volatile("" : "+v"(fi), "+v"(fg));
     if constexpr (DUAL) {
@@ -307,9 +327,9 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
           float amax = 0.f;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int c = cin ? cbase + q * 8 + fg * 4 : 0;
-            const float4 s1 = *reinterpret_cast<const float4*>(sa + (int64_t)t.e * N + c);
-            const float4 s3 = *reinterpret_cast<const float4*>(sb + (int64_t)t.e * N + c);
+            const int cl = wr * (HA * 32) + a * 32 + q * 8 + fg * 4;   // channel within the tile
+            const float4 s1 = *reinterpret_cast<const float4*>(&wsc[ws][cl]);
+            const float4 s3 = *reinterpret_cast<const float4*>(&wsc[ws][F8T_TA / 2 + cl]);
             const float w1s[4] = {s1.x, s1.y, s1.z, s1.w}, w3s[4] = {s3.x, s3.y, s3.z, s3.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -342,9 +362,10 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
         for (int a = 0; a < WA; ++a)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int c = t.ch0 + wr * (WA * 32) + a * 32 + q * 8 + fg * 4;
+            const int cl = wr * (WA * 32) + a * 32 + q * 8 + fg * 4;   // channel within the tile
+            const int c = t.ch0 + cl;
             const bool cin = c < N;
-            const float4 s2 = *reinterpret_cast<const float4*>(sa + (int64_t)t.e * N + (cin ? c : 0));
+            const float4 s2 = *reinterpret_cast<const float4*>(&wsc[ws][cl]);
             const u32x4_t v = {__float_as_uint(acc[a][b][q * 4 + 0] * s2.x), __float_as_uint(acc[a][b][q * 4 + 1] * s2.y),
                                __float_as_uint(acc[a][b][q * 4 + 2] * s2.z), __float_as_uint(acc[a][b][q * 4 + 3] * s2.w)};
             store_b128(ro, cin ? (tl * N + c) * 4 : 0x7fffffff, v);
@@ -381,7 +402,7 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
     }
     for (int kt = 0; kt < KT - 1; ++kt) iteration(g++, kt, false);
     iteration(g++, KT - 1, true);
-    epilogue(t);
+    epilogue(t, ci % 3);
   }
   wait_vmcnt<0>();   // the loads past the end land before the workgroup's LDS is released
 }
