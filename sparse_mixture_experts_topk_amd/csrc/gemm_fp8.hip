@@ -311,6 +311,13 @@ __global__ __launch_bounds__(F8T_THREADS, 1) void grouped_gemm_fp8_tiles(
   // descriptors bounded to the tile's rows, columns past N get an offset
   // beyond them.
   auto epilogue = [&](const Tile& t, int ws) __attribute__((always_inline)) {
+    // Every accumulator is final here: the matrix instructions of the last
+    // slice are not moved down into the epilogue, where their fragments would
+    // be spilled to scratch and the reload would wait for every load in flight.
+#pragma unroll
+    for (int a = 0; a < WA; ++a)
+#pragma unroll
+      for (int b = 0; b < WB; ++b) asm volatile("" : "+v"(acc[a][b]));
     int fi = lane & 31, fg = lane >> 5;
     asm volatile("" : "+v"(fi), "+v"(fg));
     if constexpr (DUAL) {
