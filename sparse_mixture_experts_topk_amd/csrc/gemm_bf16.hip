@@ -96,9 +96,18 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
   static_assert(G::SUB % 2 == 0 && NS >= 2 && (!DUAL || WA % 2 == 0) && WB >= 2, "pipeline shape");
   static_assert(!SPLIT || !DUAL, "split runs: single GEMM");
   static_assert(!DUAL || (G::TA / 2) % 16 == 0, "w3 rows start on a swizzle period");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * G::STAGE_BYTES];
-  __shared__ int32_t offs[kMaxExpertGroups + 1];
-  __shared__ int32_t tpre[kMaxExpertGroups + 1];
+  // The expert-group tables (offsets and token-tile prefix) follow the LDS
+  // ring when they fit in the 160 KiB; otherwise (the 2-stage ring of 64-wide
+  // slices fills it) the offsets are read with scalar loads, which the load
+  // stream's waits do not count, and a tile is found by a linear scan, for
+  // at most kWideMaxGroups groups.
+  constexpr int RING = NS * G::STAGE_BYTES;
+  constexpr bool LDS_TABLES = RING + 2 * (kMaxExpertGroups + 1) * 4 <= 160 * 1024;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[RING + (LDS_TABLES ? 2 * (kMaxExpertGroups + 1) * 4 : 0)];
+  int32_t* const offs = reinterpret_cast<int32_t*>(smem + RING);
+  int32_t* const tpre = offs + (kMaxExpertGroups + 1);
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const_i32* const goffs = (const_i32*)offsets;   // generic -> constant address space
 
   constexpr int HA = WA / 2;                 // dual: w1 (or w3) blocks per wavefront
   constexpr int CH_TILE = DUAL ? G::TA / 2 : G::TA;
@@ -117,17 +126,24 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
     return l;
   };
 
-  // Expert offsets and their token-tile prefix go to LDS once, so that
-  // locating a tile in the middle of the load stream issues no vector-memory
-  // read (the stream's waits count its own loads).
-  if (tid <= E) offs[tid] = offsets[tid];
-  __syncthreads();
-  if (wave == 0) build_tile_prefix(offs, E, PF_ROWS, tpre, lane);
-  __syncthreads();
+  // Expert offsets and their token-tile prefix go to LDS once (or stay in
+  // memory, read by scalar loads), so that locating a tile in the middle of
+  // the load stream issues no vector-memory read (the stream's waits count
+  // its own loads).
+  int n_token_tiles = 0;
+  if constexpr (LDS_TABLES) {
+    if (tid <= E) offs[tid] = offsets[tid];
+    __syncthreads();
+    if (wave == 0) build_tile_prefix(offs, E, PF_ROWS, tpre, lane);
+    __syncthreads();
+    n_token_tiles = __builtin_amdgcn_readfirstlane(tpre[E]);
+  } else {
+    for (int e = 0; e < E; ++e) n_token_tiles += (goffs[e + 1] - goffs[e] + PF_ROWS - 1) / PF_ROWS;
+  }
   const int KT = K / BK;
   const int slots = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const TileSplit sp = TileSplit::of(__builtin_amdgcn_readfirstlane(tpre[E]) * n_tiles, xcd, slots, KT);
+  const TileSplit sp = TileSplit::of(n_token_tiles * n_tiles, xcd, slots, KT);
   // this workgroup's items: whole tiles, then (split) up to two K-runs of tail tiles
   const int n_whole = sp.R + ((!SPLIT && slot < sp.tail) ? 1 : 0);
   const int run0 = slot * sp.P, run1 = min(run0 + sp.P, sp.tail * KT);
@@ -149,7 +165,20 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
       part = (int)blockIdx.x * 2 + (i - n_whole);
     }
     int e, r0, r1, mt, nt;
-    find_tile(offs, tpre, E, n_tiles, t_idx, e, r0, r1, mt, nt);
+    if constexpr (LDS_TABLES) {
+      find_tile(offs, tpre, E, n_tiles, t_idx, e, r0, r1, mt, nt);
+    } else {
+      e = r0 = r1 = mt = nt = 0;
+      for (int g = 0, tt = t_idx; g < E; ++g) {
+        const int a0 = goffs[g], a1 = goffs[g + 1];
+        const int m = (a1 - a0 + PF_ROWS - 1) / PF_ROWS;
+        if (tt < m * n_tiles) {
+          e = g; r0 = a0; r1 = a1; mt = tt % m; nt = tt / m;
+          break;
+        }
+        tt -= m * n_tiles;
+      }
+    }
     Tile t;   // uniform values, kept in scalar registers
     t.e = __builtin_amdgcn_readfirstlane(e);
     t.tok0 = __builtin_amdgcn_readfirstlane(r0 + mt * PF_ROWS);
@@ -450,20 +479,28 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(const int32_t* __restr
 // blocks per wavefront.  Both run 8 wavefronts (two per SIMD, 192
 // accumulators each) on a 384 x 256 tile: gate/up as 2 x 4 wavefronts of
 // 3 + 3 (w1, w3) blocks x 2 token blocks, down as 4 x 2 wavefronts of 3 x 4.
-template <bool DUAL> struct PrefillCfg;
-template <> struct PrefillCfg<true> { static constexpr int BK = 32, NS = 3, WR = 2, WC = 4, WA = 6, WB = 2; };
-template <> struct PrefillCfg<false> { static constexpr int BK = 32, NS = 3, WR = 4, WC = 2, WA = 3, WB = 4; };
-template <bool DUAL>
-using PrefillGeom = TileGeom<PrefillCfg<DUAL>::BK, PrefillCfg<DUAL>::WR, PrefillCfg<DUAL>::WC, PrefillCfg<DUAL>::WA,
-                             PrefillCfg<DUAL>::WB>;
+// With at most kWideMaxGroups expert groups a K slice is 64 wide (128-byte
+// row segments: half as many L2 requests per byte as 64-byte ones) in a ring
+// of 2 stages of 80 KiB; with more, 32 wide in 3 stages of 40 KiB, leaving
+// LDS for the group tables.
+constexpr int kWideMaxGroups = 16;
+template <bool DUAL, bool WIDE> struct PrefillCfg;
+template <> struct PrefillCfg<true, false> { static constexpr int BK = 32, NS = 3, WR = 2, WC = 4, WA = 6, WB = 2; };
+template <> struct PrefillCfg<false, false> { static constexpr int BK = 32, NS = 3, WR = 4, WC = 2, WA = 3, WB = 4; };
+template <> struct PrefillCfg<true, true> { static constexpr int BK = 64, NS = 2, WR = 2, WC = 4, WA = 6, WB = 2; };
+template <> struct PrefillCfg<false, true> { static constexpr int BK = 64, NS = 2, WR = 4, WC = 2, WA = 3, WB = 4; };
+template <bool DUAL, bool WIDE = false>
+using PrefillGeom = TileGeom<PrefillCfg<DUAL, WIDE>::BK, PrefillCfg<DUAL, WIDE>::WR, PrefillCfg<DUAL, WIDE>::WC,
+                             PrefillCfg<DUAL, WIDE>::WA, PrefillCfg<DUAL, WIDE>::WB>;
 constexpr int64_t kPartialTileBytes = (int64_t)PF_ROWS * PrefillGeom<false>::TA * 4;
+static_assert(PrefillGeom<false, true>::TA == PrefillGeom<false>::TA, "one partial tile size");
 
-template <bool DUAL>
-hipError_t launch_prefill(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
+template <bool DUAL, bool WIDE>
+hipError_t launch_prefill_cfg(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                           const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
                           float* partials, hipStream_t st) {
-  using C = PrefillCfg<DUAL>;
-  using G = PrefillGeom<DUAL>;
+  using C = PrefillCfg<DUAL, WIDE>;
+  using G = PrefillGeom<DUAL, WIDE>;
   constexpr int CH_TILE = DUAL ? G::TA / 2 : G::TA;
   const int n_tiles = (N + CH_TILE - 1) / CH_TILE;
   const int64_t max_tiles = max_token_tiles(s, PF_ROWS) * n_tiles;
@@ -486,6 +523,15 @@ hipError_t launch_prefill(const moe_shape_t& s, const uint16_t* act, const int32
                      dim3((unsigned)grid), dim3(G::THREADS), 0, st, act, offsets, expert_groups(s), wa,
                      wb, N, K, out, nullptr, n_tiles);
   return hipGetLastError();
+}
+
+template <bool DUAL>
+hipError_t launch_prefill(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
+                          const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
+                          float* partials, hipStream_t st) {
+  if (expert_groups(s) <= kWideMaxGroups)
+    return launch_prefill_cfg<DUAL, true>(s, act, offsets, wa, wb, N, K, out, partials, st);
+  return launch_prefill_cfg<DUAL, false>(s, act, offsets, wa, wb, N, K, out, partials, st);
 }
 
 // Weight streaming (decode kernels) while no expert can hold more than this many rows.
