@@ -130,7 +130,7 @@ def main():
     a = ap.parse_args()
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the MoE layer's kernels are "
+        print(json.dumps({"error": "the MoE layer runs on one GPU only: its kernels are "
                                    "single-device; --gpus N > 1 is not supported"}))
         sys.exit(2)
 
