@@ -24,11 +24,13 @@ def say(msg):
 
 
 def record(case, **metrics):
-    """Append measured error figures to gpurun_out/parity_metrics.jsonl (if that folder exists)."""
+    """Append measured error figures, one JSON line per case, to the file that the environment
+    variable MOE_PARITY_METRICS names (nothing is written when it is unset)."""
     import json
     import os
-    if os.path.isdir("gpurun_out"):
-        with open(os.path.join("gpurun_out", "parity_metrics.jsonl"), "a") as f:
+    path = os.environ.get("MOE_PARITY_METRICS")
+    if path:
+        with open(path, "a") as f:
             f.write(json.dumps({"case": case, **{k: float(v) for k, v in metrics.items()}}) + "\n")
 
 
