@@ -283,9 +283,9 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
   // read after the first WB instructions, when the accumulators leave room
   // for it; otherwise fb[b] is reloaded after its last use (a == WA - 1)
   // and the other wavefront on the SIMD covers the wait.  With `loads`, the
-  // remaining slots carry the loads of the load cursor's slice `ls`
-  // (slot numbering continues across substeps from slot0).  With `reads`,
-  // (gn, sn) is the substep whose fragments are read.
+  // remaining slots carry the loads of the load cursor's slice `ls`, PER to
+  // a slot (slot numbering starts at slot0).  With `reads`, (gn, sn) is the
+  // substep whose fragments are read.
   constexpr bool FB2 = WA * WB * 16 + 4 * (WA + 2 * WB) <= 2048 / G::NW - 32;
   bf16x8_t fa[WA], fb[FB2 ? 2 : 1][WB];
   constexpr int NI = WA * WB;
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
       if (b == WB - 1) {
         if (reads) fa[a] = read_frag(gn, fo, a);
       } else if (a >= 1 && loads) {
-        constexpr int SLOTS = FREE * (G::SUB - 1), PER = (G::DMA + SLOTS - 1) / SLOTS;
+        constexpr int SLOTS = FREE, PER = (G::DMA + SLOTS - 1) / SLOTS;
         const int sl = slot0 + (a - 1) * (WB - 1) + b;
 #pragma unroll
         for (int q = 0; q < PER; ++q)
@@ -371,9 +371,11 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
   };
 
   // Pipeline.  Slice g of the stream lives in stage g % NS.  Iteration g runs
-  // SUB substeps.  All but the last carry the loads of slice g + NS - 1,
-  // which go to the stage that slice g - 1 used (every wavefront finished
-  // reading it before the previous barrier).  Before the last substep: wait
+  // SUB substeps.  The first carries all the loads of slice g + NS - 1
+  // (PER per free slot: the earliest issue leaves the longest time before
+  // their wait, which the 2-stage ring needs), and they go to the stage that
+  // slice g - 1 used (every wavefront finished reading it before the
+  // previous barrier).  Before the last substep: wait
   // for this wavefront's loads of slice g + 1 (the loads of later slices
   // stay in flight), finish its LDS reads, barrier -- slice g + 1 is
   // complete in LDS and slice g is no longer read; the last substep then
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < G::SUB - 1; ++s)
-      substep(s & 1, g, s + 1, s * FREE, true, g + NS - 1, true);
+      substep(s & 1, g, s + 1, 0, s == 0, g + NS - 1, true);
     advance_load();
     wait_vmcnt<G::DMA * (NS - 2)>();
     wait_lgkmcnt0();
