@@ -8,9 +8,9 @@ no code, table or helper with the HIP path and never takes a value from it.
 What it computes, step by step, with the passage each step follows:
 
 1. Router logits ``x . W_g^T (+ b)`` -- "Mixtral" study notes, section "MoE
-   Layer" (``self.gate = nn.Linear(d_model, num_experts, bias=False)``); the
-   gate equation on "Mixtral and Mixture-of-Experts, Explained", section "How
-   it works".  The additive per-expert bias exists only for the skewed-routing
+   Layer" (the router is a linear map from d_model to one logit per expert,
+   without a bias term); the gate equation on "Mixtral and Mixture-of-Experts,
+   Explained", section "How it works".  The additive per-expert bias exists only for the skewed-routing
    workload (added after the dot product).
 2. Top-2 by logit, largest first; equal logits go to the lower expert index.
 3. Gate weights ``G(x) = Softmax(TopK(x . W_g))`` with every non-selected
@@ -38,8 +38,9 @@ What it computes, step by step, with the passage each step follows:
    ``silu(z) = z * sigmoid(z)`` and no biases ("Mixtral" study notes,
    MixtralExpert and section "SwiGLU Experts").
 7. ``y = sum_i G(x)_i * Expert_i(x)`` over kept slots; zero when nothing is
-   kept ("Mixtral and Mixture-of-Experts, Explained", "How it works";
-   ``output = torch.zeros_like(x)`` in the study notes' MoE layer).
+   kept ("Mixtral and Mixture-of-Experts, Explained", "How it works"; the
+   study notes' MoE layer starts from an all-zero output of x's shape and
+   adds each expert's weighted contribution).
 8. General top-k and a shared expert (the DeepSeek-V3 remark on "Mixtral 8x7B"
    interview page: many routed experts, several active per token, plus a
    shared one).  Reading: k experts by logit with the same gate (softmax
@@ -51,8 +52,17 @@ fp8-code-times-scale / MXFP4-code-times-block-scale value (``oracle/mxfp4.py``;
 MXFP4 experts keep bf16 activations); all arithmetic is float64.  For fp8 expert weights
 the computation also includes the declared activation quantisation (see
 ``oracle/fp8.py``): x and h are block-quantised per row and per 32-element
-block before the two contractions.  Parity unpinned for that emulation beyond
-the e4m3 encoder itself (the pages print no fp8 values).
+block before the two contractions (``fp8_act_quant=False`` leaves it out, for
+the report-only comparison against plain dequantised weights).  The pages
+print no fp8 values; the emulation is pinned by its definition (grid,
+exponent rule, nearest rounding, blocking axis) and a hand-worked block.
+
+Near ties.  Where the fp32 arithmetic of a GPU router and the fp64 logits
+here may order two experts differently (logit gap below ``NEAR_TIE``),
+``forward`` can take the GPU's decision instead, but only a decision that is
+a correct top-k ranking up to such near ties (``near_tie_ranking_ok``), and
+capacity / fallback marks that differ only at a cutoff near tie and keep
+every expert's count.
 """
 from __future__ import annotations
 
@@ -68,6 +78,32 @@ from . import mxfp4 as _mxfp4
 # Assignments whose deciding gap is below this are "near ties": the decision is
 # not fixed by the arithmetic precision of either side (exemption threshold).
 NEAR_TIE = 1e-4
+
+
+def near_tie_ranking_ok(row_logits: np.ndarray, ranked) -> bool:
+    """Is ``ranked`` (distinct expert ids in the order a router ranked them: ranks 1..m)
+    the exact top-m ranking of ``row_logits`` up to near ties?
+
+    True when the ids are distinct and in range, no expert left out has a logit
+    NEAR_TIE or more above one ranked, and no ranked expert has a logit NEAR_TIE
+    or more above one ranked before it.  With gaps of at least NEAR_TIE around
+    rank m and between the ranked experts this admits only the exact ranking
+    (logit descending, ties to the lower index)."""
+    ranked = [int(v) for v in ranked]
+    E = len(row_logits)
+    if len(set(ranked)) != len(ranked) or any(v < 0 or v >= E for v in ranked):
+        return False
+    if not ranked:
+        return True
+    lv = np.asarray(row_logits, dtype=np.float64)
+    sel = lv[ranked]
+    rest = np.delete(lv, ranked)
+    if rest.size and rest.max() - sel.min() >= NEAR_TIE:
+        return False
+    for i in range(1, len(ranked)):
+        if sel[i] - sel[:i].min() >= NEAR_TIE:
+            return False
+    return True
 
 
 def to_f64(t) -> np.ndarray:
@@ -286,24 +322,33 @@ def forward(inputs, tokens: Optional[Iterable[int]] = None,
             keep_override: Optional[np.ndarray] = None,
             want_h: bool = False,
             next_override: Optional[Dict[int, Iterable[int]]] = None,
-            status_override: Optional[np.ndarray] = None) -> OracleResult:
+            status_override: Optional[np.ndarray] = None,
+            fp8_act_quant: bool = True) -> OracleResult:
     """Run the layer on ``inputs`` (a MoEInputs of host tensors).
 
     tokens: compute the expert FFN / output only for these tokens (all
         routing, capacity and grouping steps still cover every token).
-    override: {token: (e0, e1)} routing decisions to use instead of the
-        oracle's own, accepted only for near-tie tokens (gap23 or gap12 below
-        NEAR_TIE), where either choice is correct; G is recomputed from the
-        oracle's fp64 logits of the given experts.
+    override: {token: (e0, .., e_{k-1})} routing decisions to use instead of
+        the oracle's own, accepted only when they are a top-k ranking of the
+        token's fp64 logits up to near ties (``near_tie_ranking_ok``): only an
+        expert tied within NEAR_TIE with the k-th may replace it, and slots may
+        swap only where their logits are that close.  G is recomputed from
+        the oracle's fp64 logits of the given experts.
     keep_override: a [T, k] keep mask replacing the capacity decision; it must
         agree with the oracle's own except for assignments whose G lies
-        within NEAR_TIE of their expert's cutoff.
-    next_override: {token: (n0, n1)} 3rd/4th-ranked experts to use instead
-        of the oracle's, accepted only where a logit gap among ranks 2..5 is
-        below NEAR_TIE.
+        within NEAR_TIE of their expert's cutoff, and keep min(load, capacity)
+        assignments of every expert.
+    next_override: {token: (n0, n1)} experts ranked k+1 and k+2 to use instead
+        of the oracle's, accepted only when the token's k experts followed by
+        them are a ranking up to near ties (-1 where E is too small, as in the
+        oracle's own).
     status_override: a [T, k] fallback-round status (0/1/2) replacing the
         oracle's, accepted only where it differs at a fallback cutoff near
-        tie (G within NEAR_TIE of the target expert's cutoff).
+        tie (G within NEAR_TIE of the target expert's cutoff) and every
+        expert takes min(offers, free slots) in the round.
+    fp8_act_quant: for fp8 expert weights, include the declared activation
+        quantisation (the default); False gives the plain SwiGLU on the
+        dequantised weights (report-only comparisons).
     """
     cfg = inputs.cfg
     E, k = cfg.n_experts, cfg.top_k
@@ -317,42 +362,67 @@ def forward(inputs, tokens: Optional[Iterable[int]] = None,
             pair = tuple(int(v) for v in pair)
             if tuple(r.ids[t]) == pair:
                 continue
-            if not (r.gap23[t] < NEAR_TIE or r.gap12[t] < NEAR_TIE):
-                raise ValueError(f"override of token {t} is not a near tie")
-            if set(pair) != set(r.ids[t].tolist()) and not r.gap23[t] < NEAR_TIE:
-                raise ValueError(f"override of token {t} changes the expert set")
+            if len(pair) != k or not near_tie_ranking_ok(logits[t], pair):
+                raise ValueError(f"override {pair} of token {t} is not a top-{k} ranking up to "
+                                 f"near ties (oracle: {tuple(r.ids[t])})")
             kl = logits[t, list(pair)]
             ex = np.exp(kl - kl.max())
             r.ids[t] = pair
             r.G[t] = ex / ex.sum()
+            # ranks k+1 and k+2 follow the experts actually taken
+            rest = [e for e in np.argsort(-logits[t], kind="stable") if e not in pair]
+            r.next_ids[t] = (rest + [-1, -1])[:2]
     keep, cutoff = capacity_select(r.ids, r.G, E, cfg.capacity)
     if keep_override is not None:
+        keep_override = np.asarray(keep_override, dtype=bool)
+        if keep_override.shape != keep.shape:
+            raise ValueError("keep override has the wrong shape")
         diff = np.argwhere(keep_override != keep)
         for t, s in diff:
             e = r.ids[t, s]
             if not (abs(r.G[t, s] - cutoff[e]) < NEAR_TIE):
                 raise ValueError(f"keep override at ({t},{s}) is not at the capacity cutoff")
-        keep = keep_override.astype(bool)
+        for e in np.unique(r.ids[tuple(diff.T)]) if len(diff) else []:
+            load = int(np.count_nonzero(r.ids == e))
+            if int(np.count_nonzero((r.ids == e) & keep_override)) != min(load, cfg.capacity):
+                raise ValueError(f"keep override changes the kept count of expert {e}")
+        keep = keep_override
     keep1 = keep
     status = final_ids = cutoff2 = None
     if cfg.capacity >= 0 and getattr(cfg, "overflow", "drop") == "next_best":
         if next_override:
+            n_next = min(2, E - k)
             for t, pair in next_override.items():
                 pair = tuple(int(v) for v in pair)
                 if tuple(r.next_ids[t]) == pair:
                     continue
-                if not min(r.gap23[t], r.gap34[t], r.gap45[t]) < NEAR_TIE:
-                    raise ValueError(f"next-expert override of token {t} is not a near tie")
+                ok = len(pair) == 2 and all(v >= 0 for v in pair[:n_next]) and \
+                    all(v == -1 for v in pair[n_next:]) and \
+                    near_tie_ranking_ok(logits[t], tuple(r.ids[t]) + pair[:n_next])
+                if not ok:
+                    raise ValueError(f"next-expert override {pair} of token {t} is not a ranking "
+                                     f"up to near ties (oracle: {tuple(r.next_ids[t])})")
                 r.next_ids[t] = pair
         final_ids, status, cutoff2 = fallback_select(r.ids, r.next_ids, r.G, keep, E, cfg.capacity)
         if status_override is not None:
+            status_override = np.asarray(status_override, dtype=np.uint8)
+            if status_override.shape != status.shape:
+                raise ValueError("status override has the wrong shape")
             target = fallback_targets(keep, r.next_ids)
-            for t, s_ in np.argwhere(status_override != status):
+            diff = np.argwhere(status_override != status)
+            for t, s_ in diff:
                 e = target[t, s_]
-                if status[t, s_] == 0 or status_override[t, s_] == 0 or e < 0 or \
+                if status[t, s_] == 0 or status_override[t, s_] not in (1, 2) or e < 0 or \
                         not abs(r.G[t, s_] - cutoff2[e]) < NEAR_TIE:
                     raise ValueError(f"status override at ({t},{s_}) is not at a fallback cutoff")
-            status = status_override.astype(np.uint8)
+            for e in np.unique(target[tuple(diff.T)]) if len(diff) else []:
+                offers = target == e
+                free = cfg.capacity - int(np.count_nonzero((r.ids == e) & keep))
+                if int(np.count_nonzero(offers & (status_override == 2))) != \
+                        min(int(np.count_nonzero(offers)), free):
+                    raise ValueError(f"status override changes what expert {e} takes in the "
+                                     "fallback round")
+            status = status_override
             final_ids = np.where(status == 2, target, r.ids)
         keep = status != 1
         perm = permutation(final_ids, keep, E, S)
@@ -382,7 +452,7 @@ def forward(inputs, tokens: Optional[Iterable[int]] = None,
         w1 = dequant_weight(inputs.w1[e], inputs.w1_scale[e] if scaled else None, cfg.w_dtype)
         w3 = dequant_weight(inputs.w3[e], inputs.w3_scale[e] if scaled else None, cfg.w_dtype)
         w2 = dequant_weight(inputs.w2[e], inputs.w2_scale[e] if scaled else None, cfg.w_dtype)
-        ffn = swiglu_act_quant if fp8 else swiglu
+        ffn = swiglu_act_quant if fp8 and fp8_act_quant else swiglu
         y_perm[rows], h = ffn(xr, w1, w3, w2)
         if want_h:
             h_all[rows] = h

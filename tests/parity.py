@@ -63,11 +63,21 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def check_next(res, gpu_next):
-    """3rd/4th-ranked experts, exact away from near ties among ranks 2..5."""
+def check_next(res, gpu_next, gpu_ids=None):
+    """Experts ranked k+1 and k+2: exact away from near ties among ranks k..k+3; at a near tie
+    the token's k experts (the GPU's, when given) followed by them must be a ranking of the
+    fp64 logits up to near ties."""
     r = res.routing
     near = np.minimum(np.minimum(r.gap23, r.gap34), r.gap45) < oracle.NEAR_TIE
     assert np.array_equal(gpu_next[~near], r.next_ids[~near]), "3rd/4th-ranked experts differ"
+    ids = r.ids if gpu_ids is None else gpu_ids
+    E, k = res.logits.shape[1], ids.shape[1]
+    n = min(2, E - k)
+    assert np.all(gpu_next[:, n:] == -1), "a next-ranked expert where none exists"
+    for t in np.flatnonzero(near):
+        seq = tuple(int(v) for v in ids[t]) + tuple(int(v) for v in gpu_next[t, :n])
+        assert oracle.near_tie_ranking_ok(res.logits[t], seq), \
+            f"token {t}: ranks k+1, k+2 {tuple(gpu_next[t])} are not a near-tie ranking"
 
 
 def check_routing(res, gpu_ids, gpu_w, gpu_logits, logit_atol):
@@ -81,6 +91,11 @@ def check_routing(res, gpu_ids, gpu_w, gpu_logits, logit_atol):
     assert np.array_equal(ids[exact], r.ids[exact]), "expert ids differ away from near ties"
     order_only = near_order & ~near_set
     assert np.array_equal(np.sort(ids[order_only], 1), np.sort(r.ids[order_only], 1))
+    # at a near tie only a tied expert may replace the k-th, and only tied slots may swap
+    for t in np.flatnonzero(~exact):
+        assert oracle.near_tie_ranking_ok(res.logits[t], ids[t]), \
+            f"token {t}: ids {tuple(ids[t])} are not a top-{k} ranking up to near ties " \
+            f"(oracle {tuple(r.ids[t])})"
     srt = np.sort(ids, 1)
     assert np.all(srt[:, 1:] != srt[:, :-1]), "a token picked one expert twice"
     assert np.all((ids >= 0) & (ids < res.logits.shape[1]))

@@ -60,7 +60,7 @@ def run_staged_and_check(cfg, inputs=None, tokens=None, check_h=True):
     logit_atol = 1e-5 if cfg.act_dtype == "f32" else 3e-4
     check_routing(base, gpu_ids, to_np(st["topk_weights"]), to_np(st["logits"]), logit_atol)
     # the router writes the 3rd/4th-ranked experts whenever asked (runner.staged always asks)
-    check_next(base, to_np(st["next_ids"]))
+    check_next(base, to_np(st["next_ids"]), gpu_ids)
     check_permutation(res, st)
     n = int(res.perm.offsets[-1])
     row_tok = token_of_slot(res.perm.perm_src, cfg.T, cfg.top_k)
@@ -468,7 +468,7 @@ def test_route_general_topk(E, k):
     torch.cuda.synchronize()
     res = oracle.forward(inp, tokens=[])
     check_routing(res, to_np(ids), to_np(w), to_np(lg), 3e-4)
-    check_next(res, to_np(nx))
+    check_next(res, to_np(nx), to_np(ids))
     if k == 1:
         assert np.all(to_np(w) == 1.0)
 
@@ -488,7 +488,7 @@ def test_route_general_topk_fp32(E, k):
     torch.cuda.synchronize()
     res = oracle.forward(inp, tokens=[])
     check_routing(res, to_np(ids), to_np(w), to_np(lg), 1e-5)
-    check_next(res, to_np(nx))
+    check_next(res, to_np(nx), to_np(ids))
 
 
 def test_route_general_topk_ties():

@@ -479,6 +479,208 @@ def test_act_quant_ffn_reduces_to_plain_ffn_on_grid_inputs():
     assert np.array_equal(y_q, y_p)
 
 
+def _h_on_block_grid(h32, block=32):
+    """Expected dequantised h: per row and 32-element block along F, the scale 2**e with e the
+    smallest integer such that fp32(amax / 448) <= 2**e (0 for an all-zero block), and torch's
+    float8_e4m3fn cast (round to nearest even) of the scaled values."""
+    R, F = h32.shape
+    out = np.empty((R, F))
+    for r in range(R):
+        for b in range(F // block):
+            blk = h32[r, b * block:(b + 1) * block]
+            amax = np.float32(np.abs(blk).max())
+            e = 0
+            if amax > 0:
+                ratio = float(np.float32(amax / np.float32(448.0)))
+                e = math.ceil(math.log2(ratio))
+                while 2.0 ** (e - 1) >= ratio:       # guard the float log2 at powers of two
+                    e -= 1
+                while 2.0 ** e < ratio:
+                    e += 1
+            q = torch.from_numpy(blk.astype(np.float64) * 2.0 ** -e).to(torch.float32)
+            out[r, b * block:(b + 1) * block] = q.to(torch.float8_e4m3fn).to(torch.float64).numpy() * 2.0 ** e
+    return out
+
+
+def test_act_quant_h_step_is_block_quantised_along_F():
+    """fp8 emulation, h step: with w2 = I (F = d) the output is the quantised h itself.  It must
+    lie on one e4m3 grid scaled by 2**e per (row, 32-block along F), equal torch's e4m3 rounding of
+    the fp32 h on that grid, and stay within 2**-4 of h (normal range).  x is put on its grid so
+    that its own quantisation is the identity; rows differ in magnitude so that blocking along the
+    wrong axis changes the scales."""
+    g = np.random.default_rng(61)
+    d = F = 128
+    R = 6
+    x = fp8.e4m3_decode(g.integers(0, 126, (R, d)).astype(np.uint8)) * np.where(g.random((R, d)) < 0.5, -1, 1)
+    x[:, ::32] = 448.0
+    x *= np.exp2(np.arange(R) * 3 - 15.0)[:, None]           # row scales 2^-15 .. 2^0
+    w1 = g.standard_normal((F, d)) * 0.05
+    w3 = g.standard_normal((F, d)) * 0.05
+    w3[:, :] *= np.exp2(g.integers(-6, 6, F))[:, None]       # channel magnitudes vary along F
+    y, hq = oracle.swiglu_act_quant(x, w1, w3, np.eye(d))
+    xt = torch.from_numpy(x)
+    h = (Fn.silu(Fn.linear(xt, torch.from_numpy(w1))) * Fn.linear(xt, torch.from_numpy(w3))).numpy()
+    h32 = h.astype(np.float32)
+    ref = _h_on_block_grid(h32)
+    assert np.array_equal(y, ref), "h is not the per-(row, 32-block along F) e4m3 quantisation"
+    assert np.array_equal(hq, ref)
+    big = np.abs(ref) >= 2.0 ** -6 * np.abs(h32).max(axis=1, keepdims=True) / 448 * 2
+    assert np.all(np.abs(ref - h32)[big] <= 2.0 ** -4 * np.abs(h32.astype(np.float64))[big])
+    assert np.linalg.norm(ref - h) / np.linalg.norm(h) > 1e-3     # the step is not the identity
+
+
+def test_act_quant_h_step_hand_worked_block():
+    """One block worked by hand.  x = e_0 (quantises exactly: 1 * 2^8 = 256 is an e4m3 value),
+    w1[:, 0] = 40 so silu(g) = 40 exactly in fp64 (exp(-40) vanishes next to 1), and w3[:, 0]
+    sets h = 40 * w3 = (100, -3.3, 0.01, 0.001, 0.0001, 0, ...).  amax 100: e = ceil(log2(100/448))
+    = -2, so the codes are e4m3 of 4h:
+      400     -> midway between 384 and 416; the even mantissa wins: 384 -> 96
+      -13.2   -> -13 (spacing 1 in [8, 16))                          -> -3.25
+      0.04    -> 10 * 2^-8 (spacing 2^-8 in [2^-5, 2^-4))            -> 0.009765625
+      0.004   -> 2 * 2^-9 (subnormal spacing 2^-9)                   -> 0.0009765625
+      0.0004  -> 0 (below half the smallest subnormal)               -> 0"""
+    d = F = 32
+    x = np.zeros((1, d))
+    x[0, 0] = 1.0
+    w1 = np.zeros((F, d))
+    w1[:, 0] = 40.0
+    w3 = np.zeros((F, d))
+    w3[:5, 0] = np.array([100.0, -3.3, 0.01, 0.001, 0.0001]) / 40.0
+    y, _ = oracle.swiglu_act_quant(x, w1, w3, np.eye(d))
+    expect = np.zeros(F)
+    expect[:4] = [96.0, -3.25, 0.009765625, 0.0009765625]
+    assert y[0].tolist() == expect.tolist()
+
+
+# ---------------------------------------------------- near-tie overrides ---
+
+def _router_inputs(logits, capacity=-1, overflow="drop", k=2, d=16):
+    """Inputs whose fp64 router logits are exactly ``logits`` (W_g = I on the first E inputs)."""
+    logits = np.asarray(logits, dtype=np.float64)
+    T, E = logits.shape
+    cfg = synthetic.MoEConfig(name="ties", T=T, d_model=d, d_ff=8, n_experts=E, top_k=k,
+                              capacity=capacity, overflow=overflow, act_dtype="f32", w_dtype="f32")
+    x = np.zeros((T, d))
+    x[:, :E] = logits
+    wg = np.zeros((E, d))
+    wg[:, :E] = np.eye(E)
+    g = np.random.default_rng(0)
+    return _Inp(cfg, x, wg, g.standard_normal((E, 8, d)), g.standard_normal((E, 8, d)),
+                g.standard_normal((E, d, 8)))
+
+
+def _refuses(inp, **kw):
+    with pytest.raises(ValueError):
+        oracle.forward(inp, tokens=[], **kw)
+
+
+def test_override_accepts_only_the_tied_expert():
+    """gap23 = 5e-5 on token 0: only expert 2 (tied with the 2nd) may replace expert 1."""
+    inp = _router_inputs([[3.0, 1.00005, 1.0, 0.5],      # set near tie (gap23 = 5e-5)
+                          [2.0, 1.0, 0.0, -1.0],         # clear gaps everywhere
+                          [1.00005, 1.0, -1.0, -2.0]])   # slot order near tie (gap12 = 5e-5)
+    base = oracle.forward(inp, tokens=[])
+    assert base.routing.ids.tolist() == [[0, 1], [0, 1], [0, 1]]
+    res = oracle.forward(inp, tokens=[], override={0: (0, 2), 2: (1, 0)})
+    assert res.routing.ids.tolist() == [[0, 2], [0, 1], [1, 0]]
+    assert abs(res.routing.G[0, 0] - 1 / (1 + math.exp(-2.0))) < 1e-15
+    assert abs(res.routing.G[2, 0] - 1 / (1 + math.exp(0.00005))) < 1e-12
+    for bad in ((0, 3), (3, 2), (1, 1), (2, 0), (1, 2), (0,), (0, 1, 2), (0, 4)):
+        _refuses(inp, override={0: bad})
+    for bad in ((0, 2), (1, 0)):
+        _refuses(inp, override={1: bad})
+    _refuses(inp, override={2: (1, 2)})          # order may swap, the set may not change
+    assert oracle.near_tie_ranking_ok(inp.x[0, :4], (0, 2))
+    assert not oracle.near_tie_ranking_ok(inp.x[0, :4], (0, 3))
+
+
+def test_next_override_accepts_only_near_tie_rankings():
+    inp = _router_inputs([[5.0, 4.0, 2.00005, 2.0, 1.0, 0.0],   # ranks 3/4 tied
+                          [5.0, 4.0, 3.0, 2.0, 1.0, 0.0],       # clear
+                          [5.0, 3.00005, 3.0, 2.0, 1.0, 0.0]],  # ranks 2/3 tied
+                         capacity=4, overflow="next_best")
+    base = oracle.forward(inp, tokens=[])
+    assert base.routing.next_ids.tolist() == [[2, 3], [2, 3], [2, 3]]
+    res = oracle.forward(inp, tokens=[], next_override={0: (3, 2)})
+    assert res.routing.next_ids[0].tolist() == [3, 2]
+    for bad in ((2, 4), (4, 3), (2, 2), (0, 3), (2, -1), (1, 3)):
+        _refuses(inp, next_override={0: bad})
+    _refuses(inp, next_override={1: (3, 2)})
+    # the GPU took expert 2 into the top-2 at the set near tie: expert 1 is then ranked 3rd
+    res = oracle.forward(inp, tokens=[], override={2: (0, 2)}, next_override={2: (1, 3)})
+    assert res.routing.next_ids[2].tolist() == [1, 3]
+    _refuses(inp, override={2: (0, 2)}, next_override={2: (2, 3)})
+
+
+def test_keep_override_only_at_the_cutoff_and_counts_kept():
+    """Capacity 1.  Expert 0 gets tokens 0, 1 (G 5e-5 apart) and 3 (far below): only the swap of
+    the two tied tokens is accepted."""
+    inp = _router_inputs([[2.0, 1.0, 0.0, -1.0],
+                          [2.00025, 1.0, 0.0, -1.0],
+                          [-3.0, -3.0, 2.0, 1.0],
+                          [0.3, -5.0, 0.0, -5.0]], capacity=1)
+    base = oracle.forward(inp, tokens=[])
+    G = base.routing.G
+    assert 0 < G[1, 0] - G[0, 0] < oracle.NEAR_TIE
+    keep = base.keep.copy()
+    assert keep[:, 0].tolist() == [False, True, True, False]
+    swap = keep.copy()
+    swap[0, 0], swap[1, 0] = True, False
+    res = oracle.forward(inp, tokens=[], keep_override=swap)
+    assert np.array_equal(res.keep, swap)
+    both = keep.copy()
+    both[0, 0] = True                      # two kept by a capacity-1 expert
+    _refuses(inp, keep_override=both)
+    far = keep.copy()
+    far[3, 0], far[1, 0] = True, False     # token 3 is far below the cutoff
+    _refuses(inp, keep_override=far)
+    clear = keep.copy()
+    clear[2, 0] = False                    # expert 2 was under capacity: no cutoff
+    _refuses(inp, keep_override=clear)
+
+
+def test_status_override_only_at_the_fallback_cutoff():
+    """Capacity 1 with the fallback: expert 0 keeps token 2; tokens 0 and 1 (G 5e-5 apart) are
+    both offered to expert 3, which has one free slot."""
+    inp = _router_inputs([[3.0, 2.0, -5.0, 1.0, -5.0],
+                          [3.00025, -5.0, 2.0, 1.0, -5.0],
+                          [8.0, -5.0, -5.0, -5.0, 4.0]], capacity=1, overflow="next_best")
+    base = oracle.forward(inp, tokens=[])
+    assert base.status.tolist() == [[1, 0], [2, 0], [0, 0]]
+    st = base.status.copy()
+    st[0, 0], st[1, 0] = 2, 1
+    res = oracle.forward(inp, tokens=[], status_override=st)
+    assert res.status.tolist() == [[2, 0], [1, 0], [0, 0]] and res.final_ids[0, 0] == 3
+    both = base.status.copy()
+    both[0, 0] = 2                         # expert 3 would take two offers into one slot
+    _refuses(inp, status_override=both)
+    kept = base.status.copy()
+    kept[0, 1] = 1                         # a slot kept by its top-2 expert cannot change
+    _refuses(inp, status_override=kept)
+    zero = base.status.copy()
+    zero[1, 0] = 0
+    _refuses(inp, status_override=zero)
+
+
+def test_check_routing_refuses_a_wrong_expert_at_a_near_tie():
+    """The GPU parity check itself: at the set near tie only the tied expert may come in."""
+    import parity
+    inp = _router_inputs([[3.0, 1.00005, 1.0, 0.5], [2.0, 1.0, 0.0, -1.0]])
+    res = oracle.forward(inp, tokens=[])
+
+    def run(ids):
+        ids = np.asarray(ids, dtype=np.int32)
+        w0 = np.array([1 / (1 + math.exp(res.logits[t, ids[t, 1]] - res.logits[t, ids[t, 0]]))
+                       for t in range(2)], dtype=np.float32)
+        w = np.stack([w0, np.float32(1) - w0], 1)
+        return parity.check_routing(res, ids, w, res.logits.astype(np.float32), 1e-6)
+
+    assert run([[0, 2], [0, 1]]) == {0: (0, 2)}
+    for bad in ([[0, 3], [0, 1]], [[3, 2], [0, 1]], [[0, 1], [0, 2]]):
+        with pytest.raises(AssertionError):
+            run(bad)
+
+
 # ------------------------------------------------- configs and inputs ---
 
 # --------------------------------------------------------------- MXFP4 ---
