@@ -175,8 +175,9 @@ moe_status_t moe_route_topk(const moe_shape_t* shape, const void* x, const void*
 /* Capacity selection (when shape->capacity >= 0) and grouping of tokens by expert.
  * Pages: "How Mixtral 8x7B uses mixture of experts", sections "Routing without
  * auxiliary loss" (capacity-limited dispatch, excess dropped) and the
- * bincount of the top-2 ids (expert activation listing); "batch tokens by
- * expert ... scatter back" in the simplified forward pass.
+ * bincount of the top-2 ids (expert activation listing); the simplified
+ * forward pass, which batches each expert's tokens and writes results back in
+ * token order.
  *   topk_ids, topk_weights [T, k] from moe_route_topk
  *   next_ids       [T, 2] from moe_route_topk; required with a capacity and
  *                  MOE_OVERFLOW_NEXT_BEST, else ignored (may be NULL)
@@ -248,7 +249,7 @@ moe_status_t moe_expert_gemm_down(const moe_shape_t* shape, const void* h, const
  * 0 when every slot is dropped and there is no shared expert; accumulated in
  * fp32 in slot order (shared last), cast to the act dtype (round to nearest even).
  * Pages: "Mixtral and Mixture-of-Experts, Explained", y = sum_i G(x)_i Expert_i(x);
- * study notes, output = zeros_like(x) then weighted accumulation.
+ * study notes, an all-zero output of x's shape, then weighted accumulation.
  *   y_perm [R, d] fp32; slot_to_row [R] int32; topk_weights [T, k] fp32
  *   y      [T, d] act dtype out.  No workspace. */
 moe_status_t moe_combine(const moe_shape_t* shape, const float* y_perm, const int32_t* slot_to_row,

@@ -1,8 +1,8 @@
 // Gate-weighted combine back to token order.
 //
 // Pages: "Mixtral and Mixture-of-Experts, Explained", y = sum_i G(x)_i *
-// Expert_i(x); "Mixtral" study notes, MoE forward (output = zeros_like(x),
-// then each expert's rows accumulated with their gate weight).
+// Expert_i(x); "Mixtral" study notes, MoE forward (the output starts at zero
+// in x's shape, then each expert's rows are accumulated with their gate weight).
 //
 // One workgroup per token row: y[t] = G0 * y_perm[row0] + G1 * y_perm[row1]
 // over the kept slots (a dropped slot has row -1 and adds nothing), computed

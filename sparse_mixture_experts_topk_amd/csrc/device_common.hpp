@@ -31,6 +31,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
+// E8M0 exponent of an fp8 activation block (x rows in the permute, h in the
+// gate/up epilogue: one rule for both): ceil(log2(fp32(amax / 448))) clamped
+// to [-127, 127]; 0 for an all-zero block.  amax / 448 is one fp32 division;
+// the exponent is read from its bits (a subnormal quotient included).
+__device__ __forceinline__ int block_exponent(float amax) {
+  if (amax == 0.0f) return 0;
+  const uint32_t bits = __float_as_uint(amax / 448.0f);
+  const int ex = (int)((bits >> 23) & 255u);
+  const uint32_t man = bits & 0x7fffffu;
+  if (ex == 0) return man > (1u << 22) ? -126 : -127;  // subnormal quotient
+  return man == 0 ? ex - 127 : ex - 126;
+}
+
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }

@@ -29,17 +29,6 @@
 namespace moe {
 namespace {
 
-// E8M0 exponent of a block: ceil(log2(fp32(amax / 448))) clamped to [-127, 127];
-// 0 for an all-zero block.
-__device__ __forceinline__ int block_exponent(float amax) {
-  if (amax == 0.0f) return 0;
-  const uint32_t bits = __float_as_uint(amax / 448.0f);
-  const int ex = (int)((bits >> 23) & 255u);
-  const uint32_t man = bits & 0x7fffffu;
-  if (ex == 0) return man > (1u << 22) ? -126 : -127;
-  return man == 0 ? ex - 127 : ex - 126;
-}
-
 // ---------------------------------------------------------------------------
 // Persistent tile kernel: the bf16 prefill kernel's pipeline with fp8 operands.
 //

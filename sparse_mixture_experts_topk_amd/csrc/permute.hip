@@ -3,8 +3,9 @@
 // Pages: "How Mixtral 8x7B uses mixture of experts" -- capacity-limited
 // dispatch ("Routing without auxiliary loss": over-capacity tokens are
 // dropped), the per-expert bincount of the top-2 ids (expert activation
-// listing) and "batch tokens by expert, run experts in parallel, scatter
-// back" (simplified forward pass).
+// listing) and the simplified forward pass, which gathers each expert's
+// tokens into one batch, runs the experts on their batches and writes the
+// results back in token order.
 //
 // capacity_select: one workgroup per expert.  Each assignment gets the
 //   64-bit key (fp32 bits of its gate weight) << 32 | (0xffffffff - token),
@@ -422,17 +423,6 @@ __global__ __launch_bounds__(256) void permute_scatter_copy_kernel(
   const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)tok * row_bytes);
   uint4* dst = reinterpret_cast<uint4*>(x_perm + (int64_t)row * row_bytes);
   for (int c = lane; c < row_bytes / 16; c += kWave) dst[c] = src[c];
-}
-
-// E8M0 exponent of a block: ceil(log2(fp32(amax / 448))) clamped to [-127, 127];
-// 0 for an all-zero block.
-__device__ __forceinline__ int block_exponent(float amax) {
-  if (amax == 0.0f) return 0;
-  const uint32_t bits = __float_as_uint(amax / 448.0f);
-  const int ex = (int)((bits >> 23) & 255u);
-  const uint32_t man = bits & 0x7fffffu;
-  if (ex == 0) return man > (1u << 22) ? -126 : -127;  // subnormal quotient
-  return man == 0 ? ex - 127 : ex - 126;
 }
 
 // 32 bf16 values -> 32 e4m3 codes with scale 2^e (exact multiply by 2^-e, one rounding).

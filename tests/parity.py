@@ -166,11 +166,15 @@ def token_of_slot(src, T, k):
     return np.where(src < T * k, src // k, src - T * k)
 
 
-def sample_tokens(res, n_random=24, seed=0, edge_groups=None):
-    """Tokens that own rows at expert and 256-row tile edges, plus random ones.
+def sample_tokens(res, n_random=24, seed=0, edge_groups=None, tile_rows=256):
+    """Tokens that own the first and last row of every ``tile_rows``-row token tile of every
+    expert group (the tiled GEMMs start a group's tiles at its first row, so every
+    (expert, token tile) -- and with it every channel tile and every K-split tail tile, which
+    a token's full output row crosses -- has checked rows), the last two rows of each group,
+    plus random tokens.
 
-    edge_groups: look at the edges of only this many expert groups, evenly
-    spread and including the last (many-expert configs)."""
+    edge_groups: look at the tiles of only this many expert groups, evenly spread and
+    including the last (many-expert configs)."""
     p = res.perm
     groups = range(len(p.counts))
     if edge_groups is not None and edge_groups < len(p.counts):
@@ -178,11 +182,26 @@ def sample_tokens(res, n_random=24, seed=0, edge_groups=None):
     rows = set()
     for e in groups:
         a, b = int(p.offsets[e]), int(p.offsets[e + 1])
-        for r in (a, a + 255, a + 256, b - 1, b - 2):
-            if a <= r < b:
-                rows.add(r)
+        for start in range(a, b, tile_rows):
+            rows.update({start, min(start + tile_rows, b) - 1})
+        rows.update(r for r in (b - 2,) if r >= a)
     T, k = res.routing.ids.shape
     toks = {int(token_of_slot(p.perm_src[r], T, k)) for r in rows}
     toks |= {0, T - 1}
     toks |= set(np.random.default_rng(seed).choice(T, size=min(n_random, T), replace=False).tolist())
     return sorted(toks)
+
+
+def tile_coverage(res, tokens, tile_rows=256):
+    """(token tiles with at least one checked row, token tiles) over all expert groups."""
+    p = res.perm
+    T, k = res.routing.ids.shape
+    n = int(p.offsets[-1])
+    checked = np.isin(token_of_slot(p.perm_src[:n], T, k), np.asarray(list(tokens)))
+    hit = tot = 0
+    for e in range(len(p.counts)):
+        a, b = int(p.offsets[e]), int(p.offsets[e + 1])
+        for start in range(a, b, tile_rows):
+            tot += 1
+            hit += bool(checked[start:min(start + tile_rows, b)].any())
+    return hit, tot

@@ -13,7 +13,8 @@ import oracle
 import sparse_mixture_experts_topk_amd as moe
 from sparse_mixture_experts_topk_amd import runner, synthetic
 from parity import (adjusted_oracle, assert_close, cached_inputs, check_next, check_permutation,
-                    check_routing, rel_errors, sample_tokens, to_np, token_of_slot, tol_key)
+                    check_routing, rel_errors, sample_tokens, tile_coverage, to_np, token_of_slot,
+                    tol_key)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,8 +93,10 @@ def run_staged_and_check(cfg, inputs=None, tokens=None, check_h=True):
     y = to_np(st["y"].float())[want]
     fro, mx = assert_close(y, res.y[want], key, "y (layer output)")
     say(f"  y rel_frob={fro:.3e} rel_max={mx:.3e}")
+    hit, tot = tile_coverage(res, want)
     record(cfg.name, h_rel_frob=h_fro, y_perm_rel_frob=yp_fro, y_rel_frob=fro, y_rel_max=mx,
-           tokens_checked=len(want), dropped=int((~res.keep).sum()))
+           tokens_checked=len(want), token_tiles_checked=hit, token_tiles=tot,
+           dropped=int((~res.keep).sum()))
     return st, res, inputs
 
 
@@ -436,11 +439,34 @@ def test_decode_mxfp4_config_full():
 
 
 def test_longctx_fp8_config_sampled():
+    """Gated against the oracle with the declared fp8 activation quantisation; also reports (not
+    gated) the error against the dequantised-weight oracle without activation quantisation and
+    against the unquantised weights the fp8 codes were drawn from ('How Mixtral 8x7B uses mixture
+    of experts', 'Quantization asymmetry': the pages quantise the experts only)."""
     cfg = synthetic.CONFIGS["longctx_fp8"]
     inp = cached_inputs("longctx_fp8")
     base = oracle.forward(inp, tokens=[])
     toks = sample_tokens(base, n_random=16)
-    run_staged_and_check(cfg, inputs=inp, tokens=toks, check_h=True)
+    st, res, _ = run_staged_and_check(cfg, inputs=inp, tokens=toks, check_h=True)
+    gpu_ids = to_np(st["topk_ids"])
+    override = {int(t): tuple(int(v) for v in gpu_ids[t]) for t in oracle.near_tie_tokens(base)}
+    y = to_np(st["y"].float())[toks]
+    deq = oracle.forward(inp, tokens=toks, override=override, fp8_act_quant=False)
+    fro_deq, mx_deq = rel_errors(y, deq.y[toks])
+    w1, w3, w2 = synthetic.unquantized_weights(cfg)
+    raw = synthetic.MoEInputs(cfg.replace(w_dtype="f32"), inp.x, inp.w_gate, inp.router_bias,
+                              w1, w3, w2)
+    unq = oracle.forward(raw, tokens=toks, override=override)
+    del w1, w3, w2, raw
+    fro_unq, mx_unq = rel_errors(y, unq.y[toks])
+    fro_act, _ = rel_errors(res.y[toks], deq.y[toks])
+    say(f"  report only: vs dequantised weights without activation quantisation "
+        f"rel_frob={fro_deq:.3e}; vs unquantised weights rel_frob={fro_unq:.3e}; "
+        f"oracle's own activation-quantisation effect {fro_act:.3e}")
+    record("longctx_fp8_report_only", y_rel_frob_vs_dequant_no_act_quant=fro_deq,
+           y_rel_max_vs_dequant_no_act_quant=mx_deq, y_rel_frob_vs_unquantized=fro_unq,
+           y_rel_max_vs_unquantized=mx_unq, oracle_act_quant_vs_no_act_quant=fro_act,
+           tokens_checked=len(toks))
 
 
 # ------------------------------------- general top-k, many experts, shared ---
