@@ -23,7 +23,9 @@
  * --------------------------------
  * - All tensor arguments are DEVICE pointers to row-major arrays owned by
  *   the caller.  The library allocates no memory, keeps no mutable global
- *   state and is re-entrant; calls on different streams may overlap.
+ *   state and is re-entrant; calls on different streams may overlap.  The one
+ *   exception is moe_forward_noalloc (below), which uses a device array of the
+ *   library's own and remembers its address per device.
  * - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
  *   stream).  Every call only enqueues work on it and returns without
  *   waiting for the device; no call reads device memory on the host.
@@ -273,6 +275,36 @@ moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const void* w_
                          void* y, int32_t* topk_ids_out, float* topk_weights_out,
                          int32_t* expert_counts_out, uint8_t* drop_mask_out, float* logits_out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the device scratch array behind moe_forward_noalloc (64 MiB per GPU). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results (bit for bit) and errors as moe_forward, without the
+ * workspace: the intermediates live in a file-scope device array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends.  This call allocates nothing and calls no
+ * allocating routine.
+ *   Limit: a shape whose moe_workspace_bytes(shape, MOE_CALL_FORWARD) exceeds
+ *   MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE with nothing enqueued.
+ *   That admits the weight-streaming (decode) shapes: at d_model 4096, d_ff
+ *   14336, top-2 bf16 a token needs about 106 KiB (T <= 64 there: larger
+ *   batches take the tiled path, whose split-tail buffer alone is larger).
+ *   Device: `stream` must belong to the current device (else
+ *   MOE_ERR_INVALID_ARG); the first call on a device looks up that device's
+ *   address of the array (MOE_ERR_HIP if that fails; at most 64 devices).
+ *   Concurrency: all calls on one GPU share its array, which keeps the last
+ *   call's contents; calls that overlap on one GPU (other streams or threads)
+ *   race on it and must be serialised by the caller.  No kernel of the layer
+ *   reads scratch it has not written in the same call, so nothing needs
+ *   clearing between calls. */
+moe_status_t moe_forward_noalloc(const moe_shape_t* shape, const void* x, const void* w_gate,
+                                 const float* router_bias, const void* w1, const void* w3,
+                                 const void* w2, const void* w1_scale, const void* w3_scale,
+                                 const void* w2_scale, void* y, int32_t* topk_ids_out,
+                                 float* topk_weights_out, int32_t* expert_counts_out,
+                                 uint8_t* drop_mask_out, float* logits_out, void* stream);
 
 #ifdef __cplusplus
 }

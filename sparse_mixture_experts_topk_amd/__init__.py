@@ -15,12 +15,13 @@ import torch
 
 from . import _lib
 from ._lib import (MOE_BF16, MOE_CALL_DOWN, MOE_CALL_FORWARD, MOE_CALL_GATE_UP,
-                   MOE_CALL_PERMUTE, MOE_CALL_ROUTE, MOE_DROPLESS, MOE_F32, MOE_FP8_E4M3, MOE_MXFP4, MOE_OVERFLOW_DROP,
-                   MOE_OVERFLOW_NEXT_BEST, MoeShape)
+                   MOE_CALL_PERMUTE, MOE_CALL_ROUTE, MOE_DROPLESS, MOE_F32, MOE_FP8_E4M3, MOE_MXFP4,
+                   MOE_NOALLOC_SCRATCH_BYTES, MOE_OVERFLOW_DROP, MOE_OVERFLOW_NEXT_BEST, MoeShape)
 
 __all__ = ["MoEError", "MoeShape", "make_shape", "moe_status_string", "moe_version",
            "moe_workspace_bytes", "moe_route_topk", "moe_permute", "moe_expert_gemm_gate_up",
-           "moe_expert_gemm_down", "moe_combine", "moe_forward", "MOE_F32", "MOE_BF16",
+           "moe_expert_gemm_down", "moe_combine", "moe_forward", "moe_forward_noalloc",
+           "MOE_NOALLOC_SCRATCH_BYTES", "MOE_F32", "MOE_BF16",
            "MOE_FP8_E4M3", "MOE_MXFP4", "MOE_DROPLESS", "MOE_CALL_PERMUTE", "MOE_CALL_GATE_UP",
            "MOE_CALL_DOWN", "MOE_CALL_FORWARD", "MOE_CALL_ROUTE", "MOE_OVERFLOW_DROP", "MOE_OVERFLOW_NEXT_BEST"]
 
@@ -139,3 +140,13 @@ def moe_forward(shape, x, w_gate, router_bias, w1, w3, w2, w1_scale, w3_scale, w
         _p(w1_scale), _p(w3_scale), _p(w2_scale), _p(y), _p(topk_ids_out),
         _p(topk_weights_out), _p(expert_counts_out), _p(drop_mask_out), _p(logits_out),
         _p(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_forward_noalloc(shape, x, w_gate, router_bias, w1, w3, w2, w1_scale, w3_scale, w2_scale, y,
+                        topk_ids_out=None, topk_weights_out=None, expert_counts_out=None,
+                        drop_mask_out=None, logits_out=None, stream=None):
+    _check("moe_forward_noalloc", _lib.load().moe_forward_noalloc(
+        ctypes.byref(shape), _p(x), _p(w_gate), _p(router_bias), _p(w1), _p(w3), _p(w2),
+        _p(w1_scale), _p(w3_scale), _p(w2_scale), _p(y), _p(topk_ids_out),
+        _p(topk_weights_out), _p(expert_counts_out), _p(drop_mask_out), _p(logits_out),
+        _stream(stream)))

@@ -11,11 +11,12 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 MOE_DROPLESS = -1
 MOE_OVERFLOW_DROP, MOE_OVERFLOW_NEXT_BEST = 0, 1
 MOE_CALL_PERMUTE, MOE_CALL_GATE_UP, MOE_CALL_DOWN, MOE_CALL_FORWARD, MOE_CALL_ROUTE = range(5)
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_bytes", "moe_route_topk",
            "moe_permute", "moe_expert_gemm_gate_up", "moe_expert_gemm_down", "moe_combine",
-           "moe_forward")
+           "moe_forward", "moe_forward_noalloc")
 
 
 class MoeShape(ctypes.Structure):
@@ -41,6 +42,7 @@ _SIGNATURES = {
     "moe_expert_gemm_down": (I32, [SHAPE, P, P, P, P, P, P, P, SZ, P]),
     "moe_combine": (I32, [SHAPE, P, P, P, P, P]),
     "moe_forward": (I32, [SHAPE, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+    "moe_forward_noalloc": (I32, [SHAPE, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]),
 }
 
 _lib = None

@@ -4,6 +4,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "launch.hpp"
@@ -178,6 +179,92 @@ ForwardLayout forward_layout(const moe_shape_t& s) {
 template <typename T>
 T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<uint8_t*>(base) + off); }
 
+moe_status_t forward_impl(const moe_shape_t* s, const void* x, const void* w_gate,
+                          const float* router_bias, const void* w1, const void* w3, const void* w2,
+                          const void* w1_scale, const void* w3_scale, const void* w2_scale,
+                          void* y, int32_t* topk_ids_out, float* topk_weights_out,
+                          int32_t* expert_counts_out, uint8_t* drop_mask_out, float* logits_out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status_t v = validate_shape(s);
+  if (v != MOE_OK) return v;
+  if (s->T == 0) return MOE_OK;
+  if ((v = check_ptrs({x, w_gate, w1, w3, w2, y},
+                      {router_bias, topk_ids_out, topk_weights_out, expert_counts_out,
+                       drop_mask_out, logits_out, w1_scale, w3_scale, w2_scale})) != MOE_OK)
+    return v;
+  const bool fp8 = s->w_dtype == MOE_FP8_E4M3;
+  const bool scaled = fp8 || s->w_dtype == MOE_MXFP4;
+  if (scaled && (w1_scale == nullptr || w3_scale == nullptr || w2_scale == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  const ForwardLayout L = forward_layout(*s);
+  if (workspace == nullptr || workspace_bytes < L.total || !aligned16(workspace))
+    return MOE_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(workspace, L.ids);
+  float* gw = topk_weights_out ? topk_weights_out : at<float>(workspace, L.weights);
+  int32_t* counts = expert_counts_out ? expert_counts_out : at<int32_t>(workspace, L.counts);
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* perm_src = at<int32_t>(workspace, L.perm_src);
+  int32_t* slot_to_row = at<int32_t>(workspace, L.slot_to_row);
+  uint8_t* drop = drop_mask_out ? drop_mask_out : at<uint8_t>(workspace, L.drop);
+  void* x_perm = at<void>(workspace, L.x_perm);
+  uint8_t* x_scale = fp8 ? at<uint8_t>(workspace, L.x_scale) : nullptr;
+  void* h = at<void>(workspace, L.h);
+  uint8_t* h_scale = fp8 ? at<uint8_t>(workspace, L.h_scale) : nullptr;
+  float* y_perm = at<float>(workspace, L.y_perm);
+  int32_t* next = fallback_on(*s) ? at<int32_t>(workspace, L.next_ids) : nullptr;
+
+  hipError_t e = moe::launch_route_topk(*s, x, w_gate, router_bias, ids, gw, logits_out, next,
+                                       at<void>(workspace, L.route_logits), st);
+  const uint8_t* drop_in = nullptr;
+  if (e == hipSuccess) {
+    if (s->capacity >= 0) {
+      e = moe::launch_capacity_select(*s, ids, gw, next, drop, st);
+      drop_in = drop;
+    } else if (drop_mask_out != nullptr) {
+      e = launch_fill_u8(drop_mask_out, (int64_t)s->T * s->top_k, 0, st);
+    }
+  }
+  if (e == hipSuccess)
+    e = moe::launch_permute_index(*s, ids, drop_in, next, counts, offsets, perm_src, slot_to_row, st);
+  if (e == hipSuccess) e = moe::launch_permute_scatter(*s, x, offsets, perm_src, x_perm, x_scale, st);
+  if (e == hipSuccess)
+    e = moe::launch_gate_up(*s, x_perm, x_scale, offsets, w1, w3, w1_scale, w3_scale, h, h_scale, st);
+  void* down_ws = down_workspace_bytes(*s) > 0 ? at<void>(workspace, L.down_ws) : nullptr;
+  if (e == hipSuccess)
+    e = moe::launch_down(*s, h, h_scale, offsets, w2, w2_scale, y_perm, down_ws, st);
+  if (e == hipSuccess) e = moe::launch_combine(*s, y_perm, slot_to_row, gw, y, st);
+  return from_hip(e);
+}
+
+
+// Device scratch of moe_forward_noalloc: the intermediates of one layer call
+// live here instead of in a caller workspace.  Every GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` is only
+// a host-side stand-in: kernels get the per-device address that
+// hipGetSymbolAddress returns (scratch_address below), never the name.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+
+// Address of device `dev`'s copy of `scratch` (dev must be the current
+// device); looked up once per device, on the first call there.
+hipError_t scratch_address(int dev, void** out) {
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess && p == nullptr) e = hipErrorInvalidSymbol;
+    g_scratch_err[dev] = e;
+    g_scratch_ptr[dev] = e == hipSuccess ? p : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -318,57 +405,36 @@ moe_status_t moe_forward(const moe_shape_t* s, const void* x, const void* w_gate
                          void* y, int32_t* topk_ids_out, float* topk_weights_out,
                          int32_t* expert_counts_out, uint8_t* drop_mask_out, float* logits_out,
                          void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_impl(s, x, w_gate, router_bias, w1, w3, w2, w1_scale, w3_scale, w2_scale, y,
+                      topk_ids_out, topk_weights_out, expert_counts_out, drop_mask_out, logits_out,
+                      workspace, workspace_bytes, stream);
+}
+
+moe_status_t moe_forward_noalloc(const moe_shape_t* s, const void* x, const void* w_gate,
+                                 const float* router_bias, const void* w1, const void* w3,
+                                 const void* w2, const void* w1_scale, const void* w3_scale,
+                                 const void* w2_scale, void* y, int32_t* topk_ids_out,
+                                 float* topk_weights_out, int32_t* expert_counts_out,
+                                 uint8_t* drop_mask_out, float* logits_out, void* stream) {
   moe_status_t v = validate_shape(s);
   if (v != MOE_OK) return v;
   if (s->T == 0) return MOE_OK;
-  if ((v = check_ptrs({x, w_gate, w1, w3, w2, y},
-                      {router_bias, topk_ids_out, topk_weights_out, expert_counts_out,
-                       drop_mask_out, logits_out, w1_scale, w3_scale, w2_scale})) != MOE_OK)
-    return v;
-  const bool fp8 = s->w_dtype == MOE_FP8_E4M3;
-  const bool scaled = fp8 || s->w_dtype == MOE_MXFP4;
-  if (scaled && (w1_scale == nullptr || w3_scale == nullptr || w2_scale == nullptr))
-    return MOE_ERR_INVALID_ARG;
-  const ForwardLayout L = forward_layout(*s);
-  if (workspace == nullptr || workspace_bytes < L.total || !aligned16(workspace))
-    return MOE_ERR_WORKSPACE;
-
+  // the shape's intermediates must fit the library's scratch array
+  if (forward_layout(*s).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(workspace, L.ids);
-  float* gw = topk_weights_out ? topk_weights_out : at<float>(workspace, L.weights);
-  int32_t* counts = expert_counts_out ? expert_counts_out : at<int32_t>(workspace, L.counts);
-  int32_t* offsets = at<int32_t>(workspace, L.offsets);
-  int32_t* perm_src = at<int32_t>(workspace, L.perm_src);
-  int32_t* slot_to_row = at<int32_t>(workspace, L.slot_to_row);
-  uint8_t* drop = drop_mask_out ? drop_mask_out : at<uint8_t>(workspace, L.drop);
-  void* x_perm = at<void>(workspace, L.x_perm);
-  uint8_t* x_scale = fp8 ? at<uint8_t>(workspace, L.x_scale) : nullptr;
-  void* h = at<void>(workspace, L.h);
-  uint8_t* h_scale = fp8 ? at<uint8_t>(workspace, L.h_scale) : nullptr;
-  float* y_perm = at<float>(workspace, L.y_perm);
-  int32_t* next = fallback_on(*s) ? at<int32_t>(workspace, L.next_ids) : nullptr;
-
-  hipError_t e = moe::launch_route_topk(*s, x, w_gate, router_bias, ids, gw, logits_out, next,
-                                       at<void>(workspace, L.route_logits), st);
-  const uint8_t* drop_in = nullptr;
-  if (e == hipSuccess) {
-    if (s->capacity >= 0) {
-      e = moe::launch_capacity_select(*s, ids, gw, next, drop, st);
-      drop_in = drop;
-    } else if (drop_mask_out != nullptr) {
-      e = launch_fill_u8(drop_mask_out, (int64_t)s->T * s->top_k, 0, st);
-    }
+  if (st != nullptr) {
+    int stream_dev = -1;
+    if (hipStreamGetDevice(st, &stream_dev) != hipSuccess || stream_dev != dev)
+      return MOE_ERR_INVALID_ARG;   // the scratch address belongs to the current device
   }
-  if (e == hipSuccess)
-    e = moe::launch_permute_index(*s, ids, drop_in, next, counts, offsets, perm_src, slot_to_row, st);
-  if (e == hipSuccess) e = moe::launch_permute_scatter(*s, x, offsets, perm_src, x_perm, x_scale, st);
-  if (e == hipSuccess)
-    e = moe::launch_gate_up(*s, x_perm, x_scale, offsets, w1, w3, w1_scale, w3_scale, h, h_scale, st);
-  void* down_ws = down_workspace_bytes(*s) > 0 ? at<void>(workspace, L.down_ws) : nullptr;
-  if (e == hipSuccess)
-    e = moe::launch_down(*s, h, h_scale, offsets, w2, w2_scale, y_perm, down_ws, st);
-  if (e == hipSuccess) e = moe::launch_combine(*s, y_perm, slot_to_row, gw, y, st);
-  return from_hip(e);
+  void* ws = nullptr;
+  if (scratch_address(dev, &ws) != hipSuccess) return MOE_ERR_HIP;
+  return forward_impl(s, x, w_gate, router_bias, w1, w3, w2, w1_scale, w3_scale, w2_scale, y,
+                      topk_ids_out, topk_weights_out, expert_counts_out, drop_mask_out, logits_out,
+                      ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

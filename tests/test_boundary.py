@@ -211,3 +211,19 @@ def test_python_binding_requires_device_tensors():
     x = torch.zeros(16, 4096, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         moe.moe_route_topk(S(), x, x, None, x, x)
+
+
+def test_noalloc_forward_rejects_shapes_beyond_its_scratch_on_the_host():
+    """moe_forward_noalloc checks the shape against its fixed scratch before any device call."""
+    lib = _lib.load()
+    fake = 1 << 20                       # aligned non-NULL; never dereferenced on this path
+    for cfg, expect in ((S(T=8192), 3), (S(T=0), 0), (S(T=16, top_k=9, n_experts=16), 2), (S(T=16, d_model=100), 2)):
+        args = [ctypes.byref(cfg)] + [fake] * 15 + [None]
+        args[3] = None                   # router bias
+        assert lib.moe_forward_noalloc(*args) == expect
+    big = ctypes.c_size_t(0)
+    lib.moe_workspace_bytes(ctypes.byref(S(T=8192)), moe.MOE_CALL_FORWARD, ctypes.byref(big))
+    assert big.value > moe.MOE_NOALLOC_SCRATCH_BYTES
+    small = ctypes.c_size_t(0)
+    lib.moe_workspace_bytes(ctypes.byref(S(T=64)), moe.MOE_CALL_FORWARD, ctypes.byref(small))
+    assert small.value <= moe.MOE_NOALLOC_SCRATCH_BYTES
