@@ -71,7 +71,7 @@ constexpr int F8T_SCG = 32;                         // slices per scale group (6
 constexpr int F8T_SCQ = F8T_TB / 4 / F8T_NW;        // scale loads per wavefront per group (4 rows each)
 constexpr int F8T_SLOTS = 3 * F8T_WB;               // load slots of a slice (the first half's instructions)
 constexpr int F8T_OOB = 0x7ff00000;                 // offset past every descriptor
-constexpr int kF8GroupN = 8;                        // channel tiles per group of the tile order
+constexpr int kF8GroupN = 4;                        // channel tiles per group of the tile order
 static_assert(F8T_JA * F8T_RPI * F8T_NW == F8T_TA && F8T_JB * F8T_RPI * F8T_NW == F8T_TB, "whole loads");
 static_assert(F8T_DMA + 1 <= F8T_SLOTS, "one load slot per matrix instruction of the first half");
 static_assert((F8T_NW * F8T_RPI) % 16 == 0, "loads of a wavefront are whole swizzle periods apart");
