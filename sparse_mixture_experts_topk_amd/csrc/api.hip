@@ -215,22 +215,35 @@ moe_status_t forward_impl(const moe_shape_t* s, const void* x, const void* w_gat
   float* y_perm = at<float>(workspace, L.y_perm);
   int32_t* next = fallback_on(*s) ? at<int32_t>(workspace, L.next_ids) : nullptr;
 
-  hipError_t e = moe::launch_route_topk(*s, x, w_gate, router_bias, ids, gw, logits_out, next,
-                                       at<void>(workspace, L.route_logits), st);
-  const uint8_t* drop_in = nullptr;
-  if (e == hipSuccess) {
-    if (s->capacity >= 0) {
-      e = moe::launch_capacity_select(*s, ids, gw, next, drop, st);
-      drop_in = drop;
-    } else if (drop_mask_out != nullptr) {
+  hipError_t e = hipSuccess;
+  if (moe::route_index_fused(*s) && s->w_dtype == MOE_BF16) {
+    // decode: router + grouping in one workgroup; gate/up reads x through perm_src
+    e = moe::launch_route_index(*s, x, w_gate, router_bias, ids, gw, logits_out, counts, offsets, perm_src,
+                                slot_to_row, st);
+    if (e == hipSuccess && drop_mask_out != nullptr)
       e = launch_fill_u8(drop_mask_out, (int64_t)s->T * s->top_k, 0, st);
+    if (e == hipSuccess)
+      e = moe::launch_gate_up_bf16_gather(*s, static_cast<const uint16_t*>(x), perm_src, offsets,
+                                          static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3),
+                                          static_cast<uint16_t*>(h), st);
+  } else {
+    e = moe::launch_route_topk(*s, x, w_gate, router_bias, ids, gw, logits_out, next,
+                               at<void>(workspace, L.route_logits), st);
+    const uint8_t* drop_in = nullptr;
+    if (e == hipSuccess) {
+      if (s->capacity >= 0) {
+        e = moe::launch_capacity_select(*s, ids, gw, next, drop, st);
+        drop_in = drop;
+      } else if (drop_mask_out != nullptr) {
+        e = launch_fill_u8(drop_mask_out, (int64_t)s->T * s->top_k, 0, st);
+      }
     }
+    if (e == hipSuccess)
+      e = moe::launch_permute_index(*s, ids, drop_in, next, counts, offsets, perm_src, slot_to_row, st);
+    if (e == hipSuccess) e = moe::launch_permute_scatter(*s, x, offsets, perm_src, x_perm, x_scale, st);
+    if (e == hipSuccess)
+      e = moe::launch_gate_up(*s, x_perm, x_scale, offsets, w1, w3, w1_scale, w3_scale, h, h_scale, st);
   }
-  if (e == hipSuccess)
-    e = moe::launch_permute_index(*s, ids, drop_in, next, counts, offsets, perm_src, slot_to_row, st);
-  if (e == hipSuccess) e = moe::launch_permute_scatter(*s, x, offsets, perm_src, x_perm, x_scale, st);
-  if (e == hipSuccess)
-    e = moe::launch_gate_up(*s, x_perm, x_scale, offsets, w1, w3, w1_scale, w3_scale, h, h_scale, st);
   void* down_ws = down_workspace_bytes(*s) > 0 ? at<void>(workspace, L.down_ws) : nullptr;
   if (e == hipSuccess)
     e = moe::launch_down(*s, h, h_scale, offsets, w2, w2_scale, y_perm, down_ws, st);

@@ -30,7 +30,7 @@ template <bool DUAL, int ROWS, int MIN_WAVES>
 __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gemm_bf16_decode(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
     const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, int N, int K,
-    void* __restrict__ out, int tok_tiles) {
+    void* __restrict__ out, int tok_tiles, const int32_t* __restrict__ gather, int k, int Tk) {
   constexpr int KB = 512 / ROWS;        // elements per row per stage
   constexpr int CPR = KB / 8;           // 16-byte chunks per row per stage
   constexpr int NL = 16 / ROWS;         // load instructions per matrix per stage
@@ -60,7 +60,14 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gem
   // matrix-core operand: lane (r, g) feeds row r, chunk 4 j + g of MFMA j
   const int r = lane & 15, g = lane >> 4;
   const bool tok_ok = r < rows;
-  const uint16_t* px = act + (int64_t)(row0 + (tok_ok ? r : 0)) * K + g * 8;
+  // token operand row: a permuted row, or (gather) the token row of x that
+  // permuted row copies (slot t*k + s -> token t; the shared expert's T*k + t -> t)
+  int arow = row0 + (tok_ok ? r : 0);
+  if (gather != nullptr) {
+    const int src = gather[arow];
+    arow = src < Tk ? src / k : src - Tk;
+  }
+  const uint16_t* px = act + (int64_t)arow * K + g * 8;
 
   f32x4_t acc[NM];
 #pragma unroll
@@ -118,14 +125,14 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gem
 template <bool DUAL, int ROWS, int MIN_WAVES>
 hipError_t launch_variant(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                           const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
-                          hipStream_t st) {
+                          hipStream_t st, const int32_t* gather = nullptr) {
   const int tok_tiles = (int)((max_rows_per_expert(s) + 15) / 16);
   const int64_t groups = (int64_t)expert_groups(s) * tok_tiles * (N / 16);
   if (groups <= 0) return hipSuccess;   // no expert can hold a row (capacity 0)
   const int64_t blocks = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
   hipLaunchKernelGGL((grouped_gemm_bf16_decode<DUAL, ROWS, MIN_WAVES>), dim3((unsigned)blocks),
                      dim3(kWavesPerBlock * kWave), 0, st, act, offsets, expert_groups(s), wa, wb, N, K,
-                     out, tok_tiles);
+                     out, tok_tiles, gather, s.top_k, s.T * s.top_k);
   return hipGetLastError();
 }
 
@@ -139,6 +146,12 @@ hipError_t launch_decode_bf16(const moe_shape_t& s, bool dual, const uint16_t* a
   if (dual) return launch_variant<true, 8, 4>(s, act, offsets, wa, wb, N, K, out, st);
   if (K % 128 == 0) return launch_variant<false, 4, 4>(s, act, offsets, wa, wb, N, K, out, st);
   return launch_variant<false, 8, 4>(s, act, offsets, wa, wb, N, K, out, st);
+}
+
+hipError_t launch_gate_up_bf16_gather(const moe_shape_t& s, const uint16_t* x, const int32_t* perm_src,
+                                      const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
+                                      uint16_t* h, hipStream_t st) {
+  return launch_variant<true, 8, 4>(s, x, offsets, w1, w3, s.d_ff, s.d_model, h, st, perm_src);
 }
 
 }  // namespace moe

@@ -21,6 +21,19 @@ hipError_t launch_route_topk(const moe_shape_t& s, const void* x, const void* w_
                              int32_t* next_ids, void* workspace, hipStream_t st);
 size_t route_workspace_bytes(const moe_shape_t& s);
 
+// Decode steps of moe_forward (bf16, T <= 16, E <= 16, top-2, dropless, no
+// shared expert): router and grouping in one workgroup (route_index_fused),
+// and the gate/up weight streamer reading token rows of x through perm_src
+// instead of a permuted copy.
+bool route_index_fused(const moe_shape_t& s);
+hipError_t launch_route_index(const moe_shape_t& s, const void* x, const void* w_gate,
+                              const float* bias, int32_t* ids, float* weights, float* logits,
+                              int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                              int32_t* slot_to_row, hipStream_t st);
+hipError_t launch_gate_up_bf16_gather(const moe_shape_t& s, const uint16_t* x, const int32_t* perm_src,
+                                      const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
+                                      uint16_t* h, hipStream_t st);
+
 // Capacity selection: writes drop_mask[T*k] (0 kept, 1 dropped); with
 // MOE_OVERFLOW_NEXT_BEST a second round re-offers the dropped assignments to
 // next_ids and marks the ones taken with 2.

@@ -191,11 +191,20 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 // products are exact in fp32 and accumulate in fp32.
 constexpr int kRouteWaves = 8;
 
-template <int EB>
+//
+// INDEX (one workgroup: T <= 16, E <= 16, top-2, nothing dropped, no shared
+// expert): the workgroup that selected the experts also groups the tokens by
+// expert, writing what the permute index kernel would (counts, offsets, the
+// rows of each expert in ascending token order, perm_src and slot_to_row), so
+// a decode step needs no separate grouping launch.
+template <int EB, bool INDEX = false>
 __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias,
     int T, int d, int E, int k, int32_t* __restrict__ ids, float* __restrict__ wout,
-    float* __restrict__ logits, int32_t* __restrict__ next) {
+    float* __restrict__ logits, int32_t* __restrict__ next, int32_t* __restrict__ counts = nullptr,
+    int32_t* __restrict__ offsets = nullptr, int32_t* __restrict__ perm_src = nullptr,
+    int32_t* __restrict__ slot_to_row = nullptr) {
+  static_assert(!INDEX || EB == 1, "the grouping epilogue takes up to 16 experts");
   static_assert(EB * 4 <= 64, "one bit per expert of a lane in the taken mask");
   __shared__ f32x4_t part[kRouteWaves - 1][EB][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -306,6 +315,31 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
     }
   }
   if (g == 0 && tok < T) store_token(v, id, k, tok, ids, wout, next);
+  if constexpr (INDEX) {
+    // lane r (< 16) is token r; a token's two experts are distinct.  The rank
+    // of a token among an expert's tokens counts the lower tokens that chose it.
+    const bool me = g == 0 && tok < T;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int run = 0, row0 = 0, row1 = 0;
+    for (int e = 0; e < E; ++e) {
+      const uint64_t b = __ballot(me && (id[0] == e || id[1] == e));
+      const int c = __popcll(b);
+      if (lane == 0) {
+        offsets[e] = run;
+        counts[e] = c;
+      }
+      const int rk = run + __popcll(b & lt_mask);
+      if (id[0] == e) row0 = rk;
+      if (id[1] == e) row1 = rk;
+      run += c;
+    }
+    if (lane == 0) offsets[E] = run;
+    if (me) {
+      perm_src[row0] = 2 * tok;
+      perm_src[row1] = 2 * tok + 1;
+      reinterpret_cast<int2*>(slot_to_row)[tok] = make_int2(row0, row1);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -505,6 +539,22 @@ hipError_t launch_dtype(const moe_shape_t& s, const void* x, const void* wg, con
 }
 
 }  // namespace
+
+bool route_index_fused(const moe_shape_t& s) {
+  return s.act_dtype == MOE_BF16 && s.n_experts <= 16 && s.top_k == 2 && s.T <= 16 &&
+         s.capacity < 0 && s.n_shared == 0;
+}
+
+hipError_t launch_route_index(const moe_shape_t& s, const void* x, const void* w_gate,
+                              const float* bias, int32_t* ids, float* weights, float* logits,
+                              int32_t* counts, int32_t* offsets, int32_t* perm_src,
+                              int32_t* slot_to_row, hipStream_t st) {
+  hipLaunchKernelGGL((route_topk_mfma_kernel<1, true>), dim3(1), dim3(kRouteWaves * 64), 0, st,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate), bias, s.T,
+                     s.d_model, s.n_experts, s.top_k, ids, weights, logits, nullptr, counts, offsets,
+                     perm_src, slot_to_row);
+  return hipGetLastError();
+}
 
 size_t route_workspace_bytes(const moe_shape_t& s) {
   return route_two_pass(s) ? (size_t)s.T * s.n_experts * 4 : 0;

@@ -305,6 +305,39 @@ def test_forward_matches_staged_bitwise_and_is_deterministic(overflow):
     assert torch.equal(st["topk_ids"], ids1) and torch.equal(st["drop_mask"], drop1)
 
 
+@pytest.mark.parametrize("T,E", [(16, 8), (1, 8), (16, 16), (7, 2), (13, 3)])
+def test_decode_forward_fused_router_matches_staged(T, E):
+    """At decode shapes moe_forward groups tokens in the router's workgroup and the gate/up
+    weight streamer reads x through perm_src; every output must equal the staged calls'."""
+    cfg = mid_cfg(f"dec_fused_T{T}_E{E}", T=T, n_experts=E, seed=60 + T + E)
+    inp = synthetic.make_inputs(cfg)
+    say(f"decode moe_forward (fused router + grouping) vs staged: T={T} E={E}")
+    di = runner.DeviceInputs.from_host(inp)
+    st = runner.staged(di)
+    b = runner.forward(di)
+    torch.cuda.synchronize()
+    assert torch.equal(st["y"], b.y) and torch.equal(st["topk_ids"], b.topk_ids)
+    assert torch.equal(st["topk_weights"], b.topk_weights) and torch.equal(st["logits"], b.logits)
+    assert torch.equal(st["expert_counts"], b.expert_counts)
+    assert not b.drop_mask.any()
+    base, res = adjusted_oracle(inp, to_np(b.topk_ids))
+    assert_close(to_np(b.y.float()), res.y, "bf16", "decode y")
+
+
+def test_decode_config_fused_forward_full():
+    cfg = synthetic.CONFIGS["decode_bf16"]
+    inp = cached_inputs("decode_bf16")
+    say("decode config via moe_forward (the benchmarked call)")
+    di = runner.DeviceInputs.from_host(inp)
+    st = runner.staged(di)
+    b = runner.forward(di)
+    torch.cuda.synchronize()
+    assert torch.equal(st["y"], b.y) and torch.equal(st["expert_counts"], b.expert_counts)
+    _, res = adjusted_oracle(inp, to_np(b.topk_ids))
+    fro, mx = assert_close(to_np(b.y.float()), res.y, "bf16", "decode y (fused call)")
+    say(f"  y rel_frob={fro:.3e} rel_max={mx:.3e}")
+
+
 def test_combine_isolated():
     cfg = mid_cfg("combine", T=500, n_experts=8, capacity=120, seed=12)
     inp = synthetic.make_inputs(cfg)
