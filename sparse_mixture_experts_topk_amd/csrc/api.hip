@@ -216,16 +216,21 @@ moe_status_t forward_impl(const moe_shape_t* s, const void* x, const void* w_gat
   int32_t* next = fallback_on(*s) ? at<int32_t>(workspace, L.next_ids) : nullptr;
 
   hipError_t e = hipSuccess;
-  if (moe::route_index_fused(*s) && s->w_dtype == MOE_BF16) {
+  if (moe::route_index_fused(*s) && (s->w_dtype == MOE_BF16 || s->w_dtype == MOE_MXFP4)) {
     // decode: router + grouping in one workgroup; gate/up reads x through perm_src
     e = moe::launch_route_index(*s, x, w_gate, router_bias, ids, gw, logits_out, counts, offsets, perm_src,
                                 slot_to_row, st);
     if (e == hipSuccess && drop_mask_out != nullptr)
       e = launch_fill_u8(drop_mask_out, (int64_t)s->T * s->top_k, 0, st);
-    if (e == hipSuccess)
+    if (e == hipSuccess && s->w_dtype == MOE_BF16)
       e = moe::launch_gate_up_bf16_gather(*s, static_cast<const uint16_t*>(x), perm_src, offsets,
                                           static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3),
                                           static_cast<uint16_t*>(h), st);
+    if (e == hipSuccess && s->w_dtype == MOE_MXFP4)
+      e = moe::launch_gate_up_mxfp4_gather(*s, static_cast<const uint16_t*>(x), perm_src, offsets,
+                                           static_cast<const uint8_t*>(w1), static_cast<const uint8_t*>(w1_scale),
+                                           static_cast<const uint8_t*>(w3), static_cast<const uint8_t*>(w3_scale),
+                                           static_cast<uint16_t*>(h), st);
   } else {
     e = moe::launch_route_topk(*s, x, w_gate, router_bias, ids, gw, logits_out, next,
                                at<void>(workspace, L.route_logits), st);

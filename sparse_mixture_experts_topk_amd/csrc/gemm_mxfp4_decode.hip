@@ -70,7 +70,8 @@ template <bool DUAL, int RB, int MIN_WAVES, int PD, int KS>
 __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxfp4_decode(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
     const uint8_t* __restrict__ wa, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ wb,
-    const uint8_t* __restrict__ sb, int N, int K, void* __restrict__ out) {
+    const uint8_t* __restrict__ sb, int N, int K, void* __restrict__ out,
+    const int32_t* __restrict__ gather, int k, int Tk, int xrows) {
   constexpr int NM = DUAL ? 2 : 1;
   constexpr int CH = 16 * RB;                       // output channels per wavefront
   constexpr int GPW = kMx4Waves / KS;               // output groups per workgroup round
@@ -151,12 +152,26 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
   // compute cursor
   int cr = 0, cst = st_begin;
   Grp cgp = locate(0);
+  // Token operand: the group's permuted rows, or (gather) the rows of x those
+  // rows copy (slot t*k + s -> token t; the shared expert's T*k + t -> t).
+  // Lanes past the group's rows read beyond the range: zeros.
   auto token_rsrc = [&]() __attribute__((always_inline)) {
+    if (gather != nullptr)
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(act), 0, xrows * K * 2, 0x00020000);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(act) + (int64_t)cgp.row0 * K, 0,
                                              cgp.rows * K * 2, 0x00020000);
   };
+  auto token_off = [&]() __attribute__((always_inline)) -> int {
+    if (tr >= cgp.rows) return 0x7ff00000;
+    int row = tr;
+    if (gather != nullptr) {
+      const int src = gather[cgp.row0 + tr];
+      row = src < Tk ? src / k : src - Tk;
+    }
+    return (row * K + g * 32) * 2;
+  };
   __amdgpu_buffer_rsrc_t xrs = token_rsrc();
-  const int xoff_in = (tr * K + g * 32) * 2;
+  int xoff_cur = token_off();
 
   f32x4_t acc[NM][RB];
 #pragma unroll
@@ -210,11 +225,12 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
     if (cr + 1 < R) {
       cgp = locate(++cr);
       xrs = token_rsrc();
+      xoff_cur = token_off();
     }
   };
 
   auto stage = [&](WOps& cur, WOps& nxt) __attribute__((always_inline)) {
-    const int xoff = tr < cgp.rows ? xoff_in : 0x7ff00000;
+    const int xoff = xoff_cur;
     uint4 x[2][4];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -272,25 +288,28 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
 template <bool DUAL, int RB, int MIN_WAVES, int PD, int KS>
 hipError_t launch_ks(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                      const uint8_t* wa, const uint8_t* sa, const uint8_t* wb, const uint8_t* sb,
-                     int N, int K, void* out, hipStream_t st) {
+                     int N, int K, void* out, hipStream_t st, const int32_t* gather) {
   constexpr int kWgPerCu = MIN_WAVES * 4 / kMx4Waves;
   static_assert(kWgPerCu >= 1, "resident workgroups");
   const int64_t grid = (int64_t)device_cu_count() * kWgPerCu;
   hipLaunchKernelGGL((grouped_gemm_mxfp4_decode<DUAL, RB, MIN_WAVES, PD, KS>), dim3((unsigned)grid),
                      dim3(kMx4Waves * kWave), 0, st, act, offsets, expert_groups(s), wa, sa, wb, sb, N,
-                     K, out);
+                     K, out, gather, s.top_k, s.T * s.top_k, s.T);
   return hipGetLastError();
 }
 
 template <bool DUAL, int RB, int MIN_WAVES, int PD>
 hipError_t launch_variant(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                           const uint8_t* wa, const uint8_t* sa, const uint8_t* wb,
-                          const uint8_t* sb, int N, int K, void* out, hipStream_t st) {
+                          const uint8_t* sb, int N, int K, void* out, hipStream_t st,
+                          const int32_t* gather = nullptr) {
   if (max_rows_per_expert(s) <= 0) return hipSuccess;   // no expert can hold a row (capacity 0)
   const int nst = K / kMx4StageK;
-  if (nst % 4 == 0) return launch_ks<DUAL, RB, MIN_WAVES, PD, 4>(s, act, offsets, wa, sa, wb, sb, N, K, out, st);
-  if (nst % 2 == 0) return launch_ks<DUAL, RB, MIN_WAVES, PD, 2>(s, act, offsets, wa, sa, wb, sb, N, K, out, st);
-  return launch_ks<DUAL, RB, MIN_WAVES, PD, 1>(s, act, offsets, wa, sa, wb, sb, N, K, out, st);
+  if (nst % 4 == 0)
+    return launch_ks<DUAL, RB, MIN_WAVES, PD, 4>(s, act, offsets, wa, sa, wb, sb, N, K, out, st, gather);
+  if (nst % 2 == 0)
+    return launch_ks<DUAL, RB, MIN_WAVES, PD, 2>(s, act, offsets, wa, sa, wb, sb, N, K, out, st, gather);
+  return launch_ks<DUAL, RB, MIN_WAVES, PD, 1>(s, act, offsets, wa, sa, wb, sb, N, K, out, st, gather);
 }
 
 }  // namespace
@@ -304,6 +323,14 @@ hipError_t launch_gate_up_mxfp4(const moe_shape_t& s, const uint16_t* x_perm,
   // 5.4 TB/s (the one-group-per-workgroup form streamed 4.8).
   return launch_variant<true, 2, 3, 1>(s, x_perm, offsets, w1, w1_scale, w3, w3_scale, s.d_ff,
                                        s.d_model, h, st);
+}
+
+hipError_t launch_gate_up_mxfp4_gather(const moe_shape_t& s, const uint16_t* x, const int32_t* perm_src,
+                                       const int32_t* offsets, const uint8_t* w1, const uint8_t* w1_scale,
+                                       const uint8_t* w3, const uint8_t* w3_scale, uint16_t* h,
+                                       hipStream_t st) {
+  return launch_variant<true, 2, 3, 1>(s, x, offsets, w1, w1_scale, w3, w3_scale, s.d_ff, s.d_model, h,
+                                       st, perm_src);
 }
 
 hipError_t launch_down_mxfp4(const moe_shape_t& s, const uint16_t* h, const int32_t* offsets,

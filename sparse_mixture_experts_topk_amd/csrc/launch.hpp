@@ -33,6 +33,10 @@ hipError_t launch_route_index(const moe_shape_t& s, const void* x, const void* w
 hipError_t launch_gate_up_bf16_gather(const moe_shape_t& s, const uint16_t* x, const int32_t* perm_src,
                                       const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                                       uint16_t* h, hipStream_t st);
+hipError_t launch_gate_up_mxfp4_gather(const moe_shape_t& s, const uint16_t* x, const int32_t* perm_src,
+                                       const int32_t* offsets, const uint8_t* w1, const uint8_t* w1_scale,
+                                       const uint8_t* w3, const uint8_t* w3_scale, uint16_t* h,
+                                       hipStream_t st);
 
 // Capacity selection: writes drop_mask[T*k] (0 kept, 1 dropped); with
 // MOE_OVERFLOW_NEXT_BEST a second round re-offers the dropped assignments to

@@ -305,11 +305,13 @@ def test_forward_matches_staged_bitwise_and_is_deterministic(overflow):
     assert torch.equal(st["topk_ids"], ids1) and torch.equal(st["drop_mask"], drop1)
 
 
-@pytest.mark.parametrize("T,E", [(16, 8), (1, 8), (16, 16), (7, 2), (13, 3)])
-def test_decode_forward_fused_router_matches_staged(T, E):
+@pytest.mark.parametrize("T,E,w", [(16, 8, "bf16"), (1, 8, "bf16"), (16, 16, "bf16"), (7, 2, "bf16"),
+                                   (13, 3, "bf16"), (16, 8, "mxfp4"), (5, 16, "mxfp4"), (1, 2, "mxfp4")])
+def test_decode_forward_fused_router_matches_staged(T, E, w):
     """At decode shapes moe_forward groups tokens in the router's workgroup and the gate/up
     weight streamer reads x through perm_src; every output must equal the staged calls'."""
-    cfg = mid_cfg(f"dec_fused_T{T}_E{E}", T=T, n_experts=E, seed=60 + T + E)
+    cfg = mid_cfg(f"dec_fused_T{T}_E{E}_{w}", T=T, n_experts=E, w_dtype=w, seed=60 + T + E,
+                  **({"d_ff": 768} if w == "mxfp4" else {}))
     inp = synthetic.make_inputs(cfg)
     say(f"decode moe_forward (fused router + grouping) vs staged: T={T} E={E}")
     di = runner.DeviceInputs.from_host(inp)
@@ -322,6 +324,18 @@ def test_decode_forward_fused_router_matches_staged(T, E):
     assert not b.drop_mask.any()
     base, res = adjusted_oracle(inp, to_np(b.topk_ids))
     assert_close(to_np(b.y.float()), res.y, "bf16", "decode y")
+
+
+def test_decode_mxfp4_config_fused_forward_full():
+    inp = cached_inputs("decode_mxfp4")
+    say("MXFP4 decode config via moe_forward (fused router + grouping, gathered rows)")
+    di = runner.DeviceInputs.from_host(inp)
+    st = runner.staged(di)
+    b = runner.forward(di)
+    torch.cuda.synchronize()
+    assert torch.equal(st["y"], b.y) and torch.equal(st["expert_counts"], b.expert_counts)
+    _, res = adjusted_oracle(inp, to_np(b.topk_ids))
+    assert_close(to_np(b.y.float()), res.y, "bf16", "MXFP4 decode y (fused call)")
 
 
 def test_decode_config_fused_forward_full():
