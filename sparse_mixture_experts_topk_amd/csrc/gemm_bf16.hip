@@ -43,12 +43,11 @@ hipError_t launch_decode_bf16(const moe_shape_t& s, bool dual, const uint16_t* a
 
 namespace {
 
-constexpr int PF_ROWS = 256;         // token rows of a tile
 
 // Layout of a tile: WR x WC wavefronts, wavefront (wr, wc) owning WA 32-row
 // weight blocks of wavefront row wr against WB 32-token blocks of column wc.
-// The weight operand has TA = 32 WR WA rows, the token operand 32 WC WB =
-// PF_ROWS rows.  One K slice of BK elements is an LDS row of BK * 2 bytes
+// The weight operand has TA = 32 WR WA rows, the token operand TB = 32 WC WB
+// rows (the token tile).  One K slice of BK elements is an LDS row of BK * 2 bytes
 // made of CPR 16-byte chunks; chunk c of row r sits at chunk position
 // c ^ key(r), which spreads the fragment reads of 16 consecutive rows (one
 // LDS phase, same logical chunk) over all 64 banks.  A 1 KiB load
@@ -69,7 +68,6 @@ struct TileGeom {
   static constexpr int JB = TB / RPI / NW;             // token loads per wavefront per slice
   static constexpr int DMA = JA + JB;
   static constexpr int SUB = BK / 16;                  // 16-wide matrix substeps
-  static_assert(TB == PF_ROWS, "token tile");
   static_assert(JA * RPI * NW == TA && JB * RPI * NW == TB, "whole load blocks per wavefront");
   __device__ static __forceinline__ int key(int row) { return (row / (16 / CPR)) & (CPR - 1); }
 };
@@ -93,6 +91,7 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
     const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, int N, int K,
     void* __restrict__ out, float* __restrict__ partials, int n_tiles) {
   using G = TileGeom<BK, WR, WC, WA, WB>;
+  constexpr int TR = G::TB;                  // token rows of a tile
   static_assert(G::SUB % 2 == 0 && NS >= 2 && (!DUAL || WA % 2 == 0) && WB >= 2, "pipeline shape");
   static_assert(!SPLIT || !DUAL, "split runs: single GEMM");
   static_assert(!DUAL || (G::TA / 2) % 16 == 0, "w3 rows start on a swizzle period");
@@ -134,11 +133,11 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
   if constexpr (LDS_TABLES) {
     if (tid <= E) offs[tid] = offsets[tid];
     __syncthreads();
-    if (wave == 0) build_tile_prefix(offs, E, PF_ROWS, tpre, lane);
+    if (wave == 0) build_tile_prefix(offs, E, TR, tpre, lane);
     __syncthreads();
     n_token_tiles = __builtin_amdgcn_readfirstlane(tpre[E]);
   } else {
-    for (int e = 0; e < E; ++e) n_token_tiles += (goffs[e + 1] - goffs[e] + PF_ROWS - 1) / PF_ROWS;
+    for (int e = 0; e < E; ++e) n_token_tiles += (goffs[e + 1] - goffs[e] + TR - 1) / TR;
   }
   const int KT = K / BK;
   const int slots = gridDim.x >> 3;
@@ -171,7 +170,7 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
       e = r0 = r1 = mt = nt = 0;
       for (int g = 0, tt = t_idx; g < E; ++g) {
         const int a0 = goffs[g], a1 = goffs[g + 1];
-        const int m = (a1 - a0 + PF_ROWS - 1) / PF_ROWS;
+        const int m = (a1 - a0 + TR - 1) / TR;
         if (tt < m * n_tiles) {
           e = g; r0 = a0; r1 = a1; mt = tt % m; nt = tt / m;
           break;
@@ -181,8 +180,8 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
     }
     Tile t;   // uniform values, kept in scalar registers
     t.e = __builtin_amdgcn_readfirstlane(e);
-    t.tok0 = __builtin_amdgcn_readfirstlane(r0 + mt * PF_ROWS);
-    t.tok_rows = __builtin_amdgcn_readfirstlane(min(PF_ROWS, r1 - t.tok0));
+    t.tok0 = __builtin_amdgcn_readfirstlane(r0 + mt * TR);
+    t.tok_rows = __builtin_amdgcn_readfirstlane(min(TR, r1 - t.tok0));
     t.ch0 = __builtin_amdgcn_readfirstlane(nt * CH_TILE);
     t.kb = __builtin_amdgcn_readfirstlane(kb);
     t.ke = __builtin_amdgcn_readfirstlane(ke);
@@ -351,8 +350,8 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
       } else {
         // a K-run of a split tile goes whole to its partial slot ([token][channel], 256 x TA)
         const bool part = SPLIT && t.part >= 0;
-        const i32x4_t dst = part ? make_desc(partials + (int64_t)t.part * (PF_ROWS * G::TA),
-                                             PF_ROWS * G::TA * 4)
+        const i32x4_t dst = part ? make_desc(partials + (int64_t)t.part * (TR * G::TA),
+                                             TR * G::TA * 4)
                                  : ro;
 #pragma unroll
         for (int a = 0; a < WA; ++a)
@@ -428,12 +427,10 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
 }
 
 // Sum of the K-runs of each split tail tile, in K order, into y_perm.  One
-// workgroup per (XCD, tail tile, group of 16 rows): lane l covers row
-// 16 g + l / 16 and channels 4 (l % 16) + 64 c, c < CH / 64, so every lane
-// has CH / 64 independent 16-byte sums in flight.
-constexpr int kFixupRowGroups = PF_ROWS / 16;
-
-template <int CH>
+// workgroup per (XCD, tail tile, group of 16 rows of the TR-row token tile):
+// lane l covers row 16 g + l / 16 and channels 4 (l % 16) + 64 c, c < CH / 64,
+// so every lane has CH / 64 independent 16-byte sums in flight.
+template <int CH, int TR>
 __global__ __launch_bounds__(256) void split_fixup_kernel(const int32_t* __restrict__ offsets, int E,
                                                           int N, int K, int BK, int n_tiles, int slots,
                                                           const float* __restrict__ partials,
@@ -443,16 +440,17 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(const int32_t* __restr
   __shared__ int32_t tpre[kMaxExpertGroups + 1];
   for (int i = threadIdx.x; i <= E; i += 256) offs[i] = offsets[i];
   __syncthreads();
-  if (threadIdx.x < 64) build_tile_prefix(offs, E, PF_ROWS, tpre, threadIdx.x);
+  if (threadIdx.x < 64) build_tile_prefix(offs, E, TR, tpre, threadIdx.x);
   __syncthreads();
-  const int rg = blockIdx.x % kFixupRowGroups;
-  const int xcd = (blockIdx.x / kFixupRowGroups) & 7, j = blockIdx.x / kFixupRowGroups >> 3;
+  constexpr int kRowGroups = TR / 16;
+  const int rg = blockIdx.x % kRowGroups;
+  const int xcd = (blockIdx.x / kRowGroups) & 7, j = blockIdx.x / kRowGroups >> 3;
   const int KT = K / BK;
   const TileSplit sp = TileSplit::of(__builtin_amdgcn_readfirstlane(tpre[E]) * n_tiles, xcd, slots, KT);
   if (j >= sp.tail) return;
   int e, r0, r1, mt, nt;
   find_tile(offs, tpre, E, n_tiles, sp.share_begin + sp.R * slots + j, e, r0, r1, mt, nt);
-  const int tok0 = r0 + mt * PF_ROWS, tok_rows = min(PF_ROWS, r1 - tok0), ch0 = nt * CH;
+  const int tok0 = r0 + mt * TR, tok_rows = min(TR, r1 - tok0), ch0 = nt * CH;
   const int r = rg * 16 + (threadIdx.x >> 4);
   if (r >= tok_rows) return;
   const int s_lo = (j * KT) / sp.P, s_hi = min(((j + 1) * KT - 1) / sp.P, slots - 1);
@@ -461,7 +459,7 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(const int32_t* __restr
   for (int c = 0; c < CPL; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = s_lo; s <= s_hi; ++s) {
     const int part = (s * 8 + xcd) * 2 + (j - (s * sp.P) / KT);
-    const float* src = partials + (int64_t)part * (PF_ROWS * CH) + r * CH + (threadIdx.x & 15) * 4;
+    const float* src = partials + (int64_t)part * (TR * CH) + r * CH + (threadIdx.x & 15) * 4;
     float4 p[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) p[c] = *reinterpret_cast<const float4*>(src + 64 * c);
@@ -478,34 +476,51 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(const int32_t* __restr
 }
 
 // Shapes of the prefill kernels: K slice, LDS ring depth, wavefront grid and
-// blocks per wavefront.  Both run 8 wavefronts (two per SIMD, 192
-// accumulators each) on a 384 x 256 tile: gate/up as 2 x 4 wavefronts of
-// 3 + 3 (w1, w3) blocks x 2 token blocks, down as 4 x 2 wavefronts of 3 x 4.
-// With at most kWideMaxGroups expert groups a K slice is 64 wide (128-byte
-// row segments: half as many L2 requests per byte as 64-byte ones) in a ring
-// of 2 stages of 80 KiB; with more, 32 wide in 3 stages of 40 KiB, leaving
-// LDS for the group tables.
+// blocks per wavefront.  All run 8 wavefronts (two per SIMD).
+//  * kWide (at most kWideMaxGroups expert groups): a 384 x 256 tile (weights x
+//    tokens; 192 accumulators per lane), gate/up as 2 x 4 wavefronts of 3 + 3
+//    (w1, w3) blocks x 2 token blocks, down as 4 x 2 wavefronts of 3 x 4.  A K
+//    slice is 64 wide (128-byte row segments: half as many L2 requests per
+//    byte as 64-byte ones) in a ring of 2 stages of 80 KiB, which fills LDS:
+//    the group offsets are read with scalar loads.
+//  * kNarrow (more groups): the same tile with 32-wide slices in 3 stages of
+//    40 KiB, leaving LDS for the group tables.
+//  * kTall (experts of at most 320 rows on average, e.g. many small experts):
+//    a 256 x 320 tile, 4 x 2 wavefronts of 2 (gate/up: 1 + 1) weight blocks x
+//    5 token blocks (160 accumulators).  An expert of up to 320 rows is one
+//    token tile, where 256-row tiles cut an expert of 257..320 rows into a
+//    full tile and a nearly empty one.  64-wide slices in 2 stages of 72 KiB
+//    leave LDS for the group tables, so any number of groups takes 128-byte
+//    row segments.
 constexpr int kWideMaxGroups = 16;
-template <bool DUAL, bool WIDE> struct PrefillCfg;
-template <> struct PrefillCfg<true, false> { static constexpr int BK = 32, NS = 3, WR = 2, WC = 4, WA = 6, WB = 2; };
-template <> struct PrefillCfg<false, false> { static constexpr int BK = 32, NS = 3, WR = 4, WC = 2, WA = 3, WB = 4; };
-template <> struct PrefillCfg<true, true> { static constexpr int BK = 64, NS = 2, WR = 2, WC = 4, WA = 6, WB = 2; };
-template <> struct PrefillCfg<false, true> { static constexpr int BK = 64, NS = 2, WR = 4, WC = 2, WA = 3, WB = 4; };
-template <bool DUAL, bool WIDE = false>
-using PrefillGeom = TileGeom<PrefillCfg<DUAL, WIDE>::BK, PrefillCfg<DUAL, WIDE>::WR, PrefillCfg<DUAL, WIDE>::WC,
-                             PrefillCfg<DUAL, WIDE>::WA, PrefillCfg<DUAL, WIDE>::WB>;
-constexpr int64_t kPartialTileBytes = (int64_t)PF_ROWS * PrefillGeom<false>::TA * 4;
-static_assert(PrefillGeom<false, true>::TA == PrefillGeom<false>::TA, "one partial tile size");
+constexpr int kTallMaxMeanRows = 320;
+enum PrefillKind { kNarrow = 0, kWide = 1, kTall = 2 };
+template <bool DUAL, int KIND> struct PrefillCfg;
+template <> struct PrefillCfg<true, kNarrow> { static constexpr int BK = 32, NS = 3, WR = 2, WC = 4, WA = 6, WB = 2; };
+template <> struct PrefillCfg<false, kNarrow> { static constexpr int BK = 32, NS = 3, WR = 4, WC = 2, WA = 3, WB = 4; };
+template <> struct PrefillCfg<true, kWide> { static constexpr int BK = 64, NS = 2, WR = 2, WC = 4, WA = 6, WB = 2; };
+template <> struct PrefillCfg<false, kWide> { static constexpr int BK = 64, NS = 2, WR = 4, WC = 2, WA = 3, WB = 4; };
+template <> struct PrefillCfg<true, kTall> { static constexpr int BK = 64, NS = 2, WR = 4, WC = 2, WA = 2, WB = 5; };
+template <> struct PrefillCfg<false, kTall> { static constexpr int BK = 64, NS = 2, WR = 4, WC = 2, WA = 2, WB = 5; };
+template <bool DUAL, int KIND>
+using PrefillGeom = TileGeom<PrefillCfg<DUAL, KIND>::BK, PrefillCfg<DUAL, KIND>::WR, PrefillCfg<DUAL, KIND>::WC,
+                             PrefillCfg<DUAL, KIND>::WA, PrefillCfg<DUAL, KIND>::WB>;
+// fp32 partial tile of a split K-run ([token][channel]), the largest of the down shapes
+constexpr int64_t kPartialTileBytes =
+    std::max((int64_t)PrefillGeom<false, kWide>::TB * PrefillGeom<false, kWide>::TA,
+             (int64_t)PrefillGeom<false, kTall>::TB * PrefillGeom<false, kTall>::TA) * 4;
+static_assert(PrefillGeom<false, kWide>::TA == PrefillGeom<false, kNarrow>::TA &&
+              PrefillGeom<false, kWide>::TB == PrefillGeom<false, kNarrow>::TB, "one partial tile shape per TA");
 
-template <bool DUAL, bool WIDE>
+template <bool DUAL, int KIND>
 hipError_t launch_prefill_cfg(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                           const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
                           float* partials, hipStream_t st) {
-  using C = PrefillCfg<DUAL, WIDE>;
-  using G = PrefillGeom<DUAL, WIDE>;
+  using C = PrefillCfg<DUAL, KIND>;
+  using G = PrefillGeom<DUAL, KIND>;
   constexpr int CH_TILE = DUAL ? G::TA / 2 : G::TA;
   const int n_tiles = (N + CH_TILE - 1) / CH_TILE;
-  const int64_t max_tiles = max_token_tiles(s, PF_ROWS) * n_tiles;
+  const int64_t max_tiles = max_token_tiles(s, G::TB) * n_tiles;
   if (max_tiles <= 0) return hipSuccess;
   const int64_t grid = persistent_grid(max_tiles);
   if constexpr (!DUAL) {
@@ -515,8 +530,8 @@ hipError_t launch_prefill_cfg(const moe_shape_t& s, const uint16_t* act, const i
                          wb, N, K, out, partials, n_tiles);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(split_fixup_kernel<G::TA>, dim3((unsigned)(grid * kFixupRowGroups)), dim3(256), 0,
-                         st, offsets, expert_groups(s), N, K, C::BK, n_tiles, (int)(grid / 8), partials,
+      hipLaunchKernelGGL((split_fixup_kernel<G::TA, G::TB>), dim3((unsigned)(grid * (G::TB / 16))), dim3(256),
+                         0, st, offsets, expert_groups(s), N, K, C::BK, n_tiles, (int)(grid / 8), partials,
                          static_cast<float*>(out));
       return hipGetLastError();
     }
@@ -527,13 +542,22 @@ hipError_t launch_prefill_cfg(const moe_shape_t& s, const uint16_t* act, const i
   return hipGetLastError();
 }
 
+// Mean rows per routed expert (the token tile shape follows it; the shared
+// expert's rows do not count).
+int64_t mean_routed_rows(const moe_shape_t& s) {
+  const int64_t r = (int64_t)s.T * s.top_k / s.n_experts;
+  return s.capacity >= 0 ? std::min<int64_t>(r, s.capacity) : r;
+}
+
 template <bool DUAL>
 hipError_t launch_prefill(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                           const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
                           float* partials, hipStream_t st) {
+  if (mean_routed_rows(s) <= kTallMaxMeanRows)
+    return launch_prefill_cfg<DUAL, kTall>(s, act, offsets, wa, wb, N, K, out, partials, st);
   if (expert_groups(s) <= kWideMaxGroups)
-    return launch_prefill_cfg<DUAL, true>(s, act, offsets, wa, wb, N, K, out, partials, st);
-  return launch_prefill_cfg<DUAL, false>(s, act, offsets, wa, wb, N, K, out, partials, st);
+    return launch_prefill_cfg<DUAL, kWide>(s, act, offsets, wa, wb, N, K, out, partials, st);
+  return launch_prefill_cfg<DUAL, kNarrow>(s, act, offsets, wa, wb, N, K, out, partials, st);
 }
 
 // Weight streaming (decode kernels) while no expert can hold more than this many rows.

@@ -683,7 +683,8 @@ def test_finegrained_prefill_config_sampled():
     cfg = synthetic.CONFIGS["finegrained_prefill_bf16"]
     inp = cached_inputs("finegrained_prefill_bf16")
     base = oracle.forward(inp, tokens=[])
-    toks = sample_tokens(base, n_random=12, edge_groups=12)
+    # experts average 256 rows: the tiled GEMMs take 320-row token tiles here
+    toks = sample_tokens(base, n_random=12, edge_groups=12, tile_rows=320)
     run_staged_and_check(cfg, inputs=inp, tokens=toks, check_h=True)
 
 
