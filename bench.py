@@ -121,6 +121,53 @@ def read_traffic(cfg_name: str, sha: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def _counter_values(csv_path: str, counter: str, kernel_re: str):
+    """Per-dispatch values of one counter from a rocprofv3 ``--pmc`` CSV, for dispatches whose
+    kernel name matches ``kernel_re`` (values summed over a dispatch's rows)."""
+    import csv
+    import re
+    per, names = {}, set()
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter or not re.search(kernel_re, row.get("Kernel_Name", "")):
+                continue
+            key = row.get("Dispatch_Id") or row.get("Correlation_Id")
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+            m = re.search(r"(grouped_gemm_\w+)<", row["Kernel_Name"])
+            names.add(m.group(1) if m else row["Kernel_Name"][:80])
+    return list(per.values()), sorted(names)
+
+
+def write_traffic(cfg, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_mib):
+    """HBM bytes per gate/up launch from two rocprofv3 counter runs of this workload (FETCH_SIZE,
+    then WRITE_SIZE; KiB per dispatch), each scaled by what the same counter reads for the plain
+    device copy of ``cal_mib`` MiB (``--calibrate-copy-mib``).  Writes
+    profiles/gate_up_<workload>_traffic.json stamped with the current kernel-source hash."""
+    gate_up = r"grouped_gemm_\w+<true"          # the dual (gate/up) instance of each GEMM family
+    fetch, kernels = _counter_values(fetch_csv, "FETCH_SIZE", gate_up)
+    write, _ = _counter_values(write_csv, "WRITE_SIZE", gate_up)
+    if not fetch or not write:
+        raise SystemExit("no gate/up dispatches in the counter files")
+    cal_kib = (cal_mib << 20) / 1024.0
+
+    def factor(path, counter):
+        v, _ = _counter_values(path, counter, r".")
+        big = sorted(x for x in v if x >= 0.25 * max(v))      # the copy dispatches (the fill reads nothing)
+        return cal_kib / big[len(big) // 2]
+
+    ff, wf = factor(cal_fetch_csv, "FETCH_SIZE"), factor(cal_write_csv, "WRITE_SIZE")
+    fk, wk = sum(fetch) / len(fetch), sum(write) / len(write)
+    out = {"workload": cfg.name, "kernel": ", ".join(kernels), "fetch_size_kib": round(fk, 1), "write_size_kib": round(wk, 1),
+           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+           "hbm_bytes_per_launch": int(round((fk * ff + wk * wf) * 1024)),
+           "launches": len(fetch), "kernel_source_sha": kernel_source_sha(cfg)}
+    p = os.path.join(ROOT, "profiles", f"gate_up_{cfg.name}_traffic.json")
+    with open(p, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def cpu_baseline(cfg, inputs, budget_tokens, min_seconds=10.0):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload."""
     import numpy as np
@@ -160,7 +207,17 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=16)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="no GPU work: turn the rocprofv3 counter CSVs of this workload and of the "
+                         "copy calibration into profiles/gate_up_<workload>_traffic.json")
+    ap.add_argument("--calibration-mib", type=int, default=1024,
+                    help="size of the calibration copy behind --write-traffic")
     a = ap.parse_args()
+
+    if a.write_traffic:
+        from sparse_mixture_experts_topk_amd import synthetic
+        write_traffic(synthetic.CONFIGS[a.config], *a.write_traffic, a.calibration_mib)
+        return
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "the MoE layer runs on one GPU only: its kernels are "

@@ -44,3 +44,35 @@ def test_decode_detection_follows_the_rows_per_expert_bound():
     # a shared expert takes every token, so a capacity does not bound its rows
     cfg = synthetic.CONFIGS["finegrained_prefill_bf16"].replace(capacity=32)
     assert not bench.is_decode(cfg)
+
+
+def _pmc_csv(path, counter, rows):
+    """A rocprofv3 --pmc CSV with the columns bench.py reads: (dispatch, kernel name, value)."""
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for disp, name, val in rows:
+            w.writerow([disp, name, counter, val])
+
+
+def test_write_traffic_scales_gate_up_counters_by_the_copy_calibration(tmp_path, monkeypatch):
+    gu = "void moe::(anonymous namespace)::grouped_gemm_bf16_prefill<true, 64, 2, 2, 4, 6, 2, false>(...)"
+    dn = "void moe::(anonymous namespace)::grouped_gemm_bf16_prefill<false, 64, 2, 4, 2, 3, 4, true>(...)"
+    _pmc_csv(tmp_path / "f.csv", "FETCH_SIZE", [(1, gu, 1000.0), (2, dn, 9e9), (3, gu, 3000.0)])
+    _pmc_csv(tmp_path / "w.csv", "WRITE_SIZE", [(1, gu, 10.0), (2, dn, 9e9), (3, gu, 30.0)])
+    # 1 MiB copy: FETCH reads half of it (factor 2), WRITE all of it; the fill (dispatch 1) reads nothing
+    _pmc_csv(tmp_path / "cf.csv", "FETCH_SIZE", [(1, "fill", 0.0), (2, "copy", 512.0), (3, "copy", 512.0)])
+    _pmc_csv(tmp_path / "cw.csv", "WRITE_SIZE", [(1, "fill", 1024.0), (2, "copy", 1024.0), (3, "copy", 1024.0)])
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    cfg = synthetic.CONFIGS["prefill_bf16"]
+    monkeypatch.setattr(bench, "kernel_source_sha", lambda c: "0123456789abcdef")
+    bench.write_traffic(cfg, str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                        str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), 1)
+    out = json.load(open(tmp_path / "profiles" / "gate_up_prefill_bf16_traffic.json"))
+    assert out["kernel"] == "grouped_gemm_bf16_prefill" and out["launches"] == 2
+    assert out["fetch_factor"] == 2.0 and out["write_factor"] == 1.0
+    assert out["hbm_bytes_per_launch"] == (2000.0 * 2 + 20.0) * 1024
+    assert bench.read_traffic("prefill_bf16", "0123456789abcdef") == out["hbm_bytes_per_launch"]
+    assert bench.read_traffic("prefill_bf16", "fedcba9876543210") is None   # stale after a change

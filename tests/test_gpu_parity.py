@@ -42,7 +42,7 @@ def mid_cfg(name, **kw):
     return synthetic.MoEConfig(**base)
 
 
-def run_staged_and_check(cfg, inputs=None, tokens=None, check_h=True):
+def run_staged_and_check(cfg, inputs=None, tokens=None, check_h=True, tile_rows=256):
     inputs = inputs if inputs is not None else synthetic.make_inputs(cfg)
     say(f"staged {cfg.name} T={cfg.T} d={cfg.d_model} F={cfg.d_ff} E={cfg.n_experts} "
         f"k={cfg.top_k} shared={cfg.n_shared} cap={cfg.capacity} overflow={cfg.overflow} "
@@ -93,7 +93,7 @@ def run_staged_and_check(cfg, inputs=None, tokens=None, check_h=True):
     y = to_np(st["y"].float())[want]
     fro, mx = assert_close(y, res.y[want], key, "y (layer output)")
     say(f"  y rel_frob={fro:.3e} rel_max={mx:.3e}")
-    hit, tot = tile_coverage(res, want)
+    hit, tot = tile_coverage(res, want, tile_rows)
     record(cfg.name, h_rel_frob=h_fro, y_perm_rel_frob=yp_fro, y_rel_frob=fro, y_rel_max=mx,
            tokens_checked=len(want), token_tiles_checked=hit, token_tiles=tot,
            dropped=int((~res.keep).sum()))
@@ -683,9 +683,10 @@ def test_finegrained_prefill_config_sampled():
     cfg = synthetic.CONFIGS["finegrained_prefill_bf16"]
     inp = cached_inputs("finegrained_prefill_bf16")
     base = oracle.forward(inp, tokens=[])
-    # experts average 256 rows: the tiled GEMMs take 320-row token tiles here
-    toks = sample_tokens(base, n_random=12, edge_groups=12, tile_rows=320)
-    run_staged_and_check(cfg, inputs=inp, tokens=toks, check_h=True)
+    # experts average 256 rows: the tiled GEMMs take 320-row token tiles here; the first and
+    # last row of every tile of all 257 groups (about 290 tokens)
+    toks = sample_tokens(base, n_random=12, tile_rows=320)
+    run_staged_and_check(cfg, inputs=inp, tokens=toks, check_h=True, tile_rows=320)
 
 
 def sweep_cfg(seed):
