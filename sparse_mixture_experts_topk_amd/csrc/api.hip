@@ -249,6 +249,14 @@ moe_status_t forward_impl(const moe_shape_t* s, const void* x, const void* w_gat
     if (e == hipSuccess)
       e = moe::launch_gate_up(*s, x_perm, x_scale, offsets, w1, w3, w1_scale, w3_scale, h, h_scale, st);
   }
+  if (moe::route_index_fused(*s) && moe::down_combine_fused(*s)) {
+    // decode, bf16 experts: down + combine in one launch (no y_perm)
+    if (e == hipSuccess)
+      e = moe::launch_down_combine_bf16(*s, static_cast<const uint16_t*>(h), offsets,
+                                        static_cast<const uint16_t*>(w2), slot_to_row, gw,
+                                        static_cast<uint16_t*>(y), st);
+    return from_hip(e);
+  }
   void* down_ws = down_workspace_bytes(*s) > 0 ? at<void>(workspace, L.down_ws) : nullptr;
   if (e == hipSuccess)
     e = moe::launch_down(*s, h, h_scale, offsets, w2, w2_scale, y_perm, down_ws, st);

@@ -26,18 +26,73 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
+// A K stage of a row group: ROWS rows x (1024 / ROWS) contiguous bytes per load
+// instruction, KB elements per row per stage.
+template <bool DUAL, int ROWS>
+struct StreamGeom {
+  static constexpr int KB = 512 / ROWS;        // elements per row per stage
+  static constexpr int CPR = KB / 8;           // 16-byte chunks per row per stage
+  static constexpr int NL = 16 / ROWS;         // load instructions per matrix per stage
+  static constexpr int NM = DUAL ? 2 : 1;
+  static constexpr int ROW_BYTES = KB * 2;
+  static constexpr int KEY_MASK = (CPR < 16 ? CPR : 16) - 1;
+  static constexpr int WAVE_LDS = NM * 16 * ROW_BYTES;   // one wavefront's private tile
+  static constexpr int LPR = kWave / ROWS;     // lanes per row (== CPR)
+};
+
+// One row group streamed over all of K into acc: the 16 weight rows at pw[m]
+// (dual: w1 and w3) against the token operand px (lane (r, g): row r, K
+// elements 8 g .. 8 g + 7 of each 32; rows r >= rows read as zero), through
+// the wavefront's private LDS tile `lds`.
+template <bool DUAL, int ROWS>
+__device__ __forceinline__ void stream_row_group(const uint16_t* const* pw, const uint16_t* px, bool tok_ok,
+                                                 int K, uint8_t* lds, f32x4_t* acc) {
+  using S = StreamGeom<DUAL, ROWS>;
+  const int lane = threadIdx.x & 63;
+  const int lrow = lane / S::LPR, lch = lane % S::LPR;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < S::NM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nst = K / S::KB;
+  for (int st = 0; st < nst; ++st) {
+    const int k0 = st * S::KB;
+    uint4 v[S::NM][S::NL];
+#pragma unroll
+    for (int m = 0; m < S::NM; ++m)
+#pragma unroll
+      for (int i = 0; i < S::NL; ++i)
+        v[m][i] = load_stream16(pw[m] + (int64_t)(i * ROWS + lrow) * K + k0 + lch * 8);
+    uint4 xv[S::KB / 32];
+#pragma unroll
+    for (int j = 0; j < S::KB / 32; ++j)
+      xv[j] = tok_ok ? *reinterpret_cast<const uint4*>(px + k0 + j * 32) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < S::NM; ++m)
+#pragma unroll
+      for (int i = 0; i < S::NL; ++i) {
+        const int row = i * ROWS + lrow;
+        const int pc = lch ^ (row & S::KEY_MASK);
+        *reinterpret_cast<uint4*>(&lds[(m * 16 + row) * S::ROW_BYTES + pc * 16]) = v[m][i];
+      }
+#pragma unroll
+    for (int j = 0; j < S::KB / 32; ++j) {
+      const int pc = (4 * j + g) ^ (r & S::KEY_MASK);
+#pragma unroll
+      for (int m = 0; m < S::NM; ++m) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&lds[(m * 16 + r) * S::ROW_BYTES + pc * 16]);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(xv[j]), acc[m], 0, 0, 0);
+      }
+    }
+  }
+}
+
 template <bool DUAL, int ROWS, int MIN_WAVES>
 __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gemm_bf16_decode(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
     const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, int N, int K,
     void* __restrict__ out, int tok_tiles, const int32_t* __restrict__ gather, int k, int Tk) {
-  constexpr int KB = 512 / ROWS;        // elements per row per stage
-  constexpr int CPR = KB / 8;           // 16-byte chunks per row per stage
-  constexpr int NL = 16 / ROWS;         // load instructions per matrix per stage
-  constexpr int NM = DUAL ? 2 : 1;
-  constexpr int ROW_BYTES = KB * 2;
-  constexpr int KEY_MASK = (CPR < 16 ? CPR : 16) - 1;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWavesPerBlock][NM][16 * ROW_BYTES];
+  using S = StreamGeom<DUAL, ROWS>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWavesPerBlock][S::WAVE_LDS];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int groups = N / 16;
@@ -51,10 +106,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gem
   const int rows = min(16, offsets[e + 1] - row0);
   if (rows <= 0) return;
 
-  // wide loader: instruction i covers rows ROWS i .. ROWS i + ROWS - 1
-  constexpr int LPR = kWave / ROWS;     // lanes per row (== CPR)
-  const int lrow = lane / LPR, lch = lane % LPR;
-  const uint16_t* pw[NM];
+  const uint16_t* pw[S::NM];
   pw[0] = wa + ((int64_t)e * N + cg * 16) * K;
   if constexpr (DUAL) pw[1] = wb + ((int64_t)e * N + cg * 16) * K;
   // matrix-core operand: lane (r, g) feeds row r, chunk 4 j + g of MFMA j
@@ -69,41 +121,8 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gem
   }
   const uint16_t* px = act + (int64_t)arow * K + g * 8;
 
-  f32x4_t acc[NM];
-#pragma unroll
-  for (int m = 0; m < NM; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int nst = K / KB;
-  for (int st = 0; st < nst; ++st) {
-    const int k0 = st * KB;
-    uint4 v[NM][NL];
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int i = 0; i < NL; ++i)
-        v[m][i] = load_stream16(pw[m] + (int64_t)(i * ROWS + lrow) * K + k0 + lch * 8);
-    uint4 xv[KB / 32];
-#pragma unroll
-    for (int j = 0; j < KB / 32; ++j)
-      xv[j] = tok_ok ? *reinterpret_cast<const uint4*>(px + k0 + j * 32) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const int row = i * ROWS + lrow;
-        const int pc = lch ^ (row & KEY_MASK);
-        *reinterpret_cast<uint4*>(&lds[w][m][row * ROW_BYTES + pc * 16]) = v[m][i];
-      }
-#pragma unroll
-    for (int j = 0; j < KB / 32; ++j) {
-      const int pc = (4 * j + g) ^ (r & KEY_MASK);
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&lds[w][m][r * ROW_BYTES + pc * 16]);
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(xv[j]), acc[m],
-                                                         0, 0, 0);
-      }
-    }
-  }
+  f32x4_t acc[S::NM];
+  stream_row_group<DUAL, ROWS>(pw, px, tok_ok, K, lds[w], acc);
 
   // 16x16 accumulator: lane holds token column (lane & 15), channels 4 * (lane >> 4) + 0..3.
   const int tcol = lane & 15;
@@ -119,6 +138,58 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gem
   } else {
     *reinterpret_cast<float4*>(static_cast<float*>(out) + orow * N + c) =
         make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+  }
+}
+
+// Down projection and combine in one launch, for a decode batch whose experts
+// hold one token tile each (T <= 16, top-2, nothing dropped, E <= 16).  A
+// workgroup owns 16 output channels; its wavefront w streams expert w's 16
+// rows of w2 against that expert's h rows (the same row group as the down
+// kernel above).  The fp32 results meet in LDS, indexed by permuted row, and
+// the workgroup then forms y[t] = fma(G1, y_e1, G0 * y_e0) for its channels in
+// the order the combine kernel uses, so the result equals the separate down +
+// combine calls bit for bit, without the y_perm round trip or the extra launch.
+constexpr int kFusedMaxExperts = 16;
+constexpr int kFusedMaxRows = 32;     // T * top_k
+
+template <int ROWS>
+__global__ __launch_bounds__(kFusedMaxExperts * kWave) void down_combine_bf16_decode(
+    const uint16_t* __restrict__ h, const int32_t* __restrict__ offsets, const uint16_t* __restrict__ w2,
+    int N, int K, const int32_t* __restrict__ slot_to_row, const float* __restrict__ gw, int T,
+    uint16_t* __restrict__ y) {
+  using S = StreamGeom<false, ROWS>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kFusedMaxExperts][S::WAVE_LDS];
+  __shared__ float4 yrow[kFusedMaxRows][4];          // [permuted row][channel quad], fp32
+
+  const int lane = threadIdx.x & 63, e = threadIdx.x >> 6;   // wavefront = expert (blockDim = 64 E)
+  const int cg = blockIdx.x;
+  const int row0 = offsets[e];
+  const int rows = min(16, offsets[e + 1] - row0);
+  if (rows > 0) {
+    const uint16_t* pw[1] = {w2 + ((int64_t)e * N + cg * 16) * K};
+    const int r = lane & 15, g = lane >> 4;
+    const bool tok_ok = r < rows;
+    const uint16_t* px = h + (int64_t)(row0 + (tok_ok ? r : 0)) * K + g * 8;
+    f32x4_t acc[1];
+    stream_row_group<false, ROWS>(pw, px, tok_ok, K, lds[e], acc);
+    if (r < rows) yrow[row0 + r][g] = make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < T * 4; o += blockDim.x) {
+    const int t = o >> 2, q = o & 3;
+    const int2 rr = reinterpret_cast<const int2*>(slot_to_row)[t];
+    const float2 gg = reinterpret_cast<const float2*>(gw)[t];
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (rr.x >= 0) {
+      const float4 a = yrow[rr.x][q];
+      v = make_float4(gg.x * a.x, gg.x * a.y, gg.x * a.z, gg.x * a.w);
+    }
+    if (rr.y >= 0) {
+      const float4 b = yrow[rr.y][q];
+      v = make_float4(fmaf(gg.y, b.x, v.x), fmaf(gg.y, b.y, v.y), fmaf(gg.y, b.z, v.z), fmaf(gg.y, b.w, v.w));
+    }
+    *reinterpret_cast<uint2*>(y + (int64_t)t * N + cg * 16 + q * 4) =
+        make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
   }
 }
 
@@ -146,6 +217,26 @@ hipError_t launch_decode_bf16(const moe_shape_t& s, bool dual, const uint16_t* a
   if (dual) return launch_variant<true, 8, 4>(s, act, offsets, wa, wb, N, K, out, st);
   if (K % 128 == 0) return launch_variant<false, 4, 4>(s, act, offsets, wa, wb, N, K, out, st);
   return launch_variant<false, 8, 4>(s, act, offsets, wa, wb, N, K, out, st);
+}
+
+bool down_combine_fused(const moe_shape_t& s) {
+  return s.act_dtype == MOE_BF16 && s.w_dtype == MOE_BF16 && s.top_k == 2 && s.n_shared == 0 &&
+         s.capacity < 0 && s.T <= 16 && s.n_experts <= kFusedMaxExperts && s.d_model % 16 == 0;
+}
+
+hipError_t launch_down_combine_bf16(const moe_shape_t& s, const uint16_t* h, const int32_t* offsets,
+                                    const uint16_t* w2, const int32_t* slot_to_row, const float* gw,
+                                    uint16_t* y, hipStream_t st) {
+  if (!down_combine_fused(s)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(s.d_model / 16)), block((unsigned)(s.n_experts * kWave));
+  // the down kernel's choice: 4 rows x 256 B per load instruction when K allows it
+  if (s.d_ff % 128 == 0)
+    hipLaunchKernelGGL((down_combine_bf16_decode<4>), grid, block, 0, st, h, offsets, w2, s.d_model,
+                       s.d_ff, slot_to_row, gw, s.T, y);
+  else
+    hipLaunchKernelGGL((down_combine_bf16_decode<8>), grid, block, 0, st, h, offsets, w2, s.d_model,
+                       s.d_ff, slot_to_row, gw, s.T, y);
+  return hipGetLastError();
 }
 
 hipError_t launch_gate_up_bf16_gather(const moe_shape_t& s, const uint16_t* x, const int32_t* perm_src,

@@ -86,6 +86,13 @@ hipError_t launch_gate_up_bf16(const moe_shape_t& s, const uint16_t* x_perm,
 hipError_t launch_down_bf16(const moe_shape_t& s, const uint16_t* h, const int32_t* offsets,
                             const uint16_t* w2, float* y_perm, void* workspace, hipStream_t st);
 size_t down_workspace_bytes_bf16(const moe_shape_t& s);
+// Down projection + combine in one launch for a decode batch (bf16, T <= 16,
+// top-2, dropless, no shared expert, E <= 16): y from h, offsets, slot_to_row
+// and the gate weights, bit for bit what launch_down_bf16 + launch_combine give.
+bool down_combine_fused(const moe_shape_t& s);
+hipError_t launch_down_combine_bf16(const moe_shape_t& s, const uint16_t* h, const int32_t* offsets,
+                                    const uint16_t* w2, const int32_t* slot_to_row, const float* gw,
+                                    uint16_t* y, hipStream_t st);
 
 // Whether the fp8 matrix-core path is built in.
 constexpr bool kFp8Available = true;

@@ -305,13 +305,15 @@ def test_forward_matches_staged_bitwise_and_is_deterministic(overflow):
     assert torch.equal(st["topk_ids"], ids1) and torch.equal(st["drop_mask"], drop1)
 
 
-@pytest.mark.parametrize("T,E,w", [(16, 8, "bf16"), (1, 8, "bf16"), (16, 16, "bf16"), (7, 2, "bf16"),
-                                   (13, 3, "bf16"), (16, 8, "mxfp4"), (5, 16, "mxfp4"), (1, 2, "mxfp4")])
-def test_decode_forward_fused_router_matches_staged(T, E, w):
-    """At decode shapes moe_forward groups tokens in the router's workgroup and the gate/up
-    weight streamer reads x through perm_src; every output must equal the staged calls'."""
-    cfg = mid_cfg(f"dec_fused_T{T}_E{E}_{w}", T=T, n_experts=E, w_dtype=w, seed=60 + T + E,
-                  **({"d_ff": 768} if w == "mxfp4" else {}))
+@pytest.mark.parametrize("T,E,w,F", [(16, 8, "bf16", 448), (1, 8, "bf16", 448), (16, 16, "bf16", 384),
+                                     (7, 2, "bf16", 448), (13, 3, "bf16", 384), (16, 8, "mxfp4", 768),
+                                     (5, 16, "mxfp4", 768), (1, 2, "mxfp4", 768)])
+def test_decode_forward_fused_router_matches_staged(T, E, w, F):
+    """At decode shapes moe_forward groups tokens in the router's workgroup, the gate/up weight
+    streamer reads x through perm_src and (bf16) one launch does the down projection and the
+    combine (load rows of 128 B when F is not a multiple of 128, else 256 B); every output must
+    equal the staged calls'."""
+    cfg = mid_cfg(f"dec_fused_T{T}_E{E}_{w}", T=T, n_experts=E, w_dtype=w, seed=60 + T + E, d_ff=F)
     inp = synthetic.make_inputs(cfg)
     say(f"decode moe_forward (fused router + grouping) vs staged: T={T} E={E}")
     di = runner.DeviceInputs.from_host(inp)
