@@ -17,6 +17,14 @@
 // in the v_mfma_f32_16x16x32_bf16 layout.  The LDS tile is private to the
 // wavefront: LDS operations of one wavefront execute in order, so no barrier
 // is needed.  The token operand (a few rows, L2-resident) is read directly.
+//
+// Workgroups are dispatched round-robin over the 8 XCDs.  In that order every
+// XCD streams row groups spread over all of w1 and w3 at once, and the gate/up
+// time then depended on where the weights were allocated: 289-336 us on four
+// copies of the same weights in one process (MI355X, Mixtral decode batch).
+// With the workgroups of each XCD on one contiguous eighth of the row groups it
+// was 276-287 us on all four.  Down (one matrix, 140 us) was slower in that
+// order (150 us) and keeps the round-robin one.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "lds_stream.hpp"
@@ -96,7 +104,10 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gem
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int groups = N / 16;
-  const int gid = blockIdx.x * kWavesPerBlock + w;
+  // gate/up: each XCD streams one contiguous eighth of the row groups (the
+  // grid is padded to a multiple of 8 workgroups); down keeps the round-robin order
+  const int vb = DUAL ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+  const int gid = vb * kWavesPerBlock + w;
   const int cg = gid % groups;
   const int rest = gid / groups;
   const int tt = rest % tok_tiles;
@@ -200,7 +211,8 @@ hipError_t launch_variant(const moe_shape_t& s, const uint16_t* act, const int32
   const int tok_tiles = (int)((max_rows_per_expert(s) + 15) / 16);
   const int64_t groups = (int64_t)expert_groups(s) * tok_tiles * (N / 16);
   if (groups <= 0) return hipSuccess;   // no expert can hold a row (capacity 0)
-  const int64_t blocks = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
+  int64_t blocks = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (DUAL) blocks = (blocks + 7) / 8 * 8;     // whole rounds of the 8 XCDs (extra waves exit)
   hipLaunchKernelGGL((grouped_gemm_bf16_decode<DUAL, ROWS, MIN_WAVES>), dim3((unsigned)blocks),
                      dim3(kWavesPerBlock * kWave), 0, st, act, offsets, expert_groups(s), wa, wb, N, K,
                      out, tok_tiles, gather, s.top_k, s.T * s.top_k);
