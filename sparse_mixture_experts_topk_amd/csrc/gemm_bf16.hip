@@ -64,11 +64,7 @@ struct TileGeom {
   static constexpr int OPB_BYTES = TB * ROW_B;
   static constexpr int STAGE_BYTES = OPA_BYTES + OPB_BYTES;
   static constexpr int RPI = 64 / CPR;
-  static constexpr int JA = TA / RPI / NW;             // weight loads per wavefront per slice
-  static constexpr int JB = TB / RPI / NW;             // token loads per wavefront per slice
-  static constexpr int DMA = JA + JB;
   static constexpr int SUB = BK / 16;                  // 16-wide matrix substeps
-  static_assert(JA * RPI * NW == TA && JB * RPI * NW == TB, "whole load blocks per wavefront");
   __device__ static __forceinline__ int key(int row) { return (row / (16 / CPR)) & (CPR - 1); }
 };
 
@@ -85,7 +81,7 @@ struct TileGeom {
 // slices of all its tiles form one stream through the LDS ring, so the
 // first slices of the next tile load while the current one finishes and
 // stores its results.  Split K-runs go to fp32 partial tiles [token][TA].
-template <bool DUAL, int BK, int NS, int WR, int WC, int WA, int WB, bool SPLIT>
+template <bool DUAL, int BK, int NS, int WR, int WC, int WA, int WB, int LW, bool SPLIT>
 __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
     const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, int N, int K,
@@ -199,14 +195,23 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
   // and j + 1 of a wavefront are NW * RPI rows apart, a whole number of
   // swizzle periods, so the lane offsets of load j are those of load 0 plus
   // j times that many rows.
+  //
+  // Only the first LW wavefronts load (LW <= NW): each then issues NW / LW
+  // times as many loads, and the others never stall on a full memory
+  // pipeline, so their matrix instructions keep the SIMD's matrix pipe busy
+  // while a loading wavefront waits to issue.
+  constexpr int JA = G::TA / G::RPI / LW, JB = G::TB / G::RPI / LW, DMA = JA + JB;
+  static_assert(JA * G::RPI * LW == G::TA && JB * G::RPI * LW == G::TB, "whole load blocks per loader");
+  static_assert(LW <= G::NW && DMA < 64, "loads in flight per wavefront");
+  const bool loader = wave < LW;                     // uniform
   const int64_t rowbytes = (int64_t)K * 2;
-  static_assert((G::NW * G::RPI) % 16 == 0, "loads of a wavefront are whole swizzle periods apart");
+  static_assert((LW * G::RPI) % 16 == 0, "loads of a wavefront are whole swizzle periods apart");
   auto voff_base = [&]() __attribute__((always_inline)) {
     const int l = lane_now();
     const int r = wave * G::RPI + l / G::CPR;       // row within the operand tile
     return (int)(r * rowbytes) + (((l % G::CPR) ^ G::key(r)) << 4);
   };
-  const int vstep = G::NW * G::RPI * (int)rowbytes;   // uniform
+  const int vstep = LW * G::RPI * (int)rowbytes;   // uniform
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
 
   // Load cursor: slice lkt (of K) of item li, the item's end and its descriptors.
@@ -233,12 +238,12 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
   auto dma = [&](int ls, int j, int vb) __attribute__((always_inline)) {
     const int soff = li < n_items ? lkt * BK * 2 : 0x7ff00000;
     const uint32_t sb = lds_base + (uint32_t)((ls % NS) * G::STAGE_BYTES);
-    if (j >= G::JA) {
-      const int q = j - G::JA;
+    if (j >= JA) {
+      const int q = j - JA;
       dma_to_lds(d_tok, vb + q * vstep, soff,
-                 __builtin_amdgcn_readfirstlane(sb + G::OPA_BYTES + (G::NW * q + wave) * 1024));
+                 __builtin_amdgcn_readfirstlane(sb + G::OPA_BYTES + (LW * q + wave) * 1024));
     } else {
-      const int blk = G::NW * j + wave;                 // uniform
+      const int blk = LW * j + wave;                    // uniform
       const bool w3 = DUAL && blk * G::RPI >= G::TA / 2;
       dma_to_lds(w3 ? d_w1 : d_w0, vb + j * vstep, soff, __builtin_amdgcn_readfirstlane(sb + blk * 1024));
     }
@@ -305,11 +310,11 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
       if (b == WB - 1) {
         if (reads) fa[a] = read_frag(gn, fo, a);
       } else if (a >= 1 && loads) {
-        constexpr int SLOTS = FREE, PER = (G::DMA + SLOTS - 1) / SLOTS;
+        constexpr int SLOTS = FREE, PER = (DMA + SLOTS - 1) / SLOTS;
         const int sl = slot0 + (a - 1) * (WB - 1) + b;
 #pragma unroll
         for (int q = 0; q < PER; ++q)
-          if (sl * PER + q < G::DMA) dma(ls, sl * PER + q, vb);
+          if (sl * PER + q < DMA && loader) dma(ls, sl * PER + q, vb);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -389,7 +394,7 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
     for (int s = 0; s < G::SUB - 1; ++s)
       substep(s & 1, g, s + 1, 0, s == 0, g + NS - 1, true);
     advance_load();
-    wait_vmcnt<G::DMA * (NS - 2)>();
+    wait_vmcnt<DMA * (NS - 2)>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -400,10 +405,11 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
   for (int s = 0; s < NS - 1; ++s) {
     const int vb = voff_base();
 #pragma unroll
-    for (int j = 0; j < G::DMA; ++j) dma(s, j, vb);
+    for (int j = 0; j < DMA; ++j)
+      if (loader) dma(s, j, vb);
     advance_load();
   }
-  wait_vmcnt<G::DMA * (NS - 2)>();
+  wait_vmcnt<DMA * (NS - 2)>();
   __builtin_amdgcn_s_barrier();
 
 #pragma unroll
@@ -475,8 +481,11 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(const int32_t* __restr
   }
 }
 
-// Shapes of the prefill kernels: K slice, LDS ring depth, wavefront grid and
-// blocks per wavefront.  All run 8 wavefronts (two per SIMD).
+// Shapes of the prefill kernels: K slice, LDS ring depth, wavefront grid,
+// blocks per wavefront and loading wavefronts.  All run 8 wavefronts (two per
+// SIMD).  The kWide gate/up kernel loads from 4 of them (one per SIMD): 3.19
+// -> 3.07 ms at the Mixtral prefill shape, 1.58 -> 1.54 ms skewed with the
+// fallback (A/B on one MI355X); its down projection gained nothing from it.
 //  * kWide (at most kWideMaxGroups expert groups): a 384 x 256 tile (weights x
 //    tokens; 192 accumulators per lane), gate/up as 2 x 4 wavefronts of 3 + 3
 //    (w1, w3) blocks x 2 token blocks, down as 4 x 2 wavefronts of 3 x 4.  A K
@@ -496,12 +505,12 @@ constexpr int kWideMaxGroups = 16;
 constexpr int kTallMaxMeanRows = 320;
 enum PrefillKind { kNarrow = 0, kWide = 1, kTall = 2 };
 template <bool DUAL, int KIND> struct PrefillCfg;
-template <> struct PrefillCfg<true, kNarrow> { static constexpr int BK = 32, NS = 3, WR = 2, WC = 4, WA = 6, WB = 2; };
-template <> struct PrefillCfg<false, kNarrow> { static constexpr int BK = 32, NS = 3, WR = 4, WC = 2, WA = 3, WB = 4; };
-template <> struct PrefillCfg<true, kWide> { static constexpr int BK = 64, NS = 2, WR = 2, WC = 4, WA = 6, WB = 2; };
-template <> struct PrefillCfg<false, kWide> { static constexpr int BK = 64, NS = 2, WR = 4, WC = 2, WA = 3, WB = 4; };
-template <> struct PrefillCfg<true, kTall> { static constexpr int BK = 64, NS = 2, WR = 4, WC = 2, WA = 2, WB = 5; };
-template <> struct PrefillCfg<false, kTall> { static constexpr int BK = 64, NS = 2, WR = 4, WC = 2, WA = 2, WB = 5; };
+template <> struct PrefillCfg<true, kNarrow> { static constexpr int BK = 32, NS = 3, WR = 2, WC = 4, WA = 6, WB = 2, LW = 8; };
+template <> struct PrefillCfg<false, kNarrow> { static constexpr int BK = 32, NS = 3, WR = 4, WC = 2, WA = 3, WB = 4, LW = 8; };
+template <> struct PrefillCfg<true, kWide> { static constexpr int BK = 64, NS = 2, WR = 2, WC = 4, WA = 6, WB = 2, LW = 4; };
+template <> struct PrefillCfg<false, kWide> { static constexpr int BK = 64, NS = 2, WR = 4, WC = 2, WA = 3, WB = 4, LW = 8; };
+template <> struct PrefillCfg<true, kTall> { static constexpr int BK = 64, NS = 2, WR = 4, WC = 2, WA = 2, WB = 5, LW = 8; };
+template <> struct PrefillCfg<false, kTall> { static constexpr int BK = 64, NS = 2, WR = 4, WC = 2, WA = 2, WB = 5, LW = 8; };
 template <bool DUAL, int KIND>
 using PrefillGeom = TileGeom<PrefillCfg<DUAL, KIND>::BK, PrefillCfg<DUAL, KIND>::WR, PrefillCfg<DUAL, KIND>::WC,
                              PrefillCfg<DUAL, KIND>::WA, PrefillCfg<DUAL, KIND>::WB>;
@@ -525,7 +534,7 @@ hipError_t launch_prefill_cfg(const moe_shape_t& s, const uint16_t* act, const i
   const int64_t grid = persistent_grid(max_tiles);
   if constexpr (!DUAL) {
     if (partials != nullptr) {   // split tail: K-runs into partial tiles, then their sum
-      hipLaunchKernelGGL((grouped_gemm_bf16_prefill<false, C::BK, C::NS, C::WR, C::WC, C::WA, C::WB, true>),
+      hipLaunchKernelGGL((grouped_gemm_bf16_prefill<false, C::BK, C::NS, C::WR, C::WC, C::WA, C::WB, C::LW, true>),
                          dim3((unsigned)grid), dim3(G::THREADS), 0, st, act, offsets, expert_groups(s), wa,
                          wb, N, K, out, partials, n_tiles);
       hipError_t e = hipGetLastError();
@@ -536,7 +545,7 @@ hipError_t launch_prefill_cfg(const moe_shape_t& s, const uint16_t* act, const i
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((grouped_gemm_bf16_prefill<DUAL, C::BK, C::NS, C::WR, C::WC, C::WA, C::WB, false>),
+  hipLaunchKernelGGL((grouped_gemm_bf16_prefill<DUAL, C::BK, C::NS, C::WR, C::WC, C::WA, C::WB, C::LW, false>),
                      dim3((unsigned)grid), dim3(G::THREADS), 0, st, act, offsets, expert_groups(s), wa,
                      wb, N, K, out, nullptr, n_tiles);
   return hipGetLastError();
