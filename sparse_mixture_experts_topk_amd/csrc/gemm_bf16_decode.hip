@@ -23,8 +23,10 @@
 // time then depended on where the weights were allocated: 289-336 us on four
 // copies of the same weights in one process (MI355X, Mixtral decode batch).
 // With the workgroups of each XCD on one contiguous eighth of the row groups it
-// was 276-287 us on all four.  Down (one matrix, 140 us) was slower in that
-// order (150 us) and keeps the round-robin one.
+// was 276-287 us on all four.  For down (one matrix) an eighth of every
+// expert's channel groups per XCD measured the same as round-robin on boxes
+// where neither was slow (138-140 us), and a contiguous eighth of all of w2
+// (one expert per XCD) was slower (150 us).
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "lds_stream.hpp"
@@ -104,12 +106,21 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gem
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int groups = N / 16;
-  // gate/up: each XCD streams one contiguous eighth of the row groups (the
-  // grid is padded to a multiple of 8 workgroups); down keeps the round-robin order
-  const int vb = DUAL ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
-  const int gid = vb * kWavesPerBlock + w;
-  const int cg = gid % groups;
-  const int rest = gid / groups;
+  // Each XCD streams its own part of the weights (the grid is whole rounds of
+  // the 8 XCDs): gate/up one contiguous eighth of all row groups, down the
+  // same eighth of every expert's channel groups.
+  int cg, rest;
+  if constexpr (DUAL) {
+    const int gid = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + w;
+    cg = gid % groups;
+    rest = gid / groups;
+  } else {
+    const int gx = (groups + 7) / 8;                           // channel groups per XCD
+    const int lw = (blockIdx.x >> 3) * kWavesPerBlock + w;     // wavefront within its XCD
+    cg = (blockIdx.x & 7) * gx + lw % gx;
+    rest = lw / gx;
+    if (cg >= groups) return;
+  }
   const int tt = rest % tok_tiles;
   const int e = rest / tok_tiles;
   if (e >= E) return;
@@ -173,7 +184,8 @@ __global__ __launch_bounds__(kFusedMaxExperts * kWave) void down_combine_bf16_de
   __shared__ float4 yrow[kFusedMaxRows][4];          // [permuted row][channel quad], fp32
 
   const int lane = threadIdx.x & 63, e = threadIdx.x >> 6;   // wavefront = expert (blockDim = 64 E)
-  const int cg = blockIdx.x;
+  const int cg = xcd_remap(blockIdx.x, gridDim.x);   // an eighth of the channels per XCD
+  if (cg >= N / 16) return;                           // the whole workgroup: no barrier reached
   const int row0 = offsets[e];
   const int rows = min(16, offsets[e + 1] - row0);
   if (rows > 0) {
@@ -211,8 +223,11 @@ hipError_t launch_variant(const moe_shape_t& s, const uint16_t* act, const int32
   const int tok_tiles = (int)((max_rows_per_expert(s) + 15) / 16);
   const int64_t groups = (int64_t)expert_groups(s) * tok_tiles * (N / 16);
   if (groups <= 0) return hipSuccess;   // no expert can hold a row (capacity 0)
-  int64_t blocks = (groups + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (DUAL) blocks = (blocks + 7) / 8 * 8;     // whole rounds of the 8 XCDs (extra waves exit)
+  // whole rounds of the 8 XCDs (waves past the work exit)
+  const int64_t per_xcd = DUAL ? (groups + 8 * kWavesPerBlock - 1) / (8 * kWavesPerBlock)
+                               : ((int64_t)(N / 16 + 7) / 8 * expert_groups(s) * tok_tiles + kWavesPerBlock - 1) /
+                                     kWavesPerBlock;
+  const int64_t blocks = 8 * per_xcd;
   hipLaunchKernelGGL((grouped_gemm_bf16_decode<DUAL, ROWS, MIN_WAVES>), dim3((unsigned)blocks),
                      dim3(kWavesPerBlock * kWave), 0, st, act, offsets, expert_groups(s), wa, wb, N, K,
                      out, tok_tiles, gather, s.top_k, s.T * s.top_k);
@@ -224,8 +239,11 @@ hipError_t launch_variant(const moe_shape_t& s, const uint16_t* act, const int32
 hipError_t launch_decode_bf16(const moe_shape_t& s, bool dual, const uint16_t* act,
                               const int32_t* offsets, const uint16_t* wa, const uint16_t* wb,
                               int N, int K, void* out, hipStream_t st) {
-  // Measured at the Mixtral shape (4 rows per expert): dual with 8 rows x 128 B
-  // per load instruction streams 6.5 TB/s; single with 4 rows x 256 B, 6.3 TB/s.
+  // 4 rows x 256 B per load instruction where K allows it.  At the Mixtral
+  // decode batch (MI355X) gate/up streams 6.9 TB/s and down 6.8 TB/s; with
+  // 8 rows x 128 B gate/up was 0.2-3% slower, down 13% slower, and with
+  // 2 rows x 512 B down was 18% slower.
+  if (dual && K % 128 == 0) return launch_variant<true, 4, 4>(s, act, offsets, wa, wb, N, K, out, st);
   if (dual) return launch_variant<true, 8, 4>(s, act, offsets, wa, wb, N, K, out, st);
   if (K % 128 == 0) return launch_variant<false, 4, 4>(s, act, offsets, wa, wb, N, K, out, st);
   return launch_variant<false, 8, 4>(s, act, offsets, wa, wb, N, K, out, st);
@@ -240,7 +258,7 @@ hipError_t launch_down_combine_bf16(const moe_shape_t& s, const uint16_t* h, con
                                     const uint16_t* w2, const int32_t* slot_to_row, const float* gw,
                                     uint16_t* y, hipStream_t st) {
   if (!down_combine_fused(s)) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)(s.d_model / 16)), block((unsigned)(s.n_experts * kWave));
+  const dim3 grid((unsigned)((s.d_model / 16 + 7) / 8 * 8)), block((unsigned)(s.n_experts * kWave));
   // the down kernel's choice: 4 rows x 256 B per load instruction when K allows it
   if (s.d_ff % 128 == 0)
     hipLaunchKernelGGL((down_combine_bf16_decode<4>), grid, block, 0, st, h, offsets, w2, s.d_model,
@@ -254,6 +272,8 @@ hipError_t launch_down_combine_bf16(const moe_shape_t& s, const uint16_t* h, con
 hipError_t launch_gate_up_bf16_gather(const moe_shape_t& s, const uint16_t* x, const int32_t* perm_src,
                                       const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                                       uint16_t* h, hipStream_t st) {
+  if (s.d_model % 128 == 0)
+    return launch_variant<true, 4, 4>(s, x, offsets, w1, w3, s.d_ff, s.d_model, h, st, perm_src);
   return launch_variant<true, 8, 4>(s, x, offsets, w1, w3, s.d_ff, s.d_model, h, st, perm_src);
 }
 
