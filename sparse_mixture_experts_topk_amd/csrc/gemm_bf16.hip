@@ -140,7 +140,7 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const TileSplit sp = TileSplit::of(n_token_tiles * n_tiles, xcd, slots, KT);
   // this workgroup's items: whole tiles, then (split) up to two K-runs of tail tiles
-  const int n_whole = sp.R + ((!SPLIT && slot < sp.tail) ? 1 : 0);
+  const int n_whole = sp.R + (((!SPLIT || sp.whole_tail) && slot < sp.tail) ? 1 : 0);
   const int run0 = slot * sp.P, run1 = min(run0 + sp.P, sp.tail * KT);
   const int n_runs = (SPLIT && run0 < run1) ? (run1 - 1) / KT - run0 / KT + 1 : 0;
   const int n_items = n_whole + n_runs;
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(256) void split_fixup_kernel(const int32_t* __restr
   const int xcd = (blockIdx.x / kRowGroups) & 7, j = blockIdx.x / kRowGroups >> 3;
   const int KT = K / BK;
   const TileSplit sp = TileSplit::of(__builtin_amdgcn_readfirstlane(tpre[E]) * n_tiles, xcd, slots, KT);
-  if (j >= sp.tail) return;
+  if (sp.whole_tail || j >= sp.tail) return;   // no runs: the tail tiles were stored whole
   int e, r0, r1, mt, nt;
   find_tile(offs, tpre, E, n_tiles, sp.share_begin + sp.R * slots + j, e, r0, r1, mt, nt);
   const int tok0 = r0 + mt * TR, tok_rows = min(TR, r1 - tok0), ch0 = nt * CH;

@@ -14,8 +14,16 @@ namespace moe {
 // near-equal runs of P slices, one per workgroup, each covering parts of at
 // most two tiles; the parts are written as fp32 partial tiles and summed by a
 // second kernel in K order, which keeps the result independent of timing.
+// A split kernel still takes the tail whole (`whole_tail`, P = 0) when whole
+// tiles would leave less than an eighth of the share's workgroup time idle:
+// the runs' partial tiles, their sum, and workgroups that no longer read the
+// same K slices at the same time cost more than that (down projection,
+// MI355X: Mixtral prefill, a last round 92% full, 1.81 -> 1.67 ms whole;
+// 256 experts, a 17th round 6% full, 1.69 -> 1.65 ms; a Zipf-skewed batch
+// with a second round 7% full needs the split, 0.68 against 1.07 ms).
 struct TileSplit {
   int share_begin, R, tail, P;
+  bool whole_tail;
 
   __device__ static TileSplit of(int total, int xcd, int slots, int KT) {
     TileSplit t;
@@ -24,7 +32,8 @@ struct TileSplit {
     const int len = max(0, min(t.share_begin + per_xcd, total) - t.share_begin);
     t.R = len / slots;
     t.tail = len - t.R * slots;
-    t.P = (t.tail * KT + slots - 1) / slots;
+    t.whole_tail = t.tail > 0 && 8 * (slots - t.tail) < slots * (t.R + 1);
+    t.P = t.whole_tail ? 0 : (t.tail * KT + slots - 1) / slots;
     return t;
   }
 };
