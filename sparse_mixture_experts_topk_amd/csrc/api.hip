@@ -245,9 +245,17 @@ moe_status_t forward_impl(const moe_shape_t* s, const void* x, const void* w_gat
     }
     if (e == hipSuccess)
       e = moe::launch_permute_index(*s, ids, drop_in, next, counts, offsets, perm_src, slot_to_row, st);
-    if (e == hipSuccess) e = moe::launch_permute_scatter(*s, x, offsets, perm_src, x_perm, x_scale, st);
-    if (e == hipSuccess)
-      e = moe::launch_gate_up(*s, x_perm, x_scale, offsets, w1, w3, w1_scale, w3_scale, h, h_scale, st);
+    if (moe::gate_up_bf16_gathers(*s)) {
+      // many small experts: gate/up reads the token rows of x through perm_src (no x_perm)
+      if (e == hipSuccess)
+        e = moe::launch_gate_up_bf16_prefill_gather(*s, static_cast<const uint16_t*>(x), perm_src, offsets,
+                                                    static_cast<const uint16_t*>(w1),
+                                                    static_cast<const uint16_t*>(w3), static_cast<uint16_t*>(h), st);
+    } else {
+      if (e == hipSuccess) e = moe::launch_permute_scatter(*s, x, offsets, perm_src, x_perm, x_scale, st);
+      if (e == hipSuccess)
+        e = moe::launch_gate_up(*s, x_perm, x_scale, offsets, w1, w3, w1_scale, w3_scale, h, h_scale, st);
+    }
   }
   if (moe::route_index_fused(*s) && moe::down_combine_fused(*s)) {
     // decode, bf16 experts: down + combine in one launch (no y_perm)

@@ -81,15 +81,22 @@ struct TileGeom {
 // slices of all its tiles form one stream through the LDS ring, so the
 // first slices of the next tile load while the current one finishes and
 // stores its results.  Split K-runs go to fp32 partial tiles [token][TA].
-template <bool DUAL, int BK, int NS, int WR, int WC, int WA, int WB, int LW, bool SPLIT>
+//
+// GATHER (gate/up only): the token operand rows are read straight from x, row
+// perm_src[row] / k of it for a routed slot (slot - T k for the shared
+// expert's), instead of from a permuted copy; each loading lane keeps the byte
+// offsets of its JB token rows of the load cursor's tile in registers.
+template <bool DUAL, int BK, int NS, int WR, int WC, int WA, int WB, int LW, bool SPLIT, bool GATHER>
 __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
     const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, int N, int K,
-    void* __restrict__ out, float* __restrict__ partials, int n_tiles) {
+    void* __restrict__ out, float* __restrict__ partials, int n_tiles,
+    const int32_t* __restrict__ gather, int k, int Tk, int xrows) {
   using G = TileGeom<BK, WR, WC, WA, WB>;
   constexpr int TR = G::TB;                  // token rows of a tile
   static_assert(G::SUB % 2 == 0 && NS >= 2 && (!DUAL || WA % 2 == 0) && WB >= 2, "pipeline shape");
   static_assert(!SPLIT || !DUAL, "split runs: single GEMM");
+  static_assert(!GATHER || DUAL, "gathered token rows: gate/up only");
   static_assert(!DUAL || (G::TA / 2) % 16 == 0, "w3 rows start on a swizzle period");
   // The expert-group tables (offsets and token-tile prefix) follow the LDS
   // ring when they fit in the 160 KiB; otherwise (the 2-stage ring of 64-wide
@@ -217,12 +224,28 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
   // Load cursor: slice lkt (of K) of item li, the item's end and its descriptors.
   i32x4_t d_tok, d_w0, d_w1;
   int li = 0, lkt = 0, lke = 0;
+  int tok_off[GATHER ? JB : 1];    // gather: this lane's token-row offsets in x (load q)
   auto load_tile = [&]() __attribute__((always_inline)) {
     if (li < n_items) {
       const Tile t = tile_of(li);
       lkt = t.kb;
       lke = t.ke;
-      d_tok = make_desc(act + (int64_t)t.tok0 * K, t.tok_rows * rowbytes);
+      if constexpr (GATHER) {
+        d_tok = make_desc(act, (int64_t)xrows * rowbytes);
+        if (loader) {
+          const int l = lane_now();
+#pragma unroll
+          for (int q = 0; q < JB; ++q) {
+            const int r = (LW * q + wave) * G::RPI + l / G::CPR;          // row within the token tile
+            const int src = gather[t.tok0 + (r < t.tok_rows ? r : 0)];
+            const int tok = src < Tk ? src / k : src - Tk;
+            tok_off[q] = r < t.tok_rows ? (int)(tok * rowbytes) + (((l % G::CPR) ^ G::key(r)) << 4)
+                                        : 0x7ff00000;                        // past x: zeros
+          }
+        }
+      } else {
+        d_tok = make_desc(act + (int64_t)t.tok0 * K, t.tok_rows * rowbytes);
+      }
       d_w0 = make_desc(wa + ((int64_t)t.e * N + t.ch0) * K, (int64_t)(N - t.ch0) * rowbytes);
       d_w1 = DUAL ? make_desc(wb + ((int64_t)t.e * N + t.ch0 - G::TA / 2) * K,
                               (int64_t)(N - t.ch0 + G::TA / 2) * rowbytes)
@@ -240,7 +263,7 @@ __global__ __launch_bounds__(64 * WR * WC, 1) void grouped_gemm_bf16_prefill(
     const uint32_t sb = lds_base + (uint32_t)((ls % NS) * G::STAGE_BYTES);
     if (j >= JA) {
       const int q = j - JA;
-      dma_to_lds(d_tok, vb + q * vstep, soff,
+      dma_to_lds(d_tok, GATHER ? tok_off[GATHER ? q : 0] : vb + q * vstep, soff,
                  __builtin_amdgcn_readfirstlane(sb + G::OPA_BYTES + (LW * q + wave) * 1024));
     } else {
       const int blk = LW * j + wave;                    // uniform
@@ -521,10 +544,10 @@ constexpr int64_t kPartialTileBytes =
 static_assert(PrefillGeom<false, kWide>::TA == PrefillGeom<false, kNarrow>::TA &&
               PrefillGeom<false, kWide>::TB == PrefillGeom<false, kNarrow>::TB, "one partial tile shape per TA");
 
-template <bool DUAL, int KIND>
+template <bool DUAL, int KIND, bool GATHER = false>
 hipError_t launch_prefill_cfg(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                           const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
-                          float* partials, hipStream_t st) {
+                          float* partials, hipStream_t st, const int32_t* gather = nullptr) {
   using C = PrefillCfg<DUAL, KIND>;
   using G = PrefillGeom<DUAL, KIND>;
   constexpr int CH_TILE = DUAL ? G::TA / 2 : G::TA;
@@ -534,9 +557,9 @@ hipError_t launch_prefill_cfg(const moe_shape_t& s, const uint16_t* act, const i
   const int64_t grid = persistent_grid(max_tiles);
   if constexpr (!DUAL) {
     if (partials != nullptr) {   // split tail: K-runs into partial tiles, then their sum
-      hipLaunchKernelGGL((grouped_gemm_bf16_prefill<false, C::BK, C::NS, C::WR, C::WC, C::WA, C::WB, C::LW, true>),
+      hipLaunchKernelGGL((grouped_gemm_bf16_prefill<false, C::BK, C::NS, C::WR, C::WC, C::WA, C::WB, C::LW, true, false>),
                          dim3((unsigned)grid), dim3(G::THREADS), 0, st, act, offsets, expert_groups(s), wa,
-                         wb, N, K, out, partials, n_tiles);
+                         wb, N, K, out, partials, n_tiles, nullptr, 1, 0, 0);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((split_fixup_kernel<G::TA, G::TB>), dim3((unsigned)(grid * (G::TB / 16))), dim3(256),
@@ -545,9 +568,9 @@ hipError_t launch_prefill_cfg(const moe_shape_t& s, const uint16_t* act, const i
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((grouped_gemm_bf16_prefill<DUAL, C::BK, C::NS, C::WR, C::WC, C::WA, C::WB, C::LW, false>),
+  hipLaunchKernelGGL((grouped_gemm_bf16_prefill<DUAL, C::BK, C::NS, C::WR, C::WC, C::WA, C::WB, C::LW, false, GATHER>),
                      dim3((unsigned)grid), dim3(G::THREADS), 0, st, act, offsets, expert_groups(s), wa,
-                     wb, N, K, out, nullptr, n_tiles);
+                     wb, N, K, out, nullptr, n_tiles, gather, s.top_k, s.T * s.top_k, s.T);
   return hipGetLastError();
 }
 
@@ -588,6 +611,19 @@ hipError_t launch_down_bf16(const moe_shape_t& s, const uint16_t* h, const int32
     return launch_decode_bf16(s, false, h, offsets, w2, nullptr, s.d_model, s.d_ff, y_perm, st);
   return launch_prefill<false>(s, h, offsets, w2, nullptr, s.d_model, s.d_ff, y_perm,
                                static_cast<float*>(workspace), st);
+}
+
+bool gate_up_bf16_gathers(const moe_shape_t& s) {
+  return s.act_dtype == MOE_BF16 && s.w_dtype == MOE_BF16 && max_rows_per_expert(s) > kDecodeMaxRows &&
+         mean_routed_rows(s) <= kTallMaxMeanRows;
+}
+
+hipError_t launch_gate_up_bf16_prefill_gather(const moe_shape_t& s, const uint16_t* x, const int32_t* perm_src,
+                                              const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
+                                              uint16_t* h, hipStream_t st) {
+  if (!gate_up_bf16_gathers(s)) return hipErrorInvalidValue;
+  return launch_prefill_cfg<true, kTall, true>(s, x, offsets, w1, w3, s.d_ff, s.d_model, h, nullptr, st,
+                                               perm_src);
 }
 
 size_t down_workspace_bytes_bf16(const moe_shape_t& s) {

@@ -90,6 +90,13 @@ size_t down_workspace_bytes_bf16(const moe_shape_t& s);
 // top-2, dropless, no shared expert, E <= 16): y from h, offsets, slot_to_row
 // and the gate weights, bit for bit what launch_down_bf16 + launch_combine give.
 bool down_combine_fused(const moe_shape_t& s);
+// Tiled gate/up reading the token rows of x through perm_src (no x_perm): bf16,
+// prefill batches whose routed experts average at most 320 rows (the 256 x 320
+// tile); the result equals launch_gate_up_bf16 on the permuted copy bit for bit.
+bool gate_up_bf16_gathers(const moe_shape_t& s);
+hipError_t launch_gate_up_bf16_prefill_gather(const moe_shape_t& s, const uint16_t* x, const int32_t* perm_src,
+                                              const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
+                                              uint16_t* h, hipStream_t st);
 hipError_t launch_down_combine_bf16(const moe_shape_t& s, const uint16_t* h, const int32_t* offsets,
                                     const uint16_t* w2, const int32_t* slot_to_row, const float* gw,
                                     uint16_t* y, hipStream_t st);

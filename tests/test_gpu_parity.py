@@ -640,7 +640,13 @@ def test_general_topk_fp32_fp8_mxfp4():
 
 
 def test_general_topk_forward_matches_staged():
+    """moe_forward equals the staged calls bitwise.  fg_fwd, fg_fwd_tall and fg_fwd_noshared take the
+    256 x 320 tile path, where moe_forward's gate/up reads the token rows of x through perm_src instead
+    of the permuted copy (ragged 320-row tiles, capacity, no shared expert, k = 2); fg_fwd_dec is the
+    weight-streaming path."""
     for cfg in (fg_cfg("fg_fwd", T=260, n_experts=64, top_k=8, capacity=40, seed=56),
+                fg_cfg("fg_fwd_tall", T=700, n_experts=16, top_k=4, seed=59),
+                fg_cfg("fg_fwd_noshared", T=1000, n_experts=8, top_k=2, n_shared=0, seed=60),
                 fg_cfg("fg_fwd_dec", T=24, n_experts=256, top_k=8, seed=57)):
         inp = synthetic.make_inputs(cfg)
         say(f"moe_forward vs staged: {cfg.name}")
