@@ -251,6 +251,17 @@ moe_status_t forward_impl(const moe_shape_t* s, const void* x, const void* w_gat
         e = moe::launch_gate_up_bf16_prefill_gather(*s, static_cast<const uint16_t*>(x), perm_src, offsets,
                                                     static_cast<const uint16_t*>(w1),
                                                     static_cast<const uint16_t*>(w3), static_cast<uint16_t*>(h), st);
+    } else if (moe::gate_up_decode_gathers(*s)) {
+      // weight streaming (e.g. many experts, a shared expert, a capacity): the same, no x_perm
+      if (e == hipSuccess && s->w_dtype == MOE_BF16)
+        e = moe::launch_gate_up_bf16_gather(*s, static_cast<const uint16_t*>(x), perm_src, offsets,
+                                            static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3),
+                                            static_cast<uint16_t*>(h), st);
+      if (e == hipSuccess && s->w_dtype == MOE_MXFP4)
+        e = moe::launch_gate_up_mxfp4_gather(*s, static_cast<const uint16_t*>(x), perm_src, offsets,
+                                             static_cast<const uint8_t*>(w1), static_cast<const uint8_t*>(w1_scale),
+                                             static_cast<const uint8_t*>(w3), static_cast<const uint8_t*>(w3_scale),
+                                             static_cast<uint16_t*>(h), st);
     } else {
       if (e == hipSuccess) e = moe::launch_permute_scatter(*s, x, offsets, perm_src, x_perm, x_scale, st);
       if (e == hipSuccess)

@@ -613,6 +613,11 @@ hipError_t launch_down_bf16(const moe_shape_t& s, const uint16_t* h, const int32
                                static_cast<float*>(workspace), st);
 }
 
+bool gate_up_decode_gathers(const moe_shape_t& s) {
+  return s.act_dtype == MOE_BF16 && (s.w_dtype == MOE_BF16 || s.w_dtype == MOE_MXFP4) &&
+         max_rows_per_expert(s) <= kDecodeMaxRows;
+}
+
 bool gate_up_bf16_gathers(const moe_shape_t& s) {
   return s.act_dtype == MOE_BF16 && s.w_dtype == MOE_BF16 && max_rows_per_expert(s) > kDecodeMaxRows &&
          mean_routed_rows(s) <= kTallMaxMeanRows;

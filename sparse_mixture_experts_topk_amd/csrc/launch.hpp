@@ -94,6 +94,10 @@ bool down_combine_fused(const moe_shape_t& s);
 // prefill batches whose routed experts average at most 320 rows (the 256 x 320
 // tile); the result equals launch_gate_up_bf16 on the permuted copy bit for bit.
 bool gate_up_bf16_gathers(const moe_shape_t& s);
+// Weight-streaming (decode) gate/up that can read token rows through perm_src
+// (launch_gate_up_bf16_gather / launch_gate_up_mxfp4_gather): bf16 activations,
+// bf16 or MXFP4 experts, at most 64 rows per expert.
+bool gate_up_decode_gathers(const moe_shape_t& s);
 hipError_t launch_gate_up_bf16_prefill_gather(const moe_shape_t& s, const uint16_t* x, const int32_t* perm_src,
                                               const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                                               uint16_t* h, hipStream_t st);

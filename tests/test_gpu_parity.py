@@ -285,9 +285,12 @@ def test_dense_reduction_all_experts_equal():
     assert_close(to_np(buf.y.float()), dense, "bf16", "dense reduction")
 
 
+@pytest.mark.parametrize("T,cap", [(900, 250), (60, 12)])
 @pytest.mark.parametrize("overflow", ["drop", "next_best"])
-def test_forward_matches_staged_bitwise_and_is_deterministic(overflow):
-    cfg = mid_cfg("fwd_vs_staged", T=900, n_experts=8, capacity=250, router_bias="zipf1.2", seed=11,
+def test_forward_matches_staged_bitwise_and_is_deterministic(overflow, T, cap):
+    """T=900: the tiled path (256 x 320 tiles, token rows gathered through perm_src in moe_forward);
+    T=60: weight streaming with a capacity (the gate/up gathers there too)."""
+    cfg = mid_cfg("fwd_vs_staged", T=T, n_experts=8, capacity=cap, router_bias="zipf1.2", seed=11,
                   overflow=overflow)
     inp = synthetic.make_inputs(cfg)
     say(f"moe_forward vs the five staged calls ({overflow}); run twice")
