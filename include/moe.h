@@ -268,11 +268,14 @@ moe_status_t moe_combine(const moe_shape_t* shape, const float* y_perm, const in
  *   moe_permute), logits_out [T, E] fp32
  * topk_ids_out are the router's choices; with MOE_OVERFLOW_NEXT_BEST a slot
  * whose drop mask is 2 was processed by its fallback expert instead.
- * Results equal the five calls above made in order, bit for bit.  For decode
- * batches (bf16 activations, T <= 16, E <= 16, top-2, dropless, no shared
- * expert) fewer kernels run: the router also groups the tokens, gate/up reads
- * the token rows of x directly (no x_perm), and with bf16 experts the down
- * projection and the combine are one kernel (no y_perm).
+ * Results equal the five calls above made in order, bit for bit.  Fewer
+ * kernels run where they can: with bf16 activations and bf16 or MXFP4 experts,
+ * gate/up reads the token rows of x through perm_src instead of a permuted
+ * copy when at most 64 rows reach any expert, and (bf16 experts) when the
+ * routed experts average at most 320 rows; for decode batches (T <= 16,
+ * E <= 16, top-2, dropless, no shared expert) the router also groups the
+ * tokens, and with bf16 experts the down projection and the combine are one
+ * kernel (no y_perm).
  * Workspace: moe_workspace_bytes(MOE_CALL_FORWARD) holds every intermediate. */
 moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const void* w_gate,
                          const float* router_bias, const void* w1, const void* w3, const void* w2,
