@@ -60,12 +60,39 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, float scale) {
   return as_bf16x8(u);
 }
 
+// Element offset, inside a 256-element stage, of matrix-instruction operand
+// c = 4 j + q of lane group g = 0 (j = c / 4 selects the 128-element half).
+__device__ __forceinline__ constexpr int operand_elem(int c) { return (c >> 2) * 128 + (c & 3) * 8; }
+
+// Each lane's value from the lane d places higher in its row of 16 lanes
+// (DPP row rotation; a rotation right by n moves lane i's value to lane i + n).
+template <int D>
+__device__ __forceinline__ uint4 from_lane_above(uint4 v) {
+  constexpr int ctrl = 0x120 + ((16 - D) & 15);   // row_ror:(16 - D)
+  return make_uint4((uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, ctrl, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, ctrl, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.z, ctrl, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, ctrl, 0xF, 0xF, false));
+}
+
+template <int V> struct IntC { static constexpr int value = V; };
+
 // Persistent form.  The grid is the resident capacity; workgroup b takes
 // rounds r = 0, 1, ... of GPW output groups (the KS wavefronts of a group
 // split its K range), groups numbered over the experts' token tiles only, so
 // no workgroup streams an empty expert.  Each wavefront's weight loads form
 // one stream across its groups: the ring keeps PD stages in flight through
 // group boundaries.  KS must divide the stage count K / 256.
+//
+// Packed token loads.  When every token tile of the launch has at most 16 / P
+// rows (P = 2, 4, 8; decided in the kernel from the offsets), one token load
+// instruction carries P of a stage's eight operands: lane (t, g) with
+// t = s (16 / P) + u loads operand i P + s of token u, and a row rotation brings
+// it to lane (u, g) for its matrix instruction.  Lanes u >= 16 / P then hold
+// other operands: columns past the tile's rows, which are never stored (a
+// column of the product depends only on its own token).  Same operands in the
+// stored columns, same instruction order: the result is the unpacked one, bit
+// for bit, with a half to an eighth of the token load instructions.
 template <bool DUAL, int RB, int MIN_WAVES, int PD, int KS>
 __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxfp4_decode(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
@@ -87,12 +114,19 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
   __syncthreads();
   const int CGN = N / CH;
   int A = 0;                                        // output groups over all token tiles
-  for (int e = 0; e < E; ++e)
-    A += (__builtin_amdgcn_readfirstlane(s_offs[e + 1] - s_offs[e]) + 15) / 16 * CGN;
+  int mrows = 0;                                    // most rows in a token tile
+  for (int e = 0; e < E; ++e) {
+    const int cnt = __builtin_amdgcn_readfirstlane(s_offs[e + 1] - s_offs[e]);
+    A += (cnt + 15) / 16 * CGN;
+    mrows = max(mrows, min(cnt, 16));
+  }
   const int per_round = gridDim.x * GPW;
   const int first = blockIdx.x * GPW;
   if (first >= A) return;                           // uniform over the workgroup
   const int R = (A - first + per_round - 1) / per_round;
+  auto run = [&](auto pc) __attribute__((always_inline)) {
+  constexpr int P = decltype(pc)::value;            // token operands per load instruction
+  constexpr int TPL = 16 / P;                       // token lanes per row of 16 lanes
 
   struct Grp { int e, cg, row0, rows; };            // rows == 0: no group (loads stay valid)
   auto locate = [&](int rd) __attribute__((always_inline)) -> Grp {
@@ -162,13 +196,14 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
                                              cgp.rows * K * 2, 0x00020000);
   };
   auto token_off = [&]() __attribute__((always_inline)) -> int {
-    if (tr >= cgp.rows) return 0x7ff00000;
-    int row = tr;
+    const int u = tr % TPL, sp = tr / TPL;          // token, operand within the instruction
+    if (u >= cgp.rows) return 0x7ff00000;
+    int row = u;
     if (gather != nullptr) {
-      const int src = gather[cgp.row0 + tr];
+      const int src = gather[cgp.row0 + u];
       row = src < Tk ? src / k : src - Tk;
     }
-    return (row * K + g * 32) * 2;
+    return (row * K + g * 32 + (P == 8 ? operand_elem(sp) : sp * 8)) * 2;
   };
   __amdgpu_buffer_rsrc_t xrs = token_rsrc();
   int xoff_cur = token_off();
@@ -231,13 +266,11 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
 
   auto stage = [&](WOps& cur, WOps& nxt) __attribute__((always_inline)) {
     const int xoff = xoff_cur;
-    uint4 x[2][4];
+    uint4 xv[8 / P];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        x[j][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                      xrs, xoff, (cst * kMx4StageK + j * 128 + q * 8) * 2, 0));
+    for (int i = 0; i < 8 / P; ++i)
+      xv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                  xrs, xoff, (cst * kMx4StageK + operand_elem(i * P)) * 2, 0));
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -249,6 +282,21 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
               cur.w[m][b][i];
         }
     load_weights(nxt);
+    uint4 x[2][4];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint4 v = xv[c / P];
+      switch (c % P * TPL) {                        // operand c sits TPL (c % P) lanes above
+        case 0: x[c >> 2][c & 3] = v; break;
+        case 2: x[c >> 2][c & 3] = from_lane_above<2>(v); break;
+        case 4: x[c >> 2][c & 3] = from_lane_above<4>(v); break;
+        case 6: x[c >> 2][c & 3] = from_lane_above<6>(v); break;
+        case 8: x[c >> 2][c & 3] = from_lane_above<8>(v); break;
+        case 10: x[c >> 2][c & 3] = from_lane_above<10>(v); break;
+        case 12: x[c >> 2][c & 3] = from_lane_above<12>(v); break;
+        default: x[c >> 2][c & 3] = from_lane_above<14>(v); break;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int chunk = 4 * j + g;
@@ -281,6 +329,11 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
 #pragma unroll
   for (int u = 0; u < PD; ++u)
     if (nfull + u < S) stage(ring[u], ring[(u + PD) % (PD + 1)]);
+  };
+  if (mrows <= 2) run(IntC<8>{});
+  else if (mrows <= 4) run(IntC<4>{});
+  else if (mrows <= 8) run(IntC<2>{});
+  else run(IntC<1>{});
 }
 
 // Workgroups per CU = MIN_WAVES wavefronts per SIMD; KS is the largest of 4, 2, 1

@@ -475,6 +475,21 @@ def test_mxfp4_edge_cases():
     assert res.perm.counts.max() <= 48 and (res.status == 2).sum() > 0
 
 
+@pytest.mark.parametrize("T,seed,most_rows", [(2, 37, 1), (4, 36, 2), (6, 36, 3), (8, 36, 4),
+                                              (10, 36, 5), (16, 37, 8), (24, 36, 9)])
+def test_mxfp4_token_tile_heights(T, seed, most_rows):
+    """The MXFP4 kernel packs 8, 4, 2 or 1 token operands per load instruction when the launch's
+    fullest token tile has at most 2, 4, 8 or 16 rows; each band and its edges against the
+    oracle (staged calls, token rows from x_perm) and the fused call (rows gathered from x)
+    bitwise against the staged one."""
+    cfg = mx4_mid_cfg(f"mx4_rows{most_rows}", T=T, seed=seed)
+    st, res, inputs = run_staged_and_check(cfg)
+    assert int(res.perm.counts.max()) == most_rows
+    b = runner.forward(runner.DeviceInputs.from_host(inputs))
+    torch.cuda.synchronize()
+    assert torch.equal(st["y"], b.y)
+
+
 def test_mxfp4_forward_matches_staged():
     cfg = mx4_mid_cfg("mx4_fwd", T=48, seed=35)
     inp = synthetic.make_inputs(cfg)
