@@ -93,7 +93,18 @@ template <int V> struct IntC { static constexpr int value = V; };
 // column of the product depends only on its own token).  Same operands in the
 // stored columns, same instruction order: the result is the unpacked one, bit
 // for bit, with a half to an eighth of the token load instructions.
-template <bool DUAL, int RB, int MIN_WAVES, int PD, int KS>
+//
+// Scale bytes.  Each stage needs the 8 scale bytes of each of the wavefront's
+// 64 weight rows, 64 cache lines for 512 bytes.  So a lane reads Q stages of
+// one row at once (Q = 2; four spill the gate/up form): lane (r, c) holds
+// Q * 8 contiguous bytes of row r of block
+// c = m RB + b, read once every Q stages, and
+// lane (t, g) takes its row's bytes of each block from lane (t, c) through the
+// cross-lane permute.  Q divides the stages of a K part, and the stage loop is
+// unrolled to a multiple of Q, so no load is conditional.  The next cycle's
+// bytes are read in the last stage of a cycle, once that stage has taken its
+// own: the two register sets are never live together.
+template <bool DUAL, int RB, int MIN_WAVES, int PD, int KS, int Q>
 __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxfp4_decode(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
     const uint8_t* __restrict__ wa, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ wb,
@@ -157,9 +168,11 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
   const int st_begin = kpart * nsp;
   const int S = R * nsp;                            // stages of this wavefront's stream
 
+  static_assert(NM * RB == 4, "one scale row per lane: four 16-row blocks per wavefront");
+  static_assert(Q == 1 || Q == 2, "scale stages per load");
+  const int s_blk = lane >> 4;                      // the block whose scale row this lane reads
   struct WOps {
     uint4 w[NM][RB][2];
-    uint2 s[NM][RB];
   };
   // load cursor
   int lr = 0, lst = st_begin;
@@ -171,16 +184,38 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
       const uint8_t* pw = (m == 0 ? wa : wb) + wrow0 * kb;
       const uint8_t* ps = (m == 0 ? sa : sb) + wrow0 * nblk;
 #pragma unroll
-      for (int b = 0; b < RB; ++b) {
+      for (int b = 0; b < RB; ++b)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
           o.w[m][b][i] = load_stream16(pw + (int64_t)(b * 16 + i * 8 + lrow) * kb + lst * kMx4RowBytes + lch * 16);
-        o.s[m][b] = *reinterpret_cast<const uint2*>(ps + (int64_t)(b * 16 + tr) * nblk + lst * 8);
-      }
     }
     if (++lst == st_begin + nsp) {                  // past the stream's end: reload its last group
       lst = st_begin;
       if (lr + 1 < R) lg = locate(++lr);
+    }
+  };
+  // scale cursor: Q stages per load
+  int sr = 0, sst = st_begin;
+  Grp sg = locate(0);
+  uint32_t s_cur[2 * Q], s_nxt[2 * Q];
+  auto load_scales = [&](uint32_t (&d)[2 * Q]) __attribute__((always_inline)) {
+    const int m = s_blk / RB, b = s_blk % RB;
+    const uint8_t* ps = (m == 0 ? sa : sb) + ((int64_t)sg.e * N + sg.cg * CH + b * 16 + tr) * nblk + sst * 8;
+    if constexpr (Q == 1) {
+      const uint2 v = *reinterpret_cast<const uint2*>(ps);
+      d[0] = v.x;
+      d[1] = v.y;
+    } else {                                        // 16-byte aligned: K is a multiple of 512
+      const uint4 v = *reinterpret_cast<const uint4*>(ps);
+      d[0] = v.x;
+      d[1] = v.y;
+      d[2] = v.z;
+      d[3] = v.w;
+    }
+    sst += Q;
+    if (sst == st_begin + nsp) {                    // past the stream's end: reload its last group
+      sst = st_begin;
+      if (sr + 1 < R) sg = locate(++sr);
     }
   };
   // compute cursor
@@ -264,7 +299,8 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
     }
   };
 
-  auto stage = [&](WOps& cur, WOps& nxt) __attribute__((always_inline)) {
+  // ph: the stage's place in its cycle of Q (a constant once the loop is unrolled)
+  auto stage = [&](WOps& cur, WOps& nxt, int ph) __attribute__((always_inline)) {
     const int xoff = xoff_cur;
     uint4 xv[8 / P];
 #pragma unroll
@@ -281,6 +317,19 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
           *reinterpret_cast<uint4*>(&lds[w][m][b][row * kMx4RowBytes + ((lch ^ lds_swizzle_key(row)) & 7) * 16]) =
               cur.w[m][b][i];
         }
+    uint32_t sc[NM][RB][2];                         // this lane's row: the stage's 8 scale bytes per block
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const int src = ((m * RB + b) * 16 + tr) * 4;
+        sc[m][b][0] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)s_cur[2 * ph]);
+        sc[m][b][1] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)s_cur[2 * ph + 1]);
+      }
+    // The next cycle's scale bytes, a stage ahead (this cycle's are all taken),
+    // issued before the weight prefetch: loads complete in order, so waiting
+    // for them next stage does not wait for weights PD stages ahead.
+    if (ph == Q - 1) load_scales(s_nxt);
     load_weights(nxt);
     uint4 x[2][4];
 #pragma unroll
@@ -306,7 +355,7 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
         for (int b = 0; b < RB; ++b) {
           const uint4 c = *reinterpret_cast<const uint4*>(
               &lds[w][m][b][tr * kMx4RowBytes + ((chunk ^ lds_swizzle_key(tr)) & 7) * 16]);
-          const uint32_t sbyte = ((j ? cur.s[m][b].y : cur.s[m][b].x) >> (8 * g)) & 255u;
+          const uint32_t sbyte = (sc[m][b][j] >> (8 * g)) & 255u;
           const float scale = e8m0_to_f32(sbyte);
           const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
@@ -315,20 +364,27 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
                                                                  as_bf16x8(x[j][q]), acc[m][b], 0, 0, 0);
         }
     }
+    if (ph == Q - 1) {
+#pragma unroll
+      for (int i = 0; i < 2 * Q; ++i) s_cur[i] = s_nxt[i];
+    }
     if (++cst == st_begin + nsp) finish();
   };
 
   WOps ring[PD + 1];
 #pragma unroll
   for (int i = 0; i < PD; ++i) load_weights(ring[i]);
-  const int nfull = S / (PD + 1) * (PD + 1);
-  for (int p0 = 0; p0 < nfull; p0 += PD + 1) {
+  load_scales(s_cur);
+  // U stages per iteration: whole turns of the ring and whole scale cycles
+  constexpr int U = (PD + 1) % Q == 0 ? PD + 1 : Q % (PD + 1) == 0 ? Q : (PD + 1) * Q;
+  const int nfull = S / U * U;
+  for (int p0 = 0; p0 < nfull; p0 += U) {
 #pragma unroll
-    for (int u = 0; u <= PD; ++u) stage(ring[u], ring[(u + PD) % (PD + 1)]);
+    for (int u = 0; u < U; ++u) stage(ring[u % (PD + 1)], ring[(u + PD) % (PD + 1)], u % Q);
   }
 #pragma unroll
-  for (int u = 0; u < PD; ++u)
-    if (nfull + u < S) stage(ring[u], ring[(u + PD) % (PD + 1)]);
+  for (int u = 0; u < U - 1; ++u)
+    if (nfull + u < S) stage(ring[u % (PD + 1)], ring[(u + PD) % (PD + 1)], u % Q);
   };
   if (mrows <= 2) run(IntC<8>{});
   else if (mrows <= 4) run(IntC<4>{});
@@ -337,18 +393,28 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
 }
 
 // Workgroups per CU = MIN_WAVES wavefronts per SIMD; KS is the largest of 4, 2, 1
-// that divides the stage count.
-template <bool DUAL, int RB, int MIN_WAVES, int PD, int KS>
-hipError_t launch_ks(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
+// that divides the stage count; Q = 2 when the stages per part are even.
+template <bool DUAL, int RB, int MIN_WAVES, int PD, int KS, int Q>
+hipError_t launch_kq(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                      const uint8_t* wa, const uint8_t* sa, const uint8_t* wb, const uint8_t* sb,
                      int N, int K, void* out, hipStream_t st, const int32_t* gather) {
   constexpr int kWgPerCu = MIN_WAVES * 4 / kMx4Waves;
   static_assert(kWgPerCu >= 1, "resident workgroups");
   const int64_t grid = (int64_t)device_cu_count() * kWgPerCu;
-  hipLaunchKernelGGL((grouped_gemm_mxfp4_decode<DUAL, RB, MIN_WAVES, PD, KS>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((grouped_gemm_mxfp4_decode<DUAL, RB, MIN_WAVES, PD, KS, Q>), dim3((unsigned)grid),
                      dim3(kMx4Waves * kWave), 0, st, act, offsets, expert_groups(s), wa, sa, wb, sb, N,
                      K, out, gather, s.top_k, s.T * s.top_k, s.T);
   return hipGetLastError();
+}
+
+template <bool DUAL, int RB, int MIN_WAVES, int PD, int KS>
+hipError_t launch_ks(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
+                     const uint8_t* wa, const uint8_t* sa, const uint8_t* wb, const uint8_t* sb,
+                     int N, int K, void* out, hipStream_t st, const int32_t* gather) {
+  const int nsp = K / kMx4StageK / KS;
+  if (nsp % 2 == 0)
+    return launch_kq<DUAL, RB, MIN_WAVES, PD, KS, 2>(s, act, offsets, wa, sa, wb, sb, N, K, out, st, gather);
+  return launch_kq<DUAL, RB, MIN_WAVES, PD, KS, 1>(s, act, offsets, wa, sa, wb, sb, N, K, out, st, gather);
 }
 
 template <bool DUAL, int RB, int MIN_WAVES, int PD>
@@ -371,9 +437,10 @@ hipError_t launch_gate_up_mxfp4(const moe_shape_t& s, const uint16_t* x_perm,
                                 const int32_t* offsets, const uint8_t* w1, const uint8_t* w1_scale,
                                 const uint8_t* w3, const uint8_t* w3_scale, uint16_t* h,
                                 hipStream_t st) {
-  // Measured at the Mixtral decode shape (4 rows per expert): 32 channels per
-  // wavefront, K split in four, one stage ahead, three workgroups per CU:
-  // 5.4 TB/s (the one-group-per-workgroup form streamed 4.8).
+  // Measured at the Mixtral decode shape (up to 6 rows per expert): 32 channels
+  // per wavefront, K split in four, one stage ahead, three workgroups per CU
+  // (the one-group-per-workgroup form was 12% slower, 64 channels per
+  // wavefront at two workgroups per CU 14% slower).
   return launch_variant<true, 2, 3, 1>(s, x_perm, offsets, w1, w1_scale, w3, w3_scale, s.d_ff,
                                        s.d_model, h, st);
 }
@@ -389,8 +456,9 @@ hipError_t launch_gate_up_mxfp4_gather(const moe_shape_t& s, const uint16_t* x, 
 hipError_t launch_down_mxfp4(const moe_shape_t& s, const uint16_t* h, const int32_t* offsets,
                              const uint8_t* w2, const uint8_t* w2_scale, float* y_perm,
                              hipStream_t st) {
-  // 64 channels per wavefront, K (14336) split in four, two stages ahead: 4.8 TB/s.
-  return launch_variant<false, 4, 2, 2>(s, h, offsets, w2, w2_scale, nullptr, nullptr, s.d_model,
+  // 64 channels per wavefront, K (14336) split in four, one stage ahead (two
+  // ahead was 5% slower once the scale bytes came two stages per load).
+  return launch_variant<false, 4, 2, 1>(s, h, offsets, w2, w2_scale, nullptr, nullptr, s.d_model,
                                         s.d_ff, y_perm, st);
 }
 
