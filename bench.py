@@ -35,6 +35,33 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s + % roofline (HBM GB/s decode, MFMA TFLOP/s prefill)"
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8_e4m3": 5000.0, "f32": 157.3}   # dense matrix-core peaks
+
+
+def mfma_peak(cfg) -> float:
+    """Dense matrix-core peak (TFLOP/s) of the type the expert GEMMs run in: fp8 e4m3 codes, fp32,
+    or bf16 (bf16 experts, and MXFP4 experts, which are dequantised to bf16 in the kernel)."""
+    if cfg.w_dtype == "fp8_e4m3":
+        return PEAK_TFLOPS["fp8_e4m3"]
+    return PEAK_TFLOPS["f32"] if cfg.act_dtype == "f32" else PEAK_TFLOPS["bf16"]
+
+
+def roofline_of(cfg, nbytes: float, flops: float, kernel_ms: float) -> dict:
+    """Roofline of one launch: the bound is the one whose minimum time is the longer, algorithmic
+    bytes at the HBM peak or algorithmic flops at the matrix-core peak (decode batches are HBM-bound,
+    large Mixtral batches MFMA-bound; many small experts with a narrow FFN can be HBM-bound at
+    prefill because every expert's weights are read once for few rows).  The other bound's figure
+    is kept beside it."""
+    sec = kernel_ms * 1e-3
+    hbm = {"bound": "hbm", "achieved": round(nbytes / sec / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    peak = mfma_peak(cfg)
+    mfma = {"bound": "mfma", "achieved": round(flops / sec / 1e12, 1), "peak": peak, "unit": "TFLOP/s"}
+    for r in (hbm, mfma):
+        r["frac"] = round(r["achieved"] / r["peak"], 4)
+    hbm_first = nbytes / (PEAK_HBM_GBS * 1e9) >= flops / (peak * 1e12)
+    main, other = (hbm, mfma) if hbm_first else (mfma, hbm)
+    return {**main, "other_bound": other}
+
+
 DEFAULTS = {"decode_bf16": (200, 20), "prefill_bf16": (20, 3), "skewed_capacity_bf16": (20, 3),
             "longctx_fp8": (10, 3), "tiny_fp32": (200, 20), "finegrained_decode_bf16": (100, 10),
             "finegrained_prefill_bf16": (10, 3)}
@@ -43,10 +70,11 @@ DEFAULTS = {"decode_bf16": (200, 20), "prefill_bf16": (20, 3), "skewed_capacity_
 _CSRC = "sparse_mixture_experts_topk_amd/csrc/"
 KERNEL_SOURCES = {
     "bf16": (_CSRC + "gemm_bf16.hip", _CSRC + "gemm_bf16_decode.hip", _CSRC + "lds_stream.hpp",
-             _CSRC + "persistent_tiles.hpp", _CSRC + "device_common.hpp"),
+             _CSRC + "persistent_tiles.hpp", _CSRC + "device_common.hpp", _CSRC + "lane_ops.hpp"),
     "fp8_e4m3": (_CSRC + "gemm_fp8.hip", _CSRC + "lds_stream.hpp", _CSRC + "persistent_tiles.hpp",
                  _CSRC + "device_common.hpp"),
-    "mxfp4": (_CSRC + "gemm_mxfp4_decode.hip", _CSRC + "lds_stream.hpp", _CSRC + "device_common.hpp"),
+    "mxfp4": (_CSRC + "gemm_mxfp4_decode.hip", _CSRC + "lds_stream.hpp", _CSRC + "device_common.hpp",
+              _CSRC + "lane_ops.hpp"),
     "f32": (_CSRC + "gemm_f32.hip", _CSRC + "device_common.hpp"),
 }
 
@@ -315,18 +343,10 @@ def main():
 
     counts = st["expert_counts"].cpu().tolist()
     nbytes, flops, touched, n_kept = gate_up_work(cfg, counts)
-    decode = is_decode(cfg)
     sha = kernel_source_sha(cfg)
     traffic = read_traffic(cfg.name, sha)
-    if decode:
-        achieved = nbytes / (kernel_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
-    else:
-        peak = PEAK_TFLOPS[cfg.w_dtype if cfg.w_dtype != "f32" else "f32"]
-        achieved = flops / (kernel_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic}
+    roof = roofline_of(cfg, nbytes, flops, kernel_ms)
+    roof["traffic"] = traffic
     roof.update({"kernel": "moe_expert_gemm_gate_up", "kernel_avg_ms": round(kernel_ms, 4),
                  "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
                  "experts_touched": touched, "rows": n_kept, "kernel_source_sha": sha})

@@ -29,6 +29,7 @@
 // (one expert per XCD) was slower (150 us).
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "lane_ops.hpp"
 #include "lds_stream.hpp"
 
 namespace moe {
@@ -51,13 +52,21 @@ struct StreamGeom {
 };
 
 // One row group streamed over all of K into acc: the 16 weight rows at pw[m]
-// (dual: w1 and w3) against the token operand px (lane (r, g): row r, K
-// elements 8 g .. 8 g + 7 of each 32; rows r >= rows read as zero), through
-// the wavefront's private LDS tile `lds`.
-template <bool DUAL, int ROWS>
+// (dual: w1 and w3) against the token operand, through the wavefront's private
+// LDS tile `lds`.  Matrix instruction j of a stage takes, in lane (t, g), K
+// elements 32 j + 8 g .. + 7 of token t.  One token load carries P of them:
+// lane (t, g) with t = s (16 / P) + u reads token u at px (its row, plus
+// 8 g + 32 s; lanes with u past the tile's rows have tok_ok false and read
+// zeros), operands s, P + s, ...; a row rotation brings operand j to lanes
+// (u, g).  The other lanes then hold other operands: columns u >= 16 / P,
+// past the tile's rows, which are never stored (a column depends only on its
+// own token), so the stored result does not depend on P.
+template <bool DUAL, int ROWS, int P>
 __device__ __forceinline__ void stream_row_group(const uint16_t* const* pw, const uint16_t* px, bool tok_ok,
                                                  int K, uint8_t* lds, f32x4_t* acc) {
   using S = StreamGeom<DUAL, ROWS>;
+  constexpr int NOP = S::KB / 32;              // token operands per stage
+  static_assert(NOP % P == 0, "whole token loads per stage");
   const int lane = threadIdx.x & 63;
   const int lrow = lane / S::LPR, lch = lane % S::LPR;
   const int r = lane & 15, g = lane >> 4;
@@ -72,10 +81,10 @@ __device__ __forceinline__ void stream_row_group(const uint16_t* const* pw, cons
 #pragma unroll
       for (int i = 0; i < S::NL; ++i)
         v[m][i] = load_stream16(pw[m] + (int64_t)(i * ROWS + lrow) * K + k0 + lch * 8);
-    uint4 xv[S::KB / 32];
+    uint4 xv[NOP / P];
 #pragma unroll
-    for (int j = 0; j < S::KB / 32; ++j)
-      xv[j] = tok_ok ? *reinterpret_cast<const uint4*>(px + k0 + j * 32) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < NOP / P; ++i)
+      xv[i] = tok_ok ? *reinterpret_cast<const uint4*>(px + k0 + i * P * 32) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int m = 0; m < S::NM; ++m)
 #pragma unroll
@@ -85,15 +94,29 @@ __device__ __forceinline__ void stream_row_group(const uint16_t* const* pw, cons
         *reinterpret_cast<uint4*>(&lds[(m * 16 + row) * S::ROW_BYTES + pc * 16]) = v[m][i];
       }
 #pragma unroll
-    for (int j = 0; j < S::KB / 32; ++j) {
+    for (int j = 0; j < NOP; ++j) {
       const int pc = (4 * j + g) ^ (r & S::KEY_MASK);
+      const uint4 xj = from_lane_above_even(xv[j / P], j % P * (16 / P));
 #pragma unroll
       for (int m = 0; m < S::NM; ++m) {
         const uint4 a = *reinterpret_cast<const uint4*>(&lds[(m * 16 + r) * S::ROW_BYTES + pc * 16]);
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(xv[j]), acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(xj), acc[m], 0, 0, 0);
       }
     }
   }
+}
+
+// Calls run(IntC<P>) with the most token operands per load (4, 2 or 1) that a
+// tile of `rows` rows allows at this stage width.
+template <int NOP, class F>
+__device__ __forceinline__ void with_token_packing(int rows, F&& run) {
+  if constexpr (NOP % 4 == 0) {
+    if (rows <= 4) return run(IntC<4>{});
+  }
+  if constexpr (NOP % 2 == 0) {
+    if (rows <= 8) return run(IntC<2>{});
+  }
+  run(IntC<1>{});
 }
 
 template <bool DUAL, int ROWS, int MIN_WAVES>
@@ -133,18 +156,21 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gem
   if constexpr (DUAL) pw[1] = wb + ((int64_t)e * N + cg * 16) * K;
   // matrix-core operand: lane (r, g) feeds row r, chunk 4 j + g of MFMA j
   const int r = lane & 15, g = lane >> 4;
-  const bool tok_ok = r < rows;
-  // token operand row: a permuted row, or (gather) the token row of x that
-  // permuted row copies (slot t*k + s -> token t; the shared expert's T*k + t -> t)
-  int arow = row0 + (tok_ok ? r : 0);
-  if (gather != nullptr) {
-    const int src = gather[arow];
-    arow = src < Tk ? src / k : src - Tk;
-  }
-  const uint16_t* px = act + (int64_t)arow * K + g * 8;
-
   f32x4_t acc[S::NM];
-  stream_row_group<DUAL, ROWS>(pw, px, tok_ok, K, lds[w], acc);
+  with_token_packing<S::KB / 32>(rows, [&](auto pc) __attribute__((always_inline)) {
+    constexpr int TPL = 16 / decltype(pc)::value;     // token lanes per row of 16 lanes
+    const int u = r % TPL;
+    const bool tok_ok = u < rows;
+    // token operand row: a permuted row, or (gather) the token row of x that
+    // permuted row copies (slot t*k + s -> token t; the shared expert's T*k + t -> t)
+    int arow = row0 + (tok_ok ? u : 0);
+    if (gather != nullptr) {
+      const int src = gather[arow];
+      arow = src < Tk ? src / k : src - Tk;
+    }
+    const uint16_t* px = act + (int64_t)arow * K + g * 8 + r / TPL * 32;
+    stream_row_group<DUAL, ROWS, decltype(pc)::value>(pw, px, tok_ok, K, lds[w], acc);
+  });
 
   // 16x16 accumulator: lane holds token column (lane & 15), channels 4 * (lane >> 4) + 0..3.
   const int tcol = lane & 15;
@@ -191,10 +217,14 @@ __global__ __launch_bounds__(kFusedMaxExperts * kWave) void down_combine_bf16_de
   if (rows > 0) {
     const uint16_t* pw[1] = {w2 + ((int64_t)e * N + cg * 16) * K};
     const int r = lane & 15, g = lane >> 4;
-    const bool tok_ok = r < rows;
-    const uint16_t* px = h + (int64_t)(row0 + (tok_ok ? r : 0)) * K + g * 8;
     f32x4_t acc[1];
-    stream_row_group<false, ROWS>(pw, px, tok_ok, K, lds[e], acc);
+    with_token_packing<S::KB / 32>(rows, [&](auto pc) __attribute__((always_inline)) {
+      constexpr int TPL = 16 / decltype(pc)::value;
+      const int u = r % TPL;
+      const bool tok_ok = u < rows;
+      const uint16_t* px = h + (int64_t)(row0 + (tok_ok ? u : 0)) * K + g * 8 + r / TPL * 32;
+      stream_row_group<false, ROWS, decltype(pc)::value>(pw, px, tok_ok, K, lds[e], acc);
+    });
     if (r < rows) yrow[row0 + r][g] = make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
   }
   __syncthreads();

@@ -32,6 +32,7 @@
 // t, so a lane's chunk covers four instructions and one scale.
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "lane_ops.hpp"
 #include "lds_stream.hpp"
 
 namespace moe {
@@ -63,19 +64,6 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t codes, float scale) {
 // Element offset, inside a 256-element stage, of matrix-instruction operand
 // c = 4 j + q of lane group g = 0 (j = c / 4 selects the 128-element half).
 __device__ __forceinline__ constexpr int operand_elem(int c) { return (c >> 2) * 128 + (c & 3) * 8; }
-
-// Each lane's value from the lane d places higher in its row of 16 lanes
-// (DPP row rotation; a rotation right by n moves lane i's value to lane i + n).
-template <int D>
-__device__ __forceinline__ uint4 from_lane_above(uint4 v) {
-  constexpr int ctrl = 0x120 + ((16 - D) & 15);   // row_ror:(16 - D)
-  return make_uint4((uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, ctrl, 0xF, 0xF, false),
-                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, ctrl, 0xF, 0xF, false),
-                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.z, ctrl, 0xF, 0xF, false),
-                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, ctrl, 0xF, 0xF, false));
-}
-
-template <int V> struct IntC { static constexpr int value = V; };
 
 // Persistent form.  The grid is the resident capacity; workgroup b takes
 // rounds r = 0, 1, ... of GPW output groups (the KS wavefronts of a group
@@ -334,17 +322,7 @@ __global__ __launch_bounds__(kMx4Waves * kWave, MIN_WAVES) void grouped_gemm_mxf
     uint4 x[2][4];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const uint4 v = xv[c / P];
-      switch (c % P * TPL) {                        // operand c sits TPL (c % P) lanes above
-        case 0: x[c >> 2][c & 3] = v; break;
-        case 2: x[c >> 2][c & 3] = from_lane_above<2>(v); break;
-        case 4: x[c >> 2][c & 3] = from_lane_above<4>(v); break;
-        case 6: x[c >> 2][c & 3] = from_lane_above<6>(v); break;
-        case 8: x[c >> 2][c & 3] = from_lane_above<8>(v); break;
-        case 10: x[c >> 2][c & 3] = from_lane_above<10>(v); break;
-        case 12: x[c >> 2][c & 3] = from_lane_above<12>(v); break;
-        default: x[c >> 2][c & 3] = from_lane_above<14>(v); break;
-      }
+      x[c >> 2][c & 3] = from_lane_above_even(xv[c / P], c % P * TPL);   // operand c: TPL (c % P) lanes above
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {

@@ -37,6 +37,31 @@ def test_gate_up_work_counts_touched_experts_and_rows():
     assert nb4 == int(8 * 2 * 14336 * 4096 * (0.5 + 1 / 32)) + 32 * 4096 * 2 + 32 * 14336 * 2
 
 
+def test_roofline_names_the_binding_bound():
+    # decode: bytes bind
+    cfg = synthetic.CONFIGS["decode_bf16"]
+    nb, fl, _, _ = bench.gate_up_work(cfg, [4] * 8)
+    r = bench.roofline_of(cfg, nb, fl, 0.25)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["other_bound"]["bound"] == "mfma"
+    assert r["frac"] == round(nb / 0.25e-3 / 1e9 / 8000.0, 4)
+    # Mixtral prefill: 2048 rows per expert, flops bind
+    cfg = synthetic.CONFIGS["prefill_bf16"]
+    nb, fl, _, _ = bench.gate_up_work(cfg, [2048] * 8)
+    r = bench.roofline_of(cfg, nb, fl, 3.0)
+    assert r["bound"] == "mfma" and r["peak"] == 2500.0
+    assert r["achieved"] == round(fl / 3e-3 / 1e12, 1)
+    # 256 experts with d_ff 2048 at 256 rows each (+ a shared expert): every expert's weights
+    # are read once for few rows, so bytes bind at prefill too
+    cfg = synthetic.CONFIGS["finegrained_prefill_bf16"]
+    nb, fl, _, _ = bench.gate_up_work(cfg, [256] * 256)
+    assert nb / 8e12 > fl / 2.5e15
+    assert bench.roofline_of(cfg, nb, fl, 2.7)["bound"] == "hbm"
+    # fp8 experts are priced at the fp8 peak, MXFP4 experts at bf16 (dequantised in the kernel)
+    assert bench.mfma_peak(synthetic.CONFIGS["longctx_fp8"]) == 5000.0
+    assert bench.mfma_peak(synthetic.CONFIGS["decode_mxfp4"]) == 2500.0
+    assert bench.mfma_peak(synthetic.CONFIGS["tiny_fp32"]) == 157.3
+
+
 def test_decode_detection_follows_the_rows_per_expert_bound():
     assert bench.is_decode(synthetic.CONFIGS["decode_bf16"])
     assert not bench.is_decode(synthetic.CONFIGS["prefill_bf16"])

@@ -188,6 +188,21 @@ def test_mid_bf16_decode_path():
     run_staged_and_check(mid_cfg("mid_decode", T=40, n_experts=8, seed=3))
 
 
+@pytest.mark.parametrize("T,seed,most_rows", [(2, 41, 1), (8, 40, 4), (10, 40, 5), (14, 54, 8),
+                                              (16, 42, 9)])
+def test_bf16_decode_token_tile_heights(T, seed, most_rows):
+    """The bf16 weight-streaming kernels pack 4, 2 or 1 token operands per load instruction for a
+    token tile of at most 4, 8 or 16 rows (gate/up at d = 512: 128-element stages, up to 4; down
+    and the fused down + combine at F = 448: 64-element stages, up to 2); each band and its edges
+    against the oracle (staged calls) and the fused call bitwise against the staged one."""
+    cfg = mid_cfg(f"bf16_rows{most_rows}", T=T, n_experts=8, seed=seed)
+    st, res, inputs = run_staged_and_check(cfg)
+    assert int(res.perm.counts.max()) == most_rows
+    b = runner.forward(runner.DeviceInputs.from_host(inputs))
+    torch.cuda.synchronize()
+    assert torch.equal(st["y"], b.y)
+
+
 def test_mid_bf16_single_token():
     run_staged_and_check(mid_cfg("mid_t1", T=1, n_experts=8, seed=6))
 
