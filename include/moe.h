@@ -22,8 +22,11 @@
  * Conventions shared by every call
  * --------------------------------
  * - All tensor arguments are DEVICE pointers to row-major arrays owned by
- *   the caller.  The library allocates no memory, keeps no mutable global
- *   state and is re-entrant; calls on different streams may overlap.  The one
+ *   the caller, each 16-byte aligned (as allocator-returned memory is; a
+ *   misaligned one returns MOE_ERR_INVALID_ARG): the kernels' vector loads
+ *   and stores stay aligned from there under the shape limits below.  The
+ *   library allocates no memory, keeps no mutable global state and is
+ *   re-entrant; calls on different streams may overlap.  The one
  *   exception is moe_forward_noalloc (below), which uses a device array of the
  *   library's own and remembers its address per device.
  * - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
@@ -90,8 +93,8 @@ extern "C" {
 
 typedef enum {
   MOE_OK = 0,
-  MOE_ERR_INVALID_ARG = 1,   /* NULL required pointer, bad shape value */
-  MOE_ERR_UNSUPPORTED = 2,   /* legal but not implemented: shape limit, dtype combo, alignment */
+  MOE_ERR_INVALID_ARG = 1,   /* NULL required pointer, pointer not 16-byte aligned, bad shape value */
+  MOE_ERR_UNSUPPORTED = 2,   /* legal but not implemented: shape limit, dtype combo */
   MOE_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than moe_workspace_bytes() */
   MOE_ERR_HIP = 4            /* a kernel launch failed */
 } moe_status_t;
