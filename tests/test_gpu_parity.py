@@ -505,6 +505,20 @@ def test_mxfp4_token_tile_heights(T, seed, most_rows):
     assert torch.equal(st["y"], b.y)
 
 
+def test_mxfp4_two_stage_scale_loads_mid():
+    """d = F = 2048: both GEMMs split K in four with two 256-element stages per part, so scale bytes
+    come two stages per load (the form the Mixtral shapes use), here with a Zipf-skewed router
+    (one expert of 50 rows: 4 token tiles, the last ragged; others of 4 to 24 rows) and several
+    output groups per workgroup; the fused call bitwise against the staged calls."""
+    cfg = mx4_mid_cfg("mx4_q2", T=60, d_model=2048, d_ff=2048, wg_std=2048 ** -0.5,
+                      router_bias="zipf1.2", seed=38)
+    st, res, inputs = run_staged_and_check(cfg)
+    assert int(res.perm.counts.max()) > 48
+    b = runner.forward(runner.DeviceInputs.from_host(inputs))
+    torch.cuda.synchronize()
+    assert torch.equal(st["y"], b.y)
+
+
 def test_mxfp4_forward_matches_staged():
     cfg = mx4_mid_cfg("mx4_fwd", T=48, seed=35)
     inp = synthetic.make_inputs(cfg)
