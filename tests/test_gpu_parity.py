@@ -505,12 +505,14 @@ def test_mxfp4_token_tile_heights(T, seed, most_rows):
     assert torch.equal(st["y"], b.y)
 
 
-def test_mxfp4_two_stage_scale_loads_mid():
-    """d = F = 2048: both GEMMs split K in four with two 256-element stages per part, so scale bytes
-    come two stages per load (the form the Mixtral shapes use), here with a Zipf-skewed router
-    (one expert of 50 rows: 4 token tiles, the last ragged; others of 4 to 24 rows) and several
-    output groups per workgroup; the fused call bitwise against the staged calls."""
-    cfg = mx4_mid_cfg("mx4_q2", T=60, d_model=2048, d_ff=2048, wg_std=2048 ** -0.5,
+@pytest.mark.parametrize("d,F", [(2048, 2048), (4096, 2048)])
+def test_mxfp4_two_stage_scale_loads_mid(d, F):
+    """K a multiple of 2048: the GEMMs split K in four with an even number of 256-element stages
+    per part, so scale bytes come two stages per load (the form the Mixtral shapes use): one
+    two-stage cycle per output group at K = 2048, two at K = 4096 (gate/up of the second case).
+    A Zipf-skewed router gives one expert 4 token tiles (the last ragged) and the others 1 or 2,
+    with several output groups per workgroup; the fused call bitwise against the staged calls."""
+    cfg = mx4_mid_cfg(f"mx4_q2_{d}_{F}", T=60, d_model=d, d_ff=F, wg_std=d ** -0.5,
                       router_bias="zipf1.2", seed=38)
     st, res, inputs = run_staged_and_check(cfg)
     assert int(res.perm.counts.max()) > 48
