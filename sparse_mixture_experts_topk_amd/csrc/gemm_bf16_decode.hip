@@ -26,7 +26,8 @@
 // was 276-287 us on all four.  For down (one matrix) an eighth of every
 // expert's channel groups per XCD measured the same as round-robin on boxes
 // where neither was slow (138-140 us), and a contiguous eighth of all of w2
-// (one expert per XCD) was slower (150 us).
+// (one expert per XCD) was slower (150 us); with many experts, several whole
+// experts per XCD, the contiguous eighth is the faster one (launch_mapped).
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "lane_ops.hpp"
@@ -119,7 +120,7 @@ __device__ __forceinline__ void with_token_packing(int rows, F&& run) {
   run(IntC<1>{});
 }
 
-template <bool DUAL, int ROWS, int MIN_WAVES>
+template <bool DUAL, int ROWS, int MIN_WAVES, bool CONTIG>
 __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gemm_bf16_decode(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
     const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, int N, int K,
@@ -130,10 +131,11 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gem
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int groups = N / 16;
   // Each XCD streams its own part of the weights (the grid is whole rounds of
-  // the 8 XCDs): gate/up one contiguous eighth of all row groups, down the
-  // same eighth of every expert's channel groups.
+  // the 8 XCDs): CONTIG (gate/up; down with many experts) one contiguous
+  // eighth of all row groups, otherwise the same eighth of every expert's
+  // channel groups.
   int cg, rest;
-  if constexpr (DUAL) {
+  if constexpr (CONTIG) {
     const int gid = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + w;
     cg = gid % groups;
     rest = gid / groups;
@@ -246,22 +248,37 @@ __global__ __launch_bounds__(kFusedMaxExperts * kWave) void down_combine_bf16_de
   }
 }
 
-template <bool DUAL, int ROWS, int MIN_WAVES>
-hipError_t launch_variant(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
-                          const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
-                          hipStream_t st, const int32_t* gather = nullptr) {
+// Down with few experts: an eighth of every expert's channel groups per XCD
+// (Mixtral decode batch: 138-140 us against 150 us with one expert per XCD);
+// with 32 or more expert groups a contiguous eighth, i.e. several whole
+// experts per XCD (256 experts top-8 + shared, 16 tokens: 0.287 -> 0.264 ms).
+constexpr int kDownContigMinGroups = 32;
+
+template <bool DUAL, int ROWS, int MIN_WAVES, bool CONTIG>
+hipError_t launch_mapped(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
+                         const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
+                         hipStream_t st, const int32_t* gather) {
   const int tok_tiles = (int)((max_rows_per_expert(s) + 15) / 16);
   const int64_t groups = (int64_t)expert_groups(s) * tok_tiles * (N / 16);
   if (groups <= 0) return hipSuccess;   // no expert can hold a row (capacity 0)
   // whole rounds of the 8 XCDs (waves past the work exit)
-  const int64_t per_xcd = DUAL ? (groups + 8 * kWavesPerBlock - 1) / (8 * kWavesPerBlock)
-                               : ((int64_t)(N / 16 + 7) / 8 * expert_groups(s) * tok_tiles + kWavesPerBlock - 1) /
-                                     kWavesPerBlock;
+  const int64_t per_xcd = CONTIG ? (groups + 8 * kWavesPerBlock - 1) / (8 * kWavesPerBlock)
+                                 : ((int64_t)(N / 16 + 7) / 8 * expert_groups(s) * tok_tiles + kWavesPerBlock - 1) /
+                                       kWavesPerBlock;
   const int64_t blocks = 8 * per_xcd;
-  hipLaunchKernelGGL((grouped_gemm_bf16_decode<DUAL, ROWS, MIN_WAVES>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((grouped_gemm_bf16_decode<DUAL, ROWS, MIN_WAVES, CONTIG>), dim3((unsigned)blocks),
                      dim3(kWavesPerBlock * kWave), 0, st, act, offsets, expert_groups(s), wa, wb, N, K,
                      out, tok_tiles, gather, s.top_k, s.T * s.top_k);
   return hipGetLastError();
+}
+
+template <bool DUAL, int ROWS, int MIN_WAVES>
+hipError_t launch_variant(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
+                          const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
+                          hipStream_t st, const int32_t* gather = nullptr) {
+  if (DUAL || expert_groups(s) >= kDownContigMinGroups)
+    return launch_mapped<DUAL, ROWS, MIN_WAVES, true>(s, act, offsets, wa, wb, N, K, out, st, gather);
+  return launch_mapped<DUAL, ROWS, MIN_WAVES, false>(s, act, offsets, wa, wb, N, K, out, st, gather);
 }
 
 }  // namespace
