@@ -26,12 +26,14 @@
 // was 276-287 us on all four.  For down (one matrix) an eighth of every
 // expert's channel groups per XCD measured the same as round-robin on boxes
 // where neither was slow (138-140 us), and a contiguous eighth of all of w2
-// (one expert per XCD) was slower (150 us); with many experts, several whole
-// experts per XCD, the contiguous eighth is the faster one (launch_mapped).
+// (one expert per XCD) was slower (150 us).  With many experts, gate/up takes
+// the persistent form (grouped_gemm_bf16_decode_tiles), which spreads the
+// touched experts' groups evenly over the XCDs, and down a contiguous eighth.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "lane_ops.hpp"
 #include "lds_stream.hpp"
+#include "persistent_tiles.hpp"
 
 namespace moe {
 namespace {
@@ -120,39 +122,16 @@ __device__ __forceinline__ void with_token_packing(int rows, F&& run) {
   run(IntC<1>{});
 }
 
-template <bool DUAL, int ROWS, int MIN_WAVES, bool CONTIG>
-__global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gemm_bf16_decode(
-    const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
-    const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, int N, int K,
-    void* __restrict__ out, int tok_tiles, const int32_t* __restrict__ gather, int k, int Tk) {
+// One output group: 16 rows of expert e's weights (dual: w1 and w3, channels
+// cg * 16 ..) against the token tile of `rows` permuted rows from row0; writes
+// h (dual: SwiGLU, bf16) or y_perm (fp32) for the tile's rows.
+template <bool DUAL, int ROWS>
+__device__ __forceinline__ void decode_group(const uint16_t* __restrict__ act, const uint16_t* __restrict__ wa,
+                                             const uint16_t* __restrict__ wb, int N, int K, void* __restrict__ out,
+                                             const int32_t* __restrict__ gather, int k, int Tk, int e, int cg,
+                                             int row0, int rows, uint8_t* lds) {
   using S = StreamGeom<DUAL, ROWS>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWavesPerBlock][S::WAVE_LDS];
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int groups = N / 16;
-  // Each XCD streams its own part of the weights (the grid is whole rounds of
-  // the 8 XCDs): CONTIG (gate/up; down with many experts) one contiguous
-  // eighth of all row groups, otherwise the same eighth of every expert's
-  // channel groups.
-  int cg, rest;
-  if constexpr (CONTIG) {
-    const int gid = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + w;
-    cg = gid % groups;
-    rest = gid / groups;
-  } else {
-    const int gx = (groups + 7) / 8;                           // channel groups per XCD
-    const int lw = (blockIdx.x >> 3) * kWavesPerBlock + w;     // wavefront within its XCD
-    cg = (blockIdx.x & 7) * gx + lw % gx;
-    rest = lw / gx;
-    if (cg >= groups) return;
-  }
-  const int tt = rest % tok_tiles;
-  const int e = rest / tok_tiles;
-  if (e >= E) return;
-  const int row0 = offsets[e] + tt * 16;
-  const int rows = min(16, offsets[e + 1] - row0);
-  if (rows <= 0) return;
-
+  const int lane = threadIdx.x & 63;
   const uint16_t* pw[S::NM];
   pw[0] = wa + ((int64_t)e * N + cg * 16) * K;
   if constexpr (DUAL) pw[1] = wb + ((int64_t)e * N + cg * 16) * K;
@@ -171,7 +150,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gem
       arow = src < Tk ? src / k : src - Tk;
     }
     const uint16_t* px = act + (int64_t)arow * K + g * 8 + r / TPL * 32;
-    stream_row_group<DUAL, ROWS, decltype(pc)::value>(pw, px, tok_ok, K, lds[w], acc);
+    stream_row_group<DUAL, ROWS, decltype(pc)::value>(pw, px, tok_ok, K, lds, acc);
   });
 
   // 16x16 accumulator: lane holds token column (lane & 15), channels 4 * (lane >> 4) + 0..3.
@@ -188,6 +167,79 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gem
   } else {
     *reinterpret_cast<float4*>(static_cast<float*>(out) + orow * N + c) =
         make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+  }
+}
+
+template <bool DUAL, int ROWS, int MIN_WAVES, bool CONTIG>
+__global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gemm_bf16_decode(
+    const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
+    const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, int N, int K,
+    void* __restrict__ out, int tok_tiles, const int32_t* __restrict__ gather, int k, int Tk) {
+  using S = StreamGeom<DUAL, ROWS>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWavesPerBlock][S::WAVE_LDS];
+
+  const int w = threadIdx.x >> 6;
+  const int groups = N / 16;
+  // Each XCD streams its own part of the weights (the grid is whole rounds of
+  // the 8 XCDs): CONTIG (gate/up) one contiguous eighth of all row groups,
+  // otherwise the same eighth of every expert's channel groups.
+  int cg, rest;
+  if constexpr (CONTIG) {
+    const int gid = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + w;
+    cg = gid % groups;
+    rest = gid / groups;
+  } else {
+    const int gx = (groups + 7) / 8;                           // channel groups per XCD
+    const int lw = (blockIdx.x >> 3) * kWavesPerBlock + w;     // wavefront within its XCD
+    cg = (blockIdx.x & 7) * gx + lw % gx;
+    rest = lw / gx;
+    if (cg >= groups) return;
+  }
+  const int tt = rest % tok_tiles;
+  const int e = rest / tok_tiles;
+  if (e >= E) return;
+  const int row0 = offsets[e] + tt * 16;
+  const int rows = min(16, offsets[e + 1] - row0);
+  if (rows <= 0) return;
+  decode_group<DUAL, ROWS>(act, wa, wb, N, K, out, gather, k, Tk, e, cg, row0, rows, lds[w]);
+}
+
+// Many experts (at most a few rows each, most of them untouched; gate/up): a grid of the
+// resident capacity.  Each workgroup builds the token-tile prefix of the expert
+// groups once (from the offsets, in LDS); the output groups are numbered over
+// the token tiles that exist only (expert-major, channel groups fastest), each
+// XCD takes a contiguous eighth of them, and its wavefronts take every
+// (grid / 8 * 4)-th group of that eighth.  With the whole grid laid over all
+// E + S groups instead, each XCD's share of real work was set by how many
+// touched experts fell in its eighth (1.22 x the mean for the busiest XCD at
+// 256 experts top-8 + shared, 16 tokens).
+template <bool DUAL, int ROWS, int MIN_WAVES>
+__global__ __launch_bounds__(kWavesPerBlock * kWave, MIN_WAVES) void grouped_gemm_bf16_decode_tiles(
+    const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets, int E,
+    const uint16_t* __restrict__ wa, const uint16_t* __restrict__ wb, int N, int K,
+    void* __restrict__ out, const int32_t* __restrict__ gather, int k, int Tk) {
+  using S = StreamGeom<DUAL, ROWS>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWavesPerBlock][S::WAVE_LDS];
+  __shared__ int32_t offs[kMaxExpertGroups + 1];
+  __shared__ int32_t pre[kMaxExpertGroups + 1];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i <= E; i += kWavesPerBlock * kWave) offs[i] = offsets[i];
+  __syncthreads();
+  if (w == 0) build_tile_prefix(offs, E, 16, pre, lane);
+  __syncthreads();
+  const int groups = N / 16;
+  const int total = __builtin_amdgcn_readfirstlane(pre[E]) * groups;   // output groups that exist
+  const int per_xcd = (total + 7) / 8;
+  const int x = blockIdx.x & 7;
+  const int nslots = (gridDim.x >> 3) * kWavesPerBlock;
+  for (int li = (blockIdx.x >> 3) * kWavesPerBlock + w; li < per_xcd; li += nslots) {
+    const int t = x * per_xcd + li;
+    if (t >= total) break;
+    int e, r0, r1, m, cg;
+    find_tile(offs, pre, E, groups, t, e, r0, r1, m, cg);
+    const int row0 = r0 + m * 16;
+    decode_group<DUAL, ROWS>(act, wa, wb, N, K, out, gather, k, Tk, e, cg, row0, min(16, r1 - row0),
+                             lds[w]);
   }
 }
 
@@ -248,11 +300,15 @@ __global__ __launch_bounds__(kFusedMaxExperts * kWave) void down_combine_bf16_de
   }
 }
 
-// Down with few experts: an eighth of every expert's channel groups per XCD
-// (Mixtral decode batch: 138-140 us against 150 us with one expert per XCD);
-// with 32 or more expert groups a contiguous eighth, i.e. several whole
-// experts per XCD (256 experts top-8 + shared, 16 tokens: 0.287 -> 0.264 ms).
-constexpr int kDownContigMinGroups = 32;
+// Gate/up with 32 or more expert groups: the persistent form above (256
+// experts top-8 + shared, 16 tokens: 0.528 -> 0.518 ms); otherwise a grid over
+// all groups, a contiguous eighth of the row groups per XCD.  Down: a
+// contiguous eighth with 32 or more expert groups, several whole experts per
+// XCD (0.287 -> 0.264 ms; the persistent form: 0.271 ms); with fewer, an
+// eighth of every expert's channel groups (Mixtral decode batch: 138-140 us
+// against 150 us with one expert per XCD).
+constexpr int kManyExpertGroups = 32;
+constexpr int kWgPerCuTiles = 4;     // resident workgroups per CU of the persistent form
 
 template <bool DUAL, int ROWS, int MIN_WAVES, bool CONTIG>
 hipError_t launch_mapped(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
@@ -276,9 +332,20 @@ template <bool DUAL, int ROWS, int MIN_WAVES>
 hipError_t launch_variant(const moe_shape_t& s, const uint16_t* act, const int32_t* offsets,
                           const uint16_t* wa, const uint16_t* wb, int N, int K, void* out,
                           hipStream_t st, const int32_t* gather = nullptr) {
-  if (DUAL || expert_groups(s) >= kDownContigMinGroups)
+  if (max_rows_per_expert(s) <= 0) return hipSuccess;   // no expert can hold a row (capacity 0)
+  if (DUAL && expert_groups(s) >= kManyExpertGroups) {
+    static_assert(kManyExpertGroups <= kMaxExpertGroups, "offset table in LDS");
+    const int64_t blocks = (int64_t)device_cu_count() * kWgPerCuTiles / 8 * 8;
+    hipLaunchKernelGGL((grouped_gemm_bf16_decode_tiles<DUAL, ROWS, MIN_WAVES>), dim3((unsigned)blocks),
+                       dim3(kWavesPerBlock * kWave), 0, st, act, offsets, expert_groups(s), wa, wb, N, K, out,
+                       gather, s.top_k, s.T * s.top_k);
+    return hipGetLastError();
+  }
+  if (DUAL || expert_groups(s) >= kManyExpertGroups)
     return launch_mapped<DUAL, ROWS, MIN_WAVES, true>(s, act, offsets, wa, wb, N, K, out, st, gather);
-  return launch_mapped<DUAL, ROWS, MIN_WAVES, false>(s, act, offsets, wa, wb, N, K, out, st, gather);
+  if constexpr (!DUAL)
+    return launch_mapped<DUAL, ROWS, MIN_WAVES, false>(s, act, offsets, wa, wb, N, K, out, st, gather);
+  return hipErrorInvalidValue;   // not reached
 }
 
 }  // namespace

@@ -661,6 +661,21 @@ def test_finegrained_decode_path():
     run_staged_and_check(fg_cfg("fg_t1", T=1, n_experts=256, seed=47))
 
 
+@pytest.mark.parametrize("E,shared", [(31, 0), (32, 0), (31, 1)])
+def test_decode_many_experts_threshold(E, shared):
+    """Weight streaming with 32 or more expert groups maps its work differently (gate/up: a
+    persistent grid over the token tiles that exist; down: a contiguous eighth of the groups per
+    XCD): 31 groups take the grid over all groups, 32 or 31 + shared the other forms; top-8
+    of about 32 experts at 64 tokens gives many experts two token tiles.  Staged calls against the
+    oracle, the fused call bitwise against them."""
+    cfg = fg_cfg(f"fg_many_E{E}_S{shared}", T=64, n_experts=E, top_k=8, n_shared=shared, seed=49)
+    st, res, inputs = run_staged_and_check(cfg)
+    assert int(res.perm.counts[:E].max()) > 16
+    b = runner.forward(runner.DeviceInputs.from_host(inputs))
+    torch.cuda.synchronize()
+    assert torch.equal(st["y"], b.y)
+
+
 def test_general_topk_without_shared_and_edge_k():
     run_staged_and_check(fg_cfg("fg_k1", T=200, n_experts=16, top_k=1, n_shared=0, seed=48))
     run_staged_and_check(fg_cfg("fg_kE", T=120, n_experts=8, top_k=8, n_shared=0, seed=49))
