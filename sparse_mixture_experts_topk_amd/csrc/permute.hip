@@ -249,165 +249,254 @@ __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __
 
 constexpr int kIndexThreads = 1024;
 constexpr int kIndexWaves = kIndexThreads / kWave;
+constexpr int kIndexBatch = 4;     // chunks whose assignments are loaded before any is counted
 
+// Grouping for top-2 with up to 64 experts, no shared expert: one workgroup
+// per chunk of 1024 tokens, a token per lane.  Every workgroup counts all
+// assignments (the totals fix the experts' offsets) and, apart, those of the
+// tokens before its chunk (where its rows start inside each expert); then it
+// ranks its own tokens with one ballot per expert and a scan over its 16
+// wavefronts.  Every workgroup derives the same totals from the same data, so
+// the rows do not depend on timing; workgroup 0 writes counts and offsets.
 __global__ __launch_bounds__(kIndexThreads) void permute_index_kernel(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ drop,
     const int32_t* __restrict__ next, int T, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
     int32_t* __restrict__ slot_to_row) {
-  __shared__ int s_count[64];
+  __shared__ int s_total[64];
+  __shared__ int s_before[64];
   __shared__ int s_base[64];
   __shared__ int s_wave[kIndexWaves][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x, n_chunks = gridDim.x;
 
-  if (tid < 64) s_count[tid] = 0;
-  __syncthreads();
-  for (int i = tid; i < 2 * T; i += kIndexThreads) {
-    const int fe = final_expert(ids, drop, next, i);
-    if (fe >= 0) atomicAdd(&s_count[fe], 1);
+  if (tid < 64) {
+    s_total[tid] = 0;
+    s_before[tid] = 0;
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      offsets[e] = run;
-      s_base[e] = run;
-      counts[e] = s_count[e];
-      run += s_count[e];
-    }
-    offsets[E] = run;
-  }
-  __syncthreads();
-
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < T; c0 += kIndexThreads) {
-    const int t = c0 + tid;
-    int e0 = -1, e1 = -1;
-    if (t < T) {
-      e0 = final_expert(ids, drop, next, 2 * t);
-      e1 = final_expert(ids, drop, next, 2 * t + 1);
-    }
-    int rank0 = 0, rank1 = 0;
-    for (int e = 0; e < E; ++e) {
-      const uint64_t b = __ballot(e0 == e || e1 == e);
-      if (lane == 0) s_wave[wave][e] = __popcll(b);
-      const int r = __popcll(b & lt_mask);
-      if (e0 == e) rank0 = r;
-      if (e1 == e) rank1 = r;
-    }
-    __syncthreads();
-    if (tid < E) {
-      int run = s_base[tid];
-      for (int w = 0; w < kIndexWaves; ++w) {
-        const int c = s_wave[w][tid];
-        s_wave[w][tid] = run;
-        run += c;
-      }
-      s_base[tid] = run;
-    }
-    __syncthreads();
-    if (t < T) {
-      int row0 = -1, row1 = -1;
-      if (e0 >= 0) {
-        row0 = s_wave[wave][e0] + rank0;
-        perm_src[row0] = 2 * t;
-      }
-      if (e1 >= 0) {
-        row1 = s_wave[wave][e1] + rank1;
-        perm_src[row1] = 2 * t + 1;
-      }
-      reinterpret_cast<int2*>(slot_to_row)[t] = make_int2(row0, row1);
-    }
-    __syncthreads();
-  }
-}
-
-constexpr int kPlaceThreads = 1024;
-constexpr int kPlaceWaves = kPlaceThreads / kWave;
-
-// Sum over the workgroup of one int per lane (every lane gets the total).
-__device__ __forceinline__ int block_sum(int v, int* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // count: chunks in batches, all of a batch's loads issued before its ballots
+  int m0 = -1, m1 = -1;                       // this lane's token of the own chunk
+  for (int c0 = 0; c0 < n_chunks; c0 += kIndexBatch) {
+    int e0[kIndexBatch], e1[kIndexBatch];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  if (lane == 0) red[wave] = v;
+    for (int q = 0; q < kIndexBatch; ++q) {
+      const int t = (c0 + q) * kIndexThreads + tid;
+      e0[q] = -1;
+      e1[q] = -1;
+      if (c0 + q < n_chunks && t < T) {
+        e0[q] = final_expert(ids, drop, next, 2 * t);
+        e1[q] = final_expert(ids, drop, next, 2 * t + 1);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kIndexBatch; ++q) {
+      if (c0 + q == chunk) {
+        m0 = e0[q];
+        m1 = e1[q];
+      }
+      for (int e = 0; e < E; ++e) {
+        const int n = __popcll(__ballot(e0[q] == e)) + __popcll(__ballot(e1[q] == e));
+        if (lane == 0 && n > 0) {
+          atomicAdd(&s_total[e], n);
+          if (c0 + q < chunk) atomicAdd(&s_before[e], n);
+        }
+      }
+    }
+  }
   __syncthreads();
-  int total = 0;
-  for (int w = 0; w < kPlaceWaves; ++w) total += red[w];
+  if (wave == 0) {
+    // exclusive scan of the totals over the experts, lane e = expert e
+    const int v = lane < E ? s_total[lane] : 0;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
+    }
+    const int excl = incl - v;
+    if (lane < E) {
+      s_base[lane] = excl + s_before[lane];
+      if (chunk == 0) {
+        offsets[lane] = excl;
+        counts[lane] = v;
+      }
+    }
+    if (chunk == 0 && lane == 63) offsets[E] = incl;
+  }
   __syncthreads();
-  return total;
+
+  // rank the own chunk's tokens: a token's two experts are distinct
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int t = chunk * kIndexThreads + tid;
+  int rank0 = 0, rank1 = 0;
+  for (int e = 0; e < E; ++e) {
+    const uint64_t b = __ballot(m0 == e || m1 == e);
+    if (lane == 0) s_wave[wave][e] = __popcll(b);
+    const int r = __popcll(b & lt_mask);
+    if (m0 == e) rank0 = r;
+    if (m1 == e) rank1 = r;
+  }
+  __syncthreads();
+  if (tid < E) {
+    int run = s_base[tid];
+    for (int w = 0; w < kIndexWaves; ++w) {
+      const int c = s_wave[w][tid];
+      s_wave[w][tid] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (t < T) {
+    int row0 = -1, row1 = -1;
+    if (m0 >= 0) {
+      row0 = s_wave[wave][m0] + rank0;
+      perm_src[row0] = 2 * t;
+    }
+    if (m1 >= 0) {
+      row1 = s_wave[wave][m1] + rank1;
+      perm_src[row1] = 2 * t + 1;
+    }
+    reinterpret_cast<int2*>(slot_to_row)[t] = make_int2(row0, row1);
+  }
 }
 
-__global__ __launch_bounds__(kPlaceThreads) void expert_count_kernel(
-    const int32_t* __restrict__ ids, const uint8_t* __restrict__ drop,
-    const int32_t* __restrict__ next, int n_assign, int32_t* __restrict__ counts) {
-  __shared__ int red[kPlaceWaves];
-  const int e = blockIdx.x;
-  int mine = 0;
-  for (int i = threadIdx.x; i < n_assign; i += kPlaceThreads)
-    mine += final_expert(ids, drop, next, i) == e ? 1 : 0;
-  const int total = block_sum(mine, red);
-  if (threadIdx.x == 0) counts[e] = total;
-}
+constexpr int kGroupTokens = 1024;                // tokens per chunk: one per lane
+constexpr int kGroupWords = kGroupTokens / 32;      // mask words per expert
+constexpr int kGroupBatch = 8;                      // assignments loaded before any is counted
 
-// Workgroup e < E: rows of routed expert e; workgroup E: the shared expert.
-__global__ __launch_bounds__(kPlaceThreads) void expert_place_kernel(
+// Grouping for any top-k, many experts and the shared expert: one workgroup
+// per chunk of 1024 tokens.  Every workgroup histograms all assignments with
+// LDS atomics: the totals fix the experts' offsets, the part from tokens
+// before its chunk where its rows start inside each expert.  For its own
+// tokens it sets bit (token - chunk start) of the final expert's 1024-bit mask
+// (a token has at most one assignment per expert), so a row's rank inside
+// the chunk is the number of bits below its own: ascending token order, the
+// same as walking the tokens, without depending on timing.  Dropped
+// assignments get row -1; the shared expert's rows follow the routed ones in
+// token order.  Workgroup 0 writes counts and offsets.
+__global__ __launch_bounds__(kGroupTokens) void group_chunks_kernel(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ drop,
     const int32_t* __restrict__ next, int T, int k, int E, int S, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
     int32_t* __restrict__ slot_to_row) {
-  __shared__ int red[kPlaceWaves];
-  __shared__ int s_wave[kPlaceWaves];
-  const int e = blockIdx.x;
+  __shared__ int s_total[kMaxExpertGroups];
+  __shared__ int s_before[kMaxExpertGroups];
+  __shared__ int s_base[kMaxExpertGroups];
+  __shared__ uint32_t s_mask[kMaxExperts][kGroupWords];
+  __shared__ uint16_t s_pre[kMaxExperts][kGroupWords];   // bits of the expert's earlier words
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int part = 0;
-  for (int j = tid; j < e && j < E; j += kPlaceThreads) part += counts[j];
-  const int base = block_sum(part, red);
-  const int64_t Tk = (int64_t)T * k;
-  if (e == E) {   // shared expert: every token, after the routed rows
-    for (int t = tid; t < T; t += kPlaceThreads) {
-      perm_src[base + t] = (int32_t)(Tk + t);
-      slot_to_row[Tk + t] = base + t;
-    }
-    if (tid == 0) {
-      counts[E] = T;
-      offsets[E] = base;
-      offsets[E + 1] = base + T;
-    }
-    return;
+  const int t0 = blockIdx.x * kGroupTokens;
+  const int G = E + S;
+  const int64_t n_assign = (int64_t)T * k;
+  const int a0 = t0 * k;                              // first assignment of the own chunk
+  const int64_t a1_full = (int64_t)(t0 + kGroupTokens) * k;
+  const int a1 = (int)(a1_full < n_assign ? a1_full : n_assign);
+
+  for (int j = tid; j < kMaxExpertGroups; j += kGroupTokens) {
+    s_total[j] = 0;
+    s_before[j] = 0;
   }
-  if (tid == 0) {
-    offsets[e] = base;
-    if (e == E - 1 && S == 0) offsets[E] = base + counts[e];
-  }
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int chunk_base = base;
-  for (int c0 = 0; c0 < T; c0 += kPlaceThreads) {
-    const int t = c0 + tid;
-    int slot = -1;
-    if (t < T) {
-      for (int s = 0; s < k; ++s) {
-        const int i = t * k + s;
-        const int fe = final_expert(ids, drop, next, i);
-        if (fe == e) slot = s;
-        else if (fe < 0 && ids[i] == e) slot_to_row[i] = -1;   // dropped: its router expert writes it
+  for (int j = tid; j < kMaxExperts * kGroupWords; j += kGroupTokens) (&s_mask[0][0])[j] = 0u;
+  __syncthreads();
+  for (int64_t i0 = tid; i0 < n_assign; i0 += (int64_t)kGroupBatch * kGroupTokens) {
+    int fe[kGroupBatch];
+#pragma unroll
+    for (int q = 0; q < kGroupBatch; ++q) {
+      const int64_t i = i0 + (int64_t)q * kGroupTokens;
+      fe[q] = i < n_assign ? final_expert(ids, drop, next, (int)i) : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kGroupBatch; ++q) {
+      const int i = (int)(i0 + (int64_t)q * kGroupTokens);
+      if (fe[q] < 0) continue;
+      atomicAdd(&s_total[fe[q]], 1);
+      if (i < a0) {
+        atomicAdd(&s_before[fe[q]], 1);
+      } else if (i < a1) {
+        const int lt = i / k - t0;
+        atomicOr(&s_mask[fe[q]][lt >> 5], 1u << (lt & 31));
       }
     }
-    const uint64_t b = __ballot(slot >= 0);
-    if (lane == 0) s_wave[wave] = __popcll(b);
-    __syncthreads();
-    int before = 0, total = 0;
-    for (int w = 0; w < kPlaceWaves; ++w) {
-      before += w < wave ? s_wave[w] : 0;
-      total += s_wave[w];
+  }
+  __syncthreads();
+  if (S > 0 && tid == 0) {
+    s_total[E] = T;
+    s_before[E] = t0;
+  }
+  // per expert, the bits of its earlier mask words: 4 lanes per expert, 8 words each
+  {
+    const int e = tid >> 2, part = tid & 3;
+    int run = 0;
+    uint16_t local[kGroupWords / 4];
+    if (e < E) {
+#pragma unroll
+      for (int w = 0; w < kGroupWords / 4; ++w) {
+        local[w] = (uint16_t)run;
+        run += __popc(s_mask[e][part * (kGroupWords / 4) + w]);
+      }
     }
-    if (slot >= 0) {
-      const int row = chunk_base + before + __popcll(b & lt_mask);
-      perm_src[row] = t * k + slot;
-      slot_to_row[t * k + slot] = row;
+    // exclusive sum of the 4 parts' counts (lanes 4e .. 4e + 3 of one wavefront)
+    const int p1 = __shfl_up(run, 1, 4), p2 = __shfl_up(run, 2, 4), p3 = __shfl_up(run, 3, 4);
+    const int off = (part >= 1 ? p1 : 0) + (part >= 2 ? p2 : 0) + (part >= 3 ? p3 : 0);
+    if (e < E) {
+#pragma unroll
+      for (int w = 0; w < kGroupWords / 4; ++w)
+        s_pre[e][part * (kGroupWords / 4) + w] = (uint16_t)(local[w] + off);
     }
-    chunk_base += total;
-    __syncthreads();
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // exclusive scan of the G totals: lane l sums groups 5 l .. 5 l + 4
+    constexpr int PER = (kMaxExpertGroups + 63) / 64;
+    int v[PER], sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int g = lane * PER + j;
+      v[j] = g < G ? s_total[g] : 0;
+      sum += v[j];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int g = lane * PER + j;
+      if (g < G) {
+        s_base[g] = run + s_before[g];
+        if (blockIdx.x == 0) {
+          offsets[g] = run;
+          counts[g] = v[j];
+        }
+      }
+      run += v[j];
+    }
+    if (blockIdx.x == 0 && lane == 63) offsets[G] = incl;
+  }
+  __syncthreads();
+  const int t = t0 + tid;
+  if (t < T) {
+    const int lt = tid;
+    for (int sl = 0; sl < k; ++sl) {
+      const int i = t * k + sl;
+      const int fe = final_expert(ids, drop, next, i);
+      int row = -1;
+      if (fe >= 0) {
+        const uint32_t below = s_mask[fe][lt >> 5] & ((1u << (lt & 31)) - 1u);
+        row = s_base[fe] + s_pre[fe][lt >> 5] + __popc(below);
+        perm_src[row] = i;
+      }
+      slot_to_row[i] = row;
+    }
+    if (S > 0) {
+      const int row = s_base[E] + lt;                 // routed rows, then the shared rows
+      perm_src[row] = (int32_t)(n_assign + t);
+      slot_to_row[n_assign + t] = row;
+    }
   }
 }
 
@@ -489,17 +578,15 @@ hipError_t launch_permute_index(const moe_shape_t& s, const int32_t* ids, const 
                                 const int32_t* next_ids, int32_t* counts, int32_t* offsets,
                                 int32_t* perm_src, int32_t* slot_to_row, hipStream_t st) {
   if (s.top_k == 2 && s.n_experts <= 64 && s.n_shared == 0) {
-    hipLaunchKernelGGL(permute_index_kernel, dim3(1), dim3(kIndexThreads), 0, st, ids, drop_mask,
+    const int chunks = std::max(1, (s.T + kIndexThreads - 1) / kIndexThreads);
+    hipLaunchKernelGGL(permute_index_kernel, dim3(chunks), dim3(kIndexThreads), 0, st, ids, drop_mask,
                        next_ids, s.T, s.n_experts, counts, offsets, perm_src, slot_to_row);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(expert_count_kernel, dim3(s.n_experts), dim3(kPlaceThreads), 0, st, ids,
-                     drop_mask, next_ids, s.T * s.top_k, counts);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(expert_place_kernel, dim3(expert_groups(s)), dim3(kPlaceThreads), 0, st, ids,
-                     drop_mask, next_ids, s.T, s.top_k, s.n_experts, s.n_shared, counts, offsets,
-                     perm_src, slot_to_row);
+  const int chunks = std::max(1, (s.T + kGroupTokens - 1) / kGroupTokens);
+  hipLaunchKernelGGL(group_chunks_kernel, dim3(chunks), dim3(kGroupTokens), 0, st, ids, drop_mask,
+                     next_ids, s.T, s.top_k, s.n_experts, s.n_shared, counts, offsets, perm_src,
+                     slot_to_row);
   return hipGetLastError();
 }
 

@@ -761,6 +761,27 @@ def test_finegrained_prefill_config_sampled():
     run_staged_and_check(cfg, inputs=inp, tokens=toks, check_h=True, tile_rows=320)
 
 
+@pytest.mark.parametrize("E,k,S,T,cap,overflow", [
+    (8, 2, 0, 2049, 500, "next_best"),   # top-2 grouping: 3 chunks of 1024 tokens, the last holds 1
+    (64, 2, 0, 3071, -1, "drop"),        # top-2, 64 experts, dropless, ragged last chunk
+    (256, 8, 1, 2049, 60, "drop"),       # general grouping: many experts, capacity, shared expert
+    (40, 3, 0, 1025, -1, "drop"),        # general grouping without a shared expert
+])
+def test_grouping_over_token_chunks(E, k, S, T, cap, overflow):
+    """Grouping runs one workgroup per 1024-token chunk; each derives the experts' totals and its
+    own start inside each expert from all assignments.  Counts, offsets, perm_src, slot_to_row and
+    drop marks must equal the oracle's exactly across chunk boundaries and a ragged last chunk
+    ("How Mixtral 8x7B uses mixture of experts", simplified forward pass: tokens batched by expert
+    in a fixed order, results written back per token)."""
+    cfg = synthetic.MoEConfig(name=f"chunks_E{E}_k{k}", T=T, d_model=64, d_ff=64, n_experts=E,
+                              top_k=k, n_shared=S, capacity=cap, overflow=overflow,
+                              act_dtype="bf16", w_dtype="bf16", x_std=1.0, wg_std=64 ** -0.5,
+                              w13_std=0.05, w2_std=0.05, seed=3000 + E + k)
+    st, res, _ = run_staged_and_check(cfg)
+    if cap >= 0:
+        assert (~res.keep).sum() > 0, "the capacity case must drop assignments"
+
+
 def sweep_cfg(seed):
     """A seeded random shape of the whole layer: expert count, top-k, shared expert, batch (the
     weight-streaming and the tiled paths), widths, capacity and overflow, and weight dtype, drawn
