@@ -25,21 +25,23 @@
 //   marks 1 into 2, so "dropped in the first round" (mark != 0) reads the
 //   same in every workgroup while others write.
 // permute_index (top-2, up to 64 experts, no shared expert): one workgroup
-//   of 1024 lanes.  Pass 1 counts kept assignments per expert with LDS
-//   atomics (order-free).  Pass 2 walks the tokens in chunks of 1024; per
-//   expert a wavefront ballot + popcount gives each assignment its rank among
-//   earlier tokens of the chunk, and a scan over the 16 wavefronts places the
-//   chunk after the previous ones, so rows inside an expert follow ascending
-//   token order (stable, deterministic).
-// expert_count + expert_place (any top-k, up to 256 experts, shared expert;
-//   the many-expert form of the DeepSeek-V3 remark on the "Mixtral 8x7B"
-//   interview page): one workgroup per expert.  The first kernel counts the
-//   expert's kept assignments; the second sums the counts of the experts
-//   before it (its offset) and walks the tokens in chunks of 1024, a token
-//   per lane, placing the token's assignment to this expert with a ballot
-//   rank plus a scan over the 16 wavefronts -- ascending token order again.
-//   The shared expert's workgroup writes its T rows (slot T*k + t) after
-//   the routed ones.
+//   of 1024 lanes per chunk of 1024 tokens.  Each counts every kept
+//   assignment per expert (wavefront ballots, the four chunks of a batch
+//   loaded before any is counted) and, apart, those of the tokens before its
+//   chunk; a scan over the experts gives the offsets and the chunk's start
+//   inside each expert.  Per expert a ballot + popcount ranks a token among
+//   the earlier tokens of its wavefront, and a scan over the 16 wavefronts
+//   places the wavefronts, so rows inside an expert follow ascending token
+//   order (stable; every workgroup derives the same totals, so deterministic).
+// group_chunks (any top-k, up to 256 experts, shared expert; the many-expert
+//   form of the DeepSeek-V3 remark on the "Mixtral 8x7B" interview page): one
+//   workgroup per chunk of 1024 tokens.  Each histograms every assignment
+//   with LDS atomics (totals, and the part before its chunk) and sets bit
+//   (token - chunk start) in a 1024-bit mask of the final expert for each of
+//   its own tokens' assignments; prefix popcounts of the mask words give a
+//   token its rank among the chunk's earlier tokens of that expert --
+//   ascending token order again.  The shared expert's T rows (slot T*k + t)
+//   follow the routed ones.
 // permute_scatter: one wavefront per permuted row copies x[token] in 16-byte
 //   vectors; for fp8 experts each lane quantises 32-element blocks to e4m3
 //   with a power-of-two (E8M0) block scale.
