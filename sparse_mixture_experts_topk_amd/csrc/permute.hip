@@ -26,7 +26,7 @@
 //   same in every workgroup while others write.
 // permute_index (top-2, up to 64 experts, no shared expert): one workgroup
 //   of 1024 lanes per chunk of 1024 tokens.  Each counts every kept
-//   assignment per expert (wavefront ballots, the four chunks of a batch
+//   assignment per expert (wavefront ballots, the eight chunks of a batch
 //   loaded before any is counted) and, apart, those of the tokens before its
 //   chunk; a scan over the experts gives the offsets and the chunk's start
 //   inside each expert.  Per expert a ballot + popcount ranks a token among
@@ -80,6 +80,58 @@ __device__ __forceinline__ int final_expert(const int32_t* ids, const uint8_t* d
   if (drop == nullptr) return ids[i];
   const uint8_t m = drop[i];
   return m == 0 ? ids[i] : m == 2 ? fallback_expert(drop, next, i) : -1;
+}
+
+// Final experts of top-2 token t from values already loaded: its two ids,
+// its two drop marks (byte s = slot s; 0 when nothing is dropped) and its two
+// fallback ids -- the same rule as final_expert and fallback_expert.
+__device__ __forceinline__ int2 final_pair(int2 id, uint32_t marks, int2 nx) {
+  const uint32_t m0 = marks & 255u, m1 = (marks >> 8) & 255u;
+  const int e0 = m0 == 0 ? id.x : m0 == 2 ? nx.x : -1;
+  const int e1 = m1 == 0 ? id.y : m1 == 2 ? (m0 != 0 ? nx.y : nx.x) : -1;
+  return make_int2(e0, e1);
+}
+
+// Loads of token t (< T) for final_pair: every load unconditional, so a
+// batch of them is in flight together.
+__device__ __forceinline__ int2 load_final_pair(const int32_t* ids, const uint8_t* drop,
+                                                const int32_t* next, int t) {
+  const int2 id = reinterpret_cast<const int2*>(ids)[t];
+  uint32_t marks = 0;
+  int2 nx = make_int2(-1, -1);
+  if (drop != nullptr) {
+    marks = reinterpret_cast<const uint16_t*>(drop)[t];
+    if (next != nullptr) nx = reinterpret_cast<const int2*>(next)[t];
+  }
+  return final_pair(id, marks, nx);
+}
+
+// Final experts of N assignments i[0..N) with every load issued before any
+// is used (the fallback exists for top-2 only: next != nullptr implies k == 2).
+template <int N>
+__device__ __forceinline__ void load_final_experts(const int32_t* ids, const uint8_t* drop,
+                                                   const int32_t* next, const int* i, int* fe) {
+  uint32_t m[N], m0[N];
+  int2 nx[N];
+#pragma unroll
+  for (int q = 0; q < N; ++q) fe[q] = ids[i[q]];
+  if (drop != nullptr) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) m[q] = drop[i[q]];
+    if (next != nullptr) {
+#pragma unroll
+      for (int q = 0; q < N; ++q) {
+        m0[q] = drop[i[q] & ~1];
+        nx[q] = reinterpret_cast<const int2*>(next)[i[q] >> 1];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      int fb = -1;
+      if (next != nullptr) fb = ((i[q] & 1) && m0[q] != 0) ? nx[q].y : nx[q].x;
+      fe[q] = m[q] == 0 ? fe[q] : m[q] == 2 ? fb : -1;
+    }
+  }
 }
 
 // FALLBACK = false: the capacity round over the top-k assignments (marks 0/1).
@@ -251,7 +303,7 @@ __global__ __launch_bounds__(1024) void capacity_select_kernel(const int32_t* __
 
 constexpr int kIndexThreads = 1024;
 constexpr int kIndexWaves = kIndexThreads / kWave;
-constexpr int kIndexBatch = 4;     // chunks whose assignments are loaded before any is counted
+constexpr int kIndexBatch = 8;     // chunks whose assignments are loaded before any is counted
 
 // Grouping for top-2 with up to 64 experts, no shared expert: one workgroup
 // per chunk of 1024 tokens, a token per lane.  Every workgroup counts all
@@ -280,16 +332,15 @@ __global__ __launch_bounds__(kIndexThreads) void permute_index_kernel(
   // count: chunks in batches, all of a batch's loads issued before its ballots
   int m0 = -1, m1 = -1;                       // this lane's token of the own chunk
   for (int c0 = 0; c0 < n_chunks; c0 += kIndexBatch) {
+    // loads from clamped (valid) tokens, then a select: no load waits for another
     int e0[kIndexBatch], e1[kIndexBatch];
 #pragma unroll
     for (int q = 0; q < kIndexBatch; ++q) {
       const int t = (c0 + q) * kIndexThreads + tid;
-      e0[q] = -1;
-      e1[q] = -1;
-      if (c0 + q < n_chunks && t < T) {
-        e0[q] = final_expert(ids, drop, next, 2 * t);
-        e1[q] = final_expert(ids, drop, next, 2 * t + 1);
-      }
+      const int2 f = load_final_pair(ids, drop, next, t < T ? t : T - 1);
+      const bool in = c0 + q < n_chunks && t < T;
+      e0[q] = in ? f.x : -1;
+      e1[q] = in ? f.y : -1;
     }
 #pragma unroll
     for (int q = 0; q < kIndexBatch; ++q) {
@@ -402,12 +453,17 @@ __global__ __launch_bounds__(kGroupTokens) void group_chunks_kernel(
   for (int j = tid; j < kMaxExperts * kGroupWords; j += kGroupTokens) (&s_mask[0][0])[j] = 0u;
   __syncthreads();
   for (int64_t i0 = tid; i0 < n_assign; i0 += (int64_t)kGroupBatch * kGroupTokens) {
-    int fe[kGroupBatch];
+    // loads from clamped (valid) assignments, then a select: no load waits for another
+    int fe[kGroupBatch], ic[kGroupBatch];
 #pragma unroll
     for (int q = 0; q < kGroupBatch; ++q) {
       const int64_t i = i0 + (int64_t)q * kGroupTokens;
-      fe[q] = i < n_assign ? final_expert(ids, drop, next, (int)i) : -1;
+      ic[q] = i < n_assign ? (int)i : (int)n_assign - 1;
     }
+    load_final_experts<kGroupBatch>(ids, drop, next, ic, fe);
+#pragma unroll
+    for (int q = 0; q < kGroupBatch; ++q)
+      if (i0 + (int64_t)q * kGroupTokens >= n_assign) fe[q] = -1;
 #pragma unroll
     for (int q = 0; q < kGroupBatch; ++q) {
       const int i = (int)(i0 + (int64_t)q * kGroupTokens);
@@ -483,9 +539,15 @@ __global__ __launch_bounds__(kGroupTokens) void group_chunks_kernel(
   const int t = t0 + tid;
   if (t < T) {
     const int lt = tid;
-    for (int sl = 0; sl < k; ++sl) {
+    int fes[kMaxTopK], ic[kMaxTopK];
+#pragma unroll
+    for (int sl = 0; sl < kMaxTopK; ++sl) ic[sl] = t * k + (sl < k ? sl : k - 1);
+    load_final_experts<kMaxTopK>(ids, drop, next, ic, fes);
+#pragma unroll
+    for (int sl = 0; sl < kMaxTopK; ++sl) {
+      if (sl >= k) break;
       const int i = t * k + sl;
-      const int fe = final_expert(ids, drop, next, i);
+      const int fe = fes[sl];
       int row = -1;
       if (fe >= 0) {
         const uint32_t below = s_mask[fe][lt >> 5] & ((1u << (lt & 31)) - 1u);
@@ -579,13 +641,14 @@ hipError_t launch_capacity_select(const moe_shape_t& s, const int32_t* ids, cons
 hipError_t launch_permute_index(const moe_shape_t& s, const int32_t* ids, const uint8_t* drop_mask,
                                 const int32_t* next_ids, int32_t* counts, int32_t* offsets,
                                 int32_t* perm_src, int32_t* slot_to_row, hipStream_t st) {
+  if (s.T <= 0) return hipSuccess;     // every entry point returns before this; loads clamp to T - 1
   if (s.top_k == 2 && s.n_experts <= 64 && s.n_shared == 0) {
-    const int chunks = std::max(1, (s.T + kIndexThreads - 1) / kIndexThreads);
+    const int chunks = (s.T + kIndexThreads - 1) / kIndexThreads;
     hipLaunchKernelGGL(permute_index_kernel, dim3(chunks), dim3(kIndexThreads), 0, st, ids, drop_mask,
                        next_ids, s.T, s.n_experts, counts, offsets, perm_src, slot_to_row);
     return hipGetLastError();
   }
-  const int chunks = std::max(1, (s.T + kGroupTokens - 1) / kGroupTokens);
+  const int chunks = (s.T + kGroupTokens - 1) / kGroupTokens;
   hipLaunchKernelGGL(group_chunks_kernel, dim3(chunks), dim3(kGroupTokens), 0, st, ids, drop_mask,
                      next_ids, s.T, s.top_k, s.n_experts, s.n_shared, counts, offsets, perm_src,
                      slot_to_row);
