@@ -26,9 +26,9 @@
 //   same in every workgroup while others write.
 // permute_index (top-2, up to 64 experts, no shared expert): one workgroup
 //   of 1024 lanes per chunk of 1024 tokens.  Each counts every kept
-//   assignment per expert (wavefront ballots, the eight chunks of a batch
-//   loaded before any is counted) and, apart, those of the tokens before its
-//   chunk; a scan over the experts gives the offsets and the chunk's start
+//   assignment per expert with LDS atomics (the eight chunks of a batch
+//   loaded before any is counted), those of the tokens before its chunk
+//   apart from the rest; a scan over the experts gives the offsets and the chunk's start
 //   inside each expert.  Per expert a ballot + popcount ranks a token among
 //   the earlier tokens of its wavefront, and a scan over the 16 wavefronts
 //   places the wavefronts, so rows inside an expert follow ascending token
@@ -36,7 +36,8 @@
 // group_chunks (any top-k, up to 256 experts, shared expert; the many-expert
 //   form of the DeepSeek-V3 remark on the "Mixtral 8x7B" interview page): one
 //   workgroup per chunk of 1024 tokens.  Each histograms every assignment
-//   with LDS atomics (totals, and the part before its chunk) and sets bit
+//   with LDS atomics (the part before its chunk apart from the rest; their
+//   sum is the total) and sets bit
 //   (token - chunk start) in a 1024-bit mask of the final expert for each of
 //   its own tokens' assignments; prefix popcounts of the mask words give a
 //   token its rank among the chunk's earlier tokens of that expert --
@@ -317,19 +318,22 @@ __global__ __launch_bounds__(kIndexThreads) void permute_index_kernel(
     const int32_t* __restrict__ next, int T, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
     int32_t* __restrict__ slot_to_row) {
-  __shared__ int s_total[64];
-  __shared__ int s_before[64];
+  __shared__ int s_rest[64];     // assignments of the own and later chunks, per expert
+  __shared__ int s_before[64];   // assignments of earlier chunks, per expert
   __shared__ int s_base[64];
   __shared__ int s_wave[kIndexWaves][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int chunk = blockIdx.x, n_chunks = gridDim.x;
 
   if (tid < 64) {
-    s_total[tid] = 0;
+    s_rest[tid] = 0;
     s_before[tid] = 0;
   }
   __syncthreads();
-  // count: chunks in batches, all of a batch's loads issued before its ballots
+  // count: chunks in batches, all of a batch's loads issued before any is
+  // counted; one LDS atomic per kept assignment, into the histogram of the
+  // earlier chunks or into that of the rest (their sum is the total)
   int m0 = -1, m1 = -1;                       // this lane's token of the own chunk
   for (int c0 = 0; c0 < n_chunks; c0 += kIndexBatch) {
     // loads from clamped (valid) tokens, then a select: no load waits for another
@@ -348,19 +352,17 @@ __global__ __launch_bounds__(kIndexThreads) void permute_index_kernel(
         m0 = e0[q];
         m1 = e1[q];
       }
-      for (int e = 0; e < E; ++e) {
-        const int n = __popcll(__ballot(e0[q] == e)) + __popcll(__ballot(e1[q] == e));
-        if (lane == 0 && n > 0) {
-          atomicAdd(&s_total[e], n);
-          if (c0 + q < chunk) atomicAdd(&s_before[e], n);
-        }
-      }
+      // chunks past the last and wavefronts past the last token count nothing
+      if ((c0 + q) * kIndexThreads + wave * kWave >= T) continue;
+      int* const h = c0 + q < chunk ? s_before : s_rest;
+      if (e0[q] >= 0) atomicAdd(&h[e0[q]], 1);
+      if (e1[q] >= 0) atomicAdd(&h[e1[q]], 1);
     }
   }
   __syncthreads();
   if (wave == 0) {
     // exclusive scan of the totals over the experts, lane e = expert e
-    const int v = lane < E ? s_total[lane] : 0;
+    const int v = lane < E ? s_before[lane] + s_rest[lane] : 0;
     int incl = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -420,8 +422,9 @@ constexpr int kGroupBatch = 8;                      // assignments loaded before
 
 // Grouping for any top-k, many experts and the shared expert: one workgroup
 // per chunk of 1024 tokens.  Every workgroup histograms all assignments with
-// LDS atomics: the totals fix the experts' offsets, the part from tokens
-// before its chunk where its rows start inside each expert.  For its own
+// LDS atomics, those of tokens before its chunk apart from the rest: the
+// totals (their sum) fix the experts' offsets, the earlier part where its rows
+// start inside each expert.  For its own
 // tokens it sets bit (token - chunk start) of the final expert's 1024-bit mask
 // (a token has at most one assignment per expert), so a row's rank inside
 // the chunk is the number of bits below its own: ascending token order, the
@@ -433,8 +436,8 @@ __global__ __launch_bounds__(kGroupTokens) void group_chunks_kernel(
     const int32_t* __restrict__ next, int T, int k, int E, int S, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
     int32_t* __restrict__ slot_to_row) {
-  __shared__ int s_total[kMaxExpertGroups];
-  __shared__ int s_before[kMaxExpertGroups];
+  __shared__ int s_rest[kMaxExpertGroups];     // own and later chunks
+  __shared__ int s_before[kMaxExpertGroups];   // earlier chunks
   __shared__ int s_base[kMaxExpertGroups];
   __shared__ uint32_t s_mask[kMaxExperts][kGroupWords];
   __shared__ uint16_t s_pre[kMaxExperts][kGroupWords];   // bits of the expert's earlier words
@@ -447,7 +450,7 @@ __global__ __launch_bounds__(kGroupTokens) void group_chunks_kernel(
   const int a1 = (int)(a1_full < n_assign ? a1_full : n_assign);
 
   for (int j = tid; j < kMaxExpertGroups; j += kGroupTokens) {
-    s_total[j] = 0;
+    s_rest[j] = 0;
     s_before[j] = 0;
   }
   for (int j = tid; j < kMaxExperts * kGroupWords; j += kGroupTokens) (&s_mask[0][0])[j] = 0u;
@@ -468,18 +471,20 @@ __global__ __launch_bounds__(kGroupTokens) void group_chunks_kernel(
     for (int q = 0; q < kGroupBatch; ++q) {
       const int i = (int)(i0 + (int64_t)q * kGroupTokens);
       if (fe[q] < 0) continue;
-      atomicAdd(&s_total[fe[q]], 1);
       if (i < a0) {
         atomicAdd(&s_before[fe[q]], 1);
-      } else if (i < a1) {
-        const int lt = i / k - t0;
-        atomicOr(&s_mask[fe[q]][lt >> 5], 1u << (lt & 31));
+      } else {
+        atomicAdd(&s_rest[fe[q]], 1);
+        if (i < a1) {
+          const int lt = i / k - t0;
+          atomicOr(&s_mask[fe[q]][lt >> 5], 1u << (lt & 31));
+        }
       }
     }
   }
   __syncthreads();
   if (S > 0 && tid == 0) {
-    s_total[E] = T;
+    s_rest[E] = T - t0;
     s_before[E] = t0;
   }
   // per expert, the bits of its earlier mask words: 4 lanes per expert, 8 words each
@@ -511,7 +516,7 @@ __global__ __launch_bounds__(kGroupTokens) void group_chunks_kernel(
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int g = lane * PER + j;
-      v[j] = g < G ? s_total[g] : 0;
+      v[j] = g < G ? s_before[g] + s_rest[g] : 0;
       sum += v[j];
     }
     int incl = sum;
