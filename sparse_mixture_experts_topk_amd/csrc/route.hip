@@ -231,25 +231,28 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
   for (int b = b0; b < b1; b += U) {
     // Unconditional 16-byte loads from clamped (always valid) addresses, then a
     // select: a conditional load would be split into guarded dword loads.
+    // Every load of the group is issued before the first is used (left to
+    // itself the scheduler waited for each pair before the next, one memory
+    // round trip per matrix instruction).
     uint4 xa[U], wa[U][EB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const int blk = b + u < b1 ? b + u : b0;
+      xa[u] = *reinterpret_cast<const uint4*>(px + blk * 32);
+#pragma unroll
+      for (int eb = 0; eb < EB; ++eb) wa[u][eb] = *reinterpret_cast<const uint4*>(pw[eb] + blk * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       const bool in = b + u < b1;
-      const int blk = in ? b + u : b0;
-      const uint4 xv = *reinterpret_cast<const uint4*>(px + blk * 32);
-      xa[u] = (in && tok_ok) ? xv : z;
+      const uint4 xv = (in && tok_ok) ? xa[u] : z;
 #pragma unroll
       for (int eb = 0; eb < EB; ++eb) {
-        const uint4 wv = *reinterpret_cast<const uint4*>(pw[eb] + blk * 32);
-        wa[u][eb] = (in && w_ok[eb]) ? wv : z;
+        const uint4 wv = (in && w_ok[eb]) ? wa[u][eb] : z;
+        acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv), as_bf16x8(xv), acc[eb], 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int eb = 0; eb < EB; ++eb)
-        acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][eb]), as_bf16x8(xa[u]),
-                                                           acc[eb], 0, 0, 0);
   }
   if (wave > 0) {
 #pragma unroll
@@ -383,33 +386,37 @@ __global__ __launch_bounds__(kLogitWaves * 64) void route_logits_kernel(
 
   const int nblk = d / 32;
   const int b0 = wave * nblk / kLogitWaves, b1 = (wave + 1) * nblk / kLogitWaves;
-  constexpr int U = 16 / (TM + EN) > 0 ? 16 / (TM + EN) : 1;   // 16-byte loads in flight per lane
+  // 16-byte loads in flight per lane: 32 for small tiles, 16 for the 4 x 4 tile
+  // (whose accumulators leave room for no more at three wavefronts per SIMD)
+  constexpr int NLD = TM + EN >= 8 ? 16 : 32;
+  constexpr int U = NLD / (TM + EN) > 0 ? NLD / (TM + EN) : 1;
   const uint4 z = make_uint4(0, 0, 0, 0);
   for (int b = b0; b < b1; b += U) {
+    // every load of the group is issued before the first is used (clamped,
+    // always valid addresses; out-of-range operands are zeroed afterwards)
     uint4 xa[U][TM], wa[U][EN];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const int blk = b + u < b1 ? b + u : b0;
+#pragma unroll
+      for (int m = 0; m < TM; ++m) xa[u][m] = *reinterpret_cast<const uint4*>(px[m] + blk * 32);
+#pragma unroll
+      for (int n = 0; n < EN; ++n) wa[u][n] = *reinterpret_cast<const uint4*>(pw[n] + blk * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       const bool in = b + u < b1;
-      const int blk = in ? b + u : b0;
 #pragma unroll
       for (int m = 0; m < TM; ++m) {
-        const uint4 v = *reinterpret_cast<const uint4*>(px[m] + blk * 32);
-        xa[u][m] = (in && x_ok[m]) ? v : z;
-      }
+        const uint4 xv = (in && x_ok[m]) ? xa[u][m] : z;
 #pragma unroll
-      for (int n = 0; n < EN; ++n) {
-        const uint4 v = *reinterpret_cast<const uint4*>(pw[n] + blk * 32);
-        wa[u][n] = (in && w_ok[n]) ? v : z;
+        for (int n = 0; n < EN; ++n) {
+          const uint4 wv = (in && w_ok[n]) ? wa[u][n] : z;
+          acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv), as_bf16x8(xv), acc[m][n], 0, 0, 0);
+        }
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int m = 0; m < TM; ++m)
-#pragma unroll
-        for (int n = 0; n < EN; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wa[u][n]), as_bf16x8(xa[u][m]),
-                                                               acc[m][n], 0, 0, 0);
   }
   if (wave > 0) {
 #pragma unroll
