@@ -134,8 +134,8 @@ moe_status_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 // Workspace layout of moe_forward (each region 256-byte aligned).
 struct ForwardLayout {
-  size_t route_logits, ids, weights, next_ids, counts, offsets, perm_src, slot_to_row, drop, x_perm, x_scale, h,
-      h_scale, y_perm, down_ws, total;
+  size_t route_logits, route_part, ids, weights, next_ids, counts, offsets, perm_src, slot_to_row, drop, x_perm,
+      x_scale, h, h_scale, y_perm, down_ws, total;
 };
 
 // The overflow fallback round runs (and needs the 3rd/4th-ranked experts).
@@ -158,6 +158,7 @@ ForwardLayout forward_layout(const moe_shape_t& s) {
   const bool fp8 = s.w_dtype == MOE_FP8_E4M3;
   size_t o = 0;
   L.route_logits = o; o += align_up(moe::route_workspace_bytes(s));
+  L.route_part = o;  o += moe::route_index_fused(s) ? align_up(moe::route_index_part_bytes()) : 0;
   L.ids = o;         o += align_up(A * 4);
   L.weights = o;     o += align_up(A * 4);
   L.next_ids = o;    o += fallback_on(s) ? align_up((size_t)s.T * 2 * 4) : 0;
@@ -217,9 +218,10 @@ moe_status_t forward_impl(const moe_shape_t* s, const void* x, const void* w_gat
 
   hipError_t e = hipSuccess;
   if (moe::route_index_fused(*s) && (s->w_dtype == MOE_BF16 || s->w_dtype == MOE_MXFP4)) {
-    // decode: router + grouping in one workgroup; gate/up reads x through perm_src
+    // decode: router partial sums over eight workgroups, then selection + grouping in
+    // one; gate/up reads x through perm_src
     e = moe::launch_route_index(*s, x, w_gate, router_bias, ids, gw, logits_out, counts, offsets, perm_src,
-                                slot_to_row, st);
+                                slot_to_row, at<void>(workspace, L.route_part), st);
     if (e == hipSuccess && drop_mask_out != nullptr)
       e = launch_fill_u8(drop_mask_out, (int64_t)s->T * s->top_k, 0, st);
     if (e == hipSuccess && s->w_dtype == MOE_BF16)

@@ -22,14 +22,16 @@ hipError_t launch_route_topk(const moe_shape_t& s, const void* x, const void* w_
 size_t route_workspace_bytes(const moe_shape_t& s);
 
 // Decode steps of moe_forward (bf16, T <= 16, E <= 16, top-2, dropless, no
-// shared expert): router and grouping in one workgroup (route_index_fused),
-// and the gate/up weight streamer reading token rows of x through perm_src
-// instead of a permuted copy.
+// shared expert): the router's partial sums over eight workgroups, then one
+// workgroup that adds them, selects and groups (route_index_fused; `part` is
+// route_index_part_bytes() of workspace), and the gate/up weight streamer
+// reading token rows of x through perm_src instead of a permuted copy.
 bool route_index_fused(const moe_shape_t& s);
+size_t route_index_part_bytes();
 hipError_t launch_route_index(const moe_shape_t& s, const void* x, const void* w_gate,
                               const float* bias, int32_t* ids, float* weights, float* logits,
                               int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                              int32_t* slot_to_row, hipStream_t st);
+                              int32_t* slot_to_row, void* part, hipStream_t st);
 hipError_t launch_gate_up_bf16_gather(const moe_shape_t& s, const uint16_t* x, const int32_t* perm_src,
                                       const int32_t* offsets, const uint16_t* w1, const uint16_t* w3,
                                       uint16_t* h, hipStream_t st);

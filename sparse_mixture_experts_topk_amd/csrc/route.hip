@@ -191,40 +191,34 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 // products are exact in fp32 and accumulate in fp32.
 constexpr int kRouteWaves = 8;
 
-//
-// INDEX (one workgroup: T <= 16, E <= 16, top-2, nothing dropped, no shared
-// expert): the workgroup that selected the experts also groups the tokens by
-// expert, writing what the permute index kernel would (counts, offsets, the
-// rows of each expert in ascending token order, perm_src and slot_to_row), so
-// a decode step needs no separate grouping launch.
-template <int EB, bool INDEX = false>
-__global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias,
-    int T, int d, int E, int k, int32_t* __restrict__ ids, float* __restrict__ wout,
-    float* __restrict__ logits, int32_t* __restrict__ next, int32_t* __restrict__ counts = nullptr,
-    int32_t* __restrict__ offsets = nullptr, int32_t* __restrict__ perm_src = nullptr,
-    int32_t* __restrict__ slot_to_row = nullptr) {
-  static_assert(!INDEX || EB == 1, "the grouping epilogue takes up to 16 experts");
-  static_assert(EB * 4 <= 64, "one bit per expert of a lane in the taken mask");
-  __shared__ f32x4_t part[kRouteWaves - 1][EB][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tok0 = blockIdx.x * 16;
-  const int r = lane & 15, g = lane >> 4;
-  const bool tok_ok = tok0 + r < T;
-  const uint16_t* px = x + (int64_t)(tok_ok ? tok0 + r : 0) * d + g * 8;
+// Pointers of lane (r, g) into the 16-token tile at tok0 and the EB blocks of
+// 16 router rows (rows past T or E read row 0 and are zeroed after the load).
+template <int EB>
+struct RouteLanes {
+  const uint16_t* px;
   const uint16_t* pw[EB];
+  bool tok_ok;
   bool w_ok[EB];
+  __device__ __forceinline__ RouteLanes(const uint16_t* x, const uint16_t* wg, int T, int d, int E,
+                                        int tok0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    tok_ok = tok0 + r < T;
+    px = x + (int64_t)(tok_ok ? tok0 + r : 0) * d + g * 8;
 #pragma unroll
-  for (int eb = 0; eb < EB; ++eb) {
-    w_ok[eb] = eb * 16 + r < E;
-    pw[eb] = wg + (int64_t)(w_ok[eb] ? eb * 16 + r : 0) * d + g * 8;
+    for (int eb = 0; eb < EB; ++eb) {
+      w_ok[eb] = eb * 16 + r < E;
+      pw[eb] = wg + (int64_t)(w_ok[eb] ? eb * 16 + r : 0) * d + g * 8;
+    }
   }
-  f32x4_t acc[EB];
+};
+
+// One wavefront's share of the router product: K blocks [b0, b1) of 32
+// elements, accumulated in block order into acc (every block's loads of a
+// group are issued before the first is used).
+template <int EB>
+__device__ __forceinline__ void route_kloop(const RouteLanes<EB>& L, int b0, int b1, f32x4_t* acc) {
 #pragma unroll
   for (int eb = 0; eb < EB; ++eb) acc[eb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nblk = d / 32;
-  const int b0 = wave * nblk / kRouteWaves, b1 = (wave + 1) * nblk / kRouteWaves;
   // all of a wavefront's K blocks in flight at once at d = 4096 (16 per wavefront)
   constexpr int U = 16 / EB;
   const uint4 z = make_uint4(0, 0, 0, 0);
@@ -238,33 +232,38 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int blk = b + u < b1 ? b + u : b0;
-      xa[u] = *reinterpret_cast<const uint4*>(px + blk * 32);
+      xa[u] = *reinterpret_cast<const uint4*>(L.px + blk * 32);
 #pragma unroll
-      for (int eb = 0; eb < EB; ++eb) wa[u][eb] = *reinterpret_cast<const uint4*>(pw[eb] + blk * 32);
+      for (int eb = 0; eb < EB; ++eb) wa[u][eb] = *reinterpret_cast<const uint4*>(L.pw[eb] + blk * 32);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool in = b + u < b1;
-      const uint4 xv = (in && tok_ok) ? xa[u] : z;
+      const uint4 xv = (in && L.tok_ok) ? xa[u] : z;
 #pragma unroll
       for (int eb = 0; eb < EB; ++eb) {
-        const uint4 wv = (in && w_ok[eb]) ? wa[u][eb] : z;
+        const uint4 wv = (in && L.w_ok[eb]) ? wa[u][eb] : z;
         acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv), as_bf16x8(xv), acc[eb], 0, 0, 0);
       }
     }
   }
-  if (wave > 0) {
-#pragma unroll
-    for (int eb = 0; eb < EB; ++eb) part[wave - 1][eb][lane] = acc[eb];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int w = 0; w < kRouteWaves - 1; ++w)
-#pragma unroll
-    for (int eb = 0; eb < EB; ++eb) acc[eb] += part[w][eb][lane];
+}
 
+// Everything after the K sum, in wavefront 0: acc holds, per lane (r, g),
+// token tok0 + r and experts 16 eb + 4 g + q.  Bias, optional logits, the
+// selection rounds and the token's outputs; with INDEX (one tile: T <= 16,
+// E <= 16, top-2, nothing dropped, no shared expert) also the grouping that
+// the permute index kernel would write (counts, offsets, the rows of each
+// expert in ascending token order, perm_src and slot_to_row).
+template <int EB, bool INDEX>
+__device__ __forceinline__ void route_finish(f32x4_t* acc, int lane, int tok0, const float* __restrict__ bias,
+                                             int T, int E, int k, int32_t* __restrict__ ids,
+                                             float* __restrict__ wout, float* __restrict__ logits,
+                                             int32_t* __restrict__ next, int32_t* __restrict__ counts,
+                                             int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+                                             int32_t* __restrict__ slot_to_row) {
+  const int r = lane & 15, g = lane >> 4;
   const int tok = tok0 + r;
 #pragma unroll
   for (int eb = 0; eb < EB; ++eb) {
@@ -343,6 +342,67 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
       reinterpret_cast<int2*>(slot_to_row)[tok] = make_int2(row0, row1);
     }
   }
+}
+
+template <int EB>
+__global__ __launch_bounds__(kRouteWaves * 64) void route_topk_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias,
+    int T, int d, int E, int k, int32_t* __restrict__ ids, float* __restrict__ wout,
+    float* __restrict__ logits, int32_t* __restrict__ next) {
+  static_assert(EB * 4 <= 64, "one bit per expert of a lane in the taken mask");
+  __shared__ f32x4_t part[kRouteWaves - 1][EB][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok0 = blockIdx.x * 16;
+  const RouteLanes<EB> L(x, wg, T, d, E, tok0, lane);
+  const int nblk = d / 32;
+  f32x4_t acc[EB];
+  route_kloop<EB>(L, wave * nblk / kRouteWaves, (wave + 1) * nblk / kRouteWaves, acc);
+  if (wave > 0) {
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) part[wave - 1][eb][lane] = acc[eb];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kRouteWaves - 1; ++w)
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) acc[eb] += part[w][eb][lane];
+  route_finish<EB, false>(acc, lane, tok0, bias, T, E, k, ids, wout, logits, next, nullptr, nullptr,
+                          nullptr, nullptr);
+}
+
+// The decode form (one tile of at most 16 tokens, up to 16 experts) in two
+// launches, so that the router rows and tokens are read by eight CUs instead
+// of one: workgroup w of route_partial_kernel (one wavefront) computes
+// exactly what wavefront w of route_topk_mfma_kernel computes and stores it;
+// route_finish_kernel adds the eight partial tiles in the order that kernel
+// adds them (wavefront 0's, then 1 .. 7), so the logits are the same bit for
+// bit, and finishes with the selection and the grouping.
+__global__ __launch_bounds__(64) void route_partial_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wg, int T, int d,
+                                                           int E, f32x4_t* __restrict__ part) {
+  const int lane = threadIdx.x, w = blockIdx.x;
+  const RouteLanes<1> L(x, wg, T, d, E, 0, lane);
+  const int nblk = d / 32;
+  f32x4_t acc[1];
+  route_kloop<1>(L, w * nblk / kRouteWaves, (w + 1) * nblk / kRouteWaves, acc);
+  part[w * 64 + lane] = acc[0];
+}
+
+__global__ __launch_bounds__(64) void route_finish_kernel(
+    const f32x4_t* __restrict__ part, const float* __restrict__ bias, int T, int E, int k,
+    int32_t* __restrict__ ids, float* __restrict__ wout, float* __restrict__ logits,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+    int32_t* __restrict__ slot_to_row) {
+  const int lane = threadIdx.x;
+  f32x4_t p[kRouteWaves];
+#pragma unroll
+  for (int w = 0; w < kRouteWaves; ++w) p[w] = part[w * 64 + lane];
+  f32x4_t acc[1] = {p[0]};
+#pragma unroll
+  for (int w = 1; w < kRouteWaves; ++w) acc[0] += p[w];
+  route_finish<1, true>(acc, lane, 0, bias, T, E, k, ids, wout, logits, nullptr, counts, offsets, perm_src,
+                        slot_to_row);
 }
 
 // ---------------------------------------------------------------------------
@@ -555,13 +615,18 @@ bool route_index_fused(const moe_shape_t& s) {
 hipError_t launch_route_index(const moe_shape_t& s, const void* x, const void* w_gate,
                               const float* bias, int32_t* ids, float* weights, float* logits,
                               int32_t* counts, int32_t* offsets, int32_t* perm_src,
-                              int32_t* slot_to_row, hipStream_t st) {
-  hipLaunchKernelGGL((route_topk_mfma_kernel<1, true>), dim3(1), dim3(kRouteWaves * 64), 0, st,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate), bias, s.T,
-                     s.d_model, s.n_experts, s.top_k, ids, weights, logits, nullptr, counts, offsets,
-                     perm_src, slot_to_row);
+                              int32_t* slot_to_row, void* part, hipStream_t st) {
+  hipLaunchKernelGGL(route_partial_kernel, dim3(kRouteWaves), dim3(64), 0, st,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_gate), s.T, s.d_model,
+                     s.n_experts, static_cast<f32x4_t*>(part));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_finish_kernel, dim3(1), dim3(64), 0, st, static_cast<const f32x4_t*>(part), bias,
+                     s.T, s.n_experts, s.top_k, ids, weights, logits, counts, offsets, perm_src, slot_to_row);
   return hipGetLastError();
 }
+
+size_t route_index_part_bytes() { return (size_t)kRouteWaves * 64 * sizeof(f32x4_t); }
 
 size_t route_workspace_bytes(const moe_shape_t& s) {
   return route_two_pass(s) ? (size_t)s.T * s.n_experts * 4 : 0;
