@@ -276,9 +276,10 @@ moe_status_t moe_combine(const moe_shape_t* shape, const float* y_perm, const in
  * gate/up reads the token rows of x through perm_src instead of a permuted
  * copy when at most 64 rows reach any expert, and (bf16 experts) when the
  * routed experts average at most 320 rows; for decode batches (T <= 16,
- * E <= 16, top-2, dropless, no shared expert) the router also groups the
- * tokens, and with bf16 experts the down projection and the combine are one
- * kernel (no y_perm).
+ * E <= 16, top-2, dropless, no shared expert) the router's product runs on
+ * eight workgroups and a ninth selects and also groups the tokens, and with
+ * bf16 experts the down projection and the combine are one kernel (no
+ * y_perm).
  * Workspace: moe_workspace_bytes(MOE_CALL_FORWARD) holds every intermediate. */
 moe_status_t moe_forward(const moe_shape_t* shape, const void* x, const void* w_gate,
                          const float* router_bias, const void* w1, const void* w3, const void* w2,
