@@ -75,17 +75,13 @@ __device__ __forceinline__ int fallback_expert(const uint8_t* drop, const int32_
 // Token of slot index i: t * k + s for routed slots, T * k + t for the shared expert's.
 __device__ __forceinline__ int slot_token(int i, int k, int Tk) { return i < Tk ? i / k : i - Tk; }
 
-// Expert that finally processes assignment i (-1: dropped).
-__device__ __forceinline__ int final_expert(const int32_t* ids, const uint8_t* drop,
-                                            const int32_t* next, int i) {
-  if (drop == nullptr) return ids[i];
-  const uint8_t m = drop[i];
-  return m == 0 ? ids[i] : m == 2 ? fallback_expert(drop, next, i) : -1;
-}
-
+// The expert that finally processes an assignment: its router expert when
+// kept (mark 0, or no drop marks at all), its fallback expert when the
+// fallback round took it (mark 2), none (-1) when dropped (mark 1).
+//
 // Final experts of top-2 token t from values already loaded: its two ids,
 // its two drop marks (byte s = slot s; 0 when nothing is dropped) and its two
-// fallback ids -- the same rule as final_expert and fallback_expert.
+// fallback ids (the rule of fallback_expert).
 __device__ __forceinline__ int2 final_pair(int2 id, uint32_t marks, int2 nx) {
   const uint32_t m0 = marks & 255u, m1 = (marks >> 8) & 255u;
   const int e0 = m0 == 0 ? id.x : m0 == 2 ? nx.x : -1;
