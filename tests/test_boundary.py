@@ -133,6 +133,19 @@ def test_route_workspace_for_many_experts():
                    16 * 256 * 4, None) == 3
 
 
+def test_forward_workspace_holds_the_decode_router_partials():
+    # decode batches (T <= 16, E <= 16, top-2, dropless, no shared expert): moe_forward's router
+    # writes eight partial 16 x 16 fp32 tiles (8 x 64 lanes x 16 B) before selecting; the same
+    # shape with a capacity takes the staged router and needs none of it
+    part = 8 * 64 * 16
+    for w in ("bf16", "mxfp4"):
+        fused = moe.moe_workspace_bytes(S(T=16, w_dtype=w))
+        staged = moe.moe_workspace_bytes(S(T=16, w_dtype=w, capacity=16))
+        assert fused - staged == part
+    assert moe.moe_workspace_bytes(S(T=16, n_experts=17)) == moe.moe_workspace_bytes(
+        S(T=16, n_experts=17, capacity=16))
+
+
 def test_down_workspace_size_and_requirement():
     # many rows per expert (bf16): fp32 partial tiles for the split tail work
     big = S(T=8192)
